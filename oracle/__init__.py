@@ -1,0 +1,10 @@
+"""CPU oracle for H2O budgeted attention: test infrastructure only.
+
+Importable by the tests, ``__graft_entry__.smoke()`` and the benchmark's
+CPU-baseline leg; never by the product path.  See ``h2o_oracle`` for the
+definitions and the readings it takes.
+"""
+from .h2o_oracle import (  # noqa: F401
+    TIE_RTOL, ParityMismatch, PrefillScores, UnitCache, default_scale, prefill_keep,
+    prefill_scores, run_unit, softmax,
+)

@@ -1,0 +1,177 @@
+"""Plant plausible mistakes in a copy of the oracle (CPU only) and check that the
+independent pins catch every one of them.
+
+Each mutation is a source edit of ``oracle/h2o_oracle.py`` loaded as a fresh
+module; the real oracle is untouched.  A mutation counts as caught when any pin
+fails (an assertion or an exception).
+"""
+import math
+import os
+import sys
+import types
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import scipy.special
+
+from test_oracle_pins import KEYS2, _brute_force_run, _brute_keep, _library_causal_weights, _sdpa_rows
+
+SRC = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "oracle", "h2o_oracle.py")
+
+MUTATIONS = {
+    "ties evict the highest position": (
+        "u = min(cand, key=lambda t: (G_score[t], G_pos[t]))",
+        "u = min(cand, key=lambda t: (G_score[t], -G_pos[t]))"),
+    "argmax instead of argmin": (
+        "u = min(cand, key=lambda t: (G_score[t], G_pos[t]))",
+        "u = max(cand, key=lambda t: (G_score[t], G_pos[t]))"),
+    "candidate bound off by one": (
+        "cand = np.nonzero(G_pos <= i - self.recent)[0]",
+        "cand = np.nonzero(G_pos < i - self.recent)[0]"),
+    "recent window not protected": (
+        "cand = np.nonzero(G_pos <= i - self.recent)[0]",
+        "cand = np.nonzero(G_pos <= i)[0]"),
+    "new token's own weight dropped": (
+        "G_score = np.concatenate([self.score, [0.0]]) + a",
+        "G_score = np.concatenate([self.score + a[:-1], [0.0]])"),
+    "decode weights not accumulated": (
+        "G_score = np.concatenate([self.score, [0.0]]) + a",
+        "G_score = np.concatenate([self.score, [a[-1]]])"),
+    "prefill ties keep the lower position": (
+        "best_first = sorted(pool, key=lambda j: (c[j], j), reverse=True)",
+        "best_first = sorted(pool, key=lambda j: (c[j], -j), reverse=True)"),
+    "prefill keeps the worst": (
+        "best_first = sorted(pool, key=lambda j: (c[j], j), reverse=True)",
+        "best_first = sorted(pool, key=lambda j: (c[j], j))"),
+    "scale 1/d": ("return 1.0 / np.sqrt(float(d))", "return 1.0 / float(d)"),
+    "row sums instead of column sums": ("col_sum=A.sum(axis=0)", "col_sum=A.sum(axis=1)"),
+    "transposed operands": ("x = scale * (K[: r + 1] @ Q[r])", "x = scale * (Q[: r + 1] @ K[r])"),
+    "diagonal excluded": ("x = scale * (K[: r + 1] @ Q[r])",
+                          "x = scale * (K[: r + 1] @ Q[r]) - np.where(np.arange(r + 1) == r, 1e300, 0.0) * (r > 0)"),
+    # (the selection threshold L > k vs L >= k is not a mutation: with the pool
+    # [0, L - recent), a prompt of exactly k tokens keeps everything either way)
+    "prefill recent window shifted": ("recent_pos = list(range(L - recent, L))",
+                                      "recent_pos = list(range(L - recent - 1, L - 1))"),
+    "cache allowed to overfill": ("if len(self.pos) < self.k:", "if len(self.pos) <= self.k:"),
+    "prefill scores not seeded": ("cache.score = ps.col_sum[kept].copy()",
+                                  "cache.score = np.zeros(len(kept))"),
+    "recent pool overlaps": ("pool = list(range(L - recent))", "pool = list(range(L))"),
+    "evicted entries stay in the normaliser": (
+        "a = softmax(x)\n        o = a @ G_V",
+        "a = softmax(x)\n        a = a * (len(x) / (len(x) + self.evicted_mass))\n        o = a @ G_V"),
+}
+
+
+_COUNTER = [0]
+
+
+def _load(src_text):
+    _COUNTER[0] += 1
+    name = f"mutant_oracle_{_COUNTER[0]}"
+    mod = types.ModuleType(name)
+    sys.modules[name] = mod  # dataclasses look their module up here
+    exec(compile(src_text, name, "exec"), mod.__dict__)
+    return mod
+
+
+def _checks(m):
+    """Yields pins; each raises on disagreement."""
+    g = np.random.default_rng(1)
+
+    def full_attention():
+        N, L, d = 20, 6, 8
+        Q, K, V = (g.standard_normal((N, d)) for _ in range(3))
+        res = m.run_unit(Q, K, V, L, N, N)
+        full = _sdpa_rows(Q, K, V, np.tril(np.ones((N, N), dtype=bool)))
+        np.testing.assert_allclose(res["out"], full[L:], rtol=1e-10, atol=1e-10)
+        W = _library_causal_weights(Q, K)
+        pos, score, _, _ = res["cache"].snapshot()
+        assert pos.tolist() == list(range(N))
+        np.testing.assert_allclose(score, W.sum(axis=0), rtol=1e-10)
+
+    def prefill_library():
+        L, d = 40, 16
+        Q, K = g.standard_normal((L, d)), g.standard_normal((L, d))
+        ps = m.prefill_scores(Q, K, m.default_scale(d))
+        np.testing.assert_allclose(ps.col_sum, _library_causal_weights(Q, K).sum(axis=0), rtol=1e-10)
+
+    def sliding_window():
+        N, L, R, d = 30, 9, 4, 6
+        Q, K, V = (g.standard_normal((N, d)) for _ in range(3))
+        res = m.run_unit(Q, K, V, L, 0, R)
+        band = np.zeros((N, N), dtype=bool)
+        for i in range(N):
+            band[i, max(0, i - R): i + 1] = True
+        win = _sdpa_rows(Q, K, V, band)
+        np.testing.assert_allclose(res["out"], win[L:], rtol=1e-10, atol=1e-10)
+        assert res["evicted"].tolist() == [i - R for i in range(L, N)]
+
+    def identical_keys():
+        L, T, h, r, d = 40, 30, 6, 5, 5
+        Q = g.standard_normal((L + T, d))
+        K = np.tile(g.standard_normal(d), (L + T, 1))
+        V = g.standard_normal((L + T, d))
+        res = m.run_unit(Q, K, V, L, h, r)
+        assert res["kept"] == list(range(h)) + list(range(L - r, L))
+        assert res["evicted"].tolist() == [L + t - r for t in range(T)]
+        H = [Fraction(0)]
+        for n in range(1, L + 1):
+            H.append(H[-1] + Fraction(1, n))
+        np.testing.assert_allclose(res["prefill"].col_sum, [float(H[L] - H[j]) for j in range(L)], rtol=1e-12)
+
+    def brute_force():
+        kinds_list = [
+            ["strong", "dead", "dead", "strong", "mid", "weak", "strong", "dead", "mid", "mid", "weak", "strong"],
+            ["mid", "mid", "weak", "weak", "strong", "dead", "mid", "strong", "weak", "mid", "dead", "weak"],
+        ]
+        for kinds in kinds_list:
+            for (L, h, r) in [(3, 3, 0), (5, 2, 2), (0, 2, 1), (7, 1, 3), (8, 2, 2)]:
+                N = len(kinds)
+                K = np.array([KEYS2[x] for x in kinds])
+                Q = np.tile([1.0, 0.0], (N, 1))
+                V = np.arange(N * 2, dtype=float).reshape(N, 2)
+                res = m.run_unit(Q, K, V, L, h, r)
+                log, S = _brute_force_run(Q, K, V, L, h, r)
+                assert res["evicted"].tolist() == log
+                assert sorted(res["cache"].pos.tolist()) == S
+
+    def keep_brute():
+        for _ in range(200):
+            n = int(g.integers(0, 12))
+            c = g.choice([0.0, 0.5, 1.0, 2.0], size=n)
+            h, r = int(g.integers(0, 4)), int(g.integers(0, 4))
+            if h + r == 0:
+                continue
+            assert m.prefill_keep(c, h, r)[0] == _brute_keep(c, h, r)
+
+    def mass():
+        N, L, d = 60, 20, 8
+        Q, K, V = (g.standard_normal((N, d)) for _ in range(3))
+        res = m.run_unit(Q, K, V, L, 5, 4)
+        c = res["cache"]
+        assert len(c.pos) == 9
+        assert abs(c.score.sum() - (c.rows - c.evicted_mass)) < 1e-9 * c.rows
+
+    return [full_attention, prefill_library, sliding_window, identical_keys, brute_force, keep_brute, mass]
+
+
+def test_unmutated_oracle_passes_every_check():
+    m = _load(open(SRC).read())
+    for chk in _checks(m):
+        chk()
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def test_mutation_is_caught(name):
+    old, new = MUTATIONS[name]
+    src = open(SRC).read()
+    assert src.count(old) >= 1, f"mutation anchor not found: {old!r}"
+    m = _load(src.replace(old, new, 1))
+    caught = []
+    for chk in _checks(m):
+        try:
+            chk()
+        except Exception as e:  # noqa: BLE001 - any failure is a catch
+            caught.append((chk.__name__, type(e).__name__))
+    assert caught, f"mutation '{name}' passed every pin"
