@@ -1,0 +1,173 @@
+/*
+ * h2o.h -- C ABI of the H2O budgeted-attention library for AMD MI355X (gfx950).
+ *
+ * H2O keeps, per attention head, a fixed budget of k cached tokens: a
+ * heavy-hitter region (the tokens that have received the most attention so
+ * far) plus a window of the most recent tokens.  Each generated token attends
+ * over the cached entries only, every entry adds the attention it just received
+ * to a running score, and once the cache is full one entry is evicted per head
+ * per step and the new token's K/V overwrite its slot in place.
+ *
+ * Sources (page title, then section):
+ *   [Report] "H2O: Heavy-Hitter Oracle for Efficient Generative Inference of
+ *            Large Language Models -- 深度解读报告" (zako-mio llm-papers-knowledge-base)
+ *            §3.1 budgeted generation, §3.3 eviction rule (the paper's
+ *            Definition 4.3 / Algorithm 1), §3.4 system layout, prefill rule and
+ *            decode rule.
+ *   [Card]   "H2O: Heavy-Hitter Oracle for Efficient Generative Inference of
+ *            Large Language Models" (phantomic12 inference-research paper card):
+ *            accumulated-attention score per token, lowest-scoring entries evicted.
+ *
+ * Conventions for every entry point:
+ *   - A *unit* is one (batch element, head); units are independent and laid out
+ *     batch-major: unit = b * heads + h.
+ *   - Positions are 0-based int32.  Step i (the i-th token overall) is the token
+ *     at position i; a prompt of L tokens occupies positions 0..L-1.
+ *   - "device" pointers are HBM addresses on the cache's GPU (e.g. a torch
+ *     tensor's data_ptr()); "host" pointers are CPU memory.  All buffers are
+ *     dense row-major, 16-byte aligned, and owned by the caller; they must stay
+ *     valid until the stream has passed the call.
+ *   - stream: a hipStream_t on the cache's device, or NULL for the null stream.
+ *     Calls are asynchronous unless stated otherwise.
+ *   - Return codes only: nothing throws across the ABI and nothing exits the
+ *     process.  Argument and state checks run before any GPU work; when one
+ *     fails the cache is left unchanged.  A fault inside an already-queued kernel
+ *     is reported as H2O_ERR_HIP by a later call (h2o_cache_read synchronises);
+ *     after it the cache contents are undefined and the cache should be
+ *     destroyed.
+ *   - One cache serves one stream from one host thread at a time; distinct
+ *     caches are independent.  A model with several layers uses one cache per
+ *     layer.
+ */
+#ifndef H2O_H_
+#define H2O_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct h2o_cache h2o_cache; /* opaque; owns all of its device memory */
+
+typedef enum {
+  H2O_F32 = 0,  /* float32 inputs and cached K/V */
+  H2O_BF16 = 1  /* bfloat16 inputs and cached K/V (fp32 arithmetic) */
+} h2o_dtype;
+
+typedef enum {
+  H2O_OK = 0,
+  H2O_ERR_INVALID_ARG = 1, /* bad pointer, size, alignment or parameter */
+  H2O_ERR_STATE = 2,       /* call not valid in the cache's current state */
+  H2O_ERR_OOM = 3,         /* device allocation failed */
+  H2O_ERR_HIP = 4,         /* HIP runtime error (launch failure, async fault) */
+  H2O_ERR_UNSUPPORTED = 5  /* valid request this build does not implement */
+} h2o_status;
+
+typedef struct {
+  int32_t batch;         /* B >= 1 */
+  int32_t heads;         /* H >= 1 */
+  int32_t head_dim;      /* d in {64, 128} */
+  int32_t heavy_budget;  /* K_h >= 0: heavy-hitter entries kept per unit */
+  int32_t recent_budget; /* K_r >= 0: most recent positions always kept */
+  int32_t dtype;         /* h2o_dtype */
+  float scale;           /* logit scale; <= 0 selects 1/sqrt(head_dim) */
+  int32_t max_prompt;    /* >= 0: longest prompt h2o_prefill will accept */
+} h2o_params;
+/* The budget is k = K_h + K_r >= 1 (Report §3.1: k < n cached tokens).
+ * B*H*max(k, max_prompt) must stay below 2^31. */
+
+/* Device bytes that h2o_cache_create would allocate for these parameters.
+ * kv_bytes (nullable): the cached K and V slots alone, 2 * B*H*k*d*sizeof(dtype).
+ * total_bytes (nullable): everything, including per-slot scores, positions and
+ * prefill/decode scratch.  Host-only; makes no GPU call.
+ * Errors: H2O_ERR_INVALID_ARG for invalid parameters. */
+h2o_status h2o_cache_bytes(const h2o_params* params, size_t* kv_bytes, size_t* total_bytes);
+
+/* Create an empty cache on `device` (-1: the calling thread's current device).
+ * Allocates all device memory up front (Report §3.4: the cache is preallocated
+ * and later overwritten in place); no later call allocates.  *out receives the
+ * cache, or NULL on failure.
+ * Errors: H2O_ERR_INVALID_ARG (params, out == NULL), H2O_ERR_UNSUPPORTED
+ * (head_dim not 64/128), H2O_ERR_OOM, H2O_ERR_HIP. */
+h2o_status h2o_cache_create(const h2o_params* params, int device, h2o_cache** out);
+
+/* Release the cache and its device memory.  Synchronises the device.  NULL is
+ * accepted and ignored. */
+h2o_status h2o_cache_destroy(h2o_cache* cache);
+
+/* Prefill (Report §3.4, prefill rule).  (Re)initialises the cache from a prompt
+ * of `prompt_len` tokens.
+ *   q, k, v: device, [B, H, prompt_len, d] in the cache dtype.
+ * For each unit: every prompt row r attends causally (positions 0..r, itself
+ * included) with a = softmax(scale * q_r . k_j); token j's score is the total
+ * attention it receives, c_j = sum_{r >= j} a_rj (Report §2.3, §3.3).  If
+ * prompt_len <= k all tokens are kept; otherwise the last K_r positions are kept
+ * plus the K_h best-scored of positions [0, prompt_len - K_r), ranked by score,
+ * equal scores ranked by position (the higher position wins).  Kept tokens'
+ * K/V rows are copied into slots with their scores; the step counter is set to
+ * prompt_len.  prompt_len == 0 gives an empty cache.  q/k/v may be NULL when
+ * prompt_len == 0.
+ * Errors: H2O_ERR_INVALID_ARG (NULL or misaligned pointers, prompt_len < 0 or
+ * > max_prompt), H2O_ERR_HIP. */
+h2o_status h2o_prefill(h2o_cache* cache, const void* q, const void* k, const void* v,
+                       int32_t prompt_len, void* stream);
+
+/* One decode step for every unit (Report §3.1, §3.3, §3.4 decode rule; Card).
+ *   q, k, v: device, [B, H, d] in the cache dtype: the new token (position i,
+ *            the cache's step counter) of every unit.
+ *   out:     device, [B, H, d] float32: attention output over the cached entries
+ *            plus the new token, normalised over those entries only.
+ *   evicted: device, [B, H] int32, nullable: the position evicted this step, or
+ *            -1 when the cache was not yet full.  With K_r == 0 it may be i
+ *            itself (the new token is then not stored).
+ * Then every cached entry adds its weight to its score (the new token's score
+ * starts at its own weight).  While fewer than k entries are cached the new
+ * token is added to a free slot.  Otherwise the victim is the entry with the
+ * lowest score among the heavy hitters and the token leaving the recent window
+ * (positions <= i - K_r), the lowest position on equal scores; the new token's
+ * K/V, position and score overwrite the victim's slot.  The caller may reuse
+ * q/k/v once the stream has passed the call.
+ * Errors: H2O_ERR_INVALID_ARG (NULL or misaligned pointers), H2O_ERR_STATE (no
+ * prefill yet, or the position counter would overflow int32), H2O_ERR_HIP. */
+h2o_status h2o_decode_step(h2o_cache* cache, const void* q, const void* k, const void* v,
+                           float* out, int32_t* evicted, void* stream);
+
+/* Copy the cache contents to host memory; synchronises `stream` first and
+ * reports any earlier asynchronous fault.  Every pointer is host and nullable.
+ *   pos:     [B, H, k] int32, the position held by each slot, -1 for empty slots
+ *   score:   [B, H, k] float32, the accumulated score of each slot
+ *   k_slots, v_slots: [B, H, k, d] in the cache dtype
+ *   meta:    int32[2] = {entries cached per unit, next position}
+ * Slot order within a unit carries no meaning; compare by position.
+ * Errors: H2O_ERR_INVALID_ARG, H2O_ERR_HIP. */
+h2o_status h2o_cache_read(h2o_cache* cache, int32_t* pos, float* score, void* k_slots,
+                          void* v_slots, int32_t* meta, void* stream);
+
+/* Copy the last prefill's per-token statistics to host memory (synchronises
+ * `stream`).  Each pointer is host, nullable, [B, H, L] float32 with L the last
+ * prompt_len:
+ *   row_max: max_j scale*q_r.k_j over j <= r
+ *   row_sum: sum_j exp(scale*q_r.k_j - row_max_r) over j <= r
+ *   col_sum: c_j, the attention token j received from the prompt rows
+ * Errors: H2O_ERR_INVALID_ARG, H2O_ERR_STATE (no prefill yet), H2O_ERR_HIP. */
+h2o_status h2o_prefill_stats_read(h2o_cache* cache, float* row_max, float* row_sum,
+                                  float* col_sum, void* stream);
+
+/* Host-side state, no GPU call: entries cached per unit, next position, and the
+ * last prompt length (-1 before the first prefill).  Pointers nullable. */
+h2o_status h2o_cache_info(const h2o_cache* cache, int32_t* count, int32_t* next_pos,
+                          int32_t* prompt_len);
+
+/* Static description of a status code. */
+const char* h2o_status_str(h2o_status status);
+
+/* Detail of the last error returned on the calling thread ("" if none). */
+const char* h2o_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* H2O_H_ */

@@ -1,0 +1,391 @@
+// The cache object behind the C ABI declared in include/h2o.h: parameter and
+// state validation, up-front device allocation, host-side step counters, and
+// launch orchestration.  Every check runs before any GPU call, so a rejected
+// call leaves the cache unchanged.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+#include <string>
+
+#include "h2o.h"
+#include "launch.h"
+
+struct h2o_cache {
+  h2o_params p;
+  int device;
+  int32_t d, k, units, esize;
+  float scale, c2;
+  // host-side state
+  int32_t count;       // entries cached per unit
+  int32_t next_pos;    // position of the next token
+  int32_t prompt_len;  // last prompt length, -1 before the first prefill
+  int32_t lpad_cap;    // row capacity of the prefill scratch (multiple of 32)
+  int32_t lpad_last;   // row stride of the last prefill's statistics
+  // device memory
+  void* kslots;
+  void* vslots;
+  float* score;
+  float* comp;
+  int32_t* pos;
+  float* part;
+  float* logits;
+  uint32_t* counters;
+  int32_t max_split;
+  float* row_max;
+  float* row_sum;
+  float* row_lse2;
+  float* col_sum;
+};
+
+namespace {
+
+// Largest budget the kernels take: per-unit LDS holds k+1 logits (decode) and
+// k kept positions (prefill select).
+constexpr int64_t kMaxK = 12288;
+// Units at or above this count run one block per unit in decode; fewer units
+// split each unit's slots across blocks.
+constexpr int32_t kSplitUnits = 512;
+constexpr int32_t kMaxSplit = 64;
+constexpr int32_t kMinSlotsPerSplit = 64;
+constexpr float kLog2e = 1.4426950408889634f;
+
+thread_local std::string g_err;
+
+h2o_status fail(h2o_status s, const std::string& msg) {
+  g_err = msg;
+  return s;
+}
+
+h2o_status hip_fail(hipError_t e, const char* what) {
+  g_err = std::string(what) + ": " + hipGetErrorString(e);
+  return e == hipErrorOutOfMemory ? H2O_ERR_OOM : H2O_ERR_HIP;
+}
+
+class DeviceGuard {
+ public:
+  explicit DeviceGuard(int dev) {
+    if (hipGetDevice(&prev_) == hipSuccess && prev_ != dev) {
+      changed_ = hipSetDevice(dev) == hipSuccess;
+    }
+  }
+  ~DeviceGuard() {
+    if (changed_) (void)hipSetDevice(prev_);
+  }
+
+ private:
+  int prev_ = -1;
+  bool changed_ = false;
+};
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int32_t round32(int32_t n) { return (n + 31) / 32 * 32; }
+
+struct Sizes {
+  size_t kv, meta, split, prefill, total;
+  int32_t max_split, lpad;
+};
+
+h2o_status check_params(const h2o_params* p, Sizes* sz) {
+  if (p == nullptr) return fail(H2O_ERR_INVALID_ARG, "params is NULL");
+  if (p->batch < 1 || p->heads < 1) return fail(H2O_ERR_INVALID_ARG, "batch and heads must be >= 1");
+  if (p->head_dim < 1) return fail(H2O_ERR_INVALID_ARG, "head_dim must be >= 1");
+  if (p->head_dim != 64 && p->head_dim != 128) return fail(H2O_ERR_UNSUPPORTED, "head_dim must be 64 or 128");
+  if (p->heavy_budget < 0 || p->recent_budget < 0) return fail(H2O_ERR_INVALID_ARG, "budgets must be >= 0");
+  const int64_t k = static_cast<int64_t>(p->heavy_budget) + p->recent_budget;
+  if (k < 1) return fail(H2O_ERR_INVALID_ARG, "heavy_budget + recent_budget must be >= 1");
+  if (k > kMaxK) return fail(H2O_ERR_UNSUPPORTED, "heavy_budget + recent_budget exceeds 12288");
+  if (p->dtype != H2O_F32 && p->dtype != H2O_BF16) return fail(H2O_ERR_INVALID_ARG, "unknown dtype");
+  if (!std::isfinite(p->scale)) return fail(H2O_ERR_INVALID_ARG, "scale must be finite");
+  if (p->max_prompt < 0) return fail(H2O_ERR_INVALID_ARG, "max_prompt must be >= 0");
+  const int64_t units = static_cast<int64_t>(p->batch) * p->heads;
+  const int64_t rows = std::max<int64_t>(k, round32(std::min<int32_t>(p->max_prompt, INT32_MAX - 31)));
+  if (units * rows >= (int64_t{1} << 31) || units * kMaxSplit >= (int64_t{1} << 31))
+    return fail(H2O_ERR_INVALID_ARG, "batch * heads * max(k, max_prompt) must stay below 2^31");
+  if (sz != nullptr) {
+    const size_t es = p->dtype == H2O_F32 ? 4 : 2;
+    const size_t u = static_cast<size_t>(units), kk = static_cast<size_t>(k), d = p->head_dim;
+    sz->kv = 2 * u * kk * d * es;
+    sz->meta = u * kk * 12;
+    sz->max_split = units < kSplitUnits ? kMaxSplit : 1;
+    sz->split = sz->max_split > 1
+                    ? u * sz->max_split * (2 + d) * 4 + u * (kk + 1) * 4 + u * 4
+                    : 0;
+    sz->lpad = round32(p->max_prompt);
+    sz->prefill = 4 * u * static_cast<size_t>(sz->lpad) * 4;
+    sz->total = sz->kv + sz->meta + sz->split + sz->prefill;
+  }
+  return H2O_OK;
+}
+
+void free_all(h2o_cache* c) {
+  void* ptrs[] = {c->kslots, c->vslots, c->score, c->comp, c->pos, c->part, c->logits,
+                  c->counters, c->row_max, c->row_sum, c->row_lse2, c->col_sum};
+  for (void* q : ptrs)
+    if (q != nullptr) (void)hipFree(q);
+}
+
+int choose_nsplit(const h2o_cache* c, int32_t count, int32_t* split_len) {
+  int ns = 1;
+  if (c->max_split > 1 && count >= 2 * kMinSlotsPerSplit) {
+    const int want = (1024 + c->units - 1) / c->units;
+    ns = std::max(1, std::min({want, count / kMinSlotsPerSplit, static_cast<int>(c->max_split)}));
+  }
+  if (ns == 1) {
+    *split_len = std::max(count, 1);
+    return 1;
+  }
+  *split_len = (count + ns - 1) / ns;
+  return (count + *split_len - 1) / *split_len;  // every split holds >= 1 slot
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* h2o_status_str(h2o_status s) {
+  switch (s) {
+    case H2O_OK: return "ok";
+    case H2O_ERR_INVALID_ARG: return "invalid argument";
+    case H2O_ERR_STATE: return "invalid state";
+    case H2O_ERR_OOM: return "out of device memory";
+    case H2O_ERR_HIP: return "HIP runtime error";
+    case H2O_ERR_UNSUPPORTED: return "unsupported";
+  }
+  return "unknown status";
+}
+
+const char* h2o_last_error(void) { return g_err.c_str(); }
+
+h2o_status h2o_cache_bytes(const h2o_params* params, size_t* kv_bytes, size_t* total_bytes) {
+  Sizes sz{};
+  const h2o_status st = check_params(params, &sz);
+  if (st != H2O_OK) return st;
+  if (kv_bytes != nullptr) *kv_bytes = sz.kv;
+  if (total_bytes != nullptr) *total_bytes = sz.total;
+  return H2O_OK;
+}
+
+h2o_status h2o_cache_create(const h2o_params* params, int device, h2o_cache** out) {
+  if (out == nullptr) return fail(H2O_ERR_INVALID_ARG, "out is NULL");
+  *out = nullptr;
+  Sizes sz{};
+  h2o_status st = check_params(params, &sz);
+  if (st != H2O_OK) return st;
+  if (device < -1) return fail(H2O_ERR_INVALID_ARG, "device must be >= -1");
+  int dev = device;
+  if (dev == -1) {
+    const hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  } else {
+    int n = 0;
+    const hipError_t e = hipGetDeviceCount(&n);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDeviceCount");
+    if (dev >= n) return fail(H2O_ERR_INVALID_ARG, "device index out of range");
+  }
+  DeviceGuard guard(dev);
+  h2o_cache* c = new (std::nothrow) h2o_cache{};
+  if (c == nullptr) return fail(H2O_ERR_OOM, "host allocation failed");
+  c->p = *params;
+  c->device = dev;
+  c->d = params->head_dim;
+  c->k = params->heavy_budget + params->recent_budget;
+  c->units = params->batch * params->heads;
+  c->esize = params->dtype == H2O_F32 ? 4 : 2;
+  c->scale = params->scale > 0.f ? params->scale : 1.f / std::sqrt(static_cast<float>(c->d));
+  c->c2 = c->scale * kLog2e;
+  c->count = 0;
+  c->next_pos = 0;
+  c->prompt_len = -1;
+  c->lpad_cap = sz.lpad;
+  c->lpad_last = 0;
+  c->max_split = sz.max_split;
+
+  const size_t u = c->units, kk = c->k, d = c->d;
+  struct Alloc {
+    void** p;
+    size_t bytes;
+  } allocs[] = {
+      {&c->kslots, u * kk * d * c->esize},
+      {&c->vslots, u * kk * d * c->esize},
+      {reinterpret_cast<void**>(&c->score), u * kk * 4},
+      {reinterpret_cast<void**>(&c->comp), u * kk * 4},
+      {reinterpret_cast<void**>(&c->pos), u * kk * 4},
+      {reinterpret_cast<void**>(&c->part), c->max_split > 1 ? u * c->max_split * (2 + d) * 4 : 0},
+      {reinterpret_cast<void**>(&c->logits), c->max_split > 1 ? u * (kk + 1) * 4 : 0},
+      {reinterpret_cast<void**>(&c->counters), c->max_split > 1 ? u * 4 : 0},
+      {reinterpret_cast<void**>(&c->row_max), u * c->lpad_cap * 4},
+      {reinterpret_cast<void**>(&c->row_sum), u * c->lpad_cap * 4},
+      {reinterpret_cast<void**>(&c->row_lse2), u * c->lpad_cap * 4},
+      {reinterpret_cast<void**>(&c->col_sum), u * c->lpad_cap * 4},
+  };
+  for (const Alloc& a : allocs) {
+    if (a.bytes == 0) continue;
+    const hipError_t e = hipMalloc(a.p, a.bytes);
+    if (e != hipSuccess) {
+      free_all(c);
+      delete c;
+      return hip_fail(e, "hipMalloc");
+    }
+  }
+  hipError_t e = h2o::launch_clear(c->pos, c->score, c->comp, u * kk, nullptr);
+  if (e == hipSuccess && c->counters != nullptr) e = hipMemset(c->counters, 0, u * 4);
+  if (e == hipSuccess) e = hipDeviceSynchronize();
+  if (e != hipSuccess) {
+    free_all(c);
+    delete c;
+    return hip_fail(e, "cache initialisation");
+  }
+  *out = c;
+  return H2O_OK;
+}
+
+h2o_status h2o_cache_destroy(h2o_cache* c) {
+  if (c == nullptr) return H2O_OK;
+  DeviceGuard guard(c->device);
+  const hipError_t e = hipDeviceSynchronize();
+  free_all(c);
+  delete c;
+  if (e != hipSuccess) return hip_fail(e, "hipDeviceSynchronize before free");
+  return H2O_OK;
+}
+
+h2o_status h2o_prefill(h2o_cache* c, const void* q, const void* k, const void* v, int32_t L, void* stream) {
+  if (c == nullptr) return fail(H2O_ERR_INVALID_ARG, "cache is NULL");
+  if (L < 0) return fail(H2O_ERR_INVALID_ARG, "prompt_len must be >= 0");
+  if (L > c->p.max_prompt) return fail(H2O_ERR_INVALID_ARG, "prompt_len exceeds max_prompt");
+  if (L > 0) {
+    if (q == nullptr || k == nullptr || v == nullptr) return fail(H2O_ERR_INVALID_ARG, "q, k, v must be non-NULL");
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v))
+      return fail(H2O_ERR_INVALID_ARG, "q, k, v must be 16-byte aligned");
+  }
+  DeviceGuard guard(c->device);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (L == 0) {
+    const hipError_t e = h2o::launch_clear(c->pos, c->score, c->comp, static_cast<size_t>(c->units) * c->k, s);
+    if (e != hipSuccess) return hip_fail(e, "clear launch");
+  } else {
+    h2o::PrefillArgs a{};
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.L = L;
+    a.Lpad = round32(L);
+    a.row_max = c->row_max;
+    a.row_sum = c->row_sum;
+    a.row_lse2 = c->row_lse2;
+    a.col_sum = c->col_sum;
+    a.kslots = c->kslots;
+    a.vslots = c->vslots;
+    a.score = c->score;
+    a.comp = c->comp;
+    a.pos = c->pos;
+    a.heavy = c->p.heavy_budget;
+    a.recent = c->p.recent_budget;
+    a.kcap = c->k;
+    a.scale = c->scale;
+    a.c2 = c->c2;
+    const hipError_t e = h2o::launch_prefill(c->p.dtype, c->d, a, c->units, s);
+    if (e != hipSuccess) return hip_fail(e, "prefill launch");
+    c->lpad_last = a.Lpad;
+  }
+  c->count = std::min(L, c->k);
+  c->next_pos = L;
+  c->prompt_len = L;
+  return H2O_OK;
+}
+
+h2o_status h2o_decode_step(h2o_cache* c, const void* q, const void* k, const void* v, float* out,
+                           int32_t* evicted, void* stream) {
+  if (c == nullptr) return fail(H2O_ERR_INVALID_ARG, "cache is NULL");
+  if (q == nullptr || k == nullptr || v == nullptr || out == nullptr)
+    return fail(H2O_ERR_INVALID_ARG, "q, k, v and out must be non-NULL");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
+    return fail(H2O_ERR_INVALID_ARG, "q, k, v and out must be 16-byte aligned");
+  if (evicted != nullptr && (reinterpret_cast<uintptr_t>(evicted) & 3u) != 0)
+    return fail(H2O_ERR_INVALID_ARG, "evicted must be 4-byte aligned");
+  if (c->prompt_len < 0) return fail(H2O_ERR_STATE, "decode before prefill");
+  if (c->next_pos == INT32_MAX) return fail(H2O_ERR_STATE, "position counter would overflow int32");
+  DeviceGuard guard(c->device);
+  h2o::DecodeArgs a{};
+  a.q = q;
+  a.knew = k;
+  a.vnew = v;
+  a.kslots = c->kslots;
+  a.vslots = c->vslots;
+  a.score = c->score;
+  a.comp = c->comp;
+  a.pos = c->pos;
+  a.out = out;
+  a.evicted = evicted;
+  a.part = c->part;
+  a.logits = c->logits;
+  a.counters = c->counters;
+  a.k = c->k;
+  a.count = c->count;
+  a.new_pos = c->next_pos;
+  a.cand_limit = c->next_pos - c->p.recent_budget;
+  a.new_is_candidate = c->p.recent_budget == 0 ? 1 : 0;
+  a.nsplit = choose_nsplit(c, c->count, &a.split_len);
+  a.c2 = c->c2;
+  const hipError_t e = h2o::launch_decode(c->p.dtype, c->d, a, c->units, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "decode launch");
+  if (c->count < c->k) ++c->count;
+  ++c->next_pos;
+  return H2O_OK;
+}
+
+h2o_status h2o_cache_read(h2o_cache* c, int32_t* pos, float* score, void* k_slots, void* v_slots, int32_t* meta,
+                          void* stream) {
+  if (c == nullptr) return fail(H2O_ERR_INVALID_ARG, "cache is NULL");
+  DeviceGuard guard(c->device);
+  hipError_t e = hipStreamSynchronize(static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "hipStreamSynchronize");
+  const size_t n = static_cast<size_t>(c->units) * c->k;
+  if (pos != nullptr && (e = hipMemcpy(pos, c->pos, n * 4, hipMemcpyDeviceToHost)) != hipSuccess)
+    return hip_fail(e, "copy pos");
+  if (score != nullptr && (e = hipMemcpy(score, c->score, n * 4, hipMemcpyDeviceToHost)) != hipSuccess)
+    return hip_fail(e, "copy score");
+  const size_t kvb = n * c->d * c->esize;
+  if (k_slots != nullptr && (e = hipMemcpy(k_slots, c->kslots, kvb, hipMemcpyDeviceToHost)) != hipSuccess)
+    return hip_fail(e, "copy k slots");
+  if (v_slots != nullptr && (e = hipMemcpy(v_slots, c->vslots, kvb, hipMemcpyDeviceToHost)) != hipSuccess)
+    return hip_fail(e, "copy v slots");
+  if (meta != nullptr) {
+    meta[0] = c->count;
+    meta[1] = c->next_pos;
+  }
+  return H2O_OK;
+}
+
+h2o_status h2o_prefill_stats_read(h2o_cache* c, float* row_max, float* row_sum, float* col_sum, void* stream) {
+  if (c == nullptr) return fail(H2O_ERR_INVALID_ARG, "cache is NULL");
+  if (c->prompt_len < 0) return fail(H2O_ERR_STATE, "no prefill yet");
+  DeviceGuard guard(c->device);
+  hipError_t e = hipStreamSynchronize(static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "hipStreamSynchronize");
+  const int32_t L = c->prompt_len;
+  if (L == 0) return H2O_OK;
+  const float* src[3] = {c->row_max, c->row_sum, c->col_sum};
+  float* dst[3] = {row_max, row_sum, col_sum};
+  for (int t = 0; t < 3; ++t) {
+    if (dst[t] == nullptr) continue;
+    e = hipMemcpy2D(dst[t], static_cast<size_t>(L) * 4, src[t], static_cast<size_t>(c->lpad_last) * 4,
+                    static_cast<size_t>(L) * 4, c->units, hipMemcpyDeviceToHost);
+    if (e != hipSuccess) return hip_fail(e, "copy prefill statistics");
+  }
+  return H2O_OK;
+}
+
+h2o_status h2o_cache_info(const h2o_cache* c, int32_t* count, int32_t* next_pos, int32_t* prompt_len) {
+  if (c == nullptr) return fail(H2O_ERR_INVALID_ARG, "cache is NULL");
+  if (count != nullptr) *count = c->count;
+  if (next_pos != nullptr) *next_pos = c->next_pos;
+  if (prompt_len != nullptr) *prompt_len = c->prompt_len;
+  return H2O_OK;
+}
+
+}  // extern "C"

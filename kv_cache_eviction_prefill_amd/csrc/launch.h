@@ -1,0 +1,64 @@
+// Internal launch interface between the cache object and the HIP kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace h2o {
+
+// One decode step over every unit of a cache.
+struct DecodeArgs {
+  const void* q;     // [units, d] new query
+  const void* knew;  // [units, d] new key
+  const void* vnew;  // [units, d] new value
+  void* kslots;      // [units, k, d]
+  void* vslots;      // [units, k, d]
+  float* score;      // [units, k] running score (Kahan sum)
+  float* comp;       // [units, k] Kahan compensation
+  int32_t* pos;      // [units, k] position per slot, -1 when empty
+  float* out;        // [units, d]
+  int32_t* evicted;  // [units] or nullptr
+  float* part;       // split mode: [units, nsplit, 2 + d] partial (max, sum, o)
+  float* logits;     // split mode: [units, k + 1] base-2 logits (new token at index k)
+  uint32_t* counters;  // split mode: [units] arrival counters, zero between launches
+  int32_t k;           // slots per unit
+  int32_t count;       // occupied slots before this step (slots 0..count-1)
+  int32_t new_pos;     // position i of the new token
+  int32_t cand_limit;  // positions <= cand_limit are eviction candidates (i - K_r)
+  int32_t new_is_candidate;  // K_r == 0: the new token competes for eviction
+  int32_t nsplit;      // blocks per unit (1: single-block path)
+  int32_t split_len;   // slots per split block
+  float c2;            // scale * log2(e)
+};
+
+hipError_t launch_decode(int dtype, int head_dim, const DecodeArgs& a, int units, hipStream_t s);
+
+// Prefill of every unit of a cache.
+struct PrefillArgs {
+  const void* q;  // [units, L, d]
+  const void* k;  // [units, L, d]
+  const void* v;  // [units, L, d]
+  int32_t L;
+  int32_t Lpad;       // stride of the per-row scratch arrays (multiple of 32, >= L)
+  float* row_max;     // [units, Lpad] max logit of each prompt row
+  float* row_sum;     // [units, Lpad] sum of exp(logit - max) of each prompt row
+  float* row_lse2;    // [units, Lpad] base-2 log-sum-exp of each row (scaled units)
+  float* col_sum;     // [units, Lpad] attention received by each prompt token
+  void* kslots;       // [units, k, d]
+  void* vslots;       // [units, k, d]
+  float* score;       // [units, k]
+  float* comp;        // [units, k]
+  int32_t* pos;       // [units, k]
+  int32_t heavy;
+  int32_t recent;
+  int32_t kcap;       // k
+  float scale;
+  float c2;           // scale * log2(e)
+};
+
+hipError_t launch_prefill(int dtype, int head_dim, const PrefillArgs& a, int units, hipStream_t s);
+
+// Mark every slot empty (pos = -1, score = comp = 0).
+hipError_t launch_clear(int32_t* pos, float* score, float* comp, size_t n, hipStream_t s);
+
+}  // namespace h2o

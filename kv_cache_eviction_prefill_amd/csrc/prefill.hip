@@ -1,0 +1,369 @@
+// H2O prefill: score every prompt token by the attention it receives under the
+// prompt's causal softmax, keep the heavy hitters plus the recent window, and
+// fill the cache slots.
+//
+// Sources: "H2O: Heavy-Hitter Oracle for Efficient Generative Inference of Large
+// Language Models -- 深度解读报告", §2.3 (heavy hitters found from the attention
+// each token has received), §3.4 (prefill rule: a long prompt keeps K heavy
+// hitters and the K most recent tokens; a short one keeps everything).
+//
+// Three launches per prefill:
+//   1. rowstats:  per prompt row r, m_r = max_j x_rj and l_r = sum_j exp(x_rj - m_r)
+//                 over j <= r (x = scale * q_r . k_j); bf16 inputs use MFMA
+//                 32x32x16 tiles of S^T = K Q^T, so one lane holds one query's
+//                 logits and the row reductions stay inside the lane.
+//   2. colsum:    c_j = sum_{r >= j} exp(x_rj - m_r) / l_r, recomputing the
+//                 logits as MFMA tiles of S = Q K^T (one lane per key column);
+//                 the causal softmax is row-normalised, so the column sums need
+//                 the row normalisers of pass 1 first.
+//   3. select_fill: per unit, a radix select on the 64-bit key (score bits,
+//                 position) finds the K_h-th best heavy-hitter candidate, a
+//                 ballot/popcount compaction assigns slots in position order,
+//                 and the kept K/V rows, positions and scores are written.
+#include <cmath>
+
+#include "h2o_device.h"
+#include "launch.h"
+
+namespace h2o {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kTile = 32;              // MFMA tile edge (rows and columns)
+constexpr int kRowsPerBlock = 128;     // 4 waves x 32
+constexpr uint64_t kNoKey = ~0ull;
+
+__device__ inline bf16x8 ld_bf16x8(const bf16_t* p) { return __builtin_bit_cast(bf16x8, ld16(p)); }
+
+// Row m of a 32x32 MFMA accumulator tile held in element i of lane `lane`
+// (the column is lane % 32).
+__device__ inline int acc_row(int i, int lane) { return 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3); }
+
+// ------------------------------------------------------------------ pass 1, bf16 (MFMA)
+template <int D>
+__global__ __launch_bounds__(kThreads) void rowstats_bf16(PrefillArgs a) {
+  const int nblk = (a.L + kRowsPerBlock - 1) / kRowsPerBlock;
+  const int unit = blockIdx.x / nblk;
+  const int qb = (nblk - 1 - blockIdx.x % nblk) * kRowsPerBlock;  // longest rows first
+  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+  const int q0 = qb + wave * kTile;
+  if (q0 >= a.L) return;
+  const bf16_t* Qu = static_cast<const bf16_t*>(a.q) + static_cast<size_t>(unit) * a.L * D;
+  const bf16_t* Ku = static_cast<const bf16_t*>(a.k) + static_cast<size_t>(unit) * a.L * D;
+  const int lrow = lane & 31, lk = (lane >> 5) * 8;
+  const int qi = q0 + lrow;
+  const int qrow = min(qi, a.L - 1);
+
+  bf16x8 bq[D / 16];
+#pragma unroll
+  for (int kk = 0; kk < D / 16; ++kk) bq[kk] = ld_bf16x8(Qu + static_cast<size_t>(qrow) * D + lk + 16 * kk);
+
+  float m = -INFINITY, l = 0.f;  // m in raw q.k units
+  const int qmax = min(q0 + kTile - 1, a.L - 1);
+  for (int k0 = 0; k0 <= qmax; k0 += kTile) {
+    const int krow = min(k0 + lrow, a.L - 1);
+    bf16x8 ak[D / 16];
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) ak[kk] = ld_bf16x8(Ku + static_cast<size_t>(krow) * D + lk + 16 * kk);
+    floatx16 acc = {};
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak[kk], bq[kk], acc, 0, 0, 0);
+    // acc[i] = q_qi . k_(k0 + acc_row(i, lane))
+    const bool diag = (k0 + kTile - 1 > q0);
+    float v[16];
+    float tm = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const bool ok = !diag || (k0 + acc_row(i, lane) <= qi);
+      v[i] = ok ? acc[i] : -INFINITY;
+      tm = fmaxf(tm, v[i]);
+    }
+    if (tm != -INFINITY) {
+      const float mn = fmaxf(m, tm);
+      const float mc = mn * a.c2;
+      float sum = 0.f;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) sum += fast_exp2(fmaf(v[i], a.c2, -mc));
+      l = fmaf(l, fast_exp2((m - mn) * a.c2), sum);
+      m = mn;
+    }
+  }
+  // lanes l and l^32 saw disjoint key subsets of the same query
+  const float m2 = __shfl_xor(m, 32, kWave), l2 = __shfl_xor(l, 32, kWave);
+  const float mn = fmaxf(m, m2);
+  const float lt = l * fast_exp2((m - mn) * a.c2) + l2 * fast_exp2((m2 - mn) * a.c2);
+  if (lane < 32 && qi < a.L) {
+    const size_t o = static_cast<size_t>(unit) * a.Lpad + qi;
+    a.row_max[o] = mn * a.scale;
+    a.row_sum[o] = lt;
+    a.row_lse2[o] = fmaf(mn, a.c2, log2f(lt));
+  }
+}
+
+// ------------------------------------------------------------------ pass 2, bf16 (MFMA)
+template <int D>
+__global__ __launch_bounds__(kThreads) void colsum_bf16(PrefillArgs a) {
+  const int nblk = (a.L + kRowsPerBlock - 1) / kRowsPerBlock;
+  const int unit = blockIdx.x / nblk;
+  const int kb = (blockIdx.x % nblk) * kRowsPerBlock;  // low keys (longest columns) first
+  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+  const int k0 = kb + wave * kTile;
+  if (k0 >= a.L) return;
+  const bf16_t* Qu = static_cast<const bf16_t*>(a.q) + static_cast<size_t>(unit) * a.L * D;
+  const bf16_t* Ku = static_cast<const bf16_t*>(a.k) + static_cast<size_t>(unit) * a.L * D;
+  const float* lse = a.row_lse2 + static_cast<size_t>(unit) * a.Lpad;
+  const int lrow = lane & 31, lk = (lane >> 5) * 8;
+  const int key = k0 + lrow;
+  const int krow = min(key, a.L - 1);
+
+  bf16x8 bk[D / 16];
+#pragma unroll
+  for (int kk = 0; kk < D / 16; ++kk) bk[kk] = ld_bf16x8(Ku + static_cast<size_t>(krow) * D + lk + 16 * kk);
+
+  float cs = 0.f;
+  for (int q0 = k0; q0 < a.L; q0 += kTile) {
+    const int qrow = min(q0 + lrow, a.L - 1);
+    bf16x8 aq[D / 16];
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) aq[kk] = ld_bf16x8(Qu + static_cast<size_t>(qrow) * D + lk + 16 * kk);
+    floatx16 acc = {};
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq[kk], bk[kk], acc, 0, 0, 0);
+    // acc[i] = q_(q0 + acc_row(i, lane)) . k_key; the row normalisers of those
+    // queries sit in 4 runs of 4 consecutive rows
+    float4 lv[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) lv[t] = *reinterpret_cast<const float4*>(lse + q0 + 8 * t + 4 * (lane >> 5));
+    const bool edge = (q0 == k0) || (q0 + kTile > a.L);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const float4& f = lv[i >> 2];
+      const float ls = (i & 3) == 0 ? f.x : (i & 3) == 1 ? f.y : (i & 3) == 2 ? f.z : f.w;
+      float p = fast_exp2(fmaf(acc[i], a.c2, -ls));
+      if (edge) {
+        const int qq = q0 + acc_row(i, lane);
+        p = (qq >= key && qq < a.L) ? p : 0.f;
+      }
+      cs += p;
+    }
+  }
+  cs += __shfl_xor(cs, 32, kWave);
+  if (lane < 32 && key < a.L) a.col_sum[static_cast<size_t>(unit) * a.Lpad + key] = cs;
+}
+
+// ------------------------------------------------------------------ fp32 (VALU) passes
+template <int D>
+__global__ __launch_bounds__(64) void rowstats_f32(PrefillArgs a) {
+  const int nblk = (a.L + 63) / 64;
+  const int unit = blockIdx.x / nblk;
+  const int r = (blockIdx.x % nblk) * 64 + threadIdx.x;
+  if (r >= a.L) return;
+  const float* Qu = static_cast<const float*>(a.q) + static_cast<size_t>(unit) * a.L * D;
+  const float* Ku = static_cast<const float*>(a.k) + static_cast<size_t>(unit) * a.L * D;
+  float q[D];
+#pragma unroll
+  for (int e = 0; e < D; ++e) q[e] = Qu[static_cast<size_t>(r) * D + e];
+  float m = -INFINITY, l = 0.f;
+  for (int j = 0; j <= r; ++j) {
+    float dot = 0.f;
+#pragma unroll
+    for (int e = 0; e < D; ++e) dot = fmaf(q[e], Ku[static_cast<size_t>(j) * D + e], dot);
+    if (dot > m) {
+      l = fmaf(l, fast_exp2((m - dot) * a.c2), 1.f);
+      m = dot;
+    } else {
+      l += fast_exp2((dot - m) * a.c2);
+    }
+  }
+  const size_t o = static_cast<size_t>(unit) * a.Lpad + r;
+  a.row_max[o] = m * a.scale;
+  a.row_sum[o] = l;
+  a.row_lse2[o] = fmaf(m, a.c2, log2f(l));
+}
+
+template <int D>
+__global__ __launch_bounds__(64) void colsum_f32(PrefillArgs a) {
+  const int nblk = (a.L + 63) / 64;
+  const int unit = blockIdx.x / nblk;
+  const int j = (blockIdx.x % nblk) * 64 + threadIdx.x;
+  if (j >= a.L) return;
+  const float* Qu = static_cast<const float*>(a.q) + static_cast<size_t>(unit) * a.L * D;
+  const float* Ku = static_cast<const float*>(a.k) + static_cast<size_t>(unit) * a.L * D;
+  const float* lse = a.row_lse2 + static_cast<size_t>(unit) * a.Lpad;
+  float kv[D];
+#pragma unroll
+  for (int e = 0; e < D; ++e) kv[e] = Ku[static_cast<size_t>(j) * D + e];
+  float cs = 0.f;
+  for (int r = j; r < a.L; ++r) {
+    float dot = 0.f;
+#pragma unroll
+    for (int e = 0; e < D; ++e) dot = fmaf(Qu[static_cast<size_t>(r) * D + e], kv[e], dot);
+    cs += fast_exp2(fmaf(dot, a.c2, -lse[r]));
+  }
+  a.col_sum[static_cast<size_t>(unit) * a.Lpad + j] = cs;
+}
+
+// ------------------------------------------------------------------ select + fill
+template <typename T, int D>
+__global__ __launch_bounds__(kThreads) void select_fill(PrefillArgs a) {
+  constexpr int EPL = Elem<T>::kPer16B;
+  constexpr int LPR = D / EPL;
+  constexpr int NG = kThreads / LPR;
+  extern __shared__ int s_kept[];  // [kcap] kept positions in slot order
+  __shared__ unsigned s_hist[256];
+  __shared__ uint64_t s_prefix;
+  __shared__ int s_need;
+  __shared__ int s_wsum[kThreads / kWave];
+
+  const int unit = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int L = a.L, kc = a.kcap;
+  const float* c = a.col_sum + static_cast<size_t>(unit) * a.Lpad;
+
+  int nkept;
+  if (L <= kc) {
+    for (int j = tid; j < L; j += kThreads) s_kept[j] = j;
+    nkept = L;
+  } else {
+    const int pool = L - a.recent;  // heavy-hitter candidates: [0, L - K_r)
+    uint64_t thr = kNoKey;
+    if (a.heavy > 0) {
+      // MSB-first radix select of the heavy-th largest key among the pool
+      uint64_t prefix = 0, mask = 0;
+      int need = a.heavy;
+      for (int shift = 56; shift >= 0; shift -= 8) {
+        for (int t = tid; t < 256; t += kThreads) s_hist[t] = 0u;
+        __syncthreads();
+        for (int j = tid; j < pool; j += kThreads) {
+          const uint64_t key = evict_key(c[j], j);
+          if ((key & mask) == prefix) atomicAdd(&s_hist[(key >> shift) & 255u], 1u);
+        }
+        __syncthreads();
+        if (tid == 0) {
+          int cum = 0, dsel = 0;
+          for (int dd = 255; dd >= 0; --dd) {
+            const int h = static_cast<int>(s_hist[dd]);
+            if (cum + h >= need) {
+              dsel = dd;
+              break;
+            }
+            cum += h;
+          }
+          s_prefix = prefix | (static_cast<uint64_t>(dsel) << shift);
+          s_need = need - cum;
+        }
+        __syncthreads();
+        prefix = s_prefix;
+        need = s_need;
+        mask |= static_cast<uint64_t>(255u) << shift;
+        __syncthreads();
+      }
+      thr = prefix;  // exactly `heavy` pool keys are >= thr (keys are unique)
+    }
+    // compaction in position order: heavy hitters first, then the recent window
+    int base_slot = 0;
+    for (int j0 = 0; j0 < L; j0 += kThreads) {
+      const int j = j0 + tid;
+      bool f;
+      if (j < pool) f = (a.heavy > 0) && (evict_key(c[j], j) >= thr);
+      else f = (j < L);
+      const uint64_t bal = __ballot(f);
+      const int lane = tid & (kWave - 1);
+      const int wpre = __popcll(bal & ((1ull << lane) - 1ull));
+      if (lane == 0) s_wsum[tid / kWave] = __popcll(bal);
+      __syncthreads();
+      int off = base_slot, tot = 0;
+#pragma unroll
+      for (int w = 0; w < kThreads / kWave; ++w) {
+        if (w < tid / kWave) off += s_wsum[w];
+        tot += s_wsum[w];
+      }
+      if (f && off + wpre < kc) s_kept[off + wpre] = j;
+      __syncthreads();
+      base_slot += tot;
+    }
+    nkept = min(base_slot, kc);
+  }
+  __syncthreads();
+
+  float* sc = a.score + static_cast<size_t>(unit) * kc;
+  float* cp = a.comp + static_cast<size_t>(unit) * kc;
+  int32_t* ps = a.pos + static_cast<size_t>(unit) * kc;
+  for (int s = tid; s < kc; s += kThreads) {
+    if (s < nkept) {
+      const int j = s_kept[s];
+      ps[s] = j;
+      sc[s] = c[j];
+    } else {
+      ps[s] = -1;
+      sc[s] = 0.f;
+    }
+    cp[s] = 0.f;
+  }
+  const T* Ku = static_cast<const T*>(a.k) + static_cast<size_t>(unit) * L * D;
+  const T* Vu = static_cast<const T*>(a.v) + static_cast<size_t>(unit) * L * D;
+  T* kd = static_cast<T*>(a.kslots) + static_cast<size_t>(unit) * kc * D;
+  T* vd = static_cast<T*>(a.vslots) + static_cast<size_t>(unit) * kc * D;
+  const int g = tid / LPR, r = tid % LPR;
+  for (int s = g; s < nkept; s += NG) {
+    const int j = s_kept[s];
+    st16(kd + static_cast<size_t>(s) * D + r * EPL, ld16(Ku + static_cast<size_t>(j) * D + r * EPL));
+    st16(vd + static_cast<size_t>(s) * D + r * EPL, ld16(Vu + static_cast<size_t>(j) * D + r * EPL));
+  }
+}
+
+__global__ void clear_kernel(int32_t* pos, float* score, float* comp, size_t n) {
+  for (size_t i = blockIdx.x * static_cast<size_t>(blockDim.x) + threadIdx.x; i < n;
+       i += static_cast<size_t>(gridDim.x) * blockDim.x) {
+    pos[i] = -1;
+    score[i] = 0.f;
+    comp[i] = 0.f;
+  }
+}
+
+template <typename T, int D>
+hipError_t launch_select(const PrefillArgs& a, int units, hipStream_t s) {
+  hipLaunchKernelGGL((select_fill<T, D>), dim3(units), dim3(kThreads),
+                     static_cast<size_t>(a.kcap) * sizeof(int), s, a);
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_bf16(const PrefillArgs& a, int units, hipStream_t s) {
+  const int nblk = (a.L + kRowsPerBlock - 1) / kRowsPerBlock;
+  hipLaunchKernelGGL((rowstats_bf16<D>), dim3(units * nblk), dim3(kThreads), 0, s, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((colsum_bf16<D>), dim3(units * nblk), dim3(kThreads), 0, s, a);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return launch_select<bf16_t, D>(a, units, s);
+}
+
+template <int D>
+hipError_t launch_f32(const PrefillArgs& a, int units, hipStream_t s) {
+  const int nblk = (a.L + 63) / 64;
+  hipLaunchKernelGGL((rowstats_f32<D>), dim3(units * nblk), dim3(64), 0, s, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((colsum_f32<D>), dim3(units * nblk), dim3(64), 0, s, a);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return launch_select<float, D>(a, units, s);
+}
+
+}  // namespace
+
+hipError_t launch_prefill(int dtype, int head_dim, const PrefillArgs& a, int units, hipStream_t s) {
+  if (dtype == 0) return head_dim == 64 ? launch_f32<64>(a, units, s) : launch_f32<128>(a, units, s);
+  return head_dim == 64 ? launch_bf16<64>(a, units, s) : launch_bf16<128>(a, units, s);
+}
+
+hipError_t launch_clear(int32_t* pos, float* score, float* comp, size_t n, hipStream_t s) {
+  if (n == 0) return hipSuccess;
+  const int blocks = static_cast<int>(std::min<size_t>((n + 255) / 256, 4096));
+  hipLaunchKernelGGL(clear_kernel, dim3(blocks), dim3(256), 0, s, pos, score, comp, n);
+  return hipGetLastError();
+}
+
+}  // namespace h2o

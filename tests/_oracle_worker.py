@@ -1,0 +1,86 @@
+"""Per-unit comparison of the GPU results with the CPU oracle.
+
+Runs in worker processes (imports numpy and the oracle only; never torch or the
+GPU library).  Tolerances:
+  * attention output: 2e-3 absolute per element;
+  * scores (prefill column sums, final accumulated scores): 1e-4 relative;
+  * prefill row statistics: row max 2e-4 absolute (logit units), row sum 1e-4
+    relative (fp32 sums of exactly-multiplied bf16 products, derived bound);
+  * kept sets and evicted positions: exact, except near-ties (1e-5 relative),
+    where the oracle adopts the GPU's choice and continues.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from oracle import ParityMismatch, run_unit
+
+OUT_ATOL = 2e-3
+SCORE_RTOL = 1e-4
+ROWMAX_ATOL = 2e-4
+ROWSUM_RTOL = 1e-4
+
+
+def _rel(a, b):
+    a = np.asarray(a, np.float64)
+    b = np.asarray(b, np.float64)
+    return np.abs(a - b) / np.maximum(np.abs(b), 1e-30)
+
+
+def check_unit(p: dict) -> dict:
+    """``p``: Q, K, V [N, d] (float32, storage-rounded), L, heavy, recent, and the
+    GPU's results for the unit: kept, evicted [T], out [T, d] (or sampled
+    steps), stats (row_max, row_sum, col_sum) or None, final (pos, score, k, v)."""
+    tag = p["tag"]
+    res = {"tag": tag, "ok": True, "msg": ""}
+    try:
+        o = run_unit(p["Q"], p["K"], p["V"], p["L"], p["heavy"], p["recent"],
+                     replay_kept=p["kept"], replay_evicted=p["evicted"])
+    except ParityMismatch as e:
+        return {"tag": tag, "ok": False, "msg": f"decision mismatch: {e}"}
+    res["ties"] = int(o["decode_ties_adopted"]) + int(o["prefill_tie_adopted"])
+    msgs = []
+    # prefill statistics
+    st = p.get("stats")
+    if st is not None and o["prefill"] is not None:
+        ps = o["prefill"]
+        e_m = np.max(np.abs(st[0] - ps.row_max))
+        e_l = np.max(_rel(st[1], ps.row_sum))
+        e_c = np.max(_rel(st[2], ps.col_sum))
+        res.update(rowmax_err=float(e_m), rowsum_rel=float(e_l), colsum_rel=float(e_c))
+        if e_m > ROWMAX_ATOL:
+            msgs.append(f"row_max err {e_m:.3g}")
+        if e_l > ROWSUM_RTOL:
+            msgs.append(f"row_sum rel {e_l:.3g}")
+        if e_c > SCORE_RTOL:
+            j = int(np.argmax(_rel(st[2], ps.col_sum)))
+            msgs.append(f"col_sum rel {e_c:.3g} at {j}: gpu {st[2][j]!r} oracle {ps.col_sum[j]!r}")
+    # per-step outputs and evictions
+    if not np.array_equal(np.asarray(p["evicted"]), o["evicted"]):
+        msgs.append("evicted log differs after replay")
+    steps = p.get("out_steps")
+    out_ref = o["out"] if steps is None else o["out"][steps]
+    if len(out_ref):
+        e_o = float(np.max(np.abs(p["out"] - out_ref)))
+        res["out_err"] = e_o
+        if e_o > OUT_ATOL:
+            msgs.append(f"out err {e_o:.3g}")
+    # final cache: same positions, scores within tolerance, K/V rows exact
+    pos, score, kr, vr = o["cache"].snapshot()
+    gpos, gscore, gk, gv = p["final"]
+    valid = gpos >= 0
+    order = np.argsort(gpos[valid])
+    gp = gpos[valid][order]
+    if not np.array_equal(gp, pos):
+        msgs.append(f"final positions differ: gpu {gp[:10]} oracle {pos[:10]}")
+    else:
+        e_s = float(np.max(_rel(gscore[valid][order], score))) if len(pos) else 0.0
+        res["score_rel"] = e_s
+        if e_s > SCORE_RTOL:
+            msgs.append(f"score rel {e_s:.3g}")
+        if not (np.array_equal(gk[valid][order], kr) and np.array_equal(gv[valid][order], vr)):
+            msgs.append("cached K/V rows differ from the inputs at those positions")
+    if msgs:
+        res["ok"] = False
+        res["msg"] = "; ".join(msgs)
+    return res

@@ -1,0 +1,103 @@
+"""Drive the HIP library through its C ABI for parity tests and hand the results
+to the CPU oracle, one unit per worker process."""
+from __future__ import annotations
+
+import multiprocessing as mp
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+from kv_cache_eviction_prefill_amd import H2OCache
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+
+
+def log(msg: str) -> None:
+    print(f"[parity {time.strftime('%H:%M:%S')}] {msg}", flush=True)
+
+
+def widen(t: torch.Tensor) -> np.ndarray:
+    return t.detach().to("cpu", torch.float32).numpy()
+
+
+def run_gpu(q, k, v, L, heavy, recent, dtype, collect_out=True, out_units=None, scale=0.0):
+    """Prefill + decode on the GPU.  ``q, k, v``: device tensors [B, H, N, d] in the
+    storage dtype.  Returns host arrays: kept [B, H] lists, stats, evicted
+    [T, B, H], out [T, B, H, d] (or [T, n, d] for ``out_units``), final cache."""
+    B, H, N, d = q.shape
+    T = N - L
+    cache = H2OCache(B, H, d, heavy, recent, dtype=dtype, scale=scale, max_prompt=max(L, 1))
+    qp, kp, vp = (x[:, :, :L].contiguous() for x in (q, k, v))
+    cache.prefill(qp, kp, vp)
+    after = cache.read()
+    stats = cache.prefill_stats() if L > 0 else None
+    del qp, kp, vp
+    qd, kd, vd = (x[:, :, L:].permute(2, 0, 1, 3).contiguous() for x in (q, k, v))
+    ev = torch.empty((T, B, H), dtype=torch.int32, device=q.device)
+    o_step = torch.empty((B, H, d), dtype=torch.float32, device=q.device)
+    sel = None
+    if out_units is not None:
+        sel = torch.tensor([b * H + h for b, h in out_units], device=q.device)
+        outs = torch.empty((T, len(out_units), d), dtype=torch.float32, device=q.device)
+    elif collect_out:
+        outs = torch.empty((T, B, H, d), dtype=torch.float32, device=q.device)
+    for t in range(T):
+        if sel is None and collect_out:
+            cache.decode_step(qd[t], kd[t], vd[t], outs[t], ev[t])
+        else:
+            cache.decode_step(qd[t], kd[t], vd[t], o_step, ev[t])
+            if sel is not None:
+                outs[t] = o_step.view(B * H, d).index_select(0, sel)
+    final = cache.read()
+    torch.cuda.synchronize()
+    res = {"kept": after, "stats": stats, "evicted": ev.cpu().numpy(), "final": final,
+           "out": outs.cpu().numpy() if (collect_out or sel is not None) else None, "info": cache.info()}
+    cache.close()
+    return res
+
+
+def unit_payload(g, b, h, Q, K, V, L, heavy, recent, out_index=None, tag=None):
+    """Pack one unit's inputs (float32 host arrays [N, d]) and GPU results."""
+    kept_pos = g["kept"]["pos"][b, h]
+    st = None
+    if g["stats"] is not None:
+        st = (g["stats"][0][b, h].astype(np.float64), g["stats"][1][b, h].astype(np.float64),
+              g["stats"][2][b, h].astype(np.float64))
+    fin = g["final"]
+    if g["out"] is None:
+        out = np.zeros((0, Q.shape[1]))
+    elif out_index is None:
+        out = g["out"][:, b, h]
+    else:
+        out = g["out"][:, out_index]
+    return {"tag": tag or f"b{b}h{h}", "Q": Q, "K": K, "V": V, "L": L, "heavy": heavy, "recent": recent,
+            "kept": sorted(int(x) for x in kept_pos[kept_pos >= 0]),
+            "evicted": g["evicted"][:, b, h].astype(np.int64), "out": out.astype(np.float64),
+            "stats": st, "final": (fin["pos"][b, h], fin["score"][b, h].astype(np.float64),
+                                   fin["k"][b, h], fin["v"][b, h])}
+
+
+def check_payloads(payloads, procs=None):
+    """Run the oracle comparison for every payload (spawned workers)."""
+    if HERE not in sys.path:
+        sys.path.insert(0, HERE)
+    import _oracle_worker
+
+    procs = procs or min(16, len(os.sched_getaffinity(0)), max(1, len(payloads)))
+    t0 = time.time()
+    if procs <= 1 or len(payloads) <= 2:
+        results = [_oracle_worker.check_unit(p) for p in payloads]
+    else:
+        ctx = mp.get_context("spawn")
+        with ctx.Pool(procs) as pool:
+            results = pool.map(_oracle_worker.check_unit, payloads, chunksize=max(1, len(payloads) // (4 * procs)))
+    bad = [r for r in results if not r["ok"]]
+    worst = {key: max((r.get(key, 0.0) for r in results), default=0.0)
+             for key in ("out_err", "score_rel", "colsum_rel", "rowsum_rel", "rowmax_err")}
+    ties = sum(r.get("ties", 0) for r in results)
+    log(f"oracle checked {len(results)} units in {time.time() - t0:.1f}s on {procs} procs; "
+        f"worst {worst}; near-ties adopted {ties}; failures {len(bad)}")
+    return results, bad

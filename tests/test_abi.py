@@ -1,0 +1,102 @@
+"""The C ABI on the CPU: the library loads, exports every function the header
+declares, and rejects bad arguments before any GPU call."""
+import ctypes
+import json
+import math
+import os
+
+import pytest
+
+from kv_cache_eviction_prefill_amd import h2o as H
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def test_every_declared_symbol_is_exported():
+    lib = H.load()
+    names = H.declared_entry_points()
+    assert {"h2o_cache_create", "h2o_cache_destroy", "h2o_prefill", "h2o_decode_step",
+            "h2o_cache_read"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), n
+        assert n in H._SIGNATURES, f"binding has no signature for {n}"
+        assert callable(getattr(H, n)), f"binding has no same-name wrapper for {n}"
+
+
+def test_status_strings():
+    for code in range(6):
+        assert H.h2o_status_str(code) not in ("", "unknown status")
+    assert H.h2o_status_str(42) == "unknown status"
+
+
+def _bytes(**kw):
+    base = dict(batch=2, heads=3, head_dim=128, heavy=4, recent=4, dtype="bf16", scale=0.0, max_prompt=64)
+    base.update(kw)
+    p = H.make_params(base["batch"], base["heads"], base["head_dim"], base["heavy"], base["recent"],
+                      base["dtype"], base["scale"], base["max_prompt"])
+    kv, tot = ctypes.c_size_t(), ctypes.c_size_t()
+    st = H.h2o_cache_bytes(ctypes.byref(p), ctypes.byref(kv), ctypes.byref(tot))
+    return st, kv.value, tot.value
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(batch=0), H.H2O_ERR_INVALID_ARG), (dict(heads=-1), H.H2O_ERR_INVALID_ARG),
+    (dict(head_dim=0), H.H2O_ERR_INVALID_ARG), (dict(head_dim=96), H.H2O_ERR_UNSUPPORTED),
+    (dict(heavy=0, recent=0), H.H2O_ERR_INVALID_ARG), (dict(heavy=-1), H.H2O_ERR_INVALID_ARG),
+    (dict(heavy=10000, recent=5000), H.H2O_ERR_UNSUPPORTED), (dict(dtype=7), H.H2O_ERR_INVALID_ARG),
+    (dict(scale=float("nan")), H.H2O_ERR_INVALID_ARG), (dict(max_prompt=-1), H.H2O_ERR_INVALID_ARG),
+    (dict(batch=1 << 16, heads=1 << 10, max_prompt=4096), H.H2O_ERR_INVALID_ARG),
+    (dict(), H.H2O_OK), (dict(heavy=0, recent=1), H.H2O_OK), (dict(head_dim=64, dtype="f32"), H.H2O_OK),
+])
+def test_param_validation(kw, status):
+    assert _bytes(**kw)[0] == status
+    if status != H.H2O_OK:
+        assert H.h2o_last_error() != ""
+
+
+def test_cache_bytes_accounting():
+    st, kv, tot = _bytes(batch=2, heads=3, head_dim=128, heavy=4, recent=4, dtype="bf16", max_prompt=64)
+    assert st == 0 and kv == 2 * 6 * 8 * 128 * 2
+    # + scores, compensation, positions (12 B / slot) + split scratch (few units) + 4 prefill rows
+    assert tot == kv + 6 * 8 * 12 + (6 * 64 * 130 * 4 + 6 * 9 * 4 + 6 * 4) + 4 * 6 * 64 * 4
+    st, kv32, _ = _bytes(dtype="f32")
+    assert kv32 == 2 * kv
+
+
+def test_kv_size_matches_reported_example():
+    with open(os.path.join(GOLDEN, "kv_size.json")) as f:
+        g = json.load(f)
+    heads = g["hidden"] // 128
+    st, kv, _ = _bytes(batch=g["batch"], heads=heads, head_dim=128, heavy=g["seq_len"] // 2,
+                       recent=g["seq_len"] // 2, dtype="bf16", max_prompt=0)
+    assert st == 0
+    total_gb = kv * g["layers"] / 1e9
+    assert math.isclose(total_gb, g["reported_gb"], rel_tol=g["rel_tol"])
+
+
+def test_null_and_state_checks_make_no_gpu_call():
+    lib = H.load()
+    assert H.h2o_cache_destroy(None) == H.H2O_OK
+    assert H.h2o_prefill(None, None, None, None, 0, None) == H.H2O_ERR_INVALID_ARG
+    assert H.h2o_decode_step(None, None, None, None, None, None, None) == H.H2O_ERR_INVALID_ARG
+    assert H.h2o_cache_read(None, None, None, None, None, None, None) == H.H2O_ERR_INVALID_ARG
+    assert H.h2o_prefill_stats_read(None, None, None, None, None) == H.H2O_ERR_INVALID_ARG
+    assert H.h2o_cache_info(None, None, None, None) == H.H2O_ERR_INVALID_ARG
+    p = H.make_params(1, 1, 64, 2, 2, "f32")
+    assert H.h2o_cache_create(ctypes.byref(p), -1, None) == H.H2O_ERR_INVALID_ARG
+    out = ctypes.c_void_p(1234)
+    bad = H.make_params(1, 1, 96, 2, 2, "f32")
+    assert H.h2o_cache_create(ctypes.byref(bad), -1, ctypes.byref(out)) == H.H2O_ERR_UNSUPPORTED
+    assert out.value is None  # *out is cleared on failure
+    assert H.h2o_cache_create(ctypes.byref(p), -5, ctypes.byref(out)) == H.H2O_ERR_INVALID_ARG
+    assert lib is H.load()
+
+
+def test_create_without_gpu_reports_hip_error(gpu_available):
+    if gpu_available:
+        pytest.skip("a GPU is present")
+    p = H.make_params(1, 1, 64, 2, 2, "f32")
+    out = ctypes.c_void_p()
+    st = H.h2o_cache_create(ctypes.byref(p), -1, ctypes.byref(out))
+    assert st in (H.H2O_ERR_HIP, H.H2O_ERR_OOM) and out.value is None
+    assert H.h2o_last_error() != ""
