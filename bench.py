@@ -1,0 +1,283 @@
+"""Benchmark of the H2O hot path on one MI355X.
+
+One *step* is the whole hot path over one batch of synthetic input: prefill of
+every layer's prompt (row statistics, column sums, select + fill), then every
+decode step of every layer (attention over the budgeted cache, score
+accumulation, eviction and in-place overwrite), in model order (all layers of
+token t before token t + 1).
+
+Default workload: an OPT-6.7B-shaped 32-layer stack of independent attention
+layers (32 heads, head_dim 128, bf16 K/V, fp32 arithmetic), batch 64, prompt
+2048, 1024 generated tokens, 20% budget (205 heavy hitters + 205 recent).
+Inputs are generated on the GPU before timing and stay resident in HBM.
+
+Prints ONE JSON line.  ``value`` is generated tokens per second over the whole
+step (prefill included); the line also carries decode-only and prefill rates,
+the dominant kernel's roofline and the CPU oracle's rate on a bounded sample.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "H2O decode tokens/s + achieved HBM GB/s (% peak) at OPT-6.7B shape, 20% budget"
+HBM_PEAK_GBS = 8000.0
+BF16_MFMA_PEAK_TFLOPS = 2500.0
+
+
+def decode_bytes_per_unit(c: int, d: int, s: int) -> int:
+    """Algorithmic HBM bytes of one decode step of one unit with c cached slots:
+    K and V slot reads (2cds), score read+write (8c), position read (4c), the new
+    token's q/k/v reads (3ds), its K/V slot write (2ds), fp32 output (4d)."""
+    return c * (2 * d * s + 12) + d * (5 * s + 4)
+
+
+def prefill_flops_per_unit(L: int, d: int) -> int:
+    """MFMA flops of the two causal QK^T passes over the L(L+1)/2 pairs."""
+    return 2 * L * (L + 1) * d
+
+
+def prefill_bytes_per_unit(L: int, k: int, d: int, s: int) -> int:
+    """Q and K read once (2Lds); kept V rows gathered, K/V slots written (3 min(L,k) ds); meta."""
+    kept = min(L, k)
+    return 2 * L * d * s + 3 * kept * d * s + 12 * kept
+
+
+TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "hbm_traffic-opt6.7b-32L-b64.md")
+
+
+def measured_traffic(workload: str):
+    """Decode HBM bytes per launch from the committed rocprofv3 counter summary,
+    or None when the workload differs or the kernel sources changed since."""
+    import hashlib
+
+    if workload != "opt6.7b-32L-b64" or not os.path.exists(TRAFFIC_PROFILE):
+        return None
+    fields = {}
+    for line in open(TRAFFIC_PROFILE):
+        if ":" in line and line.split(":", 1)[0] in ("decode_traffic_bytes_per_launch", "decode_source_sha256",
+                                                      "decode_source_files"):
+            k, v = line.split(":", 1)
+            fields[k] = v.strip()
+    if len(fields) != 3:
+        return None
+    h = hashlib.sha256()
+    for f in fields["decode_source_files"].split():
+        h.update(open(os.path.join(ROOT, f), "rb").read())
+    return float(fields["decode_traffic_bytes_per_launch"]) if h.hexdigest() == fields["decode_source_sha256"] else None
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=2)
+    ap.add_argument("--warmup", type=int, default=1)
+    ap.add_argument("--workload", default="opt6.7b-32L-b64")
+    ap.add_argument("--layers", type=int, default=None, help="override the layer count (profiling runs)")
+    ap.add_argument("--decode-steps", type=int, default=None, help="override decode steps (profiling runs)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-units", type=int, default=8, help="units in the CPU-oracle sample")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 1 GiB device copy (calibrates HBM byte counters)")
+    return ap.parse_args()
+
+
+def _warm(_):
+    import oracle  # noqa: F401 - import before timing
+    return 0
+
+
+def _cpu_unit(args):
+    """Worker: time the oracle on one unit (prefill + every decode step)."""
+    import time as _t
+
+    from oracle import run_unit
+
+    Q, K, V, L, kh, kr = args
+    t0 = _t.perf_counter()
+    run_unit(Q, K, V, L, kh, kr)
+    return _t.perf_counter() - t0
+
+
+def cpu_baseline(w, samples, procs):
+    import multiprocessing as mp
+
+    ctx = mp.get_context("spawn")
+    with ctx.Pool(procs) as pool:
+        pool.map(_warm, range(procs), chunksize=1)  # start every worker before timing
+        t0 = time.perf_counter()
+        per_unit = pool.map(_cpu_unit, samples, chunksize=1)
+        wall = time.perf_counter() - t0
+    units_total = w.layers * w.batch * w.heads
+    # units are independent and equally sized: whole-job time = mean unit time x units / cores
+    job_seconds = (sum(per_unit) / len(per_unit)) * units_total / procs
+    return {"value": w.batch * w.decode_steps / job_seconds, "unit": "tokens/s", "cores": procs,
+            "kind": "oracle",
+            "sample": f"{len(samples)} of {units_total} (layer, batch, head) units, each a full prefill of "
+                      f"{w.prompt_len} tokens plus {w.decode_steps} decode steps (float64 NumPy, one unit per "
+                      f"process, {procs} processes); mean {sum(per_unit) / len(per_unit):.3f} s per unit, "
+                      f"whole job extrapolated to {job_seconds:.0f} s; sample wall {wall:.2f} s"}
+
+
+def main():
+    a = parse()
+    if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: units are independent and the path has no cross-GPU step, "
+              "so only --gpus 1 is supported on this build.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from kv_cache_eviction_prefill_amd import H2OCache, h2o
+    from workload import get, scaled, synth
+
+    w = get(a.workload)
+    if a.layers is not None or a.decode_steps is not None:
+        w = scaled(w, layers=a.layers or w.layers, decode_steps=a.decode_steps or w.decode_steps)
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    B, H, d, L, T, NL = w.batch, w.heads, w.head_dim, w.prompt_len, w.decode_steps, w.layers
+    s = w.elem_bytes
+    lib = h2o.load()
+    stream = torch.cuda.current_stream(dev)
+    sp = stream.cuda_stream
+
+    # ---------------------------------------------------------------- inputs (untimed)
+    t_gen = time.time()
+    pre, dec = [], []
+    for layer in range(NL):
+        q, k, v = synth.torch_qkv(w, layer, 0, w.n_positions, dev)
+        pre.append(tuple(x[:, :, :L].contiguous() for x in (q, k, v)))
+        dec.append(tuple(x[:, :, L:].permute(2, 0, 1, 3).contiguous() for x in (q, k, v)))
+        del q, k, v
+    caches = [H2OCache(B, H, d, w.heavy_budget, w.recent_budget, dtype=w.dtype, max_prompt=L) for _ in range(NL)]
+    out = torch.empty((NL, B, H, d), dtype=torch.float32, device=dev)
+    ev = torch.empty((NL, B, H), dtype=torch.int32, device=dev)
+    torch.cuda.synchronize()
+    gen_s = time.time() - t_gen
+
+    # raw pointers: the timed loop only marshals integers into the C entry points
+    handles = [c.handle for c in caches]
+    pre_ptr = [tuple(x.data_ptr() for x in p) for p in pre]
+    dec_ptr = [[tuple(x[t].data_ptr() for x in dq) for t in range(T)] for dq in dec]
+    out_ptr = [out[l].data_ptr() for l in range(NL)]
+    ev_ptr = [ev[l].data_ptr() for l in range(NL)]
+    prefill_c, decode_c = lib.h2o_prefill, lib.h2o_decode_step
+
+    def one_step(evs=None):
+        if evs is not None:
+            evs[0].record(stream)
+        for l in range(NL):
+            st = prefill_c(handles[l], *pre_ptr[l], L, sp)
+            if st:
+                raise h2o.H2OError(st, "h2o_prefill", h2o.h2o_last_error())
+        if evs is not None:
+            evs[1].record(stream)
+        for t in range(T):
+            for l in range(NL):
+                qp, kp, vp = dec_ptr[l][t]
+                st = decode_c(handles[l], qp, kp, vp, out_ptr[l], ev_ptr[l], sp)
+                if st:
+                    raise h2o.H2OError(st, "h2o_decode_step", h2o.h2o_last_error())
+        if evs is not None:
+            evs[2].record(stream)
+
+    if a.copy_calibration:  # plain copy of known size for counter calibration
+        src = torch.empty(1 << 28, dtype=torch.float32, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    for _ in range(a.warmup):
+        one_step()
+    torch.cuda.synchronize()
+
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(a.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(a.steps):
+        one_step(events[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    t_pre = sum(e[0].elapsed_time(e[1]) for e in events) / 1e3
+    t_dec = sum(e[1].elapsed_time(e[2]) for e in events) / 1e3
+    t_all = sum(e[0].elapsed_time(e[2]) for e in events) / 1e3
+
+    # sanity: the caches hold min(k, L + T) entries and advanced by T
+    cnt, nxt, pl = caches[0].info()
+    assert (cnt, nxt, pl) == (min(L + T, w.k), L + T, L), (cnt, nxt, pl)
+    assert bool((ev >= -1).all())
+
+    K = a.steps
+    tokens = B * T * K
+    launches = NL * T * K
+    # slots read by decode step t: the cached count before it, min(k, L + t)
+    dec_bytes_launch = B * H * sum(decode_bytes_per_unit(min(w.k, L + t), d, s) for t in range(T)) / T
+    avg_dec_s = t_dec / launches
+    achieved = dec_bytes_launch / avg_dec_s / 1e9
+    pf_flops = NL * B * H * prefill_flops_per_unit(L, d) * K
+    pf_bytes = NL * B * H * prefill_bytes_per_unit(L, w.k, d, s) * K
+    res = {
+        "metric": METRIC,
+        "value": tokens / t_all,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": a.warmup,
+        "ms_per_step": 1e3 * t_all / K,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "layers": NL, "batch": B, "heads": H, "head_dim": d,
+                   "prompt_len": L, "decode_steps": T, "heavy_budget": w.heavy_budget,
+                   "recent_budget": w.recent_budget, "storage": w.dtype, "accumulate": "fp32"},
+        "roofline": {"kernel": "decode_kernel<bf16,128>", "bound": "hbm", "achieved": achieved,
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic(w.name) if a.layers is None else None,
+                     "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
+                     "bytes_per_launch": dec_bytes_launch, "avg_launch_us": 1e6 * avg_dec_s,
+                     "launches": launches},
+        "decode": {"tokens_per_s": tokens / t_dec, "ms_per_token_step": 1e3 * t_dec / (T * K),
+                   "GBps": achieved, "hbm_frac": achieved / HBM_PEAK_GBS},
+        "prefill": {"tokens_per_s": B * L * K / t_pre, "ms": 1e3 * t_pre / K,
+                    "mfma_tflops": pf_flops / t_pre / 1e12,
+                    "mfma_frac": pf_flops / t_pre / 1e12 / BF16_MFMA_PEAK_TFLOPS,
+                    "alg_GBps": pf_bytes / t_pre / 1e9},
+        "timing": {"wall_s": wall, "event_s": t_all, "input_gen_s": gen_s},
+    }
+
+    if not a.no_cpu_baseline:
+        g = np.random.default_rng(7)
+        picks = [(int(g.integers(NL)), int(g.integers(B)), int(g.integers(H))) for _ in range(a.cpu_units)]
+        samples = []
+        for (l, b, h) in picks:
+            qf = torch.cat([pre[l][0][b, h], dec[l][0][:, b, h]]).float().cpu().numpy()
+            kf = torch.cat([pre[l][1][b, h], dec[l][1][:, b, h]]).float().cpu().numpy()
+            vf = torch.cat([pre[l][2][b, h], dec[l][2][:, b, h]]).float().cpu().numpy()
+            samples.append((qf, kf, vf, L, w.heavy_budget, w.recent_budget))
+        procs = min(len(os.sched_getaffinity(0)), 16, len(samples))
+        os.environ.setdefault("OMP_NUM_THREADS", "1")
+        os.environ.setdefault("OPENBLAS_NUM_THREADS", "1")
+        res["cpu_baseline"] = cpu_baseline(w, samples, procs)
+    else:
+        res["cpu_baseline"] = None
+
+    for cch in caches:
+        cch.close()
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()
