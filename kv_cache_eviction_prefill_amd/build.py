@@ -23,8 +23,10 @@ LIB = os.path.join(PKG, "libh2o.so")
 ARCH = "gfx950"
 # Packed fp32 instructions stay off: hipcc -O3 would otherwise form them from
 # plain float code.
+# MFMA results go straight to VGPRs (no AGPR round trips in the softmax epilogues).
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+          "-mllvm", "-amdgpu-mfma-vgpr-form",
           "-I", INCLUDE, "-I", CSRC]
 
 

@@ -30,7 +30,6 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kTile = 32;              // MFMA tile edge (rows and columns)
-constexpr int kRowsPerBlock = 128;     // 4 waves x 32
 constexpr uint64_t kNoKey = ~0ull;
 
 __device__ inline bf16x8 ld_bf16x8(const bf16_t* p) { return __builtin_bit_cast(bf16x8, ld16(p)); }
@@ -39,116 +38,249 @@ __device__ inline bf16x8 ld_bf16x8(const bf16_t* p) { return __builtin_bit_cast(
 // (the column is lane % 32).
 __device__ inline int acc_row(int i, int lane) { return 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3); }
 
-// ------------------------------------------------------------------ pass 1, bf16 (MFMA)
+// ------------------------------------------------------------------ bf16 MFMA passes
+// A block owns kBlockRows consecutive rows (pass 1: queries, pass 2: keys) of
+// one unit; each of its 4 waves owns 64 of them as two 32-row subtiles whose
+// operands stay in registers.  The other operand streams through LDS in 32-row
+// tiles (double-buffered, rows padded by 16 bytes so the fragment reads of 32
+// consecutive rows spread over the banks), loaded cooperatively with 16-byte
+// global loads.  The blocks of one unit are numbered so they land on the same
+// XCD (blocks are dealt to the 8 XCDs round-robin), keeping the unit's Q and K
+// in that XCD's L2 while its blocks run.
+constexpr int kBlockRows = 256;
+constexpr int kWaveRows = 64;
+constexpr int kXcds = 8;
+
 template <int D>
-__global__ __launch_bounds__(kThreads) void rowstats_bf16(PrefillArgs a) {
-  const int nblk = (a.L + kRowsPerBlock - 1) / kRowsPerBlock;
-  const int unit = blockIdx.x / nblk;
-  const int qb = (nblk - 1 - blockIdx.x % nblk) * kRowsPerBlock;  // longest rows first
-  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
-  const int q0 = qb + wave * kTile;
-  if (q0 >= a.L) return;
-  const bf16_t* Qu = static_cast<const bf16_t*>(a.q) + static_cast<size_t>(unit) * a.L * D;
-  const bf16_t* Ku = static_cast<const bf16_t*>(a.k) + static_cast<size_t>(unit) * a.L * D;
-  const int lrow = lane & 31, lk = (lane >> 5) * 8;
-  const int qi = q0 + lrow;
-  const int qrow = min(qi, a.L - 1);
+struct TileCfg {
+  static constexpr int kLdw = D + 8;                     // LDS row stride (bf16 elements)
+  static constexpr int kChunksPerRow = D * 2 / 16;       // 16-byte chunks per row
+  static constexpr int kChunks = kTile * kChunksPerRow;  // per 32-row tile
+  static constexpr int kPerThread = kChunks / kThreads;  // 2 (d = 128) or 1 (d = 64)
+  static_assert(kChunks % kThreads == 0, "tile must split evenly over the block");
+};
 
-  bf16x8 bq[D / 16];
-#pragma unroll
-  for (int kk = 0; kk < D / 16; ++kk) bq[kk] = ld_bf16x8(Qu + static_cast<size_t>(qrow) * D + lk + 16 * kk);
+// (unit, row block) of this block; false for the padding blocks of the last group.
+__device__ inline bool block_coords(int nblk, int units, int* unit, int* blk) {
+  const int b = blockIdx.x;
+  const int slot = b / kXcds;
+  *unit = (slot / nblk) * kXcds + b % kXcds;
+  *blk = slot % nblk;
+  return *unit < units;
+}
 
-  float m = -INFINITY, l = 0.f;  // m in raw q.k units
-  const int qmax = min(q0 + kTile - 1, a.L - 1);
-  for (int k0 = 0; k0 <= qmax; k0 += kTile) {
-    const int krow = min(k0 + lrow, a.L - 1);
-    bf16x8 ak[D / 16];
+template <int D>
+__device__ inline void tile_gload(const bf16_t* base, int row0, int L, uint4* pre) {
+  using C = TileCfg<D>;
 #pragma unroll
-    for (int kk = 0; kk < D / 16; ++kk) ak[kk] = ld_bf16x8(Ku + static_cast<size_t>(krow) * D + lk + 16 * kk);
-    floatx16 acc = {};
-#pragma unroll
-    for (int kk = 0; kk < D / 16; ++kk) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak[kk], bq[kk], acc, 0, 0, 0);
-    // acc[i] = q_qi . k_(k0 + acc_row(i, lane))
-    const bool diag = (k0 + kTile - 1 > q0);
-    float v[16];
-    float tm = -INFINITY;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const bool ok = !diag || (k0 + acc_row(i, lane) <= qi);
-      v[i] = ok ? acc[i] : -INFINITY;
-      tm = fmaxf(tm, v[i]);
-    }
-    if (tm != -INFINITY) {
-      const float mn = fmaxf(m, tm);
-      const float mc = mn * a.c2;
-      float sum = 0.f;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) sum += fast_exp2(fmaf(v[i], a.c2, -mc));
-      l = fmaf(l, fast_exp2((m - mn) * a.c2), sum);
-      m = mn;
-    }
-  }
-  // lanes l and l^32 saw disjoint key subsets of the same query
-  const float m2 = __shfl_xor(m, 32, kWave), l2 = __shfl_xor(l, 32, kWave);
-  const float mn = fmaxf(m, m2);
-  const float lt = l * fast_exp2((m - mn) * a.c2) + l2 * fast_exp2((m2 - mn) * a.c2);
-  if (lane < 32 && qi < a.L) {
-    const size_t o = static_cast<size_t>(unit) * a.Lpad + qi;
-    a.row_max[o] = mn * a.scale;
-    a.row_sum[o] = lt;
-    a.row_lse2[o] = fmaf(mn, a.c2, log2f(lt));
+  for (int c = 0; c < C::kPerThread; ++c) {
+    const int ch = threadIdx.x + kThreads * c;
+    const int r = ch / C::kChunksPerRow, cc = ch % C::kChunksPerRow;
+    const int row = row0 + r;
+    pre[c] = row < L ? ld16(base + static_cast<size_t>(row) * D + cc * 8) : make_uint4(0u, 0u, 0u, 0u);
   }
 }
 
-// ------------------------------------------------------------------ pass 2, bf16 (MFMA)
 template <int D>
-__global__ __launch_bounds__(kThreads) void colsum_bf16(PrefillArgs a) {
-  const int nblk = (a.L + kRowsPerBlock - 1) / kRowsPerBlock;
-  const int unit = blockIdx.x / nblk;
-  const int kb = (blockIdx.x % nblk) * kRowsPerBlock;  // low keys (longest columns) first
+__device__ inline void tile_lstore(bf16_t* tile, const uint4* pre) {
+  using C = TileCfg<D>;
+#pragma unroll
+  for (int c = 0; c < C::kPerThread; ++c) {
+    const int ch = threadIdx.x + kThreads * c;
+    const int r = ch / C::kChunksPerRow, cc = ch % C::kChunksPerRow;
+    st16(tile + r * C::kLdw + cc * 8, pre[c]);
+  }
+}
+
+// Fragment of a 32-row LDS tile as an MFMA A operand (row = lane % 32).
+template <int D>
+__device__ inline void tile_frag(const bf16_t* tile, int lane, bf16x8* f) {
+  const bf16_t* p = tile + (lane & 31) * TileCfg<D>::kLdw + (lane >> 5) * 8;
+#pragma unroll
+  for (int kk = 0; kk < D / 16; ++kk) f[kk] = __builtin_bit_cast(bf16x8, ld16(p + 16 * kk));
+}
+
+// Row fragment straight from global memory (an operand that stays in registers).
+template <int D>
+__device__ inline void row_frag(const bf16_t* base, int row, int L, int lane, bf16x8* f) {
+  const bf16_t* p = base + static_cast<size_t>(min(row, L - 1)) * D + (lane >> 5) * 8;
+#pragma unroll
+  for (int kk = 0; kk < D / 16; ++kk) f[kk] = ld_bf16x8(p + 16 * kk);
+}
+
+// Pass 1: S^T = K Q^T per 32x32 tile, so a lane holds 16 logits of one query and
+// the online row max / row sum stay inside the lane.
+template <int D>
+__global__ __launch_bounds__(kThreads) void rowstats_bf16(PrefillArgs a, int nblk, int units) {
+  __shared__ __align__(16) bf16_t sK[2][kTile * TileCfg<D>::kLdw];
+  int unit, blk;
+  if (!block_coords(nblk, units, &unit, &blk)) return;
+  const int L = a.L;
+  const int qb = (nblk - 1 - blk) * kBlockRows;  // longest rows first
   const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
-  const int k0 = kb + wave * kTile;
-  if (k0 >= a.L) return;
-  const bf16_t* Qu = static_cast<const bf16_t*>(a.q) + static_cast<size_t>(unit) * a.L * D;
-  const bf16_t* Ku = static_cast<const bf16_t*>(a.k) + static_cast<size_t>(unit) * a.L * D;
-  const float* lse = a.row_lse2 + static_cast<size_t>(unit) * a.Lpad;
-  const int lrow = lane & 31, lk = (lane >> 5) * 8;
-  const int key = k0 + lrow;
-  const int krow = min(key, a.L - 1);
+  const int qw = qb + wave * kWaveRows;
+  const bf16_t* Qu = static_cast<const bf16_t*>(a.q) + static_cast<size_t>(unit) * L * D;
+  const bf16_t* Ku = static_cast<const bf16_t*>(a.k) + static_cast<size_t>(unit) * L * D;
 
-  bf16x8 bk[D / 16];
+  bf16x8 bq[2][D / 16];
 #pragma unroll
-  for (int kk = 0; kk < D / 16; ++kk) bk[kk] = ld_bf16x8(Ku + static_cast<size_t>(krow) * D + lk + 16 * kk);
+  for (int s = 0; s < 2; ++s) row_frag<D>(Qu, qw + 32 * s + (lane & 31), L, lane, bq[s]);
 
-  float cs = 0.f;
-  for (int q0 = k0; q0 < a.L; q0 += kTile) {
-    const int qrow = min(q0 + lrow, a.L - 1);
-    bf16x8 aq[D / 16];
+  const int ntile = (min(qb + kBlockRows, L) - 1) / kTile + 1;
+  // a finite floor instead of -inf keeps (m - max) finite before a lane sees its first key
+  float m[2] = {-1e30f, -1e30f}, l[2] = {0.f, 0.f};
+  uint4 pre[TileCfg<D>::kPerThread];
+  tile_gload<D>(Ku, 0, L, pre);
+  tile_lstore<D>(sK[0], pre);
+  __syncthreads();
+  for (int t = 0; t < ntile; ++t) {
+    const int k0 = t * kTile;
+    if (t + 1 < ntile) tile_gload<D>(Ku, k0 + kTile, L, pre);
+    // the wave has work while its last query is at or after the tile's first key;
+    // a subtile entirely above the diagonal is masked to -inf and leaves (m, l) as is
+    if (qw < L && k0 <= qw + kWaveRows - 1) {
+      bf16x8 ak[D / 16];
+      tile_frag<D>(sK[t & 1], lane, ak);
+      floatx16 acc[2];
+      acc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak[0], bq[0][0], floatx16{}, 0, 0, 0);
+      acc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak[0], bq[1][0], floatx16{}, 0, 0, 0);
 #pragma unroll
-    for (int kk = 0; kk < D / 16; ++kk) aq[kk] = ld_bf16x8(Qu + static_cast<size_t>(qrow) * D + lk + 16 * kk);
-    floatx16 acc = {};
-#pragma unroll
-    for (int kk = 0; kk < D / 16; ++kk) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq[kk], bk[kk], acc, 0, 0, 0);
-    // acc[i] = q_(q0 + acc_row(i, lane)) . k_key; the row normalisers of those
-    // queries sit in 4 runs of 4 consecutive rows
-    float4 lv[4];
-#pragma unroll
-    for (int t = 0; t < 4; ++t) lv[t] = *reinterpret_cast<const float4*>(lse + q0 + 8 * t + 4 * (lane >> 5));
-    const bool edge = (q0 == k0) || (q0 + kTile > a.L);
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const float4& f = lv[i >> 2];
-      const float ls = (i & 3) == 0 ? f.x : (i & 3) == 1 ? f.y : (i & 3) == 2 ? f.z : f.w;
-      float p = fast_exp2(fmaf(acc[i], a.c2, -ls));
-      if (edge) {
-        const int qq = q0 + acc_row(i, lane);
-        p = (qq >= key && qq < a.L) ? p : 0.f;
+      for (int kk = 1; kk < D / 16; ++kk) {
+        acc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak[kk], bq[0][kk], acc[0], 0, 0, 0);
+        acc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak[kk], bq[1][kk], acc[1], 0, 0, 0);
       }
-      cs += p;
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        const int q = qw + 32 * s + (lane & 31);
+        float v[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) v[i] = acc[s][i];
+        if (k0 + kTile - 1 > qw + 32 * s) {  // tile reaches past this subtile's first query
+#pragma unroll
+          for (int i = 0; i < 16; ++i) v[i] = k0 + acc_row(i, lane) <= q ? v[i] : -INFINITY;
+        }
+        float tm = v[0];
+#pragma unroll
+        for (int i = 1; i < 16; ++i) tm = fmaxf(tm, v[i]);
+        const float mn = fmaxf(m[s], tm);
+        const float mc = mn * a.c2;
+        float sum = 0.f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) sum += fast_exp2(fmaf(v[i], a.c2, -mc));
+        l[s] = fmaf(l[s], fast_exp2((m[s] - mn) * a.c2), sum);
+        m[s] = mn;
+      }
+    }
+    if (t + 1 < ntile) tile_lstore<D>(sK[(t + 1) & 1], pre);
+    __syncthreads();
+  }
+  // lanes l and l^32 saw disjoint key subsets of the same query
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+    const float m2 = __shfl_xor(m[s], 32, kWave), l2 = __shfl_xor(l[s], 32, kWave);
+    const float mn = fmaxf(m[s], m2);
+    const float lt = l[s] * fast_exp2((m[s] - mn) * a.c2) + l2 * fast_exp2((m2 - mn) * a.c2);
+    const int q = qw + 32 * s + lane;
+    if (lane < 32 && q < L) {
+      const size_t o = static_cast<size_t>(unit) * a.Lpad + q;
+      a.row_max[o] = mn * a.scale;
+      a.row_sum[o] = lt;
+      a.row_lse2[o] = fmaf(mn, a.c2, log2f(lt));
     }
   }
-  cs += __shfl_xor(cs, 32, kWave);
-  if (lane < 32 && key < a.L) a.col_sum[static_cast<size_t>(unit) * a.Lpad + key] = cs;
+}
+
+// Pass 2: S = Q K^T per 32x32 tile, so a lane holds 16 rows of one key column;
+// c_j accumulates exp2(S c2 - lse2_r) over the rows r >= j.
+template <int D>
+__global__ __launch_bounds__(kThreads) void colsum_bf16(PrefillArgs a, int nblk, int units) {
+  __shared__ __align__(16) bf16_t sQ[2][kTile * TileCfg<D>::kLdw];
+  __shared__ __align__(16) float sL[2][kTile];
+  int unit, blk;
+  if (!block_coords(nblk, units, &unit, &blk)) return;
+  const int L = a.L;
+  const int kb = blk * kBlockRows;  // low keys (longest columns) first
+  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+  const int kw = kb + wave * kWaveRows;
+  const bf16_t* Qu = static_cast<const bf16_t*>(a.q) + static_cast<size_t>(unit) * L * D;
+  const bf16_t* Ku = static_cast<const bf16_t*>(a.k) + static_cast<size_t>(unit) * L * D;
+  const float* lse = a.row_lse2 + static_cast<size_t>(unit) * a.Lpad;
+
+  bf16x8 bk[2][D / 16];
+#pragma unroll
+  for (int s = 0; s < 2; ++s) row_frag<D>(Ku, kw + 32 * s + (lane & 31), L, lane, bk[s]);
+
+  const int t0 = kb / kTile, tn = (L - 1) / kTile;
+  float cs[2] = {0.f, 0.f};
+  uint4 pre[TileCfg<D>::kPerThread];
+  float lpre = 0.f;
+  auto lse_load = [&](int row0) {
+    if (threadIdx.x < kTile) lpre = row0 + static_cast<int>(threadIdx.x) < L ? lse[row0 + threadIdx.x] : 0.f;
+  };
+  tile_gload<D>(Qu, t0 * kTile, L, pre);
+  lse_load(t0 * kTile);
+  tile_lstore<D>(sQ[0], pre);
+  if (threadIdx.x < kTile) sL[0][threadIdx.x] = lpre;
+  __syncthreads();
+  for (int t = t0; t <= tn; ++t) {
+    const int q0 = t * kTile;
+    const int buf = (t - t0) & 1;
+    if (t < tn) {
+      tile_gload<D>(Qu, q0 + kTile, L, pre);
+      lse_load(q0 + kTile);
+    }
+    // the wave has work once the tile's last query reaches its first key; a
+    // subtile whose keys all follow the tile's queries is masked to zero
+    if (kw < L && q0 + kTile - 1 >= kw) {
+      bf16x8 aq[D / 16];
+      tile_frag<D>(sQ[buf], lane, aq);
+      floatx16 acc[2];
+      acc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq[0], bk[0][0], floatx16{}, 0, 0, 0);
+      acc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq[0], bk[1][0], floatx16{}, 0, 0, 0);
+#pragma unroll
+      for (int kk = 1; kk < D / 16; ++kk) {
+        acc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq[kk], bk[0][kk], acc[0], 0, 0, 0);
+        acc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq[kk], bk[1][kk], acc[1], 0, 0, 0);
+      }
+      // the 16 rows of this lane sit in 4 runs of 4 consecutive rows
+      float4 lv[4];
+#pragma unroll
+      for (int g = 0; g < 4; ++g) lv[g] = *reinterpret_cast<const float4*>(&sL[buf][8 * g + 4 * (lane >> 5)]);
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        const int key = kw + 32 * s + (lane & 31);
+        float p[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const float4& f = lv[i >> 2];
+          const float ls = (i & 3) == 0 ? f.x : (i & 3) == 1 ? f.y : (i & 3) == 2 ? f.z : f.w;
+          p[i] = fast_exp2(fmaf(acc[s][i], a.c2, -ls));
+        }
+        if (q0 < kw + 32 * s + 32 || q0 + kTile > L) {  // diagonal or ragged last tile
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int qq = q0 + acc_row(i, lane);
+            p[i] = (qq >= key && qq < L) ? p[i] : 0.f;
+          }
+        }
+        float sum = 0.f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) sum += p[i];
+        cs[s] += sum;
+      }
+    }
+    if (t < tn) {
+      tile_lstore<D>(sQ[buf ^ 1], pre);
+      if (threadIdx.x < kTile) sL[buf ^ 1][threadIdx.x] = lpre;
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+    const float c = cs[s] + __shfl_xor(cs[s], 32, kWave);
+    const int key = kw + 32 * s + lane;
+    if (lane < 32 && key < L) a.col_sum[static_cast<size_t>(unit) * a.Lpad + key] = c;
+  }
 }
 
 // ------------------------------------------------------------------ fp32 (VALU) passes
@@ -330,11 +462,13 @@ hipError_t launch_select(const PrefillArgs& a, int units, hipStream_t s) {
 
 template <int D>
 hipError_t launch_bf16(const PrefillArgs& a, int units, hipStream_t s) {
-  const int nblk = (a.L + kRowsPerBlock - 1) / kRowsPerBlock;
-  hipLaunchKernelGGL((rowstats_bf16<D>), dim3(units * nblk), dim3(kThreads), 0, s, a);
+  const int nblk = (a.L + kBlockRows - 1) / kBlockRows;
+  const int groups = (units + kXcds - 1) / kXcds;
+  const dim3 grid(groups * kXcds * nblk);
+  hipLaunchKernelGGL((rowstats_bf16<D>), grid, dim3(kThreads), 0, s, a, nblk, units);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((colsum_bf16<D>), dim3(units * nblk), dim3(kThreads), 0, s, a);
+  hipLaunchKernelGGL((colsum_bf16<D>), grid, dim3(kThreads), 0, s, a, nblk, units);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   return launch_select<bf16_t, D>(a, units, s);
