@@ -31,7 +31,8 @@ namespace h2o {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kUnroll = 4;
+constexpr int kUnroll = 2;    // slots in flight per row group (K and V each)
+constexpr int kPrefetch = 2;  // score-pass slots per thread whose metadata is loaded up front
 constexpr uint64_t kNoKey = ~0ull;
 constexpr int kNewSlot = -2;
 
@@ -41,16 +42,19 @@ struct Layout {
   static constexpr int LPR = D / EPL;           // lanes per K/V row
   static constexpr int NG = kThreads / LPR;     // row groups per block
   static_assert((LPR & (LPR - 1)) == 0 && LPR <= kWave, "row must map to a power-of-two lane group");
+  static_assert(LPR >= kUnroll, "one lane per in-flight slot stores its logit");
 };
 
+// 8 waves per SIMD: all blocks of a 2048-unit launch are resident at once.
 template <typename T, int D, bool SPLIT>
-__global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(kThreads, 8) void decode_kernel(DecodeArgs a) {
   using Lay = Layout<T, D>;
   constexpr int EPL = Lay::EPL, LPR = Lay::LPR, NG = Lay::NG;
   extern __shared__ float s_logit[];  // single-block path: [k + 1], new token at index k
-  __shared__ float s_m[NG], s_l[NG], s_w[NG];
+  __shared__ float s_m[NG], s_l[NG];
   __shared__ float s_o[NG][D];
   __shared__ uint64_t s_key[kThreads / kWave];
+  __shared__ uint4 s_knew[LPR], s_vnew[LPR];
   __shared__ int s_slot;
   __shared__ int s_last;
 
@@ -67,9 +71,35 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
   const T* kn = static_cast<const T*>(a.knew) + static_cast<size_t>(unit) * D;
   const T* vn = static_cast<const T*>(a.vnew) + static_cast<size_t>(unit) * D;
   float* glog = SPLIT ? a.logits + static_cast<size_t>(unit) * (a.k + 1) : nullptr;
+  float* sc = a.score + static_cast<size_t>(unit) * a.k;
+  float* cp = a.comp + static_cast<size_t>(unit) * a.k;
+  int32_t* ps = a.pos + static_cast<size_t>(unit) * a.k;
 
   float qf[EPL];
   Elem<T>::unpack(ld16(qn + r * EPL), qf);
+  // The new token's rows are loaded once: group 0 attends to them and parks them
+  // in LDS for the overwrite at the end.
+  uint4 kn_raw = make_uint4(0u, 0u, 0u, 0u), vn_raw = make_uint4(0u, 0u, 0u, 0u);
+  if (g == 0) {
+    kn_raw = ld16(kn + r * EPL);
+    vn_raw = ld16(vn + r * EPL);
+    s_knew[r] = kn_raw;
+    s_vnew[r] = vn_raw;
+  }
+  // Score-pass metadata of this thread's first slots: loaded now, it arrives
+  // under the K/V stream instead of after it.
+  float pf_s[kPrefetch], pf_c[kPrefetch];
+  int32_t pf_p[kPrefetch];
+  if (!SPLIT) {
+#pragma unroll
+    for (int i = 0; i < kPrefetch; ++i) {
+      const int j = tid + i * kThreads;
+      const bool ok = j < a.count;
+      pf_s[i] = ok ? sc[j] : 0.f;
+      pf_c[i] = ok ? cp[j] : 0.f;
+      pf_p[i] = ok ? ps[j] : 0;
+    }
+  }
 
   float m = -INFINITY, l = 0.f, o[EPL];
 #pragma unroll
@@ -79,8 +109,8 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
   // block seeds its running softmax with it.
   if (split == 0 && g == 0) {
     float kf[EPL], vf[EPL];
-    Elem<T>::unpack(ld16(kn + r * EPL), kf);
-    Elem<T>::unpack(ld16(vn + r * EPL), vf);
+    Elem<T>::unpack(kn_raw, kf);
+    Elem<T>::unpack(vn_raw, vf);
     float dot = 0.f;
 #pragma unroll
     for (int e = 0; e < EPL; ++e) dot = fmaf(qf[e], kf[e], dot);
@@ -116,14 +146,15 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
       x[u] = (base + u * NG < s1) ? dot * a.c2 : -INFINITY;
       mx = fmaxf(mx, x[u]);
     }
-    if (r == 0) {
+    // lane u of the group stores the logit of in-flight slot u
+    if (r < kUnroll) {
+      const int j = base + r * NG;
+      float xr = x[0];
 #pragma unroll
-      for (int u = 0; u < kUnroll; ++u) {
-        const int j = base + u * NG;
-        if (j < s1) {
-          if (SPLIT) glog[j] = x[u];
-          else s_logit[j] = x[u];
-        }
+      for (int u = 1; u < kUnroll; ++u) xr = r == u ? x[u] : xr;
+      if (j < s1) {
+        if (SPLIT) glog[j] = xr;
+        else s_logit[j] = xr;
       }
     }
     const float alpha = fast_exp2(m - mx);
@@ -142,7 +173,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
     m = mx;
   }
 
-  // ---- merge the row groups of this block
+  // ---- merge the row groups of this block (every thread derives the weights)
   if (r == 0) {
     s_m[g] = m;
     s_l[g] = l;
@@ -151,33 +182,25 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
   for (int e = 0; e < EPL; ++e) s_o[g][r * EPL + e] = o[e];
   __syncthreads();
   float M = -INFINITY;
-#pragma unroll
+#pragma unroll 8
   for (int t = 0; t < NG; ++t) M = fmaxf(M, s_m[t]);
-  if (tid < NG) s_w[tid] = fast_exp2(s_m[tid] - M);
-  __syncthreads();
-  float Ls = 0.f;
-#pragma unroll
-  for (int t = 0; t < NG; ++t) Ls = fmaf(s_l[t], s_w[t], Ls);
+  float Ls = 0.f, acc = 0.f;
+#pragma unroll 8
+  for (int t = 0; t < NG; ++t) {
+    const float wt = fast_exp2(s_m[t] - M);
+    Ls = fmaf(s_l[t], wt, Ls);
+    if (tid < D) acc = fmaf(s_o[t][tid], wt, acc);
+  }
 
   if constexpr (!SPLIT) {
-    if (tid < D) {
-      float acc = 0.f;
-#pragma unroll
-      for (int t = 0; t < NG; ++t) acc = fmaf(s_o[t][tid], s_w[t], acc);
-      a.out[static_cast<size_t>(unit) * D + tid] = acc / Ls;
-    }
+    if (tid < D) a.out[static_cast<size_t>(unit) * D + tid] = acc / Ls;
   } else {
     float* pp = a.part + (static_cast<size_t>(unit) * a.nsplit + split) * (2 + D);
     if (tid == 0) {
       pp[0] = M;
       pp[1] = Ls;
     }
-    if (tid < D) {
-      float acc = 0.f;
-#pragma unroll
-      for (int t = 0; t < NG; ++t) acc = fmaf(s_o[t][tid], s_w[t], acc);
-      pp[2 + tid] = acc;
-    }
+    if (tid < D) pp[2 + tid] = acc;
     // Publish the partial and the logits, then count arrivals; the last block
     // of the unit finishes the step.
     __threadfence();
@@ -192,47 +215,57 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
     const float* pu = a.part + static_cast<size_t>(unit) * a.nsplit * (2 + D);
     float Mg = -INFINITY;
     for (int s = 0; s < a.nsplit; ++s) Mg = fmaxf(Mg, pu[s * (2 + D)]);
-    float Lg = 0.f;
-    for (int s = 0; s < a.nsplit; ++s) Lg = fmaf(pu[s * (2 + D) + 1], fast_exp2(pu[s * (2 + D)] - Mg), Lg);
-    if (tid < D) {
-      float acc = 0.f;
-      for (int s = 0; s < a.nsplit; ++s)
-        acc = fmaf(pu[s * (2 + D) + 2 + tid], fast_exp2(pu[s * (2 + D)] - Mg), acc);
-      a.out[static_cast<size_t>(unit) * D + tid] = acc / Lg;
+    float Lg = 0.f, og = 0.f;
+    for (int s = 0; s < a.nsplit; ++s) {
+      const float ws = fast_exp2(pu[s * (2 + D)] - Mg);
+      Lg = fmaf(pu[s * (2 + D) + 1], ws, Lg);
+      if (tid < D) og = fmaf(pu[s * (2 + D) + 2 + tid], ws, og);
     }
+    if (tid < D) a.out[static_cast<size_t>(unit) * D + tid] = og / Lg;
     if (tid == 0) a.counters[unit] = 0u;  // ready for the next step
     M = Mg;
     Ls = Lg;
+
   }
 
   // ---- score accumulation over G, then at most one eviction
   const float invL = 1.f / Ls;
   const int cnt = a.count;
   const bool full = (cnt == a.k);
-  float* sc = a.score + static_cast<size_t>(unit) * a.k;
-  float* cp = a.comp + static_cast<size_t>(unit) * a.k;
-  int32_t* ps = a.pos + static_cast<size_t>(unit) * a.k;
   const float* lg = SPLIT ? glog : s_logit;
 
   uint64_t best = kNoKey;
   int best_slot = -1;
-  for (int j = tid; j < cnt; j += kThreads) {
+  for (int i = 0, j = tid; j < cnt; ++i, j += kThreads) {
     const float w = fast_exp2(lg[j] - M) * invL;
-    float s = sc[j], c = cp[j];
-    const float y = w - c;  // Kahan-compensated add of this step's weight
-    const float t = s + y;
-    c = (t - s) - y;
-    s = t;
-    sc[j] = s;
-    cp[j] = c;
-    if (full) {
-      const int32_t p = ps[j];
-      if (p <= a.cand_limit) {
-        const uint64_t key = evict_key(s, p);
-        if (key < best) {
-          best = key;
-          best_slot = j;
-        }
+    float sj, cj;
+    int32_t pj;
+    if (!SPLIT && i < kPrefetch) {
+      sj = pf_s[0];
+      cj = pf_c[0];
+      pj = pf_p[0];
+#pragma unroll
+      for (int t = 1; t < kPrefetch; ++t) {
+        sj = i == t ? pf_s[t] : sj;
+        cj = i == t ? pf_c[t] : cj;
+        pj = i == t ? pf_p[t] : pj;
+      }
+    } else {
+      sj = sc[j];
+      cj = cp[j];
+      pj = ps[j];
+    }
+    const float y = w - cj;  // Kahan-compensated add of this step's weight
+    const float t = sj + y;
+    cj = (t - sj) - y;
+    sj = t;
+    sc[j] = sj;
+    cp[j] = cj;
+    if (full && pj <= a.cand_limit) {
+      const uint64_t key = evict_key(sj, pj);
+      if (key < best) {
+        best = key;
+        best_slot = j;
       }
     }
   }
@@ -248,7 +281,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
         best_slot = kNewSlot;
       }
     }
-    const uint64_t wm = wave_min_u64(best);
+    const uint64_t wm = wave_min_key(best);
     if ((tid & (kWave - 1)) == 0) s_key[tid / kWave] = wm;
     __syncthreads();
     uint64_t bm = s_key[0];
@@ -265,11 +298,11 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
       cp[dst] = 0.f;
       ps[dst] = a.new_pos;
     }
-    if (g == 0) {
+    if (g == 0) {  // s_knew/s_vnew were written before the merge barrier
       T* kd = static_cast<T*>(a.kslots) + (static_cast<size_t>(unit) * a.k + dst) * D;
       T* vd = static_cast<T*>(a.vslots) + (static_cast<size_t>(unit) * a.k + dst) * D;
-      st16(kd + r * EPL, ld16(kn + r * EPL));
-      st16(vd + r * EPL, ld16(vn + r * EPL));
+      st16(kd + r * EPL, s_knew[r]);
+      st16(vd + r * EPL, s_vnew[r]);
     }
   }
   if (tid == 0 && a.evicted != nullptr) a.evicted[unit] = ev;

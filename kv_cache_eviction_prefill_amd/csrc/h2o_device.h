@@ -58,27 +58,71 @@ __device__ inline uint4 ld16_stream(const void* p) {
 
 __device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// Sum over aligned groups of G lanes (G a power of two <= 64).
+// DPP lane moves inside rows of 16 lanes: register-to-register, no LDS traffic.
+constexpr int kDppQuadXor1 = 0xB1;       // quad_perm [1,0,3,2]
+constexpr int kDppQuadXor2 = 0x4E;       // quad_perm [2,3,0,1]
+constexpr int kDppRowRor1 = 0x121;       // row_ror:1
+constexpr int kDppRowRor2 = 0x122;       // row_ror:2
+constexpr int kDppRowRor4 = 0x124;       // row_ror:4
+constexpr int kDppRowRor8 = 0x128;       // row_ror:8
+constexpr int kDppRowHalfMirror = 0x141; // reverse each half-row of 8 lanes
+
+template <int CTRL>
+__device__ inline int dpp_i(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, false);
+}
+template <int CTRL>
+__device__ inline float dpp_f(float v) {
+  return __int_as_float(dpp_i<CTRL>(__float_as_int(v)));
+}
+
+// Sum over aligned groups of G lanes (G a power of two <= 64); every lane of the
+// group receives the total.  Groups of 16 and 8 use DPP.
 template <int G>
 __device__ inline float group_sum(float v) {
+  if constexpr (G == 16) {
+    v += dpp_f<kDppRowRor8>(v);
+    v += dpp_f<kDppRowRor4>(v);
+    v += dpp_f<kDppRowRor2>(v);
+    v += dpp_f<kDppRowRor1>(v);
+  } else if constexpr (G == 8) {
+    v += dpp_f<kDppQuadXor1>(v);
+    v += dpp_f<kDppQuadXor2>(v);
+    v += dpp_f<kDppRowHalfMirror>(v);
+  } else {
 #pragma unroll
-  for (int m = G / 2; m >= 1; m >>= 1) v += __shfl_xor(v, m, kWave);
+    for (int m = G / 2; m >= 1; m >>= 1) v += __shfl_xor(v, m, kWave);
+  }
   return v;
 }
 
-__device__ inline uint64_t wave_min_u64(uint64_t v) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) {
-    uint64_t o = __shfl_xor(v, m, kWave);
-    v = o < v ? o : v;
-  }
-  return v;
+// Minimum over the wave, returned wave-uniform: DPP within rows of 16, then the
+// four row minima through readlane.
+__device__ inline uint32_t wave_min_u32(uint32_t v) {
+  v = min(v, static_cast<uint32_t>(dpp_i<kDppRowRor8>(static_cast<int>(v))));
+  v = min(v, static_cast<uint32_t>(dpp_i<kDppRowRor4>(static_cast<int>(v))));
+  v = min(v, static_cast<uint32_t>(dpp_i<kDppRowRor2>(static_cast<int>(v))));
+  v = min(v, static_cast<uint32_t>(dpp_i<kDppRowRor1>(static_cast<int>(v))));
+  const uint32_t r0 = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v), 0));
+  const uint32_t r1 = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v), 16));
+  const uint32_t r2 = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v), 32));
+  const uint32_t r3 = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v), 48));
+  return min(min(r0, r1), min(r2, r3));
 }
 
 // Eviction order key: scores are non-negative, so their IEEE bit patterns order
 // like the values; the low word breaks ties by position (lower position first).
 __device__ inline uint64_t evict_key(float score, int32_t pos) {
   return (static_cast<uint64_t>(__float_as_uint(score)) << 32) | static_cast<uint32_t>(pos);
+}
+
+// Wave-uniform lexicographic minimum of (score bits, position) pairs: the
+// minimum score first, then the minimum position among the lanes holding it.
+__device__ inline uint64_t wave_min_key(uint64_t key) {
+  const uint32_t hi = static_cast<uint32_t>(key >> 32), lo = static_cast<uint32_t>(key);
+  const uint32_t mhi = wave_min_u32(hi);
+  const uint32_t mlo = wave_min_u32(hi == mhi ? lo : 0xffffffffu);
+  return (static_cast<uint64_t>(mhi) << 32) | mlo;
 }
 
 }  // namespace h2o

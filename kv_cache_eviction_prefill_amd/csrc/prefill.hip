@@ -39,14 +39,16 @@ __device__ inline bf16x8 ld_bf16x8(const bf16_t* p) { return __builtin_bit_cast(
 __device__ inline int acc_row(int i, int lane) { return 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3); }
 
 // ------------------------------------------------------------------ bf16 MFMA passes
-// A block owns kBlockRows consecutive rows (pass 1: queries, pass 2: keys) of
-// one unit; each of its 4 waves owns 64 of them as two 32-row subtiles whose
-// operands stay in registers.  The other operand streams through LDS in 32-row
-// tiles (double-buffered, rows padded by 16 bytes so the fragment reads of 32
-// consecutive rows spread over the banks), loaded cooperatively with 16-byte
-// global loads.  The blocks of one unit are numbered so they land on the same
-// XCD (blocks are dealt to the 8 XCDs round-robin), keeping the unit's Q and K
-// in that XCD's L2 while its blocks run.
+// Each of a block's 4 waves owns 64 rows (pass 1: queries, pass 2: keys) as two
+// 32-row subtiles whose operands stay in registers; the other operand streams
+// through LDS in 32-row tiles (double-buffered, rows padded by 16 bytes so the
+// fragment reads of 32 consecutive rows spread over the banks), loaded
+// cooperatively with 16-byte global loads.  A block handles the row blocks b
+// and nblk-1-b of its unit, so every block does the same amount of causal work.
+// The blocks of one unit are numbered so they land on the same XCD (blocks are
+// dealt to the 8 XCDs round-robin) and walk the streamed tiles in the same order
+// (pass 1 upwards from key 0, pass 2 downwards from the last query), so each
+// tile is fetched once into that XCD's L2 and shared.
 constexpr int kBlockRows = 256;
 constexpr int kWaveRows = 64;
 constexpr int kXcds = 8;
@@ -109,177 +111,181 @@ __device__ inline void row_frag(const bf16_t* base, int row, int L, int lane, bf
 }
 
 // Pass 1: S^T = K Q^T per 32x32 tile, so a lane holds 16 logits of one query and
-// the online row max / row sum stay inside the lane.
+// the online row max / row sum stay inside the lane.  A block handles the row
+// blocks blk and nblk-1-blk of its unit (equal work per block).
 template <int D>
 __global__ __launch_bounds__(kThreads) void rowstats_bf16(PrefillArgs a, int nblk, int units) {
   __shared__ __align__(16) bf16_t sK[2][kTile * TileCfg<D>::kLdw];
-  int unit, blk;
-  if (!block_coords(nblk, units, &unit, &blk)) return;
+  const int npair = (nblk + 1) / 2;
+  int unit, pb;
+  if (!block_coords(npair, units, &unit, &pb)) return;
   const int L = a.L;
-  const int qb = (nblk - 1 - blk) * kBlockRows;  // longest rows first
   const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
-  const int qw = qb + wave * kWaveRows;
   const bf16_t* Qu = static_cast<const bf16_t*>(a.q) + static_cast<size_t>(unit) * L * D;
   const bf16_t* Ku = static_cast<const bf16_t*>(a.k) + static_cast<size_t>(unit) * L * D;
-
-  bf16x8 bq[2][D / 16];
+  for (int h = 0; h < 2; ++h) {
+    const int blk = h == 0 ? nblk - 1 - pb : pb;
+    if (h == 1 && blk == nblk - 1 - pb) break;  // odd count: the middle block is alone
+    const int qb = blk * kBlockRows;
+    const int qw = qb + wave * kWaveRows;
+    bf16x8 bq[2][D / 16];
 #pragma unroll
-  for (int s = 0; s < 2; ++s) row_frag<D>(Qu, qw + 32 * s + (lane & 31), L, lane, bq[s]);
-
-  const int ntile = (min(qb + kBlockRows, L) - 1) / kTile + 1;
-  // a finite floor instead of -inf keeps (m - max) finite before a lane sees its first key
-  float m[2] = {-1e30f, -1e30f}, l[2] = {0.f, 0.f};
-  uint4 pre[TileCfg<D>::kPerThread];
-  tile_gload<D>(Ku, 0, L, pre);
-  tile_lstore<D>(sK[0], pre);
-  __syncthreads();
-  for (int t = 0; t < ntile; ++t) {
-    const int k0 = t * kTile;
-    if (t + 1 < ntile) tile_gload<D>(Ku, k0 + kTile, L, pre);
-    // the wave has work while its last query is at or after the tile's first key;
-    // a subtile entirely above the diagonal is masked to -inf and leaves (m, l) as is
-    if (qw < L && k0 <= qw + kWaveRows - 1) {
-      bf16x8 ak[D / 16];
-      tile_frag<D>(sK[t & 1], lane, ak);
-      floatx16 acc[2];
-      acc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak[0], bq[0][0], floatx16{}, 0, 0, 0);
-      acc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak[0], bq[1][0], floatx16{}, 0, 0, 0);
-#pragma unroll
-      for (int kk = 1; kk < D / 16; ++kk) {
-        acc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak[kk], bq[0][kk], acc[0], 0, 0, 0);
-        acc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak[kk], bq[1][kk], acc[1], 0, 0, 0);
-      }
-#pragma unroll
-      for (int s = 0; s < 2; ++s) {
-        const int q = qw + 32 * s + (lane & 31);
-        float v[16];
-#pragma unroll
-        for (int i = 0; i < 16; ++i) v[i] = acc[s][i];
-        if (k0 + kTile - 1 > qw + 32 * s) {  // tile reaches past this subtile's first query
-#pragma unroll
-          for (int i = 0; i < 16; ++i) v[i] = k0 + acc_row(i, lane) <= q ? v[i] : -INFINITY;
-        }
-        float tm = v[0];
-#pragma unroll
-        for (int i = 1; i < 16; ++i) tm = fmaxf(tm, v[i]);
-        const float mn = fmaxf(m[s], tm);
-        const float mc = mn * a.c2;
-        float sum = 0.f;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) sum += fast_exp2(fmaf(v[i], a.c2, -mc));
-        l[s] = fmaf(l[s], fast_exp2((m[s] - mn) * a.c2), sum);
-        m[s] = mn;
-      }
-    }
-    if (t + 1 < ntile) tile_lstore<D>(sK[(t + 1) & 1], pre);
+    for (int s = 0; s < 2; ++s) row_frag<D>(Qu, qw + 32 * s + (lane & 31), L, lane, bq[s]);
+    const int ntile = (min(qb + kBlockRows, L) - 1) / kTile + 1;
+    float m[2] = {-1e30f, -1e30f}, l[2] = {0.f, 0.f};
+    uint4 pre[TileCfg<D>::kPerThread];
+    tile_gload<D>(Ku, 0, L, pre);
+    tile_lstore<D>(sK[0], pre);
     __syncthreads();
-  }
-  // lanes l and l^32 saw disjoint key subsets of the same query
+    for (int t = 0; t < ntile; ++t) {
+      const int k0 = t * kTile;
+      if (t + 1 < ntile) tile_gload<D>(Ku, k0 + kTile, L, pre);
+      if (qw < L && k0 <= qw + kWaveRows - 1) {
+        bf16x8 ak[D / 16];
+        tile_frag<D>(sK[t & 1], lane, ak);
+        floatx16 acc[2];
+        acc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak[0], bq[0][0], floatx16{}, 0, 0, 0);
+        acc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak[0], bq[1][0], floatx16{}, 0, 0, 0);
 #pragma unroll
-  for (int s = 0; s < 2; ++s) {
-    const float m2 = __shfl_xor(m[s], 32, kWave), l2 = __shfl_xor(l[s], 32, kWave);
-    const float mn = fmaxf(m[s], m2);
-    const float lt = l[s] * fast_exp2((m[s] - mn) * a.c2) + l2 * fast_exp2((m2 - mn) * a.c2);
-    const int q = qw + 32 * s + lane;
-    if (lane < 32 && q < L) {
-      const size_t o = static_cast<size_t>(unit) * a.Lpad + q;
-      a.row_max[o] = mn * a.scale;
-      a.row_sum[o] = lt;
-      a.row_lse2[o] = fmaf(mn, a.c2, log2f(lt));
+        for (int kk = 1; kk < D / 16; ++kk) {
+          acc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak[kk], bq[0][kk], acc[0], 0, 0, 0);
+          acc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak[kk], bq[1][kk], acc[1], 0, 0, 0);
+        }
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+          const int q = qw + 32 * s + (lane & 31);
+          float v[16];
+#pragma unroll
+          for (int i = 0; i < 16; ++i) v[i] = acc[s][i];
+          if (k0 + kTile - 1 > qw + 32 * s) {
+            const int rel = q - k0 - 4 * (lane >> 5);
+#pragma unroll
+            for (int i = 0; i < 16; ++i) v[i] = (8 * (i >> 2) + (i & 3)) <= rel ? v[i] : -INFINITY;
+          }
+          float tm = fmaxf(v[0], v[1]);
+#pragma unroll
+          for (int i = 2; i < 16; i += 2) tm = fmaxf(tm, fmaxf(v[i], v[i + 1]));
+          const float mn = fmaxf(m[s], tm);
+          const float mc = mn * a.c2;
+          float sum = 0.f;
+#pragma unroll
+          for (int i = 0; i < 16; ++i) sum += fast_exp2(fmaf(v[i], a.c2, -mc));
+          l[s] = fmaf(l[s], fast_exp2((m[s] - mn) * a.c2), sum);
+          m[s] = mn;
+        }
+      }
+      if (t + 1 < ntile) tile_lstore<D>(sK[(t + 1) & 1], pre);
+      __syncthreads();
+    }
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const float m2 = __shfl_xor(m[s], 32, kWave), l2 = __shfl_xor(l[s], 32, kWave);
+      const float mn = fmaxf(m[s], m2);
+      const float lt = l[s] * fast_exp2((m[s] - mn) * a.c2) + l2 * fast_exp2((m2 - mn) * a.c2);
+      const int q = qw + 32 * s + lane;
+      if (lane < 32 && q < L) {
+        const size_t o = static_cast<size_t>(unit) * a.Lpad + q;
+        a.row_max[o] = mn * a.scale;
+        a.row_sum[o] = lt;
+        a.row_lse2[o] = fmaf(mn, a.c2, log2f(lt));
+      }
     }
   }
 }
 
 // Pass 2: S = Q K^T per 32x32 tile, so a lane holds 16 rows of one key column;
-// c_j accumulates exp2(S c2 - lse2_r) over the rows r >= j.
+// c_j accumulates exp2(S c2 - lse2_r) over the rows r >= j.  Query tiles are
+// walked from the last one down, so the blocks of a unit read the same tiles at
+// the same time (L2 reuse).  A block handles key blocks blk and nblk-1-blk.
 template <int D>
 __global__ __launch_bounds__(kThreads) void colsum_bf16(PrefillArgs a, int nblk, int units) {
   __shared__ __align__(16) bf16_t sQ[2][kTile * TileCfg<D>::kLdw];
   __shared__ __align__(16) float sL[2][kTile];
-  int unit, blk;
-  if (!block_coords(nblk, units, &unit, &blk)) return;
+  const int npair = (nblk + 1) / 2;
+  int unit, pb;
+  if (!block_coords(npair, units, &unit, &pb)) return;
   const int L = a.L;
-  const int kb = blk * kBlockRows;  // low keys (longest columns) first
   const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
-  const int kw = kb + wave * kWaveRows;
   const bf16_t* Qu = static_cast<const bf16_t*>(a.q) + static_cast<size_t>(unit) * L * D;
   const bf16_t* Ku = static_cast<const bf16_t*>(a.k) + static_cast<size_t>(unit) * L * D;
   const float* lse = a.row_lse2 + static_cast<size_t>(unit) * a.Lpad;
-
-  bf16x8 bk[2][D / 16];
+  for (int h = 0; h < 2; ++h) {
+    const int blk = h == 0 ? pb : nblk - 1 - pb;
+    if (h == 1 && blk == pb) break;
+    const int kb = blk * kBlockRows;
+    const int kw = kb + wave * kWaveRows;
+    bf16x8 bk[2][D / 16];
 #pragma unroll
-  for (int s = 0; s < 2; ++s) row_frag<D>(Ku, kw + 32 * s + (lane & 31), L, lane, bk[s]);
-
-  const int t0 = kb / kTile, tn = (L - 1) / kTile;
-  float cs[2] = {0.f, 0.f};
-  uint4 pre[TileCfg<D>::kPerThread];
-  float lpre = 0.f;
-  auto lse_load = [&](int row0) {
-    if (threadIdx.x < kTile) lpre = row0 + static_cast<int>(threadIdx.x) < L ? lse[row0 + threadIdx.x] : 0.f;
-  };
-  tile_gload<D>(Qu, t0 * kTile, L, pre);
-  lse_load(t0 * kTile);
-  tile_lstore<D>(sQ[0], pre);
-  if (threadIdx.x < kTile) sL[0][threadIdx.x] = lpre;
-  __syncthreads();
-  for (int t = t0; t <= tn; ++t) {
-    const int q0 = t * kTile;
-    const int buf = (t - t0) & 1;
-    if (t < tn) {
-      tile_gload<D>(Qu, q0 + kTile, L, pre);
-      lse_load(q0 + kTile);
-    }
-    // the wave has work once the tile's last query reaches its first key; a
-    // subtile whose keys all follow the tile's queries is masked to zero
-    if (kw < L && q0 + kTile - 1 >= kw) {
-      bf16x8 aq[D / 16];
-      tile_frag<D>(sQ[buf], lane, aq);
-      floatx16 acc[2];
-      acc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq[0], bk[0][0], floatx16{}, 0, 0, 0);
-      acc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq[0], bk[1][0], floatx16{}, 0, 0, 0);
-#pragma unroll
-      for (int kk = 1; kk < D / 16; ++kk) {
-        acc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq[kk], bk[0][kk], acc[0], 0, 0, 0);
-        acc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq[kk], bk[1][kk], acc[1], 0, 0, 0);
+    for (int s = 0; s < 2; ++s) row_frag<D>(Ku, kw + 32 * s + (lane & 31), L, lane, bk[s]);
+    const int t0 = kb / kTile, tn = (L - 1) / kTile;
+    float cs[2] = {0.f, 0.f};
+    uint4 pre[TileCfg<D>::kPerThread];
+    float lpre = 0.f;
+    auto lse_load = [&](int row0) {
+      if (threadIdx.x < kTile) lpre = row0 + static_cast<int>(threadIdx.x) < L ? lse[row0 + threadIdx.x] : 0.f;
+    };
+    tile_gload<D>(Qu, tn * kTile, L, pre);
+    lse_load(tn * kTile);
+    tile_lstore<D>(sQ[0], pre);
+    if (threadIdx.x < kTile) sL[0][threadIdx.x] = lpre;
+    __syncthreads();
+    for (int t = tn; t >= t0; --t) {
+      const int q0 = t * kTile;
+      const int buf = (tn - t) & 1;
+      if (t > t0) {
+        tile_gload<D>(Qu, q0 - kTile, L, pre);
+        lse_load(q0 - kTile);
       }
-      // the 16 rows of this lane sit in 4 runs of 4 consecutive rows
-      float4 lv[4];
+      if (kw < L && q0 + kTile - 1 >= kw) {
+        bf16x8 aq[D / 16];
+        tile_frag<D>(sQ[buf], lane, aq);
+        floatx16 acc[2];
+        acc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq[0], bk[0][0], floatx16{}, 0, 0, 0);
+        acc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq[0], bk[1][0], floatx16{}, 0, 0, 0);
 #pragma unroll
-      for (int g = 0; g < 4; ++g) lv[g] = *reinterpret_cast<const float4*>(&sL[buf][8 * g + 4 * (lane >> 5)]);
-#pragma unroll
-      for (int s = 0; s < 2; ++s) {
-        const int key = kw + 32 * s + (lane & 31);
-        float p[16];
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const float4& f = lv[i >> 2];
-          const float ls = (i & 3) == 0 ? f.x : (i & 3) == 1 ? f.y : (i & 3) == 2 ? f.z : f.w;
-          p[i] = fast_exp2(fmaf(acc[s][i], a.c2, -ls));
+        for (int kk = 1; kk < D / 16; ++kk) {
+          acc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq[kk], bk[0][kk], acc[0], 0, 0, 0);
+          acc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq[kk], bk[1][kk], acc[1], 0, 0, 0);
         }
-        if (q0 < kw + 32 * s + 32 || q0 + kTile > L) {  // diagonal or ragged last tile
+        float4 lv[4];
+#pragma unroll
+        for (int g = 0; g < 4; ++g) lv[g] = *reinterpret_cast<const float4*>(&sL[buf][8 * g + 4 * (lane >> 5)]);
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+          const int key = kw + 32 * s + (lane & 31);
+          float p[16];
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
-            const int qq = q0 + acc_row(i, lane);
-            p[i] = (qq >= key && qq < L) ? p[i] : 0.f;
+            const float4& f = lv[i >> 2];
+            const float ls = (i & 3) == 0 ? f.x : (i & 3) == 1 ? f.y : (i & 3) == 2 ? f.z : f.w;
+            p[i] = fast_exp2(fmaf(acc[s][i], a.c2, -ls));
           }
+          if (q0 < kw + 32 * s + 32 || q0 + kTile > L) {
+            const int lo = key - q0 - 4 * (lane >> 5), hi = L - q0 - 4 * (lane >> 5);
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+              const int r = 8 * (i >> 2) + (i & 3);
+              p[i] = (r >= lo && r < hi) ? p[i] : 0.f;
+            }
+          }
+          float sum = 0.f;
+#pragma unroll
+          for (int i = 0; i < 16; ++i) sum += p[i];
+          cs[s] += sum;
         }
-        float sum = 0.f;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) sum += p[i];
-        cs[s] += sum;
       }
+      if (t > t0) {
+        tile_lstore<D>(sQ[buf ^ 1], pre);
+        if (threadIdx.x < kTile) sL[buf ^ 1][threadIdx.x] = lpre;
+      }
+      __syncthreads();
     }
-    if (t < tn) {
-      tile_lstore<D>(sQ[buf ^ 1], pre);
-      if (threadIdx.x < kTile) sL[buf ^ 1][threadIdx.x] = lpre;
-    }
-    __syncthreads();
-  }
 #pragma unroll
-  for (int s = 0; s < 2; ++s) {
-    const float c = cs[s] + __shfl_xor(cs[s], 32, kWave);
-    const int key = kw + 32 * s + lane;
-    if (lane < 32 && key < L) a.col_sum[static_cast<size_t>(unit) * a.Lpad + key] = c;
+    for (int s = 0; s < 2; ++s) {
+      const float c = cs[s] + __shfl_xor(cs[s], 32, kWave);
+      const int key = kw + 32 * s + lane;
+      if (lane < 32 && key < L) a.col_sum[static_cast<size_t>(unit) * a.Lpad + key] = c;
+    }
   }
 }
 
@@ -464,7 +470,7 @@ template <int D>
 hipError_t launch_bf16(const PrefillArgs& a, int units, hipStream_t s) {
   const int nblk = (a.L + kBlockRows - 1) / kBlockRows;
   const int groups = (units + kXcds - 1) / kXcds;
-  const dim3 grid(groups * kXcds * nblk);
+  const dim3 grid(groups * kXcds * ((nblk + 1) / 2));
   hipLaunchKernelGGL((rowstats_bf16<D>), grid, dim3(kThreads), 0, s, a, nblk, units);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
