@@ -1,0 +1,106 @@
+"""GPU ↔ oracle parity at the full workload shapes, in the launch configuration
+the benchmark times, on sampled units (needs an MI355X).
+
+Inputs come from the device-side generator; the oracle reads the sampled units'
+inputs back from those tensors (generator output, not GPU-path output) and runs
+each unit in full.  Properties that hold for every unit (budget, recent window,
+candidate bound, no re-entry) are checked on all units.
+"""
+import numpy as np
+import pytest
+import torch
+
+from workload import get, scaled, synth
+
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():
+    pytest.skip("no GPU", allow_module_level=True)
+
+from gpu_harness import check_payloads, log, run_gpu, unit_payload  # noqa: E402
+
+DEV = torch.device("cuda", 0)
+
+
+def _sample(w, n, seed):
+    g = np.random.default_rng(seed)
+    idx = g.choice(w.batch * w.heads, size=min(n, w.batch * w.heads), replace=False)
+    return [(int(i) // w.heads, int(i) % w.heads) for i in sorted(idx)]
+
+
+def _host_unit(q, k, v, b, h):
+    return tuple(x[b, h].to(torch.float32).cpu().numpy() for x in (q, k, v))
+
+
+def _check_properties(w, g, L, T):
+    """Budget, recent window, candidate bound and no re-entry, for every unit."""
+    k = w.k
+    kept = g["kept"]["pos"]
+    ev = g["evicted"]  # [T, B, H]
+    fin = g["final"]["pos"]
+    n_kept = (kept >= 0).sum(-1)
+    assert (n_kept == min(L, k)).all()
+    assert ((fin >= 0).sum(-1) == min(L + T, k)).all()
+    for t in range(T):
+        i = L + t
+        e = ev[t]
+        if min(L, k) + t < k:
+            assert (e == -1).all(), t
+        else:
+            assert (e >= 0).all() and (e <= i - w.recent_budget).all(), t
+    # final set = kept + new tokens - evicted, and the recent window is resident
+    for b in range(w.batch):
+        for h in range(w.heads):
+            s = set(kept[b, h][kept[b, h] >= 0].tolist()) | set(range(L, L + T))
+            s -= set(ev[:, b, h][ev[:, b, h] >= 0].tolist())
+            assert s == set(fin[b, h][fin[b, h] >= 0].tolist()), (b, h)
+            assert set(range(max(0, L + T - w.recent_budget), L + T)) <= s
+
+
+def _run_sampled(w, layer, units, T=None, check_props=True):
+    L = w.prompt_len
+    T = w.decode_steps if T is None else T
+    q, k, v = synth.torch_qkv(w, layer, 0, L + T, DEV)
+    log(f"case {w.name} layer {layer}: B={w.batch} H={w.heads} L={L} T={T} k={w.k}; "
+        f"{len(units)} sampled units")
+    g = run_gpu(q, k, v, L, w.heavy_budget, w.recent_budget, w.dtype, out_units=units)
+    if check_props:
+        _check_properties(w, g, L, T)
+    payloads = []
+    for n, (b, h) in enumerate(units):
+        Q, K, V = _host_unit(q, k, v, b, h)
+        payloads.append(unit_payload(g, b, h, Q, K, V, L, w.heavy_budget, w.recent_budget, out_index=n,
+                                     tag=f"{w.name}/L{layer}/b{b}h{h}"))
+    del q, k, v
+    torch.cuda.empty_cache()
+    results, bad = check_payloads(payloads)
+    assert not bad, bad[:3]
+    for r in results:
+        assert "score_rel" in r and "out_err" in r and "colsum_rel" in r, r
+    return g, results
+
+
+@pytest.mark.parametrize("layer", [0, 31])
+def test_opt67b_32layer_b64_full_shape(layer):
+    # the benchmark's launch configuration: 2048 units, prompt 2048, 1024 decode steps, k = 410
+    w = get("opt6.7b-32L-b64")
+    _run_sampled(w, layer, _sample(w, 12, layer))
+
+
+def test_opt30b_b128_4pct_full_shape():
+    w = get("opt30b-b128-4pct")
+    _run_sampled(w, 0, _sample(w, 10, 4))
+
+
+def test_opt30b_b128_100pct_is_full_attention():
+    # k = N: nothing is ever evicted and every output is full causal attention
+    w = get("opt30b-b128-100pct")
+    g, _ = _run_sampled(w, 0, _sample(w, 8, 100))
+    assert (g["evicted"] == -1).all()
+
+
+def test_llama7b_stream_split_path():
+    # one head per unit, 32 units: the slots of each unit are split over blocks;
+    # the first eviction happens at step k - L = 1536
+    w = get("llama7b-stream-4m")
+    _run_sampled(w, 0, _sample(w, 4, 7), T=6000)
