@@ -76,7 +76,8 @@ typedef struct {
   int32_t max_prompt;    /* >= 0: longest prompt h2o_prefill will accept */
 } h2o_params;
 /* The budget is k = K_h + K_r >= 1 (Report §3.1: k < n cached tokens).
- * B*H*max(k, max_prompt) must stay below 2^31. */
+ * B*H*max(k, max_prompt) must stay below 2^31, and one unit's prompt matrix,
+ * max_prompt*d*sizeof(dtype), below 2^32 bytes. */
 
 /* Device bytes that h2o_cache_create would allocate for these parameters.
  * kv_bytes (nullable): the cached K and V slots alone, 2 * B*H*k*d*sizeof(dtype).
@@ -148,12 +149,11 @@ h2o_status h2o_cache_read(h2o_cache* cache, int32_t* pos, float* score, void* k_
 /* Copy the last prefill's per-token statistics to host memory (synchronises
  * `stream`).  Each pointer is host, nullable, [B, H, L] float32 with L the last
  * prompt_len:
- *   row_max: max_j scale*q_r.k_j over j <= r
- *   row_sum: sum_j exp(scale*q_r.k_j - row_max_r) over j <= r
+ *   row_lse: log sum_j exp(scale*q_r.k_j) over j <= r, the natural log of the
+ *            normaliser of prompt row r's causal softmax
  *   col_sum: c_j, the attention token j received from the prompt rows
  * Errors: H2O_ERR_INVALID_ARG, H2O_ERR_STATE (no prefill yet), H2O_ERR_HIP. */
-h2o_status h2o_prefill_stats_read(h2o_cache* cache, float* row_max, float* row_sum,
-                                  float* col_sum, void* stream);
+h2o_status h2o_prefill_stats_read(h2o_cache* cache, float* row_lse, float* col_sum, void* stream);
 
 /* Host-side state, no GPU call: entries cached per unit, next position, and the
  * last prompt length (-1 before the first prefill).  Pointers nullable. */

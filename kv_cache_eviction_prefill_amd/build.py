@@ -60,6 +60,15 @@ def build(verbose: bool = False) -> str:
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"link failed:\n{res.stdout}{res.stderr}")
+    # A kernel template whose host-side instantiation fails leaves its launch stub
+    # undefined without a compile error; refuse such a library here.
+    nm = shutil.which("nm")
+    if nm:
+        res = subprocess.run([nm, "-uC", tmp], capture_output=True, text=True)
+        missing = [l.strip() for l in res.stdout.splitlines() if "__device_stub__" in l]
+        if missing:
+            os.remove(tmp)
+            raise RuntimeError("undefined kernel launch stubs in libh2o.so:\n" + "\n".join(missing))
     os.replace(tmp, LIB)
     return LIB
 

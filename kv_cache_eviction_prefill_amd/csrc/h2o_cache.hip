@@ -34,8 +34,6 @@ struct h2o_cache {
   float* logits;
   uint32_t* counters;
   int32_t max_split;
-  float* row_max;
-  float* row_sum;
   float* row_lse2;
   float* col_sum;
 };
@@ -105,6 +103,11 @@ h2o_status check_params(const h2o_params* p, Sizes* sz) {
   const int64_t rows = std::max<int64_t>(k, round32(std::min<int32_t>(p->max_prompt, INT32_MAX - 31)));
   if (units * rows >= (int64_t{1} << 31) || units * kMaxSplit >= (int64_t{1} << 31))
     return fail(H2O_ERR_INVALID_ARG, "batch * heads * max(k, max_prompt) must stay below 2^31");
+  // the prefill kernels address one unit's [L, d] matrix through a 32-bit byte range
+  const int64_t esize = p->dtype == H2O_F32 ? 4 : 2;
+  if (static_cast<int64_t>(round32(std::min<int32_t>(p->max_prompt, INT32_MAX - 31))) * p->head_dim * esize >=
+      (int64_t{1} << 32))
+    return fail(H2O_ERR_INVALID_ARG, "max_prompt * head_dim * element size must stay below 2^32 bytes");
   if (sz != nullptr) {
     const size_t es = p->dtype == H2O_F32 ? 4 : 2;
     const size_t u = static_cast<size_t>(units), kk = static_cast<size_t>(k), d = p->head_dim;
@@ -115,7 +118,7 @@ h2o_status check_params(const h2o_params* p, Sizes* sz) {
                     ? u * sz->max_split * (2 + d) * 4 + u * (kk + 1) * 4 + u * 4
                     : 0;
     sz->lpad = round32(p->max_prompt);
-    sz->prefill = 4 * u * static_cast<size_t>(sz->lpad) * 4;
+    sz->prefill = 2 * u * static_cast<size_t>(sz->lpad) * 4;
     sz->total = sz->kv + sz->meta + sz->split + sz->prefill;
   }
   return H2O_OK;
@@ -123,7 +126,7 @@ h2o_status check_params(const h2o_params* p, Sizes* sz) {
 
 void free_all(h2o_cache* c) {
   void* ptrs[] = {c->kslots, c->vslots, c->score, c->comp, c->pos, c->part, c->logits,
-                  c->counters, c->row_max, c->row_sum, c->row_lse2, c->col_sum};
+                  c->counters, c->row_lse2, c->col_sum};
   for (void* q : ptrs)
     if (q != nullptr) (void)hipFree(q);
 }
@@ -217,8 +220,6 @@ h2o_status h2o_cache_create(const h2o_params* params, int device, h2o_cache** ou
       {reinterpret_cast<void**>(&c->part), c->max_split > 1 ? u * c->max_split * (2 + d) * 4 : 0},
       {reinterpret_cast<void**>(&c->logits), c->max_split > 1 ? u * (kk + 1) * 4 : 0},
       {reinterpret_cast<void**>(&c->counters), c->max_split > 1 ? u * 4 : 0},
-      {reinterpret_cast<void**>(&c->row_max), u * c->lpad_cap * 4},
-      {reinterpret_cast<void**>(&c->row_sum), u * c->lpad_cap * 4},
       {reinterpret_cast<void**>(&c->row_lse2), u * c->lpad_cap * 4},
       {reinterpret_cast<void**>(&c->col_sum), u * c->lpad_cap * 4},
   };
@@ -274,8 +275,6 @@ h2o_status h2o_prefill(h2o_cache* c, const void* q, const void* k, const void* v
     a.v = v;
     a.L = L;
     a.Lpad = round32(L);
-    a.row_max = c->row_max;
-    a.row_sum = c->row_sum;
     a.row_lse2 = c->row_lse2;
     a.col_sum = c->col_sum;
     a.kslots = c->kslots;
@@ -361,7 +360,7 @@ h2o_status h2o_cache_read(h2o_cache* c, int32_t* pos, float* score, void* k_slot
   return H2O_OK;
 }
 
-h2o_status h2o_prefill_stats_read(h2o_cache* c, float* row_max, float* row_sum, float* col_sum, void* stream) {
+h2o_status h2o_prefill_stats_read(h2o_cache* c, float* row_lse, float* col_sum, void* stream) {
   if (c == nullptr) return fail(H2O_ERR_INVALID_ARG, "cache is NULL");
   if (c->prompt_len < 0) return fail(H2O_ERR_STATE, "no prefill yet");
   DeviceGuard guard(c->device);
@@ -369,13 +368,18 @@ h2o_status h2o_prefill_stats_read(h2o_cache* c, float* row_max, float* row_sum, 
   if (e != hipSuccess) return hip_fail(e, "hipStreamSynchronize");
   const int32_t L = c->prompt_len;
   if (L == 0) return H2O_OK;
-  const float* src[3] = {c->row_max, c->row_sum, c->col_sum};
-  float* dst[3] = {row_max, row_sum, col_sum};
-  for (int t = 0; t < 3; ++t) {
+  const float* src[2] = {c->row_lse2, c->col_sum};
+  float* dst[2] = {row_lse, col_sum};
+  for (int t = 0; t < 2; ++t) {
     if (dst[t] == nullptr) continue;
     e = hipMemcpy2D(dst[t], static_cast<size_t>(L) * 4, src[t], static_cast<size_t>(c->lpad_last) * 4,
                     static_cast<size_t>(L) * 4, c->units, hipMemcpyDeviceToHost);
     if (e != hipSuccess) return hip_fail(e, "copy prefill statistics");
+  }
+  if (row_lse != nullptr) {  // the kernels keep log2 of the normaliser
+    const float ln2 = 0.6931471805599453f;
+    const size_t n = static_cast<size_t>(L) * c->units;
+    for (size_t i = 0; i < n; ++i) row_lse[i] *= ln2;
   }
   return H2O_OK;
 }

@@ -40,9 +40,7 @@ struct PrefillArgs {
   const void* v;  // [units, L, d]
   int32_t L;
   int32_t Lpad;       // stride of the per-row scratch arrays (multiple of 32, >= L)
-  float* row_max;     // [units, Lpad] max logit of each prompt row
-  float* row_sum;     // [units, Lpad] sum of exp(logit - max) of each prompt row
-  float* row_lse2;    // [units, Lpad] base-2 log-sum-exp of each row (scaled units)
+  float* row_lse2;    // [units, Lpad] log2 sum_j exp2(c2 q_r.k_j) of each row; 0 past L
   float* col_sum;     // [units, Lpad] attention received by each prompt token
   void* kslots;       // [units, k, d]
   void* vslots;       // [units, k, d]

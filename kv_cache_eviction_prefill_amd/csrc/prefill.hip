@@ -8,11 +8,11 @@
 // hitters and the K most recent tokens; a short one keeps everything).
 //
 // Three launches per prefill:
-//   1. rowstats:  per prompt row r, m_r = max_j x_rj and l_r = sum_j exp(x_rj - m_r)
-//                 over j <= r (x = scale * q_r . k_j); bf16 inputs use MFMA
-//                 32x32x16 tiles of S^T = K Q^T, so one lane holds one query's
-//                 logits and the row reductions stay inside the lane.
-//   2. colsum:    c_j = sum_{r >= j} exp(x_rj - m_r) / l_r, recomputing the
+//   1. rowstats:  per prompt row r, the base-2 log of its softmax normaliser,
+//                 lse2_r = log2 sum_{j<=r} exp2(c2 q_r.k_j) with c2 = scale*log2(e);
+//                 bf16 inputs use MFMA 32x32x16 tiles of S^T = K Q^T, so one lane
+//                 holds one query's logits and the row sum stays inside the lane.
+//   2. colsum:    c_j = sum_{r>=j} exp2(c2 q_r.k_j - lse2_r), recomputing the
 //                 logits as MFMA tiles of S = Q K^T (one lane per key column);
 //                 the causal softmax is row-normalised, so the column sums need
 //                 the row normalisers of pass 1 first.
@@ -20,6 +20,12 @@
 //                 position) finds the K_h-th best heavy-hitter candidate, a
 //                 ballot/popcount compaction assigns slots in position order,
 //                 and the kept K/V rows, positions and scores are written.
+//
+// Cost model of the MFMA passes on gfx950 (measured): per 32x32 logit tile the
+// MFMAs take 8 x 32 cycles, and the exponentials alone (one v_exp per logit, at
+// half the VALU rate) take as long, so each logit gets exactly one fma, one exp
+// and one add on the common path.  Overlap of the matrix cores with the VALU
+// needs several waves per SIMD: registers are kept to 128 (4 waves per SIMD).
 #include <cmath>
 
 #include "h2o_device.h"
@@ -29,80 +35,123 @@ namespace h2o {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kTile = 32;              // MFMA tile edge (rows and columns)
+constexpr int kTile = 32;  // MFMA tile edge (rows and columns)
 constexpr uint64_t kNoKey = ~0ull;
 
 __device__ inline bf16x8 ld_bf16x8(const bf16_t* p) { return __builtin_bit_cast(bf16x8, ld16(p)); }
 
-// Row m of a 32x32 MFMA accumulator tile held in element i of lane `lane`
-// (the column is lane % 32).
-__device__ inline int acc_row(int i, int lane) { return 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3); }
-
 // ------------------------------------------------------------------ bf16 MFMA passes
 // Each of a block's 4 waves owns 64 rows (pass 1: queries, pass 2: keys) as two
-// 32-row subtiles whose operands stay in registers; the other operand streams
-// through LDS in 32-row tiles (double-buffered, rows padded by 16 bytes so the
-// fragment reads of 32 consecutive rows spread over the banks), loaded
-// cooperatively with 16-byte global loads.  A block handles the row blocks b
-// and nblk-1-b of its unit, so every block does the same amount of causal work.
-// The blocks of one unit are numbered so they land on the same XCD (blocks are
-// dealt to the 8 XCDs round-robin) and walk the streamed tiles in the same order
-// (pass 1 upwards from key 0, pass 2 downwards from the last query), so each
-// tile is fetched once into that XCD's L2 and shared.
+// 32-row subtiles whose operand stays in registers.  The other operand streams
+// through a ring of three 32-row LDS tiles, loaded straight from global memory to
+// LDS (buffer loads with the LDS flag: no registers, no LDS-store instructions),
+// two tiles ahead of the one in use, with one barrier per tile.  A block handles
+// the row blocks b and nblk-1-b of its unit, so every block does the same amount
+// of causal work.  The blocks of one unit are numbered so they land on the same
+// XCD (blocks are dealt to the 8 XCDs round-robin) and walk the streamed tiles in
+// the same order (pass 1 upwards from key 0, pass 2 downwards from the last
+// query), so each tile is fetched once into that XCD's L2 and shared.
 constexpr int kBlockRows = 256;
 constexpr int kWaveRows = 64;
 constexpr int kXcds = 8;
+constexpr int kBufs = 3;
 
 template <int D>
-struct TileCfg {
-  static constexpr int kLdw = D + 8;                     // LDS row stride (bf16 elements)
-  static constexpr int kChunksPerRow = D * 2 / 16;       // 16-byte chunks per row
-  static constexpr int kChunks = kTile * kChunksPerRow;  // per 32-row tile
-  static constexpr int kPerThread = kChunks / kThreads;  // 2 (d = 128) or 1 (d = 64)
-  static_assert(kChunks % kThreads == 0, "tile must split evenly over the block");
+struct Tile {
+  static constexpr int kRowBytes = D * 2;
+  static constexpr int kChunks = D / 8;                    // 16-byte chunks per row
+  static constexpr int kBytes = kTile * kRowBytes;         // 8 KB (d = 128) or 4 KB
+  static constexpr int kLoads = kBytes / (kThreads * 16);  // 16-byte loads per thread per tile
+  static constexpr int kSwz = kChunks - 1;
+  static_assert(kBytes % (kThreads * 16) == 0, "tile must split evenly over the block");
+  static_assert(kBytes % 256 == 0, "tiles must keep 256-byte alignment");
 };
 
-// (unit, row block) of this block; false for the padding blocks of the last group.
-__device__ inline bool block_coords(int nblk, int units, int* unit, int* blk) {
+// (unit, row-block pair) of this block; false for the padding blocks of the last group.
+__device__ inline bool block_coords(int npair, int units, int* unit, int* pair) {
   const int b = blockIdx.x;
   const int slot = b / kXcds;
-  *unit = (slot / nblk) * kXcds + b % kXcds;
-  *blk = slot % nblk;
+  *unit = (slot / npair) * kXcds + b % kXcds;
+  *pair = slot % npair;
   return *unit < units;
 }
 
-template <int D>
-__device__ inline void tile_gload(const bf16_t* base, int row0, int L, uint4* pre) {
-  using C = TileCfg<D>;
-#pragma unroll
-  for (int c = 0; c < C::kPerThread; ++c) {
-    const int ch = threadIdx.x + kThreads * c;
-    const int r = ch / C::kChunksPerRow, cc = ch % C::kChunksPerRow;
-    const int row = row0 + r;
-    pre[c] = row < L ? ld16(base + static_cast<size_t>(row) * D + cc * 8) : make_uint4(0u, 0u, 0u, 0u);
-  }
+template <int N>
+__device__ inline void wait_vm() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
-template <int D>
-__device__ inline void tile_lstore(bf16_t* tile, const uint4* pre) {
-  using C = TileCfg<D>;
-#pragma unroll
-  for (int c = 0; c < C::kPerThread; ++c) {
-    const int ch = threadIdx.x + kThreads * c;
-    const int r = ch / C::kChunksPerRow, cc = ch % C::kChunksPerRow;
-    st16(tile + r * C::kLdw + cc * 8, pre[c]);
-  }
+// Workgroup barrier without the memory fence of __syncthreads (which would also
+// wait for the tiles still in flight).  The tile loads into LDS are tracked with
+// explicit vmcnt waits; LDS reads are drained first so a tile can be overwritten
+// once every wave has passed the barrier.
+__device__ inline void tile_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
 }
 
-// Fragment of a 32-row LDS tile as an MFMA A operand (row = lane % 32).
-template <int D>
-__device__ inline void tile_frag(const bf16_t* tile, int lane, bf16x8* f) {
-  const bf16_t* p = tile + (lane & 31) * TileCfg<D>::kLdw + (lane >> 5) * 8;
-#pragma unroll
-  for (int kk = 0; kk < D / 16; ++kk) f[kk] = __builtin_bit_cast(bf16x8, ld16(p + 16 * kk));
+__device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, 0x00020000);
 }
 
-// Row fragment straight from global memory (an operand that stays in registers).
+// LDS placement of a streamed tile: chunk c of tile row r sits at chunk
+// c ^ (r & kSwz) of the LDS row, so the 32 rows of one fragment read fall in
+// different banks.  Each wave-wide load fills 1 KB of consecutive LDS; a lane's
+// source offset inside the tile is the same for every tile (tile_voff).
+template <int D>
+__device__ inline int tile_voff() {
+  using T = Tile<D>;
+  const int o = threadIdx.x * 16;  // load c adds c * kThreads * 16 bytes
+  const int r = o / T::kRowBytes, p = (o % T::kRowBytes) / 16;
+  return r * T::kRowBytes + ((p ^ (r & T::kSwz)) * 16);
+}
+
+// Rows row0..row0+31 of a [L, D] matrix into an LDS tile through a buffer
+// descriptor over the matrix: rows past L read as zero.
+__device__ inline void tile_async(__amdgpu_buffer_rsrc_t rs, int voff, int row0, unsigned char* tile,
+                                  int row_bytes, int loads) {
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+#pragma unroll
+  for (int c = 0; c < loads; ++c)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, tile + (c * kThreads + wave * kWave) * 16, 16, voff,
+                                             row0 * row_bytes + c * kThreads * 16, 0, 0);
+}
+
+// The 32 row normalisers (128 bytes) of the query tile starting at row0, by
+// lanes 0..7 of wave 0, whose tile offset `voff` is lane * 16.
+__device__ inline void lse_async(__amdgpu_buffer_rsrc_t rl, int voff, int row0, unsigned char* dst) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rl, dst, 16, voff, row0 * 4, 0, 0);
+}
+
+// LDS reads by byte address.  These do not alias any compiler-visible store, so
+// the only ordering with the tile loads is the explicit vmcnt wait + barrier.
+typedef __attribute__((address_space(3))) const unsigned char lds_u8;
+typedef __attribute__((address_space(3))) const uint4 lds_u4;
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+__device__ inline uint32_t lds_addr(const void* p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_u8*)p));
+}
+__device__ inline f32x4 lds_float4(uint32_t addr) {
+  return __builtin_bit_cast(f32x4, *(lds_u4*)(static_cast<uintptr_t>(addr)));
+}
+__device__ inline bf16x8 lds_frag(uint32_t addr) {
+  return __builtin_bit_cast(bf16x8, *(lds_u4*)(static_cast<uintptr_t>(addr)));
+}
+
+// Lane offset of its MFMA A-operand fragment inside a swizzled tile: row fr =
+// lane % 32, k-chunk 2kk + lane/32, with the row's swizzle folded in for kk = 0.
+// Tiles are 256-byte aligned and the swizzle only touches bits 4..7 of the
+// offset, so the fragment of step kk is at (tile + xo) ^ 32kk.
+template <int D>
+__device__ inline uint32_t frag_offset(int lane) {
+  using T = Tile<D>;
+  const int fr = lane & 31;
+  return fr * T::kRowBytes + (((((lane >> 5) ^ fr) & 1) << 4) | (((fr & T::kSwz) & ~1) << 4));
+}
+__device__ inline bf16x8 tile_frag_kk(uint32_t base, int kk) { return lds_frag(base ^ static_cast<uint32_t>(kk * 32)); }
+
+// Row fragment straight from global memory (the operand that stays in registers).
 template <int D>
 __device__ inline void row_frag(const bf16_t* base, int row, int L, int lane, bf16x8* f) {
   const bf16_t* p = base + static_cast<size_t>(min(row, L - 1)) * D + (lane >> 5) * 8;
@@ -110,176 +159,222 @@ __device__ inline void row_frag(const bf16_t* base, int row, int L, int lane, bf
   for (int kk = 0; kk < D / 16; ++kk) f[kk] = ld_bf16x8(p + 16 * kk);
 }
 
-// Pass 1: S^T = K Q^T per 32x32 tile, so a lane holds 16 logits of one query and
-// the online row max / row sum stay inside the lane.  A block handles the row
-// blocks blk and nblk-1-blk of its unit (equal work per block).
+// Wait here (once per row block) for the register operand, so the compiler leaves
+// no wait for it inside the tile loop, where it would also wait for the tiles in
+// flight.
 template <int D>
-__global__ __launch_bounds__(kThreads) void rowstats_bf16(PrefillArgs a, int nblk, int units) {
-  __shared__ __align__(16) bf16_t sK[2][kTile * TileCfg<D>::kLdw];
+__device__ inline void settle(bf16x8 (&f)[2][D / 16]) {
+#pragma unroll
+  for (int s = 0; s < 2; ++s)
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) asm volatile("" : "+v"(f[s][kk]));
+}
+
+// S tile pair (two 32-row subtiles of the register operand) against the LDS tile
+// at `fb`: 2 x D/16 MFMAs, fragments read two steps ahead.
+template <int D>
+__device__ inline void tile_mfma(uint32_t fb, const bf16x8 (&b)[2][D / 16], floatx16 (&acc)[2]) {
+  bf16x8 f2[2] = {tile_frag_kk(fb, 0), tile_frag_kk(fb, 1)};
+  acc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f2[0], b[0][0], floatx16{}, 0, 0, 0);
+  acc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f2[0], b[1][0], floatx16{}, 0, 0, 0);
+  f2[0] = tile_frag_kk(fb, 2);
+#pragma unroll
+  for (int kk = 1; kk < D / 16; ++kk) {
+    acc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f2[kk & 1], b[0][kk], acc[0], 0, 0, 0);
+    acc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f2[kk & 1], b[1][kk], acc[1], 0, 0, 0);
+    if (kk + 2 < D / 16) f2[kk & 1] = tile_frag_kk(fb, kk + 2);
+  }
+  __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // 2 LDS reads, then (2 MFMA, 1 LDS read)...
+#pragma unroll
+  for (int kk = 0; kk < D / 16 - 2; ++kk) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+  }
+  __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+}
+
+// sum_i exp2(v_i * c + b) over the 16 elements, as four interleaved partial sums.
+__device__ inline float sum_exp2_16(const floatx16& v, float c, float b) {
+  float part[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) part[i] = fast_exp2(fmaf(v[i], c, b));
+#pragma unroll
+  for (int i = 4; i < 16; ++i) part[i & 3] += fast_exp2(fmaf(v[i], c, b));
+  return (part[0] + part[1]) + (part[2] + part[3]);
+}
+
+// Pass 1: S^T = K Q^T per 32x32 tile, so a lane holds 16 logits of one query
+// (element i is key row 8(i/4) + 4(lane/32) + i%4 of the tile).  The row sum is
+// kept against a running offset m (base 2, scaled) that only moves when a tile
+// would push a term past 2^64: the common tile costs one fma, one exp and one add
+// per logit; the first tile and any tile with a far larger logit rescale.  Any
+// offset at or below the row maximum gives the same normaliser, and no term can
+// overflow, so the result equals the usual max-shifted sum.
+template <int D>
+__global__ __launch_bounds__(kThreads, 4) void rowstats_bf16(PrefillArgs a, int nblk, int units) {
+  using T = Tile<D>;
+  __shared__ __align__(256) unsigned char sK[kBufs][T::kBytes];
   const int npair = (nblk + 1) / 2;
   int unit, pb;
   if (!block_coords(npair, units, &unit, &pb)) return;
   const int L = a.L;
-  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave), lane = threadIdx.x % kWave;
+  const int fr = lane & 31;
   const bf16_t* Qu = static_cast<const bf16_t*>(a.q) + static_cast<size_t>(unit) * L * D;
   const bf16_t* Ku = static_cast<const bf16_t*>(a.k) + static_cast<size_t>(unit) * L * D;
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(Ku, static_cast<uint32_t>(L) * T::kRowBytes);
+  const int voff = tile_voff<D>();
+  const uint32_t xo = frag_offset<D>(lane);
   for (int h = 0; h < 2; ++h) {
     const int blk = h == 0 ? nblk - 1 - pb : pb;
     if (h == 1 && blk == nblk - 1 - pb) break;  // odd count: the middle block is alone
     const int qb = blk * kBlockRows;
     const int qw = qb + wave * kWaveRows;
+    const int ntile = (min(qb + kBlockRows, L) - 1) / kTile + 1;
+    if (h == 1) tile_barrier();  // the first row block's tiles are no longer read
     bf16x8 bq[2][D / 16];
 #pragma unroll
-    for (int s = 0; s < 2; ++s) row_frag<D>(Qu, qw + 32 * s + (lane & 31), L, lane, bq[s]);
-    const int ntile = (min(qb + kBlockRows, L) - 1) / kTile + 1;
+    for (int s = 0; s < 2; ++s) row_frag<D>(Qu, qw + 32 * s + fr, L, lane, bq[s]);
+    tile_async(rk, voff, 0, sK[0], T::kRowBytes, T::kLoads);
+    if (ntile > 1) tile_async(rk, voff, kTile, sK[1], T::kRowBytes, T::kLoads);
+    settle<D>(bq);
     float m[2] = {-1e30f, -1e30f}, l[2] = {0.f, 0.f};
-    uint4 pre[TileCfg<D>::kPerThread];
-    tile_gload<D>(Ku, 0, L, pre);
-    tile_lstore<D>(sK[0], pre);
-    __syncthreads();
     for (int t = 0; t < ntile; ++t) {
+      if (t + 1 < ntile) wait_vm<T::kLoads>();  // this tile landed; the next may be in flight
+      else wait_vm<0>();
+      tile_barrier();
+      if (t + 2 < ntile) tile_async(rk, voff, (t + 2) * kTile, sK[(t + 2) % kBufs], T::kRowBytes, T::kLoads);
       const int k0 = t * kTile;
-      if (t + 1 < ntile) tile_gload<D>(Ku, k0 + kTile, L, pre);
       if (qw < L && k0 <= qw + kWaveRows - 1) {
-        bf16x8 ak[D / 16];
-        tile_frag<D>(sK[t & 1], lane, ak);
+        uint32_t fb = lds_addr(sK[t % kBufs]) + xo;
+        asm volatile("" : "+v"(fb));  // keep the per-step offsets inside the loop
         floatx16 acc[2];
-        acc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak[0], bq[0][0], floatx16{}, 0, 0, 0);
-        acc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak[0], bq[1][0], floatx16{}, 0, 0, 0);
-#pragma unroll
-        for (int kk = 1; kk < D / 16; ++kk) {
-          acc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak[kk], bq[0][kk], acc[0], 0, 0, 0);
-          acc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak[kk], bq[1][kk], acc[1], 0, 0, 0);
-        }
+        tile_mfma<D>(fb, bq, acc);
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
-          const int q = qw + 32 * s + (lane & 31);
-          float v[16];
+          if (k0 + kTile - 1 > qw + 32 * s) {  // diagonal tile: keys after the query leave the row
+            const int rel = qw + 32 * s + fr - k0 - 4 * (lane >> 5);
 #pragma unroll
-          for (int i = 0; i < 16; ++i) v[i] = acc[s][i];
-          if (k0 + kTile - 1 > qw + 32 * s) {
-            const int rel = q - k0 - 4 * (lane >> 5);
-#pragma unroll
-            for (int i = 0; i < 16; ++i) v[i] = (8 * (i >> 2) + (i & 3)) <= rel ? v[i] : -INFINITY;
+            for (int i = 0; i < 16; ++i) acc[s][i] = (8 * (i >> 2) + (i & 3)) <= rel ? acc[s][i] : -INFINITY;
           }
-          float tm = fmaxf(v[0], v[1]);
+          float ts = sum_exp2_16(acc[s], a.c2, -m[s]);
+          if (!(ts <= 0x1p64f)) {  // first tile, or a logit far above the offset: rescale
+            float tm = fmaxf(acc[s][0], acc[s][1]);
 #pragma unroll
-          for (int i = 2; i < 16; i += 2) tm = fmaxf(tm, fmaxf(v[i], v[i + 1]));
-          const float mn = fmaxf(m[s], tm);
-          const float mc = mn * a.c2;
-          float sum = 0.f;
-#pragma unroll
-          for (int i = 0; i < 16; ++i) sum += fast_exp2(fmaf(v[i], a.c2, -mc));
-          l[s] = fmaf(l[s], fast_exp2((m[s] - mn) * a.c2), sum);
-          m[s] = mn;
+            for (int i = 2; i < 16; i += 2) tm = fmaxf(tm, fmaxf(acc[s][i], acc[s][i + 1]));
+            const float mn = fmaxf(m[s], tm * a.c2);
+            ts = sum_exp2_16(acc[s], a.c2, -mn);
+            l[s] *= fast_exp2(m[s] - mn);
+            m[s] = mn;
+          }
+          l[s] += ts;
         }
       }
-      if (t + 1 < ntile) tile_lstore<D>(sK[(t + 1) & 1], pre);
-      __syncthreads();
     }
+    // lanes l and l+32 hold the same queries over different key rows
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
       const float m2 = __shfl_xor(m[s], 32, kWave), l2 = __shfl_xor(l[s], 32, kWave);
       const float mn = fmaxf(m[s], m2);
-      const float lt = l[s] * fast_exp2((m[s] - mn) * a.c2) + l2 * fast_exp2((m2 - mn) * a.c2);
+      const float lt = l[s] * fast_exp2(m[s] - mn) + l2 * fast_exp2(m2 - mn);
       const int q = qw + 32 * s + lane;
-      if (lane < 32 && q < L) {
-        const size_t o = static_cast<size_t>(unit) * a.Lpad + q;
-        a.row_max[o] = mn * a.scale;
-        a.row_sum[o] = lt;
-        a.row_lse2[o] = fmaf(mn, a.c2, log2f(lt));
-      }
+      // rows L..Lpad-1 get 0 so pass 2 reads finite normalisers for its masked rows
+      if (lane < 32 && q < a.Lpad)
+        a.row_lse2[static_cast<size_t>(unit) * a.Lpad + q] = q < L ? mn + log2f(lt) : 0.f;
     }
   }
 }
 
-// Pass 2: S = Q K^T per 32x32 tile, so a lane holds 16 rows of one key column;
-// c_j accumulates exp2(S c2 - lse2_r) over the rows r >= j.  Query tiles are
-// walked from the last one down, so the blocks of a unit read the same tiles at
-// the same time (L2 reuse).  A block handles key blocks blk and nblk-1-blk.
+// Pass 2: S = Q K^T per 32x32 tile, so a lane holds 16 query rows of one key
+// column; c_j accumulates exp2(S c2 - lse2_r) over the rows r >= j.  Query tiles
+// are walked from the last one down.  Each tile buffer carries the tile's 32 row
+// normalisers after its 32 rows (brought by lanes 0..7 of wave 0).
 template <int D>
-__global__ __launch_bounds__(kThreads) void colsum_bf16(PrefillArgs a, int nblk, int units) {
-  __shared__ __align__(16) bf16_t sQ[2][kTile * TileCfg<D>::kLdw];
-  __shared__ __align__(16) float sL[2][kTile];
+__global__ __launch_bounds__(kThreads, 4) void colsum_bf16(PrefillArgs a, int nblk, int units) {
+  using T = Tile<D>;
+  constexpr int kBufBytes = T::kBytes + 256;  // tile, normalisers, padding to 256 bytes
+  __shared__ __align__(256) unsigned char sQ[kBufs][kBufBytes];
   const int npair = (nblk + 1) / 2;
   int unit, pb;
   if (!block_coords(npair, units, &unit, &pb)) return;
   const int L = a.L;
-  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave), lane = threadIdx.x % kWave;
+  const int fr = lane & 31;
   const bf16_t* Qu = static_cast<const bf16_t*>(a.q) + static_cast<size_t>(unit) * L * D;
   const bf16_t* Ku = static_cast<const bf16_t*>(a.k) + static_cast<size_t>(unit) * L * D;
   const float* lse = a.row_lse2 + static_cast<size_t>(unit) * a.Lpad;
+  const __amdgpu_buffer_rsrc_t rq = make_rsrc(Qu, static_cast<uint32_t>(L) * T::kRowBytes);
+  const __amdgpu_buffer_rsrc_t rl = make_rsrc(lse, static_cast<uint32_t>(a.Lpad) * 4);
+  const int voff = tile_voff<D>();  // for lanes 0..7 of wave 0 this is lane * 16
+  const uint32_t xo = frag_offset<D>(lane);
+  const bool lse_lane = wave == 0 && lane < 8;
   for (int h = 0; h < 2; ++h) {
     const int blk = h == 0 ? pb : nblk - 1 - pb;
     if (h == 1 && blk == pb) break;
     const int kb = blk * kBlockRows;
     const int kw = kb + wave * kWaveRows;
+    const int t0 = kb / kTile, tn = (L - 1) / kTile;
+    if (h == 1) tile_barrier();
     bf16x8 bk[2][D / 16];
 #pragma unroll
-    for (int s = 0; s < 2; ++s) row_frag<D>(Ku, kw + 32 * s + (lane & 31), L, lane, bk[s]);
-    const int t0 = kb / kTile, tn = (L - 1) / kTile;
+    for (int s = 0; s < 2; ++s) row_frag<D>(Ku, kw + 32 * s + fr, L, lane, bk[s]);
+    // the tile of query rows t*32.. and its normalisers into buffer `buf`
+#define H2O_COLSUM_ISSUE(t, buf)                                             \
+  do {                                                                       \
+    tile_async(rq, voff, (t) * kTile, sQ[buf], T::kRowBytes, T::kLoads);     \
+    if (lse_lane) lse_async(rl, voff, (t) * kTile, sQ[buf] + T::kBytes);     \
+  } while (0)
+    H2O_COLSUM_ISSUE(tn, 0);
+    if (tn > t0) H2O_COLSUM_ISSUE(tn - 1, 1);
+    settle<D>(bk);
     float cs[2] = {0.f, 0.f};
-    uint4 pre[TileCfg<D>::kPerThread];
-    float lpre = 0.f;
-    auto lse_load = [&](int row0) {
-      if (threadIdx.x < kTile) lpre = row0 + static_cast<int>(threadIdx.x) < L ? lse[row0 + threadIdx.x] : 0.f;
-    };
-    tile_gload<D>(Qu, tn * kTile, L, pre);
-    lse_load(tn * kTile);
-    tile_lstore<D>(sQ[0], pre);
-    if (threadIdx.x < kTile) sL[0][threadIdx.x] = lpre;
-    __syncthreads();
     for (int t = tn; t >= t0; --t) {
+      const int it = tn - t;
+      if (t == t0) wait_vm<0>();
+      else if (wave == 0) wait_vm<T::kLoads + 1>();  // wave 0 also brings the normalisers
+      else wait_vm<T::kLoads>();
+      tile_barrier();
+      if (t - 2 >= t0) H2O_COLSUM_ISSUE(t - 2, (it + 2) % kBufs);
       const int q0 = t * kTile;
-      const int buf = (tn - t) & 1;
-      if (t > t0) {
-        tile_gload<D>(Qu, q0 - kTile, L, pre);
-        lse_load(q0 - kTile);
-      }
       if (kw < L && q0 + kTile - 1 >= kw) {
-        bf16x8 aq[D / 16];
-        tile_frag<D>(sQ[buf], lane, aq);
+        const uint32_t tile = lds_addr(sQ[it % kBufs]);
+        uint32_t fb = tile + xo;
+        asm volatile("" : "+v"(fb));
         floatx16 acc[2];
-        acc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq[0], bk[0][0], floatx16{}, 0, 0, 0);
-        acc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq[0], bk[1][0], floatx16{}, 0, 0, 0);
+        tile_mfma<D>(fb, bk, acc);
+        if (q0 < kw + kWaveRows || q0 + kTile > L) {  // diagonal or ragged last tile
+          // rows above the key and rows past L leave the column: logit -> -inf
+          const int h4 = 4 * (lane >> 5);
 #pragma unroll
-        for (int kk = 1; kk < D / 16; ++kk) {
-          acc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq[kk], bk[0][kk], acc[0], 0, 0, 0);
-          acc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq[kk], bk[1][kk], acc[1], 0, 0, 0);
-        }
-        float4 lv[4];
-#pragma unroll
-        for (int g = 0; g < 4; ++g) lv[g] = *reinterpret_cast<const float4*>(&sL[buf][8 * g + 4 * (lane >> 5)]);
-#pragma unroll
-        for (int s = 0; s < 2; ++s) {
-          const int key = kw + 32 * s + (lane & 31);
-          float p[16];
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const float4& f = lv[i >> 2];
-            const float ls = (i & 3) == 0 ? f.x : (i & 3) == 1 ? f.y : (i & 3) == 2 ? f.z : f.w;
-            p[i] = fast_exp2(fmaf(acc[s][i], a.c2, -ls));
-          }
-          if (q0 < kw + 32 * s + 32 || q0 + kTile > L) {
-            const int lo = key - q0 - 4 * (lane >> 5), hi = L - q0 - 4 * (lane >> 5);
+          for (int s = 0; s < 2; ++s) {
+            const int lo = kw + 32 * s + fr - q0 - h4, hi = L - q0 - h4;
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
               const int r = 8 * (i >> 2) + (i & 3);
-              p[i] = (r >= lo && r < hi) ? p[i] : 0.f;
+              acc[s][i] = (r >= lo && r < hi) ? acc[s][i] : -INFINITY;
             }
           }
-          float sum = 0.f;
+        }
+        // the 16 rows of this lane sit in 4 runs of 4 consecutive rows: one float4
+        // of normalisers per run
+        const uint32_t lrow = tile + T::kBytes + 16 * (lane >> 5);
 #pragma unroll
-          for (int i = 0; i < 16; ++i) sum += p[i];
-          cs[s] += sum;
+        for (int s = 0; s < 2; ++s) {
+          float part[4];
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const f32x4 f = lds_float4(lrow + 32 * g);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              const float p = fast_exp2(fmaf(acc[s][4 * g + j], a.c2, -f[j]));
+              part[j] = g == 0 ? p : part[j] + p;
+            }
+          }
+          cs[s] += (part[0] + part[1]) + (part[2] + part[3]);
         }
       }
-      if (t > t0) {
-        tile_lstore<D>(sQ[buf ^ 1], pre);
-        if (threadIdx.x < kTile) sL[buf ^ 1][threadIdx.x] = lpre;
-      }
-      __syncthreads();
     }
+#undef H2O_COLSUM_ISSUE
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
       const float c = cs[s] + __shfl_xor(cs[s], 32, kWave);
@@ -313,10 +408,7 @@ __global__ __launch_bounds__(64) void rowstats_f32(PrefillArgs a) {
       l += fast_exp2((dot - m) * a.c2);
     }
   }
-  const size_t o = static_cast<size_t>(unit) * a.Lpad + r;
-  a.row_max[o] = m * a.scale;
-  a.row_sum[o] = l;
-  a.row_lse2[o] = fmaf(m, a.c2, log2f(l));
+  a.row_lse2[static_cast<size_t>(unit) * a.Lpad + r] = fmaf(m, a.c2, log2f(l));
 }
 
 template <int D>
@@ -468,7 +560,7 @@ hipError_t launch_select(const PrefillArgs& a, int units, hipStream_t s) {
 
 template <int D>
 hipError_t launch_bf16(const PrefillArgs& a, int units, hipStream_t s) {
-  const int nblk = (a.L + kBlockRows - 1) / kBlockRows;
+  const int nblk = (a.L + kBlockRows - 1) / kBlockRows;  // row blocks; a block takes a pair
   const int groups = (units + kXcds - 1) / kXcds;
   const dim3 grid(groups * kXcds * ((nblk + 1) / 2));
   hipLaunchKernelGGL((rowstats_bf16<D>), grid, dim3(kThreads), 0, s, a, nblk, units);

@@ -49,7 +49,7 @@ _SIGNATURES = {
     "h2o_prefill": (_i32, [_vp, _vp, _vp, _vp, _i32, _vp]),
     "h2o_decode_step": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp]),
     "h2o_cache_read": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp]),
-    "h2o_prefill_stats_read": (_i32, [_vp, _vp, _vp, _vp, _vp]),
+    "h2o_prefill_stats_read": (_i32, [_vp, _vp, _vp, _vp]),
     "h2o_cache_info": (_i32, [_vp, _p32, _p32, _p32]),
     "h2o_status_str": (ctypes.c_char_p, [_i32]),
     "h2o_last_error": (ctypes.c_char_p, []),
@@ -105,8 +105,8 @@ def h2o_cache_read(cache, pos, score, k_slots, v_slots, meta, stream):
     return load().h2o_cache_read(cache, pos, score, k_slots, v_slots, meta, stream)
 
 
-def h2o_prefill_stats_read(cache, row_max, row_sum, col_sum, stream):
-    return load().h2o_prefill_stats_read(cache, row_max, row_sum, col_sum, stream)
+def h2o_prefill_stats_read(cache, row_lse, col_sum, stream):
+    return load().h2o_prefill_stats_read(cache, row_lse, col_sum, stream)
 
 
 def h2o_cache_info(cache, count, next_pos, prompt_len):
@@ -208,7 +208,7 @@ class H2OCache:
 
     def prefill_stats(self, stream=None):
         L = self.info()[2]
-        arrs = [np.empty((self.B, self.H, max(L, 0)), np.float32) for _ in range(3)]
+        arrs = [np.empty((self.B, self.H, max(L, 0)), np.float32) for _ in range(2)]
         check(h2o_prefill_stats_read(self.handle, *(_np_ptr(a) for a in arrs), self._stream(stream)),
               "h2o_prefill_stats_read")
         return tuple(arrs)

@@ -64,8 +64,7 @@ def unit_payload(g, b, h, Q, K, V, L, heavy, recent, out_index=None, tag=None):
     kept_pos = g["kept"]["pos"][b, h]
     st = None
     if g["stats"] is not None:
-        st = (g["stats"][0][b, h].astype(np.float64), g["stats"][1][b, h].astype(np.float64),
-              g["stats"][2][b, h].astype(np.float64))
+        st = (g["stats"][0][b, h].astype(np.float64), g["stats"][1][b, h].astype(np.float64))
     fin = g["final"]
     if g["out"] is None:
         out = np.zeros((0, Q.shape[1]))
@@ -96,7 +95,7 @@ def check_payloads(payloads, procs=None):
             results = pool.map(_oracle_worker.check_unit, payloads, chunksize=max(1, len(payloads) // (4 * procs)))
     bad = [r for r in results if not r["ok"]]
     worst = {key: max((r.get(key, 0.0) for r in results), default=0.0)
-             for key in ("out_err", "score_rel", "colsum_rel", "rowsum_rel", "rowmax_err")}
+             for key in ("out_err", "score_rel", "colsum_rel", "lse_err")}
     ties = sum(r.get("ties", 0) for r in results)
     log(f"oracle checked {len(results)} units in {time.time() - t0:.1f}s on {procs} procs; "
         f"worst {worst}; near-ties adopted {ties}; failures {len(bad)}")

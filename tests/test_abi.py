@@ -46,6 +46,9 @@ def _bytes(**kw):
     (dict(heavy=10000, recent=5000), H.H2O_ERR_UNSUPPORTED), (dict(dtype=7), H.H2O_ERR_INVALID_ARG),
     (dict(scale=float("nan")), H.H2O_ERR_INVALID_ARG), (dict(max_prompt=-1), H.H2O_ERR_INVALID_ARG),
     (dict(batch=1 << 16, heads=1 << 10, max_prompt=4096), H.H2O_ERR_INVALID_ARG),
+    # one unit's [max_prompt, d] bf16 prompt matrix must stay below 2^32 bytes
+    (dict(batch=1, heads=1, max_prompt=1 << 24), H.H2O_ERR_INVALID_ARG),
+    (dict(batch=1, heads=1, max_prompt=(1 << 24) - 32), H.H2O_OK),
     (dict(), H.H2O_OK), (dict(heavy=0, recent=1), H.H2O_OK), (dict(head_dim=64, dtype="f32"), H.H2O_OK),
 ])
 def test_param_validation(kw, status):
@@ -57,8 +60,9 @@ def test_param_validation(kw, status):
 def test_cache_bytes_accounting():
     st, kv, tot = _bytes(batch=2, heads=3, head_dim=128, heavy=4, recent=4, dtype="bf16", max_prompt=64)
     assert st == 0 and kv == 2 * 6 * 8 * 128 * 2
-    # + scores, compensation, positions (12 B / slot) + split scratch (few units) + 4 prefill rows
-    assert tot == kv + 6 * 8 * 12 + (6 * 64 * 130 * 4 + 6 * 9 * 4 + 6 * 4) + 4 * 6 * 64 * 4
+    # + scores, compensation, positions (12 B / slot) + split scratch (few units)
+    # + 2 prefill rows (row normaliser, column sum) per prompt position
+    assert tot == kv + 6 * 8 * 12 + (6 * 64 * 130 * 4 + 6 * 9 * 4 + 6 * 4) + 2 * 6 * 64 * 4
     st, kv32, _ = _bytes(dtype="f32")
     assert kv32 == 2 * kv
 
@@ -80,7 +84,7 @@ def test_null_and_state_checks_make_no_gpu_call():
     assert H.h2o_prefill(None, None, None, None, 0, None) == H.H2O_ERR_INVALID_ARG
     assert H.h2o_decode_step(None, None, None, None, None, None, None) == H.H2O_ERR_INVALID_ARG
     assert H.h2o_cache_read(None, None, None, None, None, None, None) == H.H2O_ERR_INVALID_ARG
-    assert H.h2o_prefill_stats_read(None, None, None, None, None) == H.H2O_ERR_INVALID_ARG
+    assert H.h2o_prefill_stats_read(None, None, None, None) == H.H2O_ERR_INVALID_ARG
     assert H.h2o_cache_info(None, None, None, None) == H.H2O_ERR_INVALID_ARG
     p = H.make_params(1, 1, 64, 2, 2, "f32")
     assert H.h2o_cache_create(ctypes.byref(p), -1, None) == H.H2O_ERR_INVALID_ARG
