@@ -85,7 +85,8 @@ def parse():
     ap.add_argument("--layers", type=int, default=None, help="override the layer count (profiling runs)")
     ap.add_argument("--decode-steps", type=int, default=None, help="override decode steps (profiling runs)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-units", type=int, default=8, help="units in the CPU-oracle sample")
+    ap.add_argument("--cpu-units", type=int, default=96,
+                    help="units in the CPU-oracle sample (about 15 s of CPU work at this shape)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (calibrates HBM byte counters)")
     return ap.parse_args()

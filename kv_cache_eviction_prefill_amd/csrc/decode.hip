@@ -71,9 +71,9 @@ __global__ __launch_bounds__(kThreads, 8) void decode_kernel(DecodeArgs a) {
   const T* kn = static_cast<const T*>(a.knew) + static_cast<size_t>(unit) * D;
   const T* vn = static_cast<const T*>(a.vnew) + static_cast<size_t>(unit) * D;
   float* glog = SPLIT ? a.logits + static_cast<size_t>(unit) * (a.k + 1) : nullptr;
-  float* sc = a.score + static_cast<size_t>(unit) * a.k;
-  float* cp = a.comp + static_cast<size_t>(unit) * a.k;
-  int32_t* ps = a.pos + static_cast<size_t>(unit) * a.k;
+  float* sc = a.score + static_cast<size_t>(unit) * a.kstride;
+  float* cp = a.comp + static_cast<size_t>(unit) * a.kstride;
+  int32_t* ps = a.pos + static_cast<size_t>(unit) * a.kstride;
 
   float qf[EPL];
   Elem<T>::unpack(ld16(qn + r * EPL), qf);

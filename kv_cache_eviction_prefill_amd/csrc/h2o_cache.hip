@@ -17,6 +17,7 @@ struct h2o_cache {
   h2o_params p;
   int device;
   int32_t d, k, units, esize;
+  int32_t kstride;  // per-unit stride of score/comp/pos: k rounded up to 32 entries
   float scale, c2;
   // host-side state
   int32_t count;       // entries cached per unit
@@ -112,7 +113,7 @@ h2o_status check_params(const h2o_params* p, Sizes* sz) {
     const size_t es = p->dtype == H2O_F32 ? 4 : 2;
     const size_t u = static_cast<size_t>(units), kk = static_cast<size_t>(k), d = p->head_dim;
     sz->kv = 2 * u * kk * d * es;
-    sz->meta = u * kk * 12;
+    sz->meta = u * static_cast<size_t>(round32(static_cast<int32_t>(k))) * 12;
     sz->max_split = units < kSplitUnits ? kMaxSplit : 1;
     sz->split = sz->max_split > 1
                     ? u * sz->max_split * (2 + d) * 4 + u * (kk + 1) * 4 + u * 4
@@ -196,6 +197,7 @@ h2o_status h2o_cache_create(const h2o_params* params, int device, h2o_cache** ou
   c->device = dev;
   c->d = params->head_dim;
   c->k = params->heavy_budget + params->recent_budget;
+  c->kstride = round32(c->k);
   c->units = params->batch * params->heads;
   c->esize = params->dtype == H2O_F32 ? 4 : 2;
   c->scale = params->scale > 0.f ? params->scale : 1.f / std::sqrt(static_cast<float>(c->d));
@@ -214,9 +216,9 @@ h2o_status h2o_cache_create(const h2o_params* params, int device, h2o_cache** ou
   } allocs[] = {
       {&c->kslots, u * kk * d * c->esize},
       {&c->vslots, u * kk * d * c->esize},
-      {reinterpret_cast<void**>(&c->score), u * kk * 4},
-      {reinterpret_cast<void**>(&c->comp), u * kk * 4},
-      {reinterpret_cast<void**>(&c->pos), u * kk * 4},
+      {reinterpret_cast<void**>(&c->score), u * c->kstride * 4},
+      {reinterpret_cast<void**>(&c->comp), u * c->kstride * 4},
+      {reinterpret_cast<void**>(&c->pos), u * c->kstride * 4},
       {reinterpret_cast<void**>(&c->part), c->max_split > 1 ? u * c->max_split * (2 + d) * 4 : 0},
       {reinterpret_cast<void**>(&c->logits), c->max_split > 1 ? u * (kk + 1) * 4 : 0},
       {reinterpret_cast<void**>(&c->counters), c->max_split > 1 ? u * 4 : 0},
@@ -232,7 +234,7 @@ h2o_status h2o_cache_create(const h2o_params* params, int device, h2o_cache** ou
       return hip_fail(e, "hipMalloc");
     }
   }
-  hipError_t e = h2o::launch_clear(c->pos, c->score, c->comp, u * kk, nullptr);
+  hipError_t e = h2o::launch_clear(c->pos, c->score, c->comp, u * c->kstride, nullptr);
   if (e == hipSuccess && c->counters != nullptr) e = hipMemset(c->counters, 0, u * 4);
   if (e == hipSuccess) e = hipDeviceSynchronize();
   if (e != hipSuccess) {
@@ -266,7 +268,7 @@ h2o_status h2o_prefill(h2o_cache* c, const void* q, const void* k, const void* v
   DeviceGuard guard(c->device);
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (L == 0) {
-    const hipError_t e = h2o::launch_clear(c->pos, c->score, c->comp, static_cast<size_t>(c->units) * c->k, s);
+    const hipError_t e = h2o::launch_clear(c->pos, c->score, c->comp, static_cast<size_t>(c->units) * c->kstride, s);
     if (e != hipSuccess) return hip_fail(e, "clear launch");
   } else {
     h2o::PrefillArgs a{};
@@ -285,6 +287,7 @@ h2o_status h2o_prefill(h2o_cache* c, const void* q, const void* k, const void* v
     a.heavy = c->p.heavy_budget;
     a.recent = c->p.recent_budget;
     a.kcap = c->k;
+    a.kstride = c->kstride;
     a.scale = c->scale;
     a.c2 = c->c2;
     const hipError_t e = h2o::launch_prefill(c->p.dtype, c->d, a, c->units, s);
@@ -324,6 +327,7 @@ h2o_status h2o_decode_step(h2o_cache* c, const void* q, const void* k, const voi
   a.logits = c->logits;
   a.counters = c->counters;
   a.k = c->k;
+  a.kstride = c->kstride;
   a.count = c->count;
   a.new_pos = c->next_pos;
   a.cand_limit = c->next_pos - c->p.recent_budget;
@@ -344,9 +348,12 @@ h2o_status h2o_cache_read(h2o_cache* c, int32_t* pos, float* score, void* k_slot
   hipError_t e = hipStreamSynchronize(static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "hipStreamSynchronize");
   const size_t n = static_cast<size_t>(c->units) * c->k;
-  if (pos != nullptr && (e = hipMemcpy(pos, c->pos, n * 4, hipMemcpyDeviceToHost)) != hipSuccess)
+  const size_t row = static_cast<size_t>(c->k) * 4, pitch = static_cast<size_t>(c->kstride) * 4;
+  if (pos != nullptr &&
+      (e = hipMemcpy2D(pos, row, c->pos, pitch, row, c->units, hipMemcpyDeviceToHost)) != hipSuccess)
     return hip_fail(e, "copy pos");
-  if (score != nullptr && (e = hipMemcpy(score, c->score, n * 4, hipMemcpyDeviceToHost)) != hipSuccess)
+  if (score != nullptr &&
+      (e = hipMemcpy2D(score, row, c->score, pitch, row, c->units, hipMemcpyDeviceToHost)) != hipSuccess)
     return hip_fail(e, "copy score");
   const size_t kvb = n * c->d * c->esize;
   if (k_slots != nullptr && (e = hipMemcpy(k_slots, c->kslots, kvb, hipMemcpyDeviceToHost)) != hipSuccess)

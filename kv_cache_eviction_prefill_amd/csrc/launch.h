@@ -13,15 +13,16 @@ struct DecodeArgs {
   const void* vnew;  // [units, d] new value
   void* kslots;      // [units, k, d]
   void* vslots;      // [units, k, d]
-  float* score;      // [units, k] running score (Kahan sum)
-  float* comp;       // [units, k] Kahan compensation
-  int32_t* pos;      // [units, k] position per slot, -1 when empty
+  float* score;      // [units, kstride] running score (Kahan sum)
+  float* comp;       // [units, kstride] Kahan compensation
+  int32_t* pos;      // [units, kstride] position per slot, -1 when empty
   float* out;        // [units, d]
   int32_t* evicted;  // [units] or nullptr
   float* part;       // split mode: [units, nsplit, 2 + d] partial (max, sum, o)
   float* logits;     // split mode: [units, k + 1] base-2 logits (new token at index k)
   uint32_t* counters;  // split mode: [units] arrival counters, zero between launches
   int32_t k;           // slots per unit
+  int32_t kstride;     // per-unit stride of score/comp/pos: k rounded up to 32 (128-byte rows)
   int32_t count;       // occupied slots before this step (slots 0..count-1)
   int32_t new_pos;     // position i of the new token
   int32_t cand_limit;  // positions <= cand_limit are eviction candidates (i - K_r)
@@ -44,12 +45,13 @@ struct PrefillArgs {
   float* col_sum;     // [units, Lpad] attention received by each prompt token
   void* kslots;       // [units, k, d]
   void* vslots;       // [units, k, d]
-  float* score;       // [units, k]
-  float* comp;        // [units, k]
-  int32_t* pos;       // [units, k]
+  float* score;       // [units, kstride]
+  float* comp;        // [units, kstride]
+  int32_t* pos;       // [units, kstride]
   int32_t heavy;
   int32_t recent;
   int32_t kcap;       // k
+  int32_t kstride;    // per-unit stride of score/comp/pos
   float scale;
   float c2;           // scale * log2(e)
 };

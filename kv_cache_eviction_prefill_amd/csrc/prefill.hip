@@ -516,9 +516,9 @@ __global__ __launch_bounds__(kThreads) void select_fill(PrefillArgs a) {
   }
   __syncthreads();
 
-  float* sc = a.score + static_cast<size_t>(unit) * kc;
-  float* cp = a.comp + static_cast<size_t>(unit) * kc;
-  int32_t* ps = a.pos + static_cast<size_t>(unit) * kc;
+  float* sc = a.score + static_cast<size_t>(unit) * a.kstride;
+  float* cp = a.comp + static_cast<size_t>(unit) * a.kstride;
+  int32_t* ps = a.pos + static_cast<size_t>(unit) * a.kstride;
   for (int s = tid; s < kc; s += kThreads) {
     if (s < nkept) {
       const int j = s_kept[s];

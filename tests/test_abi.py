@@ -60,9 +60,9 @@ def test_param_validation(kw, status):
 def test_cache_bytes_accounting():
     st, kv, tot = _bytes(batch=2, heads=3, head_dim=128, heavy=4, recent=4, dtype="bf16", max_prompt=64)
     assert st == 0 and kv == 2 * 6 * 8 * 128 * 2
-    # + scores, compensation, positions (12 B / slot) + split scratch (few units)
-    # + 2 prefill rows (row normaliser, column sum) per prompt position
-    assert tot == kv + 6 * 8 * 12 + (6 * 64 * 130 * 4 + 6 * 9 * 4 + 6 * 4) + 2 * 6 * 64 * 4
+    # + scores, compensation, positions (12 B / slot, rows padded to 32 slots)
+    # + split scratch (few units) + 2 prefill rows (row normaliser, column sum)
+    assert tot == kv + 6 * 32 * 12 + (6 * 64 * 130 * 4 + 6 * 9 * 4 + 6 * 4) + 2 * 6 * 64 * 4
     st, kv32, _ = _bytes(dtype="f32")
     assert kv32 == 2 * kv
 
