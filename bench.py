@@ -41,15 +41,18 @@ def decode_bytes_per_unit(c: int, d: int, s: int) -> int:
     return c * (2 * d * s + 12) + d * (5 * s + 4)
 
 
-def prefill_flops_per_unit(L: int, d: int) -> int:
-    """MFMA flops of the two causal QK^T passes over the L(L+1)/2 pairs."""
-    return 2 * L * (L + 1) * d
+def prefill_flops_per_unit(L: int, d: int, with_out: bool = False) -> int:
+    """MFMA flops of the two causal QK^T passes over the L(L+1)/2 pairs; with the
+    prompt's attention output, its pass adds one more QK^T and a PV over the pairs."""
+    return 2 * L * (L + 1) * d * (2 if with_out else 1)
 
 
-def prefill_bytes_per_unit(L: int, k: int, d: int, s: int) -> int:
-    """Q and K read once (2Lds); kept V rows gathered, K/V slots written (3 min(L,k) ds); meta."""
+def prefill_bytes_per_unit(L: int, k: int, d: int, s: int, with_out: bool = False) -> int:
+    """Q and K read once (2Lds); kept V rows gathered, K/V slots written (3 min(L,k) ds); meta.
+    With the prompt's attention output: V read once (Lds) and the fp32 output written (4Ld)."""
     kept = min(L, k)
-    return 2 * L * d * s + 3 * kept * d * s + 12 * kept
+    extra = L * d * s + 4 * L * d if with_out else 0
+    return 2 * L * d * s + 3 * kept * d * s + 12 * kept + extra
 
 
 TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "hbm_traffic-opt6.7b-32L-b64.md")
@@ -85,6 +88,8 @@ def parse():
     ap.add_argument("--layers", type=int, default=None, help="override the layer count (profiling runs)")
     ap.add_argument("--decode-steps", type=int, default=None, help="override decode steps (profiling runs)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--prefill-out", action="store_true",
+                    help="prefill also writes the prompt's attention output (fp32 [B, H, L, d])")
     ap.add_argument("--cpu-units", type=int, default=96,
                     help="units in the CPU-oracle sample (about 15 s of CPU work at this shape)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -163,6 +168,9 @@ def main():
         del q, k, v
     caches = [H2OCache(B, H, d, w.heavy_budget, w.recent_budget, dtype=w.dtype, max_prompt=L) for _ in range(NL)]
     out = torch.empty((NL, B, H, d), dtype=torch.float32, device=dev)
+    # the prompt attention output, when asked for: one buffer shared by the layers
+    pout = torch.empty((B, H, L, d), dtype=torch.float32, device=dev) if a.prefill_out else None
+    pout_ptr = pout.data_ptr() if pout is not None else None
     ev = torch.empty((NL, B, H), dtype=torch.int32, device=dev)
     torch.cuda.synchronize()
     gen_s = time.time() - t_gen
@@ -179,7 +187,7 @@ def main():
         if evs is not None:
             evs[0].record(stream)
         for l in range(NL):
-            st = prefill_c(handles[l], *pre_ptr[l], L, sp)
+            st = prefill_c(handles[l], *pre_ptr[l], L, pout_ptr, sp)
             if st:
                 raise h2o.H2OError(st, "h2o_prefill", h2o.h2o_last_error())
         if evs is not None:
@@ -227,8 +235,8 @@ def main():
     dec_bytes_launch = B * H * sum(decode_bytes_per_unit(min(w.k, L + t), d, s) for t in range(T)) / T
     avg_dec_s = t_dec / launches
     achieved = dec_bytes_launch / avg_dec_s / 1e9
-    pf_flops = NL * B * H * prefill_flops_per_unit(L, d) * K
-    pf_bytes = NL * B * H * prefill_bytes_per_unit(L, w.k, d, s) * K
+    pf_flops = NL * B * H * prefill_flops_per_unit(L, d, a.prefill_out) * K
+    pf_bytes = NL * B * H * prefill_bytes_per_unit(L, w.k, d, s, a.prefill_out) * K
     res = {
         "metric": METRIC,
         "value": tokens / t_all,
@@ -244,7 +252,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "layers": NL, "batch": B, "heads": H, "head_dim": d,
                    "prompt_len": L, "decode_steps": T, "heavy_budget": w.heavy_budget,
-                   "recent_budget": w.recent_budget, "storage": w.dtype, "accumulate": "fp32"},
+                   "recent_budget": w.recent_budget, "storage": w.dtype, "accumulate": "fp32",
+                   "prefill_out": bool(a.prefill_out)},
         "roofline": {"kernel": "decode_kernel<bf16,128>", "bound": "hbm", "achieved": achieved,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic(w.name) if a.layers is None else None,
                      "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",

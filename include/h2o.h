@@ -101,6 +101,10 @@ h2o_status h2o_cache_destroy(h2o_cache* cache);
 /* Prefill (Report §3.4, prefill rule).  (Re)initialises the cache from a prompt
  * of `prompt_len` tokens.
  *   q, k, v: device, [B, H, prompt_len, d] in the cache dtype.
+ *   out:     device, nullable, [B, H, prompt_len, d] float32: when non-NULL it
+ *            receives the prompt's own attention output o_r = sum_{j<=r} a_rj v_j
+ *            (every prompt row attends fully; eviction starts after the prompt).
+ *            bf16 caches form it from bf16-rounded weights a_rj.
  * For each unit: every prompt row r attends causally (positions 0..r, itself
  * included) with a = softmax(scale * q_r . k_j); token j's score is the total
  * attention it receives, c_j = sum_{r >= j} a_rj (Report §2.3, §3.3).  If
@@ -108,12 +112,12 @@ h2o_status h2o_cache_destroy(h2o_cache* cache);
  * plus the K_h best-scored of positions [0, prompt_len - K_r), ranked by score,
  * equal scores ranked by position (the higher position wins).  Kept tokens'
  * K/V rows are copied into slots with their scores; the step counter is set to
- * prompt_len.  prompt_len == 0 gives an empty cache.  q/k/v may be NULL when
+ * prompt_len.  prompt_len == 0 gives an empty cache.  q/k/v/out may be NULL when
  * prompt_len == 0.
  * Errors: H2O_ERR_INVALID_ARG (NULL or misaligned pointers, prompt_len < 0 or
  * > max_prompt), H2O_ERR_HIP. */
 h2o_status h2o_prefill(h2o_cache* cache, const void* q, const void* k, const void* v,
-                       int32_t prompt_len, void* stream);
+                       int32_t prompt_len, float* out, void* stream);
 
 /* One decode step for every unit (Report §3.1, §3.3, §3.4 decode rule; Card).
  *   q, k, v: device, [B, H, d] in the cache dtype: the new token (position i,

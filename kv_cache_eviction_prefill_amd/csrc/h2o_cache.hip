@@ -256,7 +256,8 @@ h2o_status h2o_cache_destroy(h2o_cache* c) {
   return H2O_OK;
 }
 
-h2o_status h2o_prefill(h2o_cache* c, const void* q, const void* k, const void* v, int32_t L, void* stream) {
+h2o_status h2o_prefill(h2o_cache* c, const void* q, const void* k, const void* v, int32_t L, float* out,
+                       void* stream) {
   if (c == nullptr) return fail(H2O_ERR_INVALID_ARG, "cache is NULL");
   if (L < 0) return fail(H2O_ERR_INVALID_ARG, "prompt_len must be >= 0");
   if (L > c->p.max_prompt) return fail(H2O_ERR_INVALID_ARG, "prompt_len exceeds max_prompt");
@@ -264,6 +265,7 @@ h2o_status h2o_prefill(h2o_cache* c, const void* q, const void* k, const void* v
     if (q == nullptr || k == nullptr || v == nullptr) return fail(H2O_ERR_INVALID_ARG, "q, k, v must be non-NULL");
     if (!aligned16(q) || !aligned16(k) || !aligned16(v))
       return fail(H2O_ERR_INVALID_ARG, "q, k, v must be 16-byte aligned");
+    if (out != nullptr && !aligned16(out)) return fail(H2O_ERR_INVALID_ARG, "out must be 16-byte aligned");
   }
   DeviceGuard guard(c->device);
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -279,6 +281,7 @@ h2o_status h2o_prefill(h2o_cache* c, const void* q, const void* k, const void* v
     a.Lpad = round32(L);
     a.row_lse2 = c->row_lse2;
     a.col_sum = c->col_sum;
+    a.out = out;
     a.kslots = c->kslots;
     a.vslots = c->vslots;
     a.score = c->score;

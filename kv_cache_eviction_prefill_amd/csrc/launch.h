@@ -43,6 +43,7 @@ struct PrefillArgs {
   int32_t Lpad;       // stride of the per-row scratch arrays (multiple of 32, >= L)
   float* row_lse2;    // [units, Lpad] log2 sum_j exp2(c2 q_r.k_j) of each row; 0 past L
   float* col_sum;     // [units, Lpad] attention received by each prompt token
+  float* out;         // [units, L, d] prompt attention output, or nullptr
   void* kslots;       // [units, k, d]
   void* vslots;       // [units, k, d]
   float* score;       // [units, kstride]

@@ -16,6 +16,8 @@
 //                 logits as MFMA tiles of S = Q K^T (one lane per key column);
 //                 the causal softmax is row-normalised, so the column sums need
 //                 the row normalisers of pass 1 first.
+//   (optional) attnout: the prompt's own attention output o_r = sum_j a_rj v_j,
+//                 recomputing the logits with the exact row normalisers.
 //   3. select_fill: per unit, a radix select on the 64-bit key (score bits,
 //                 position) finds the K_h-th best heavy-hitter candidate, a
 //                 ballot/popcount compaction assigns slots in position order,
@@ -384,6 +386,162 @@ __global__ __launch_bounds__(kThreads, 4) void colsum_bf16(PrefillArgs a, int nb
   }
 }
 
+// ------------------------------------------------------------------ prompt attention output
+// Pass 3, run only when the caller asks for the prompt's own attention output:
+// o_r = sum_{j<=r} exp2(c2 q_r.k_j - lse2_r) v_j with the exact row normalisers of
+// pass 1, so no running rescale is needed.  Each of a block's 4 waves keeps 32
+// query rows in registers; K and V tiles stream through two rings of three
+// swizzled LDS tiles (global -> LDS loads).  S^T = K Q^T per tile gives each lane
+// one query's weights for 16 keys; rounded to bf16 they are the B operand of
+// O^T += V^T P^T.  The V^T operand comes from the transposing LDS read: in each
+// group of 16 lanes, output lane 4a+b takes element b of the 8-byte reads of
+// lanes a, a+4, a+8, a+12, so pointing those lanes at 4 consecutive d values of
+// 4 different key rows hands every lane 4 keys of one d column - in the key order
+// of the S^T accumulator (element i of lane l is key 8(i/4) + 4(l/32) + i%4).
+constexpr int kOutRows = 128;  // 4 waves x 32 query rows
+
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+__device__ inline i16x4 lds_tr16(uint32_t addr) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(static_cast<uintptr_t>(addr)));
+}
+
+// Byte offset, inside a swizzled tile, of 16-bit element `col` of tile row `key`.
+template <int D>
+__device__ inline uint32_t tile_elem_offset(int key, int col) {
+  using T = Tile<D>;
+  const int byte = 2 * col;
+  return key * T::kRowBytes + ((((byte >> 4) ^ (key & T::kSwz))) << 4) + (byte & 15);
+}
+
+template <int D>
+__global__ __launch_bounds__(kThreads, 3) void attnout_bf16(PrefillArgs a, int nblk, int units) {
+  using T = Tile<D>;
+  constexpr int NDB = D / 32;  // 32-wide column blocks of the output
+  __shared__ __align__(256) unsigned char sK[kBufs][T::kBytes];
+  __shared__ __align__(256) unsigned char sV[kBufs][T::kBytes];
+  const int npair = (nblk + 1) / 2;
+  int unit, pb;
+  if (!block_coords(npair, units, &unit, &pb)) return;
+  const int L = a.L;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave), lane = threadIdx.x % kWave;
+  const int fr = lane & 31, hh = lane >> 5;
+  const bf16_t* Qu = static_cast<const bf16_t*>(a.q) + static_cast<size_t>(unit) * L * D;
+  const bf16_t* Ku = static_cast<const bf16_t*>(a.k) + static_cast<size_t>(unit) * L * D;
+  const bf16_t* Vu = static_cast<const bf16_t*>(a.v) + static_cast<size_t>(unit) * L * D;
+  const float* lse = a.row_lse2 + static_cast<size_t>(unit) * a.Lpad;
+  float* out = a.out + static_cast<size_t>(unit) * L * D;
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(Ku, static_cast<uint32_t>(L) * T::kRowBytes);
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc(Vu, static_cast<uint32_t>(L) * T::kRowBytes);
+  const int voff = tile_voff<D>();
+  const uint32_t xo = frag_offset<D>(lane);
+  // this lane's role as a source of the transposing read: key row 4(g/2) + j
+  // (+ 8 for the second read, + 16 for the second 16-key block), d columns
+  // 16(g%2) + 4a .. +3 (+ 32 per column block), g = lane / 16, a = lane % 4,
+  // j = (lane / 4) % 4
+  const int tkey = 4 * (lane >> 5) + ((lane >> 2) & 3);
+  const int tcol = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+  for (int h = 0; h < 2; ++h) {
+    const int blk = h == 0 ? nblk - 1 - pb : pb;
+    if (h == 1 && blk == nblk - 1 - pb) break;
+    const int qw = blk * kOutRows + wave * 32;
+    const int ntile = (min(blk * kOutRows + kOutRows, L) - 1) / kTile + 1;
+    if (h == 1) tile_barrier();
+    bf16x8 bq[D / 16];
+    row_frag<D>(Qu, qw + fr, L, lane, bq);
+    const float lq = qw + fr < L ? lse[qw + fr] : 0.f;
+    tile_async(rk, voff, 0, sK[0], T::kRowBytes, T::kLoads);
+    tile_async(rv, voff, 0, sV[0], T::kRowBytes, T::kLoads);
+    if (ntile > 1) {
+      tile_async(rk, voff, kTile, sK[1], T::kRowBytes, T::kLoads);
+      tile_async(rv, voff, kTile, sV[1], T::kRowBytes, T::kLoads);
+    }
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) asm volatile("" : "+v"(bq[kk]));
+    floatx16 o[NDB];
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) o[db] = floatx16{};
+    for (int t = 0; t < ntile; ++t) {
+      if (t + 1 < ntile) wait_vm<2 * T::kLoads>();  // K and V of this tile landed
+      else wait_vm<0>();
+      tile_barrier();
+      if (t + 2 < ntile) {
+        tile_async(rk, voff, (t + 2) * kTile, sK[(t + 2) % kBufs], T::kRowBytes, T::kLoads);
+        tile_async(rv, voff, (t + 2) * kTile, sV[(t + 2) % kBufs], T::kRowBytes, T::kLoads);
+      }
+      const int k0 = t * kTile;
+      if (qw < L && k0 <= qw + 31) {
+        uint32_t fb = lds_addr(sK[t % kBufs]) + xo;
+        asm volatile("" : "+v"(fb));
+        floatx16 sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tile_frag_kk(fb, 0), bq[0], floatx16{}, 0, 0, 0);
+#pragma unroll
+        for (int kk = 1; kk < D / 16; ++kk)
+          sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tile_frag_kk(fb, kk), bq[kk], sacc, 0, 0, 0);
+        if (k0 + kTile - 1 > qw) {  // diagonal tile: keys after the query get weight 0
+          const int rel = qw + fr - k0 - 4 * hh;
+#pragma unroll
+          for (int i = 0; i < 16; ++i) sacc[i] = (8 * (i >> 2) + (i & 3)) <= rel ? sacc[i] : -INFINITY;
+        }
+        bf16x8 pw[2];  // weights of keys 16kb.. as the B operand, kb = 0, 1
+#pragma unroll
+        for (int i = 0; i < 16; ++i) pw[i >> 3][i & 7] = static_cast<__bf16>(fast_exp2(fmaf(sacc[i], a.c2, -lq)));
+        uint32_t vt = lds_addr(sV[t % kBufs]);
+        asm volatile("" : "+v"(vt));
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb) {
+            const i16x4 lo = lds_tr16(vt + tile_elem_offset<D>(tkey + 16 * kb, tcol + 32 * db));
+            const i16x4 hi = lds_tr16(vt + tile_elem_offset<D>(tkey + 16 * kb + 8, tcol + 32 * db));
+            const bf16x8 av = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+            o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pw[kb], o[db], 0, 0, 0);
+          }
+        }
+      }
+    }
+    // o[db] element i of lane (fr, hh) is d = 32 db + 8(i/4) + 4 hh + i%4 of query qw + fr
+    if (qw + fr < L) {
+      float* orow = out + static_cast<size_t>(qw + fr) * D;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+          *reinterpret_cast<float4*>(orow + 32 * db + 8 * g + 4 * hh) =
+              make_float4(o[db][4 * g], o[db][4 * g + 1], o[db][4 * g + 2], o[db][4 * g + 3]);
+    }
+  }
+}
+
+// fp32 inputs: one thread per prompt row, VALU.
+template <int D>
+__global__ __launch_bounds__(64) void attnout_f32(PrefillArgs a) {
+  const int nblk = (a.L + 63) / 64;
+  const int unit = blockIdx.x / nblk;
+  const int r = (blockIdx.x % nblk) * 64 + threadIdx.x;
+  if (r >= a.L) return;
+  const float* Qu = static_cast<const float*>(a.q) + static_cast<size_t>(unit) * a.L * D;
+  const float* Ku = static_cast<const float*>(a.k) + static_cast<size_t>(unit) * a.L * D;
+  const float* Vu = static_cast<const float*>(a.v) + static_cast<size_t>(unit) * a.L * D;
+  const float lq = a.row_lse2[static_cast<size_t>(unit) * a.Lpad + r];
+  float q[D], o[D];
+#pragma unroll
+  for (int e = 0; e < D; ++e) {
+    q[e] = Qu[static_cast<size_t>(r) * D + e];
+    o[e] = 0.f;
+  }
+  for (int j = 0; j <= r; ++j) {
+    float dot = 0.f;
+#pragma unroll
+    for (int e = 0; e < D; ++e) dot = fmaf(q[e], Ku[static_cast<size_t>(j) * D + e], dot);
+    const float p = fast_exp2(fmaf(dot, a.c2, -lq));
+#pragma unroll
+    for (int e = 0; e < D; ++e) o[e] = fmaf(p, Vu[static_cast<size_t>(j) * D + e], o[e]);
+  }
+  float* orow = a.out + (static_cast<size_t>(unit) * a.L + r) * D;
+#pragma unroll
+  for (int e = 0; e < D; ++e) orow[e] = o[e];
+}
+
 // ------------------------------------------------------------------ fp32 (VALU) passes
 template <int D>
 __global__ __launch_bounds__(64) void rowstats_f32(PrefillArgs a) {
@@ -569,6 +727,13 @@ hipError_t launch_bf16(const PrefillArgs& a, int units, hipStream_t s) {
   hipLaunchKernelGGL((colsum_bf16<D>), grid, dim3(kThreads), 0, s, a, nblk, units);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
+  if (a.out != nullptr) {
+    const int nb3 = (a.L + kOutRows - 1) / kOutRows;
+    const dim3 grid3(groups * kXcds * ((nb3 + 1) / 2));
+    hipLaunchKernelGGL((attnout_bf16<D>), grid3, dim3(kThreads), 0, s, a, nb3, units);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   return launch_select<bf16_t, D>(a, units, s);
 }
 
@@ -581,6 +746,11 @@ hipError_t launch_f32(const PrefillArgs& a, int units, hipStream_t s) {
   hipLaunchKernelGGL((colsum_f32<D>), dim3(units * nblk), dim3(64), 0, s, a);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
+  if (a.out != nullptr) {
+    hipLaunchKernelGGL((attnout_f32<D>), dim3(units * nblk), dim3(64), 0, s, a);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   return launch_select<float, D>(a, units, s);
 }
 

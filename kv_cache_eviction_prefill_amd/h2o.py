@@ -46,7 +46,7 @@ _SIGNATURES = {
                                ctypes.POINTER(ctypes.c_size_t)]),
     "h2o_cache_create": (_i32, [ctypes.POINTER(h2o_params), ctypes.c_int, ctypes.POINTER(_vp)]),
     "h2o_cache_destroy": (_i32, [_vp]),
-    "h2o_prefill": (_i32, [_vp, _vp, _vp, _vp, _i32, _vp]),
+    "h2o_prefill": (_i32, [_vp, _vp, _vp, _vp, _i32, _vp, _vp]),
     "h2o_decode_step": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp]),
     "h2o_cache_read": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp]),
     "h2o_prefill_stats_read": (_i32, [_vp, _vp, _vp, _vp]),
@@ -93,8 +93,8 @@ def h2o_cache_destroy(cache):
     return load().h2o_cache_destroy(cache)
 
 
-def h2o_prefill(cache, q, k, v, prompt_len, stream):
-    return load().h2o_prefill(cache, q, k, v, prompt_len, stream)
+def h2o_prefill(cache, q, k, v, prompt_len, out, stream):
+    return load().h2o_prefill(cache, q, k, v, prompt_len, out, stream)
 
 
 def h2o_decode_step(cache, q, k, v, out, evicted, stream):
@@ -168,11 +168,13 @@ class H2OCache:
         return t.data_ptr()
 
     # -- entry points
-    def prefill(self, q, k, v, stream=None):
+    def prefill(self, q, k, v, out=None, stream=None):
+        """``out``: optional float32 [B, H, L, d] tensor for the prompt's attention output."""
         L = q.shape[2] if q is not None else 0
         shape = (self.B, self.H, L, self.d)
         ptrs = [self._check_t(t, shape, self.tdtype, n) if L > 0 else None for t, n in ((q, "q"), (k, "k"), (v, "v"))]
-        check(h2o_prefill(self.handle, *ptrs, L, self._stream(stream)), "h2o_prefill")
+        op = self._check_t(out, shape, self.torch.float32, "out") if (out is not None and L > 0) else None
+        check(h2o_prefill(self.handle, *ptrs, L, op, self._stream(stream)), "h2o_prefill")
 
     def decode_step(self, q, k, v, out=None, evicted=None, stream=None):
         torch = self.torch

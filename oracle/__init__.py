@@ -6,5 +6,5 @@ definitions and the readings it takes.
 """
 from .h2o_oracle import (  # noqa: F401
     TIE_RTOL, ParityMismatch, PrefillScores, UnitCache, default_scale, prefill_keep,
-    prefill_scores, run_unit, softmax,
+    prefill_output, prefill_scores, run_unit, softmax,
 )

@@ -94,6 +94,16 @@ def prefill_scores(Q: np.ndarray, K: np.ndarray, scale: float) -> PrefillScores:
     return PrefillScores(col_sum=A.sum(axis=0), row_max=row_max, row_sum=row_sum, weights=A)
 
 
+def prefill_output(Q: np.ndarray, K: np.ndarray, V: np.ndarray, scale: float) -> np.ndarray:
+    """The prompt's own attention output o_r = sum over j <= r of a_rj v_j, with the
+    causal weights of ``prefill_scores``.  The prompt is attended in full: H2O
+    bounds the cache only from the first generated token on.  [Report §3.4,
+    prefill rule]
+    """
+    A = prefill_scores(Q, K, scale).weights
+    return A @ np.asarray(V, np.float64)
+
+
 def prefill_keep(c: np.ndarray, heavy: int, recent: int, prefer=None, tie_rtol: float = TIE_RTOL):
     """Positions kept after the prompt.  [Report §3.4, prefill rule]
 

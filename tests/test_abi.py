@@ -81,7 +81,7 @@ def test_kv_size_matches_reported_example():
 def test_null_and_state_checks_make_no_gpu_call():
     lib = H.load()
     assert H.h2o_cache_destroy(None) == H.H2O_OK
-    assert H.h2o_prefill(None, None, None, None, 0, None) == H.H2O_ERR_INVALID_ARG
+    assert H.h2o_prefill(None, None, None, None, 0, None, None) == H.H2O_ERR_INVALID_ARG
     assert H.h2o_decode_step(None, None, None, None, None, None, None) == H.H2O_ERR_INVALID_ARG
     assert H.h2o_cache_read(None, None, None, None, None, None, None) == H.H2O_ERR_INVALID_ARG
     assert H.h2o_prefill_stats_read(None, None, None, None) == H.H2O_ERR_INVALID_ARG

@@ -1,0 +1,139 @@
+"""The prompt's own attention output (optional ``out`` of the prefill) against the
+oracle, through the C ABI (needs an MI355X).
+
+Tolerance, per output element (r, e), derived from the arithmetic:
+  - f32 caches: logits, normaliser and weights in fp32, so every weight carries a
+    relative error of a few fp32 ulps times the logit magnitude; 2e-5 relative to
+    m_re = sum_j a_rj |v_je| covers it.
+  - bf16 caches: the weights a_rj are rounded to bfloat16 (relative error at most
+    2^-8) before the product with V, so |o - o_exact| <= 2^-8 m_re plus the fp32
+    terms above.
+A wrong weight, key or value row gives errors of the order of m_re itself.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from workload import get, scaled, synth
+
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():
+    pytest.skip("no GPU", allow_module_level=True)
+
+from gpu_harness import log  # noqa: E402
+from kv_cache_eviction_prefill_amd import H2OCache  # noqa: E402
+from oracle import prefill_output, prefill_scores  # noqa: E402
+
+DEV = torch.device("cuda", 0)
+REL = {"f32": 2e-5, "bf16": 2.0 ** -8 + 2e-5}
+ABS = {"f32": 1e-6, "bf16": 1e-5}
+
+
+def _gpu_prefill_out(w, q, k, v):
+    B, H, L, d = q.shape
+    cache = H2OCache(B, H, d, w.heavy_budget, w.recent_budget, dtype=w.dtype, max_prompt=L)
+    out = torch.full((B, H, L, d), float("nan"), dtype=torch.float32, device=DEV)
+    cache.prefill(q, k, v, out=out)
+    res = {"out": out, "kept": cache.read(), "stats": cache.prefill_stats()}
+    cache.close()
+    return res
+
+
+def _check_unit(w, Q, K, V, o, tag):
+    """Compare one unit's [L, d] output with the oracle; returns the worst err/bound."""
+    Q, K, V = (np.asarray(x, np.float64) for x in (Q, K, V))
+    scale = 1.0 / math.sqrt(Q.shape[1])
+    ref = prefill_output(Q, K, V, scale)
+    mag = prefill_scores(Q, K, scale).weights @ np.abs(V)
+    bound = REL[w.dtype] * mag + ABS[w.dtype]
+    assert np.isfinite(o).all(), f"{tag}: output not fully written"
+    err = np.abs(o.astype(np.float64) - ref)
+    worst = float((err / bound).max())
+    bad = np.argwhere(err > bound)
+    assert bad.size == 0, (f"{tag}: {len(bad)} elements outside the bound, first (row, col) "
+                           f"{bad[0].tolist()}: got {o[tuple(bad[0])]}, oracle {ref[tuple(bad[0])]}")
+    return worst
+
+
+def _run(w, units=None):
+    Q, K, V = synth.batch_qkv(w, 0, 0, w.prompt_len)
+    q, k, v = (synth.to_torch(w, x, DEV) for x in (Q, K, V))
+    g = _gpu_prefill_out(w, q, k, v)
+    g["out"] = g["out"].cpu().numpy()
+    units = units or [(b, h) for b in range(w.batch) for h in range(w.heads)]
+    worst = max(_check_unit(w, Q[b, h], K[b, h], V[b, h], g["out"][b, h], f"b{b}h{h}") for b, h in units)
+    log(f"prefill output {w.dtype} d={w.head_dim} L={w.prompt_len} units={len(units)}: worst err/bound {worst:.3f}")
+    return g, (q, k, v)
+
+
+def test_tiny_fp32_prefill_output():
+    _run(get("tiny-fp32"))
+
+
+@pytest.mark.parametrize("d,L", [(128, 70), (64, 1), (64, 129)])
+def test_fp32_shapes(d, L):
+    _run(scaled(get("tiny-fp32"), batch=2, heads=2, head_dim=d, prompt_len=L, decode_steps=0,
+                n_anchors=max(1, L // 50)))
+
+
+@pytest.mark.parametrize("d,L,B,H", [
+    (128, 1, 2, 2),       # one row: o_0 = v_0
+    (128, 31, 2, 2),      # shorter than one key tile
+    (128, 77, 2, 3),      # ragged, inside one 128-row block
+    (64, 128, 2, 2),      # exactly one row block
+    (64, 513, 1, 2),      # five row blocks and a one-row tail
+    (128, 300, 1, 4),     # three row blocks, ragged
+    (128, 1000, 1, 2),    # many key tiles, two rows of blocks per pair
+])
+def test_bf16_shapes(d, L, B, H):
+    w = scaled(get("opt6.7b-layer-b16"), batch=B, heads=H, head_dim=d, prompt_len=L, decode_steps=0,
+               n_anchors=max(1, L // 50))
+    _run(w)
+
+
+def test_output_leaves_cache_and_statistics_unchanged():
+    w = scaled(get("opt6.7b-layer-b16"), batch=2, heads=3, prompt_len=300, decode_steps=0,
+               heavy_budget=30, recent_budget=30)
+    g, (q, k, v) = _run(w)
+    cache = H2OCache(w.batch, w.heads, w.head_dim, 30, 30, dtype="bf16", max_prompt=300)
+    cache.prefill(q, k, v)
+    plain = {"kept": cache.read(), "stats": cache.prefill_stats()}
+    cache.close()
+    for key in ("pos", "score", "k", "v"):
+        assert np.array_equal(np.asarray(g["kept"][key]), np.asarray(plain["kept"][key])), key
+    for s in range(len(plain["stats"])):
+        assert np.array_equal(g["stats"][s].view(np.uint32), plain["stats"][s].view(np.uint32))
+
+
+def test_identical_keys_running_mean():
+    # equal keys: row r weights positions 0..r equally (1/(r+1), rounded to bf16)
+    w = scaled(get("opt6.7b-layer-b16"), batch=1, heads=2, prompt_len=260, decode_steps=0, n_anchors=5)
+    Q, K, V = synth.batch_qkv(w, 0, 0, w.prompt_len)
+    K[:] = K[:, :, :1].copy()
+    q, k, v = (synth.to_torch(w, x, DEV) for x in (Q, K, V))
+    g = _gpu_prefill_out(w, q, k, v)
+    g["out"] = g["out"].cpu().numpy()
+    n = np.arange(1, w.prompt_len + 1)[:, None]
+    mean = np.cumsum(V.astype(np.float64), axis=2) / n
+    mag = np.cumsum(np.abs(V.astype(np.float64)), axis=2) / n
+    assert (np.abs(g["out"] - mean) <= REL["bf16"] * mag + ABS["bf16"]).all()
+
+
+def test_bench_shape_sampled_units():
+    # the benchmark's launch configuration (2048 units, prompt 2048, d = 128) on sampled units
+    w = get("opt6.7b-32L-b64")
+    L = w.prompt_len
+    q, k, v = synth.torch_qkv(w, 0, 0, L, DEV)
+    log(f"prefill output at full shape: B={w.batch} H={w.heads} L={L}")
+    g = _gpu_prefill_out(w, q, k, v)
+    rng = np.random.default_rng(21)
+    idx = rng.choice(w.batch * w.heads, size=4, replace=False)
+    worst = 0.0
+    for i in sorted(idx):
+        b, h = int(i) // w.heads, int(i) % w.heads
+        Q, K, V = (x[b, h].to(torch.float32).cpu().numpy() for x in (q, k, v))
+        worst = max(worst, _check_unit(w, Q, K, V, g["out"][b, h].cpu().numpy(), f"b{b}h{h}"))
+    log(f"full shape: worst err/bound {worst:.3f}")

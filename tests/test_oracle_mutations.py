@@ -57,6 +57,11 @@ MUTATIONS = {
     "prefill scores not seeded": ("cache.score = ps.col_sum[kept].copy()",
                                   "cache.score = np.zeros(len(kept))"),
     "recent pool overlaps": ("pool = list(range(L - recent))", "pool = list(range(L))"),
+    "prefill output from transposed weights": ("return A @ np.asarray(V, np.float64)",
+                                               "return A.T @ np.asarray(V, np.float64)"),
+    "prefill output mixes keys": ("return A @ np.asarray(V, np.float64)", "return A @ np.asarray(K, np.float64)"),
+    "prefill output one row late": ("return A @ np.asarray(V, np.float64)",
+                                    "return np.vstack([np.zeros((1, V.shape[1])), (A @ V)[:-1]])"),
     "evicted entries stay in the normaliser": (
         "a = softmax(x)\n        o = a @ G_V",
         "a = softmax(x)\n        a = a * (len(x) / (len(x) + self.evicted_mass))\n        o = a @ G_V"),
@@ -95,6 +100,16 @@ def _checks(m):
         Q, K = g.standard_normal((L, d)), g.standard_normal((L, d))
         ps = m.prefill_scores(Q, K, m.default_scale(d))
         np.testing.assert_allclose(ps.col_sum, _library_causal_weights(Q, K).sum(axis=0), rtol=1e-10)
+
+    def prefill_out():
+        L, d = 33, 7
+        Q, K, V = (g.standard_normal((L, d)) for _ in range(3))
+        O = m.prefill_output(Q, K, V, 1 / math.sqrt(d))
+        ref = _sdpa_rows(Q, K, V, np.tril(np.ones((L, L), dtype=bool)))
+        np.testing.assert_allclose(O, ref, rtol=1e-10, atol=1e-10)
+        Ks = np.tile(K[0], (L, 1))
+        O = m.prefill_output(Q, Ks, V, 0.37)
+        np.testing.assert_allclose(O, np.cumsum(V, axis=0) / np.arange(1, L + 1)[:, None], rtol=1e-10)
 
     def sliding_window():
         N, L, R, d = 30, 9, 4, 6
@@ -153,7 +168,7 @@ def _checks(m):
         assert len(c.pos) == 9
         assert abs(c.score.sum() - (c.rows - c.evicted_mass)) < 1e-9 * c.rows
 
-    return [full_attention, prefill_library, sliding_window, identical_keys, brute_force, keep_brute, mass]
+    return [full_attention, prefill_library, prefill_out, sliding_window, identical_keys, brute_force, keep_brute, mass]
 
 
 def test_unmutated_oracle_passes_every_check():

@@ -14,7 +14,7 @@ import scipy.special
 import torch
 from hypothesis import given, settings, strategies as st, HealthCheck
 
-from oracle import ParityMismatch, UnitCache, prefill_keep, prefill_scores, run_unit
+from oracle import ParityMismatch, UnitCache, prefill_keep, prefill_output, prefill_scores, run_unit
 
 torch.set_default_dtype(torch.float64)
 
@@ -56,6 +56,27 @@ def test_prefill_column_sums_match_library_softmax(L, d, seed):
     assert abs(ps.col_sum.sum() - L) < 1e-9 * L
     assert ps.col_sum[0] >= 1.0 - 1e-12
     assert ps.col_sum[-1] == pytest.approx(W[-1, -1], rel=1e-12)
+
+
+@pytest.mark.parametrize("L,d,seed", [(1, 4, 10), (9, 3, 11), (70, 16, 12), (129, 64, 13)])
+def test_prefill_output_matches_library_attention(L, d, seed):
+    # the prompt's own output is full causal attention: torch SDPA (float64)
+    Q, K, V = _rand(L, d, seed)
+    O = prefill_output(Q, K, V, 1 / math.sqrt(d))
+    ref = _sdpa_rows(Q, K, V, np.tril(np.ones((L, L), dtype=bool)))
+    np.testing.assert_allclose(O, ref, rtol=1e-12, atol=1e-12)
+
+
+def test_prefill_output_identical_keys_is_running_mean():
+    # equal keys: row r weights positions 0..r equally, so o_r is the mean of v_0..v_r
+    L, d = 23, 5
+    g = np.random.default_rng(14)
+    Q = g.standard_normal((L, d))
+    K = np.tile(g.standard_normal(d), (L, 1))
+    V = g.standard_normal((L, d))
+    O = prefill_output(Q, K, V, 0.37)
+    ref = np.cumsum(V, axis=0) / np.arange(1, L + 1)[:, None]
+    np.testing.assert_allclose(O, ref, rtol=1e-12, atol=1e-12)
 
 
 def test_prefill_single_token():
