@@ -43,8 +43,8 @@ def decode_bytes_per_unit(c: int, d: int, s: int) -> int:
 
 def prefill_flops_per_unit(L: int, d: int, with_out: bool = False) -> int:
     """MFMA flops of the two causal QK^T passes over the L(L+1)/2 pairs; with the
-    prompt's attention output, its pass adds one more QK^T and a PV over the pairs."""
-    return 2 * L * (L + 1) * d * (2 if with_out else 1)
+    prompt's attention output, the first pass adds a PV product over the pairs."""
+    return L * (L + 1) * d * (3 if with_out else 2)
 
 
 def prefill_bytes_per_unit(L: int, k: int, d: int, s: int, with_out: bool = False) -> int:

@@ -16,8 +16,9 @@
 //                 logits as MFMA tiles of S = Q K^T (one lane per key column);
 //                 the causal softmax is row-normalised, so the column sums need
 //                 the row normalisers of pass 1 first.
-//   (optional) attnout: the prompt's own attention output o_r = sum_j a_rj v_j,
-//                 recomputing the logits with the exact row normalisers.
+//      (rowout instead, when the caller asks for the prompt's own attention
+//                 output o_r = sum_j a_rj v_j: the same normalisers and the output
+//                 from one sweep over K and V)
 //   3. select_fill: per unit, a radix select on the 64-bit key (score bits,
 //                 position) finds the K_h-th best heavy-hitter candidate, a
 //                 ballot/popcount compaction assigns slots in position order,
@@ -195,23 +196,69 @@ __device__ inline void tile_mfma(uint32_t fb, const bf16x8 (&b)[2][D / 16], floa
   __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
 }
 
-// sum_i exp2(v_i * c + b) over the 16 elements, as four interleaved partial sums.
-__device__ inline float sum_exp2_16(const floatx16& v, float c, float b) {
-  float part[4];
+// exp2(v_i * c + b) for the 16 logits of a lane, and their sum as four
+// interleaved partial sums (one fixed order, shared by every pass that needs it).
+__device__ inline floatx16 exp2_16(const floatx16& v, float c, float b) {
+  floatx16 p;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) part[i] = fast_exp2(fmaf(v[i], c, b));
+  for (int i = 0; i < 16; ++i) p[i] = fast_exp2(fmaf(v[i], c, b));
+  return p;
+}
+__device__ inline float sum16(const floatx16& p) {
+  float part[4] = {p[0], p[1], p[2], p[3]};
 #pragma unroll
-  for (int i = 4; i < 16; ++i) part[i & 3] += fast_exp2(fmaf(v[i], c, b));
+  for (int i = 4; i < 16; ++i) part[i & 3] += p[i];
   return (part[0] + part[1]) + (part[2] + part[3]);
+}
+
+// Running base-2 normaliser of one query row over one 32-key S^T tile.  Lanes l
+// and l^32 hold the same query over different keys; they keep the same offset m,
+// which moves only when a tile would push a term of either lane past 2^64 (the
+// first tile always does), and each keeps its own partial sum l.  p receives the
+// tile's terms exp2(c2 s - m) against the offset after the update; the return
+// value is exp2(m_before - m_after), 1 where the offset did not move, and `moved`
+// (wave-uniform) says whether any lane's did.  Any offset at or below the row
+// maximum gives the same normaliser and no term can overflow, so the result
+// equals the usual max-shifted sum.
+// kTerms = false drops p (the pass without the output only needs the sums).
+template <bool kTerms>
+__device__ inline float row_update(const floatx16& s, float c2, int lane, float& m, float& l, floatx16& p,
+                                   bool& moved) {
+  float ts;
+  if (kTerms) {
+    p = exp2_16(s, c2, -m);
+    ts = sum16(p);
+  } else {
+    ts = sum16(exp2_16(s, c2, -m));
+  }
+  float r = 1.f;
+  const uint64_t need = __ballot(!(ts <= 0x1p64f));
+  moved = need != 0;
+  const uint32_t pair = static_cast<uint32_t>(need) | static_cast<uint32_t>(need >> 32);
+  if ((pair >> (lane & 31)) & 1u) {
+    float tm = fmaxf(s[0], s[1]);
+#pragma unroll
+    for (int i = 2; i < 16; i += 2) tm = fmaxf(tm, fmaxf(s[i], s[i + 1]));
+    tm = fmaxf(tm, __shfl_xor(tm, 32, kWave));
+    const float mn = fmaxf(m, tm * c2);
+    if (kTerms) {
+      p = exp2_16(s, c2, -mn);
+      ts = sum16(p);
+    } else {
+      ts = sum16(exp2_16(s, c2, -mn));
+    }
+    r = fast_exp2(m - mn);
+    m = mn;
+  }
+  l = fmaf(l, r, ts);
+  return r;
 }
 
 // Pass 1: S^T = K Q^T per 32x32 tile, so a lane holds 16 logits of one query
 // (element i is key row 8(i/4) + 4(lane/32) + i%4 of the tile).  The row sum is
-// kept against a running offset m (base 2, scaled) that only moves when a tile
-// would push a term past 2^64: the common tile costs one fma, one exp and one add
-// per logit; the first tile and any tile with a far larger logit rescale.  Any
-// offset at or below the row maximum gives the same normaliser, and no term can
-// overflow, so the result equals the usual max-shifted sum.
+// kept by row_update against a lazily moved offset: the common tile costs one
+// fma, one exp and one add per logit.  The pass with the attention output runs
+// the same per-query arithmetic, so both give the same normalisers bit for bit.
 template <int D>
 __global__ __launch_bounds__(kThreads, 4) void rowstats_bf16(PrefillArgs a, int nblk, int units) {
   using T = Tile<D>;
@@ -259,30 +306,20 @@ __global__ __launch_bounds__(kThreads, 4) void rowstats_bf16(PrefillArgs a, int 
 #pragma unroll
             for (int i = 0; i < 16; ++i) acc[s][i] = (8 * (i >> 2) + (i & 3)) <= rel ? acc[s][i] : -INFINITY;
           }
-          float ts = sum_exp2_16(acc[s], a.c2, -m[s]);
-          if (!(ts <= 0x1p64f)) {  // first tile, or a logit far above the offset: rescale
-            float tm = fmaxf(acc[s][0], acc[s][1]);
-#pragma unroll
-            for (int i = 2; i < 16; i += 2) tm = fmaxf(tm, fmaxf(acc[s][i], acc[s][i + 1]));
-            const float mn = fmaxf(m[s], tm * a.c2);
-            ts = sum_exp2_16(acc[s], a.c2, -mn);
-            l[s] *= fast_exp2(m[s] - mn);
-            m[s] = mn;
-          }
-          l[s] += ts;
+          floatx16 p;
+          bool moved;
+          row_update<false>(acc[s], a.c2, lane, m[s], l[s], p, moved);
         }
       }
     }
     // lanes l and l+32 hold the same queries over different key rows
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
-      const float m2 = __shfl_xor(m[s], 32, kWave), l2 = __shfl_xor(l[s], 32, kWave);
-      const float mn = fmaxf(m[s], m2);
-      const float lt = l[s] * fast_exp2(m[s] - mn) + l2 * fast_exp2(m2 - mn);
+      const float lt = l[s] + __shfl_xor(l[s], 32, kWave);
       const int q = qw + 32 * s + lane;
       // rows L..Lpad-1 get 0 so pass 2 reads finite normalisers for its masked rows
       if (lane < 32 && q < a.Lpad)
-        a.row_lse2[static_cast<size_t>(unit) * a.Lpad + q] = q < L ? mn + log2f(lt) : 0.f;
+        a.row_lse2[static_cast<size_t>(unit) * a.Lpad + q] = q < L ? m[s] + log2f(lt) : 0.f;
     }
   }
 }
@@ -387,17 +424,20 @@ __global__ __launch_bounds__(kThreads, 4) void colsum_bf16(PrefillArgs a, int nb
 }
 
 // ------------------------------------------------------------------ prompt attention output
-// Pass 3, run only when the caller asks for the prompt's own attention output:
-// o_r = sum_{j<=r} exp2(c2 q_r.k_j - lse2_r) v_j with the exact row normalisers of
-// pass 1, so no running rescale is needed.  Each of a block's 4 waves keeps 32
-// query rows in registers; K and V tiles stream through two rings of three
-// swizzled LDS tiles (global -> LDS loads).  S^T = K Q^T per tile gives each lane
-// one query's weights for 16 keys; rounded to bf16 they are the B operand of
-// O^T += V^T P^T.  The V^T operand comes from the transposing LDS read: in each
-// group of 16 lanes, output lane 4a+b takes element b of the 8-byte reads of
-// lanes a, a+4, a+8, a+12, so pointing those lanes at 4 consecutive d values of
-// 4 different key rows hands every lane 4 keys of one d column - in the key order
-// of the S^T accumulator (element i of lane l is key 8(i/4) + 4(l/32) + i%4).
+// Pass 1 with the prompt's own attention output, run instead of pass 1 when the
+// caller asks for o_r = sum_{j<=r} a_rj v_j: one sweep over the keys gives both
+// the row normaliser and the output (the FlashAttention order).  Each of a
+// block's 4 waves keeps 32 query rows in registers; K and V tiles stream through
+// two rings of three swizzled LDS tiles (global -> LDS loads).  S^T = K Q^T per
+// tile gives each lane one query's logits for 16 keys; row_update turns them
+// into terms exp2(c2 s - m) against the running offset, and, rounded to bf16,
+// those terms are the B operand of O^T += V^T P^T.  When the offset moves, O is
+// rescaled with it; at the end O is divided by the row sum.  The V^T operand
+// comes from the transposing LDS read: in each group of 16 lanes, output lane
+// 4a+b takes element b of the 8-byte reads of lanes a, a+4, a+8, a+12, so
+// pointing those lanes at 4 consecutive d values of 4 different key rows hands
+// every lane 4 keys of one d column - in the key order of the S^T accumulator
+// (element i of lane l is key 8(i/4) + 4(l/32) + i%4).
 constexpr int kOutRows = 128;  // 4 waves x 32 query rows
 
 typedef short i16x4 __attribute__((ext_vector_type(4)));
@@ -415,7 +455,7 @@ __device__ inline uint32_t tile_elem_offset(int key, int col) {
 }
 
 template <int D>
-__global__ __launch_bounds__(kThreads, 3) void attnout_bf16(PrefillArgs a, int nblk, int units) {
+__global__ __launch_bounds__(kThreads, 3) void rowout_bf16(PrefillArgs a, int nblk, int units) {
   using T = Tile<D>;
   constexpr int NDB = D / 32;  // 32-wide column blocks of the output
   __shared__ __align__(256) unsigned char sK[kBufs][T::kBytes];
@@ -429,7 +469,6 @@ __global__ __launch_bounds__(kThreads, 3) void attnout_bf16(PrefillArgs a, int n
   const bf16_t* Qu = static_cast<const bf16_t*>(a.q) + static_cast<size_t>(unit) * L * D;
   const bf16_t* Ku = static_cast<const bf16_t*>(a.k) + static_cast<size_t>(unit) * L * D;
   const bf16_t* Vu = static_cast<const bf16_t*>(a.v) + static_cast<size_t>(unit) * L * D;
-  const float* lse = a.row_lse2 + static_cast<size_t>(unit) * a.Lpad;
   float* out = a.out + static_cast<size_t>(unit) * L * D;
   const __amdgpu_buffer_rsrc_t rk = make_rsrc(Ku, static_cast<uint32_t>(L) * T::kRowBytes);
   const __amdgpu_buffer_rsrc_t rv = make_rsrc(Vu, static_cast<uint32_t>(L) * T::kRowBytes);
@@ -449,7 +488,6 @@ __global__ __launch_bounds__(kThreads, 3) void attnout_bf16(PrefillArgs a, int n
     if (h == 1) tile_barrier();
     bf16x8 bq[D / 16];
     row_frag<D>(Qu, qw + fr, L, lane, bq);
-    const float lq = qw + fr < L ? lse[qw + fr] : 0.f;
     tile_async(rk, voff, 0, sK[0], T::kRowBytes, T::kLoads);
     tile_async(rv, voff, 0, sV[0], T::kRowBytes, T::kLoads);
     if (ntile > 1) {
@@ -461,6 +499,7 @@ __global__ __launch_bounds__(kThreads, 3) void attnout_bf16(PrefillArgs a, int n
     floatx16 o[NDB];
 #pragma unroll
     for (int db = 0; db < NDB; ++db) o[db] = floatx16{};
+    float m = -1e30f, l = 0.f;
     for (int t = 0; t < ntile; ++t) {
       if (t + 1 < ntile) wait_vm<2 * T::kLoads>();  // K and V of this tile landed
       else wait_vm<0>();
@@ -482,9 +521,18 @@ __global__ __launch_bounds__(kThreads, 3) void attnout_bf16(PrefillArgs a, int n
 #pragma unroll
           for (int i = 0; i < 16; ++i) sacc[i] = (8 * (i >> 2) + (i & 3)) <= rel ? sacc[i] : -INFINITY;
         }
-        bf16x8 pw[2];  // weights of keys 16kb.. as the B operand, kb = 0, 1
+        floatx16 p;
+        bool moved;
+        const float r = row_update<true>(sacc, a.c2, lane, m, l, p, moved);
+        if (moved) {  // the lane's offset moved (r = 1 where it did not)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) pw[i >> 3][i & 7] = static_cast<__bf16>(fast_exp2(fmaf(sacc[i], a.c2, -lq)));
+          for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) o[db][i] *= r;
+        }
+        bf16x8 pw[2];  // terms of keys 16kb.. as the B operand, kb = 0, 1
+#pragma unroll
+        for (int i = 0; i < 16; ++i) pw[i >> 3][i & 7] = static_cast<__bf16>(p[i]);
         uint32_t vt = lds_addr(sV[t % kBufs]);
         asm volatile("" : "+v"(vt));
 #pragma unroll
@@ -499,15 +547,21 @@ __global__ __launch_bounds__(kThreads, 3) void attnout_bf16(PrefillArgs a, int n
         }
       }
     }
+    // lanes l and l+32 hold the same query over different keys
+    const float lt = l + __shfl_xor(l, 32, kWave);
+    const int q = qw + lane;
+    // rows L..Lpad-1 get 0 so pass 2 reads finite normalisers for its masked rows
+    if (lane < 32 && q < a.Lpad) a.row_lse2[static_cast<size_t>(unit) * a.Lpad + q] = q < L ? m + log2f(lt) : 0.f;
     // o[db] element i of lane (fr, hh) is d = 32 db + 8(i/4) + 4 hh + i%4 of query qw + fr
     if (qw + fr < L) {
+      const float inv = 1.f / lt;
       float* orow = out + static_cast<size_t>(qw + fr) * D;
 #pragma unroll
       for (int db = 0; db < NDB; ++db)
 #pragma unroll
         for (int g = 0; g < 4; ++g)
           *reinterpret_cast<float4*>(orow + 32 * db + 8 * g + 4 * hh) =
-              make_float4(o[db][4 * g], o[db][4 * g + 1], o[db][4 * g + 2], o[db][4 * g + 3]);
+              make_float4(o[db][4 * g] * inv, o[db][4 * g + 1] * inv, o[db][4 * g + 2] * inv, o[db][4 * g + 3] * inv);
     }
   }
 }
@@ -721,19 +775,18 @@ hipError_t launch_bf16(const PrefillArgs& a, int units, hipStream_t s) {
   const int nblk = (a.L + kBlockRows - 1) / kBlockRows;  // row blocks; a block takes a pair
   const int groups = (units + kXcds - 1) / kXcds;
   const dim3 grid(groups * kXcds * ((nblk + 1) / 2));
-  hipLaunchKernelGGL((rowstats_bf16<D>), grid, dim3(kThreads), 0, s, a, nblk, units);
+  if (a.out != nullptr) {
+    const int nbo = (a.L + kOutRows - 1) / kOutRows;
+    const dim3 grid_o(groups * kXcds * ((nbo + 1) / 2));
+    hipLaunchKernelGGL((rowout_bf16<D>), grid_o, dim3(kThreads), 0, s, a, nbo, units);
+  } else {
+    hipLaunchKernelGGL((rowstats_bf16<D>), grid, dim3(kThreads), 0, s, a, nblk, units);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((colsum_bf16<D>), grid, dim3(kThreads), 0, s, a, nblk, units);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  if (a.out != nullptr) {
-    const int nb3 = (a.L + kOutRows - 1) / kOutRows;
-    const dim3 grid3(groups * kXcds * ((nb3 + 1) / 2));
-    hipLaunchKernelGGL((attnout_bf16<D>), grid3, dim3(kThreads), 0, s, a, nb3, units);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
   return launch_select<bf16_t, D>(a, units, s);
 }
 
