@@ -32,6 +32,7 @@ if ROOT not in sys.path:
 METRIC = "H2O decode tokens/s + achieved HBM GB/s (% peak) at OPT-6.7B shape, 20% budget"
 HBM_PEAK_GBS = 8000.0
 BF16_MFMA_PEAK_TFLOPS = 2500.0
+MALL_BYTES = 256 * 2 ** 20
 
 
 def decode_bytes_per_unit(c: int, d: int, s: int) -> int:
@@ -235,6 +236,7 @@ def main():
     dec_bytes_launch = B * H * sum(decode_bytes_per_unit(min(w.k, L + t), d, s) for t in range(T)) / T
     avg_dec_s = t_dec / launches
     achieved = dec_bytes_launch / avg_dec_s / 1e9
+    kv_cache_bytes = B * H * w.k * (2 * d * s + 12)
     pf_flops = NL * B * H * prefill_flops_per_unit(L, d, a.prefill_out) * K
     pf_bytes = NL * B * H * prefill_bytes_per_unit(L, w.k, d, s, a.prefill_out) * K
     res = {
@@ -248,19 +250,22 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "bf16" if w.dtype == "bf16" else "f32",
         "data": "synthetic",
         "config": {"workload": w.name, "layers": NL, "batch": B, "heads": H, "head_dim": d,
                    "prompt_len": L, "decode_steps": T, "heavy_budget": w.heavy_budget,
                    "recent_budget": w.recent_budget, "storage": w.dtype, "accumulate": "fp32",
                    "prefill_out": bool(a.prefill_out)},
-        "roofline": {"kernel": "decode_kernel<bf16,128>", "bound": "hbm", "achieved": achieved,
+        "roofline": {"kernel": f"decode_kernel<{w.dtype},{d}>", "bound": "hbm", "achieved": achieved,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic(w.name) if a.layers is None else None,
                      "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
                      "bytes_per_launch": dec_bytes_launch, "avg_launch_us": 1e6 * avg_dec_s,
                      "launches": launches},
         "decode": {"tokens_per_s": tokens / t_dec, "ms_per_token_step": 1e3 * t_dec / (T * K),
-                   "GBps": achieved, "hbm_frac": achieved / HBM_PEAK_GBS},
+                   "GBps": achieved, "hbm_frac": achieved / HBM_PEAK_GBS,
+                   # a cache that fits the 256 MB Infinity Cache is read from there, not HBM:
+                   # its GB/s is an effective rate
+                   "mall_resident": kv_cache_bytes <= MALL_BYTES, "cache_bytes_per_layer": kv_cache_bytes},
         "prefill": {"tokens_per_s": B * L * K / t_pre, "ms": 1e3 * t_pre / K,
                     "mfma_tflops": pf_flops / t_pre / 1e12,
                     "mfma_frac": pf_flops / t_pre / 1e12 / BF16_MFMA_PEAK_TFLOPS,

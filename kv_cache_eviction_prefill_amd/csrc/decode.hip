@@ -22,8 +22,11 @@
 //     which orders by score then position exactly; a wave/LDS min picks the
 //     victim, whose slot the new token's K/V, position and score overwrite.
 //   * Split path (few units): nsplit blocks per unit each stream a slice of the
-//     slots and publish (max, sum, o) partials; the last block to arrive merges
-//     them and runs the score pass.
+//     slots and write (max, sum, o) partials and their logits; a second launch,
+//     one block per unit, merges the partials and runs the score pass.  The
+//     launch boundary orders the two: no block waits for another and no
+//     device-scope fence is needed (on gfx950 each such fence writes back and
+//     invalidates the whole L2 of its XCD).
 #include "h2o_device.h"
 #include "launch.h"
 
@@ -35,6 +38,8 @@ constexpr int kUnroll = 2;    // slots in flight per row group (K and V each)
 constexpr int kPrefetch = 2;  // score-pass slots per thread whose metadata is loaded up front
 constexpr uint64_t kNoKey = ~0ull;
 constexpr int kNewSlot = -2;
+constexpr int kMaxSplitBlocks = 64;  // most blocks one unit's slots are split over
+constexpr int kFinishPrefetch = 8;   // slots per thread whose metadata the finish launch loads first
 
 template <typename T, int D>
 struct Layout {
@@ -44,6 +49,105 @@ struct Layout {
   static_assert((LPR & (LPR - 1)) == 0 && LPR <= kWave, "row must map to a power-of-two lane group");
   static_assert(LPR >= kUnroll, "one lane per in-flight slot stores its logit");
 };
+
+// Score pass of one unit (whole block): every occupied slot adds its weight
+// exp2(x_j - M) / L with a Kahan-compensated fp32 sum; when the cache is full the
+// eviction candidates (pos <= i - K_r, and the new token when K_r = 0) compete on
+// the 64-bit key (score bits, pos) through a wave and LDS min, and the new
+// token's K/V, position and score overwrite the victim's slot.  pf_*: this
+// thread's first NP slots' metadata, loaded early by the caller; lg: the unit's
+// logits, the new token's at index k; s_knew/s_vnew: its K/V rows, in LDS.
+template <typename T, int D, int NP, bool kPfX>
+__device__ inline void score_pass(const DecodeArgs& a, int unit, float M, float invL, const float* lg, float x_new,
+                                  const float (&pf_s)[NP], const float (&pf_c)[NP], const int32_t (&pf_p)[NP],
+                                  const float (&pf_x)[NP], const uint4* s_knew, const uint4* s_vnew,
+                                  uint64_t* s_key, int* s_slot) {
+  using Lay = Layout<T, D>;
+  constexpr int EPL = Lay::EPL, LPR = Lay::LPR;
+  const int tid = threadIdx.x, g = tid / LPR, r = tid % LPR;
+  float* sc = a.score + static_cast<size_t>(unit) * a.kstride;
+  float* cp = a.comp + static_cast<size_t>(unit) * a.kstride;
+  int32_t* ps = a.pos + static_cast<size_t>(unit) * a.kstride;
+  const int cnt = a.count;
+  const bool full = (cnt == a.k);
+
+  uint64_t best = kNoKey;
+  int best_slot = -1;
+  for (int i = 0, j = tid; j < cnt; ++i, j += kThreads) {
+    float xj, sj, cj;
+    int32_t pj;
+    if (i < NP) {
+      xj = pf_x[0];
+      sj = pf_s[0];
+      cj = pf_c[0];
+      pj = pf_p[0];
+#pragma unroll
+      for (int t = 1; t < NP; ++t) {
+        xj = i == t ? pf_x[t] : xj;
+        sj = i == t ? pf_s[t] : sj;
+        cj = i == t ? pf_c[t] : cj;
+        pj = i == t ? pf_p[t] : pj;
+      }
+      if (!kPfX) xj = lg[j];
+    } else {
+      xj = lg[j];
+      sj = sc[j];
+      cj = cp[j];
+      pj = ps[j];
+    }
+    const float w = fast_exp2(xj - M) * invL;
+    const float y = w - cj;  // Kahan-compensated add of this step's weight
+    const float t = sj + y;
+    cj = (t - sj) - y;
+    sj = t;
+    sc[j] = sj;
+    cp[j] = cj;
+    if (full && pj <= a.cand_limit) {
+      const uint64_t key = evict_key(sj, pj);
+      if (key < best) {
+        best = key;
+        best_slot = j;
+      }
+    }
+  }
+  const float w_new = fast_exp2(x_new - M) * invL;
+
+  int dst = cnt;  // cache not full: the new token takes the next free slot
+  int32_t ev = -1;
+  if (full) {
+    if (a.new_is_candidate && tid == 0) {
+      const uint64_t key = evict_key(w_new, a.new_pos);
+      if (key < best) {
+        best = key;
+        best_slot = kNewSlot;
+      }
+    }
+    const uint64_t wm = wave_min_key(best);
+    if ((tid & (kWave - 1)) == 0) s_key[tid / kWave] = wm;
+    __syncthreads();
+    uint64_t bm = s_key[0];
+#pragma unroll
+    for (int w = 1; w < kThreads / kWave; ++w) bm = s_key[w] < bm ? s_key[w] : bm;
+    if (best == bm) *s_slot = best_slot;  // keys are unique: exactly one owner
+    __syncthreads();
+    ev = static_cast<int32_t>(static_cast<uint32_t>(bm & 0xffffffffu));
+    dst = *s_slot == kNewSlot ? -1 : *s_slot;
+  }
+  if (dst >= 0) {
+    if (tid == dst % kThreads) {  // the thread that last wrote this slot's score
+      sc[dst] = w_new;
+      cp[dst] = 0.f;
+      ps[dst] = a.new_pos;
+    }
+    if (g == 0) {  // s_knew/s_vnew were written before an earlier barrier
+      T* kd = static_cast<T*>(a.kslots) + (static_cast<size_t>(unit) * a.k + dst) * D;
+      T* vd = static_cast<T*>(a.vslots) + (static_cast<size_t>(unit) * a.k + dst) * D;
+      st16(kd + r * EPL, s_knew[r]);
+      st16(vd + r * EPL, s_vnew[r]);
+    }
+  }
+  if (tid == 0 && a.evicted != nullptr) a.evicted[unit] = ev;
+}
 
 // 8 waves per SIMD: all blocks of a 2048-unit launch are resident at once.
 template <typename T, int D, bool SPLIT>
@@ -56,7 +160,6 @@ __global__ __launch_bounds__(kThreads, 8) void decode_kernel(DecodeArgs a) {
   __shared__ uint64_t s_key[kThreads / kWave];
   __shared__ uint4 s_knew[LPR], s_vnew[LPR];
   __shared__ int s_slot;
-  __shared__ int s_last;
 
   const int tid = threadIdx.x;
   const int g = tid / LPR, r = tid % LPR;
@@ -192,120 +295,80 @@ __global__ __launch_bounds__(kThreads, 8) void decode_kernel(DecodeArgs a) {
     if (tid < D) acc = fmaf(s_o[t][tid], wt, acc);
   }
 
-  if constexpr (!SPLIT) {
-    if (tid < D) a.out[static_cast<size_t>(unit) * D + tid] = acc / Ls;
-  } else {
+  if constexpr (SPLIT) {
     float* pp = a.part + (static_cast<size_t>(unit) * a.nsplit + split) * (2 + D);
     if (tid == 0) {
       pp[0] = M;
       pp[1] = Ls;
     }
     if (tid < D) pp[2 + tid] = acc;
-    // Publish the partial and the logits, then count arrivals; the last block
-    // of the unit finishes the step.
-    __threadfence();
-    __syncthreads();
-    if (tid == 0) {
-      const unsigned prev = atomicAdd(&a.counters[unit], 1u);
-      s_last = (prev == static_cast<unsigned>(a.nsplit - 1));
-    }
-    __syncthreads();
-    if (!s_last) return;
-    __threadfence();
-    const float* pu = a.part + static_cast<size_t>(unit) * a.nsplit * (2 + D);
-    float Mg = -INFINITY;
-    for (int s = 0; s < a.nsplit; ++s) Mg = fmaxf(Mg, pu[s * (2 + D)]);
-    float Lg = 0.f, og = 0.f;
-    for (int s = 0; s < a.nsplit; ++s) {
-      const float ws = fast_exp2(pu[s * (2 + D)] - Mg);
-      Lg = fmaf(pu[s * (2 + D) + 1], ws, Lg);
-      if (tid < D) og = fmaf(pu[s * (2 + D) + 2 + tid], ws, og);
-    }
-    if (tid < D) a.out[static_cast<size_t>(unit) * D + tid] = og / Lg;
-    if (tid == 0) a.counters[unit] = 0u;  // ready for the next step
-    M = Mg;
-    Ls = Lg;
-
+  } else {
+    if (tid < D) a.out[static_cast<size_t>(unit) * D + tid] = acc / Ls;
+    score_pass<T, D, kPrefetch, false>(a, unit, M, 1.f / Ls, s_logit, s_logit[a.k], pf_s, pf_c, pf_p, pf_s, s_knew,
+                                       s_vnew, s_key, &s_slot);
   }
+}
 
-  // ---- score accumulation over G, then at most one eviction
-  const float invL = 1.f / Ls;
-  const int cnt = a.count;
-  const bool full = (cnt == a.k);
-  const float* lg = SPLIT ? glog : s_logit;
-
-  uint64_t best = kNoKey;
-  int best_slot = -1;
-  for (int i = 0, j = tid; j < cnt; ++i, j += kThreads) {
-    const float w = fast_exp2(lg[j] - M) * invL;
-    float sj, cj;
-    int32_t pj;
-    if (!SPLIT && i < kPrefetch) {
-      sj = pf_s[0];
-      cj = pf_c[0];
-      pj = pf_p[0];
+// Second launch of the split path: one block per unit merges the nsplit
+// partials of the first launch into the output and runs the score pass over the
+// logits it wrote.
+template <typename T, int D>
+__global__ __launch_bounds__(kThreads) void decode_finish(DecodeArgs a) {
+  using Lay = Layout<T, D>;
+  constexpr int EPL = Lay::EPL, LPR = Lay::LPR;
+  constexpr int NP = kFinishPrefetch;
+  __shared__ float s_pm[kMaxSplitBlocks], s_pl[kMaxSplitBlocks];
+  __shared__ uint64_t s_key[kThreads / kWave];
+  __shared__ uint4 s_knew[LPR], s_vnew[LPR];
+  __shared__ int s_slot;
+  const int tid = threadIdx.x, unit = blockIdx.x;
+  const float* sc = a.score + static_cast<size_t>(unit) * a.kstride;
+  const float* cp = a.comp + static_cast<size_t>(unit) * a.kstride;
+  const int32_t* ps = a.pos + static_cast<size_t>(unit) * a.kstride;
+  const float* lg = a.logits + static_cast<size_t>(unit) * (a.k + 1);
+  const float* pu = a.part + static_cast<size_t>(unit) * a.nsplit * (2 + D);
+  // Every load is issued here, before any result is used: the metadata and
+  // logits of this thread's first NP slots, its output column of every partial,
+  // the partials' (max, sum) and the new token's rows.
+  float pf_s[NP], pf_c[NP], pf_x[NP];
+  int32_t pf_p[NP];
 #pragma unroll
-      for (int t = 1; t < kPrefetch; ++t) {
-        sj = i == t ? pf_s[t] : sj;
-        cj = i == t ? pf_c[t] : cj;
-        pj = i == t ? pf_p[t] : pj;
-      }
-    } else {
-      sj = sc[j];
-      cj = cp[j];
-      pj = ps[j];
-    }
-    const float y = w - cj;  // Kahan-compensated add of this step's weight
-    const float t = sj + y;
-    cj = (t - sj) - y;
-    sj = t;
-    sc[j] = sj;
-    cp[j] = cj;
-    if (full && pj <= a.cand_limit) {
-      const uint64_t key = evict_key(sj, pj);
-      if (key < best) {
-        best = key;
-        best_slot = j;
-      }
-    }
+  for (int i = 0; i < NP; ++i) {
+    const int j = tid + i * kThreads;
+    const bool ok = j < a.count;
+    pf_x[i] = ok ? lg[j] : 0.f;
+    pf_s[i] = ok ? sc[j] : 0.f;
+    pf_c[i] = ok ? cp[j] : 0.f;
+    pf_p[i] = ok ? ps[j] : 0;
   }
-  const float w_new = fast_exp2(lg[a.k] - M) * invL;
-
-  int dst = cnt;  // cache not full: the new token takes the next free slot
-  int32_t ev = -1;
-  if (full) {
-    if (a.new_is_candidate && tid == 0) {
-      const uint64_t key = evict_key(w_new, a.new_pos);
-      if (key < best) {
-        best = key;
-        best_slot = kNewSlot;
-      }
-    }
-    const uint64_t wm = wave_min_key(best);
-    if ((tid & (kWave - 1)) == 0) s_key[tid / kWave] = wm;
-    __syncthreads();
-    uint64_t bm = s_key[0];
+  const float x_new = lg[a.k];
+  float po[kMaxSplitBlocks];
 #pragma unroll
-    for (int w = 1; w < kThreads / kWave; ++w) bm = s_key[w] < bm ? s_key[w] : bm;
-    if (best == bm) s_slot = best_slot;  // keys are unique: exactly one owner
-    __syncthreads();
-    ev = static_cast<int32_t>(static_cast<uint32_t>(bm & 0xffffffffu));
-    dst = s_slot == kNewSlot ? -1 : s_slot;
+  for (int s = 0; s < kMaxSplitBlocks; ++s)
+    po[s] = (tid < D && s < a.nsplit) ? pu[s * (2 + D) + 2 + tid] : 0.f;
+  if (tid < a.nsplit) {
+    s_pm[tid] = pu[tid * (2 + D)];
+    s_pl[tid] = pu[tid * (2 + D) + 1];
   }
-  if (dst >= 0) {
-    if (tid == dst % kThreads) {  // the thread that last wrote this slot's score
-      sc[dst] = w_new;
-      cp[dst] = 0.f;
-      ps[dst] = a.new_pos;
-    }
-    if (g == 0) {  // s_knew/s_vnew were written before the merge barrier
-      T* kd = static_cast<T*>(a.kslots) + (static_cast<size_t>(unit) * a.k + dst) * D;
-      T* vd = static_cast<T*>(a.vslots) + (static_cast<size_t>(unit) * a.k + dst) * D;
-      st16(kd + r * EPL, s_knew[r]);
-      st16(vd + r * EPL, s_vnew[r]);
+  if (tid < LPR) {
+    s_knew[tid] = ld16(static_cast<const T*>(a.knew) + static_cast<size_t>(unit) * D + tid * EPL);
+    s_vnew[tid] = ld16(static_cast<const T*>(a.vnew) + static_cast<size_t>(unit) * D + tid * EPL);
+  }
+  __syncthreads();
+  float Mg = -INFINITY;
+  for (int s = 0; s < a.nsplit; ++s) Mg = fmaxf(Mg, s_pm[s]);
+  float Lg = 0.f, og = 0.f;
+#pragma unroll
+  for (int s = 0; s < kMaxSplitBlocks; ++s) {
+    if (s < a.nsplit) {
+      const float ws = fast_exp2(s_pm[s] - Mg);
+      Lg = fmaf(s_pl[s], ws, Lg);
+      og = fmaf(po[s], ws, og);
     }
   }
-  if (tid == 0 && a.evicted != nullptr) a.evicted[unit] = ev;
+  if (tid < D) a.out[static_cast<size_t>(unit) * D + tid] = og / Lg;
+  score_pass<T, D, NP, true>(a, unit, Mg, 1.f / Lg, lg, x_new, pf_s, pf_c, pf_p, pf_x, s_knew, s_vnew, s_key,
+                             &s_slot);
 }
 
 template <typename T, int D>
@@ -315,6 +378,9 @@ hipError_t launch_typed(const DecodeArgs& a, int units, hipStream_t s) {
     hipLaunchKernelGGL((decode_kernel<T, D, false>), dim3(units), dim3(kThreads), shm, s, a);
   } else {
     hipLaunchKernelGGL((decode_kernel<T, D, true>), dim3(units * a.nsplit), dim3(kThreads), 0, s, a);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((decode_finish<T, D>), dim3(units), dim3(kThreads), 0, s, a);
   }
   return hipGetLastError();
 }

@@ -33,7 +33,6 @@ struct h2o_cache {
   int32_t* pos;
   float* part;
   float* logits;
-  uint32_t* counters;
   int32_t max_split;
   float* row_lse2;
   float* col_sum;
@@ -116,7 +115,7 @@ h2o_status check_params(const h2o_params* p, Sizes* sz) {
     sz->meta = u * static_cast<size_t>(round32(static_cast<int32_t>(k))) * 12;
     sz->max_split = units < kSplitUnits ? kMaxSplit : 1;
     sz->split = sz->max_split > 1
-                    ? u * sz->max_split * (2 + d) * 4 + u * (kk + 1) * 4 + u * 4
+                    ? u * sz->max_split * (2 + d) * 4 + u * (kk + 1) * 4
                     : 0;
     sz->lpad = round32(p->max_prompt);
     sz->prefill = 2 * u * static_cast<size_t>(sz->lpad) * 4;
@@ -127,7 +126,7 @@ h2o_status check_params(const h2o_params* p, Sizes* sz) {
 
 void free_all(h2o_cache* c) {
   void* ptrs[] = {c->kslots, c->vslots, c->score, c->comp, c->pos, c->part, c->logits,
-                  c->counters, c->row_lse2, c->col_sum};
+                  c->row_lse2, c->col_sum};
   for (void* q : ptrs)
     if (q != nullptr) (void)hipFree(q);
 }
@@ -221,7 +220,6 @@ h2o_status h2o_cache_create(const h2o_params* params, int device, h2o_cache** ou
       {reinterpret_cast<void**>(&c->pos), u * c->kstride * 4},
       {reinterpret_cast<void**>(&c->part), c->max_split > 1 ? u * c->max_split * (2 + d) * 4 : 0},
       {reinterpret_cast<void**>(&c->logits), c->max_split > 1 ? u * (kk + 1) * 4 : 0},
-      {reinterpret_cast<void**>(&c->counters), c->max_split > 1 ? u * 4 : 0},
       {reinterpret_cast<void**>(&c->row_lse2), u * c->lpad_cap * 4},
       {reinterpret_cast<void**>(&c->col_sum), u * c->lpad_cap * 4},
   };
@@ -235,7 +233,6 @@ h2o_status h2o_cache_create(const h2o_params* params, int device, h2o_cache** ou
     }
   }
   hipError_t e = h2o::launch_clear(c->pos, c->score, c->comp, u * c->kstride, nullptr);
-  if (e == hipSuccess && c->counters != nullptr) e = hipMemset(c->counters, 0, u * 4);
   if (e == hipSuccess) e = hipDeviceSynchronize();
   if (e != hipSuccess) {
     free_all(c);
@@ -328,7 +325,6 @@ h2o_status h2o_decode_step(h2o_cache* c, const void* q, const void* k, const voi
   a.evicted = evicted;
   a.part = c->part;
   a.logits = c->logits;
-  a.counters = c->counters;
   a.k = c->k;
   a.kstride = c->kstride;
   a.count = c->count;

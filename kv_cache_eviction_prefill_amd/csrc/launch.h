@@ -20,7 +20,6 @@ struct DecodeArgs {
   int32_t* evicted;  // [units] or nullptr
   float* part;       // split mode: [units, nsplit, 2 + d] partial (max, sum, o)
   float* logits;     // split mode: [units, k + 1] base-2 logits (new token at index k)
-  uint32_t* counters;  // split mode: [units] arrival counters, zero between launches
   int32_t k;           // slots per unit
   int32_t kstride;     // per-unit stride of score/comp/pos: k rounded up to 32 (128-byte rows)
   int32_t count;       // occupied slots before this step (slots 0..count-1)

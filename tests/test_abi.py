@@ -62,7 +62,7 @@ def test_cache_bytes_accounting():
     assert st == 0 and kv == 2 * 6 * 8 * 128 * 2
     # + scores, compensation, positions (12 B / slot, rows padded to 32 slots)
     # + split scratch (few units) + 2 prefill rows (row normaliser, column sum)
-    assert tot == kv + 6 * 32 * 12 + (6 * 64 * 130 * 4 + 6 * 9 * 4 + 6 * 4) + 2 * 6 * 64 * 4
+    assert tot == kv + 6 * 32 * 12 + (6 * 64 * 130 * 4 + 6 * 9 * 4) + 2 * 6 * 64 * 4
     st, kv32, _ = _bytes(dtype="f32")
     assert kv32 == 2 * kv
 
