@@ -171,6 +171,7 @@ class UnitCache:
     next_pos: int = 0
     evicted_mass: float = 0.0
     rows: int = 0  # attention rows processed (prompt rows + decode steps)
+    fixed: np.ndarray = None  # per-position scores fixed in advance (global comparator), or None
 
     def __post_init__(self):
         if self.K is None:
@@ -185,25 +186,32 @@ class UnitCache:
     # ------------------------------------------------------------------ prefill
     @classmethod
     def from_prompt(cls, Qp, Kp, Vp, heavy: int, recent: int, scale: float | None = None,
-                    prefer_kept=None, tie_rtol: float = TIE_RTOL):
+                    prefer_kept=None, tie_rtol: float = TIE_RTOL, fixed=None):
         """Prefill: score the prompt, keep per ``prefill_keep``, seed the scores
         of the kept entries with their column sums.  READING: prefill column sums
-        seed the running scores (the decode steps keep adding to them)."""
+        seed the running scores (the decode steps keep adding to them).
+
+        ``fixed``: scores for every position of the sequence, fixed in advance
+        (the global comparator).  The prompt is then ranked by ``fixed[:L]``
+        instead of its own column sums, and decode steps add nothing."""
         Qp, Kp, Vp = (np.asarray(x, np.float64) for x in (Qp, Kp, Vp))
         L, d = Kp.shape if Kp.ndim == 2 else (0, Qp.shape[-1])
         scale = default_scale(d) if scale is None else scale
         cache = cls(heavy=heavy, recent=recent, scale=scale, d=d)
+        if fixed is not None:
+            cache.fixed = np.asarray(fixed, np.float64)
         if L == 0:
             return cache, None, {"selected": False, "tie_adopted": False, "band": []}
-        ps = prefill_scores(Qp, Kp, scale)
-        kept, info = prefill_keep(ps.col_sum, heavy, recent, prefer=prefer_kept, tie_rtol=tie_rtol)
+        ps = prefill_scores(Qp, Kp, scale) if fixed is None else None
+        c = ps.col_sum if fixed is None else cache.fixed[:L]
+        kept, info = prefill_keep(c, heavy, recent, prefer=prefer_kept, tie_rtol=tie_rtol)
         kept = np.asarray(kept, np.int64)
         cache.pos = kept
         cache.K = Kp[kept].copy()
         cache.V = Vp[kept].copy()
-        cache.score = ps.col_sum[kept].copy()
+        cache.score = c[kept].copy()
         dropped = np.setdiff1d(np.arange(L), kept)
-        cache.evicted_mass = float(ps.col_sum[dropped].sum())
+        cache.evicted_mass = float(c[dropped].sum())
         cache.next_pos = L
         cache.rows = L
         return cache, ps, info
@@ -218,7 +226,9 @@ class UnitCache:
            READING: attention happens before eviction; step i's scores decide it.
         2. Every entry of G adds the attention it just received to its score; the
            new token's score starts at its own weight a_i.  [Report §3.3; Card]
-           READING: scores only accumulate (no decay, no reset).
+           READING: scores only accumulate (no decay, no reset).  With fixed
+           scores (the global comparator) nothing is added and the new token's
+           score is its fixed score.
         3. While |S| < k, S = G and nothing is evicted.  Otherwise one entry u
            leaves: the candidates are the entries at positions j <= i - recent
            (the heavy hitters plus the token that just left the recent window;
@@ -245,7 +255,10 @@ class UnitCache:
         x = self.scale * (G_K @ q)
         a = softmax(x)
         o = a @ G_V
-        G_score = np.concatenate([self.score, [0.0]]) + a
+        if self.fixed is None:
+            G_score = np.concatenate([self.score, [0.0]]) + a
+        else:
+            G_score = np.concatenate([self.score, [self.fixed[i]]])
         info = {"tie_adopted": False, "band": [], "weights": a, "positions": G_pos}
         self.rows += 1
         self.next_pos = i + 1
@@ -283,12 +296,13 @@ class UnitCache:
 # =============================================================================== driver
 def run_unit(Q, K, V, prompt_len: int, heavy: int, recent: int, scale: float | None = None,
              replay_kept=None, replay_evicted=None, tie_rtol: float = TIE_RTOL,
-             keep_weights: bool = False):
+             keep_weights: bool = False, fixed=None):
     """Prefill then decode one unit over positions 0..N-1 of ``Q, K, V`` ([N, d]).
 
     ``replay_kept`` / ``replay_evicted``: the other side's prefill kept set and
     per-step eviction log; they are adopted only at near-ties (see
-    ``prefill_keep`` and ``UnitCache.step``).
+    ``prefill_keep`` and ``UnitCache.step``).  ``fixed``: per-position scores
+    [N] fixed in advance (see ``run_unit_global``); None for H2O itself.
 
     Returns a dict: prefill stats (or None), ``kept`` (sorted prefill kept set),
     ``out`` [T, d], ``evicted`` [T], the final ``cache`` and tie counters.
@@ -297,7 +311,7 @@ def run_unit(Q, K, V, prompt_len: int, heavy: int, recent: int, scale: float | N
     N, d = Q.shape
     L = prompt_len
     cache, ps, pinfo = UnitCache.from_prompt(Q[:L], K[:L], V[:L], heavy, recent, scale,
-                                             prefer_kept=replay_kept, tie_rtol=tie_rtol)
+                                             prefer_kept=replay_kept, tie_rtol=tie_rtol, fixed=fixed)
     kept = [int(p) for p in cache.pos]
     T = N - L
     out = np.zeros((T, d))
@@ -315,3 +329,34 @@ def run_unit(Q, K, V, prompt_len: int, heavy: int, recent: int, scale: float | N
     return {"prefill": ps, "kept": kept, "prefill_tie_adopted": pinfo["tie_adopted"],
             "out": out, "evicted": evicted, "cache": cache, "decode_ties_adopted": ties,
             "weights": weights}
+
+
+# =============================================================================== global comparator
+def global_scores(Q, K, scale: float) -> np.ndarray:
+    """The attention each token receives from every row of the whole sequence:
+    c_j = sum over r >= j of a_rj, with a the causal softmax over all N rows
+    (prompt and generated alike).  This is the score a heavy-hitter rule could
+    use if it saw the future; the pages contrast it with the greedy local score.
+    [Report §2.3, the local-versus-global comparison of Figure 2(d)]
+    READING: "global" means the column sums of the full causal attention of the
+    sequence the unit will see, computed once."""
+    return prefill_scores(Q, K, scale).col_sum
+
+
+def run_unit_global(Q, K, V, prompt_len: int, heavy: int, recent: int, scale: float | None = None,
+                    replay_kept=None, replay_evicted=None, tie_rtol: float = TIE_RTOL):
+    """The global comparator: the same prefill keep and decode eviction rule as
+    ``run_unit``, but every token's score is its global score (``global_scores``
+    over all N rows), fixed in advance; decode steps accumulate nothing.  The
+    attention itself is unchanged (normalised over the cached entries only).
+    [Report §2.3, Figure 2(d)]
+    READING: the recent window, the candidate set (positions <= i - K_r), the tie
+    rule and the one-victim-per-step budget are those of H2O; only the score
+    differs.  Returns ``run_unit``'s dict plus ``scores`` (the global scores)."""
+    Q, K, V = (np.asarray(x, np.float64) for x in (Q, K, V))
+    scale = default_scale(Q.shape[1]) if scale is None else scale
+    g = global_scores(Q, K, scale)
+    res = run_unit(Q, K, V, prompt_len, heavy, recent, scale, replay_kept=replay_kept,
+                   replay_evicted=replay_evicted, tie_rtol=tie_rtol, fixed=g)
+    res["scores"] = g
+    return res

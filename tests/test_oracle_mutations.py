@@ -15,7 +15,8 @@ import numpy as np
 import pytest
 import scipy.special
 
-from test_oracle_pins import KEYS2, _brute_force_run, _brute_keep, _library_causal_weights, _sdpa_rows
+from test_oracle_pins import (KEYS2, _brute_force_run, _brute_keep, _brute_topk_sets, _library_causal_weights,
+                              _replay_sets, _sdpa_rows)
 
 SRC = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "oracle", "h2o_oracle.py")
 
@@ -54,7 +55,7 @@ MUTATIONS = {
     "prefill recent window shifted": ("recent_pos = list(range(L - recent, L))",
                                       "recent_pos = list(range(L - recent - 1, L - 1))"),
     "cache allowed to overfill": ("if len(self.pos) < self.k:", "if len(self.pos) <= self.k:"),
-    "prefill scores not seeded": ("cache.score = ps.col_sum[kept].copy()",
+    "prefill scores not seeded": ("cache.score = c[kept].copy()",
                                   "cache.score = np.zeros(len(kept))"),
     "recent pool overlaps": ("pool = list(range(L - recent))", "pool = list(range(L))"),
     "prefill output from transposed weights": ("return A @ np.asarray(V, np.float64)",
@@ -62,6 +63,17 @@ MUTATIONS = {
     "prefill output mixes keys": ("return A @ np.asarray(V, np.float64)", "return A @ np.asarray(K, np.float64)"),
     "prefill output one row late": ("return A @ np.asarray(V, np.float64)",
                                     "return np.vstack([np.zeros((1, V.shape[1])), (A @ V)[:-1]])"),
+    "fixed scores still accumulate": ("G_score = np.concatenate([self.score, [self.fixed[i]]])",
+                                      "G_score = np.concatenate([self.score, [self.fixed[i]]]) + a"),
+    "new token's fixed score dropped": ("G_score = np.concatenate([self.score, [self.fixed[i]]])",
+                                        "G_score = np.concatenate([self.score, [0.0]])"),
+    "fixed prompt ranked by its own column sums": (
+        "c = ps.col_sum if fixed is None else cache.fixed[:L]",
+        "c = prefill_scores(Qp, Kp, scale).col_sum"),
+    "global scores from the prompt rows only": (
+        "g = global_scores(Q, K, scale)",
+        "g = np.concatenate([global_scores(Q[:max(prompt_len, 1)], K[:max(prompt_len, 1)], scale), "
+        "np.zeros(len(Q) - max(prompt_len, 1))])"),
     "evicted entries stay in the normaliser": (
         "a = softmax(x)\n        o = a @ G_V",
         "a = softmax(x)\n        a = a * (len(x) / (len(x) + self.evicted_mass))\n        o = a @ G_V"),
@@ -110,6 +122,19 @@ def _checks(m):
         Ks = np.tile(K[0], (L, 1))
         O = m.prefill_output(Q, Ks, V, 0.37)
         np.testing.assert_allclose(O, np.cumsum(V, axis=0) / np.arange(1, L + 1)[:, None], rtol=1e-10)
+
+    def global_comparator():
+        for (L, T, h, r) in [(20, 30, 5, 4), (25, 20, 6, 0), (3, 30, 4, 4)]:
+            Q, K, V = (g.standard_normal((L + T, 6)) for _ in range(3))
+            res = m.run_unit_global(Q, K, V, L, h, r)
+            lib = _library_causal_weights(Q, K).sum(axis=0)
+            np.testing.assert_allclose(res["scores"], lib, rtol=1e-10)
+            assert _replay_sets(res, L, T, h + r) == _brute_topk_sets(lib, L, T, h, r)
+        for (L, T, h, r) in [(30, 40, 6, 5), (4, 50, 5, 3), (25, 30, 7, 0)]:
+            Q, K, V = (g.standard_normal((L + T, 6)) for _ in range(3))
+            sc = g.integers(0, 6, size=L + T).astype(float) / 4  # ties on purpose
+            res = m.run_unit(Q, K, V, L, h, r, fixed=sc)
+            assert _replay_sets(res, L, T, h + r) == _brute_topk_sets(sc, L, T, h, r)
 
     def sliding_window():
         N, L, R, d = 30, 9, 4, 6
@@ -168,7 +193,7 @@ def _checks(m):
         assert len(c.pos) == 9
         assert abs(c.score.sum() - (c.rows - c.evicted_mass)) < 1e-9 * c.rows
 
-    return [full_attention, prefill_library, prefill_out, sliding_window, identical_keys, brute_force, keep_brute, mass]
+    return [full_attention, prefill_library, prefill_out, global_comparator, sliding_window, identical_keys, brute_force, keep_brute, mass]
 
 
 def test_unmutated_oracle_passes_every_check():

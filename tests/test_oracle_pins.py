@@ -14,7 +14,8 @@ import scipy.special
 import torch
 from hypothesis import given, settings, strategies as st, HealthCheck
 
-from oracle import ParityMismatch, UnitCache, prefill_keep, prefill_output, prefill_scores, run_unit
+from oracle import (ParityMismatch, UnitCache, global_scores, prefill_keep, prefill_output, prefill_scores, run_unit,
+                    run_unit_global)
 
 torch.set_default_dtype(torch.float64)
 
@@ -367,3 +368,79 @@ def test_decode_replay_adopts_only_within_band():
     assert run_unit(Q, K, V, 3, 3, 0, replay_evicted=[2])["evicted"].tolist() == [2]
     with pytest.raises(ParityMismatch):
         run_unit(Q, K, V, 3, 3, 0, replay_evicted=[0])
+
+
+# ----------------------------------------------------------------------------- global comparator
+def _brute_topk_sets(scores, L, T, heavy, recent):
+    """Cached position sets after each decode step under fixed scores, by direct
+    enumeration: the recent window plus the K_h best (score, then position) of
+    every earlier position; all positions while the budget is not yet full."""
+    k = heavy + recent
+    sets = []
+    for t in range(T):
+        i = L + t
+        if i + 1 <= k:
+            sets.append(set(range(i + 1)))
+            continue
+        pool = list(range(0, i - recent + 1))
+        best = sorted(pool, key=lambda j: (scores[j], j), reverse=True)[:heavy]
+        sets.append(set(best) | set(range(i - recent + 1, i + 1)))
+    return sets
+
+
+def _replay_sets(res, L, T, k):
+    kept = set(res["kept"])
+    out = []
+    for t in range(T):
+        kept = kept | {L + t}
+        u = int(res["evicted"][t])
+        if u >= 0:
+            kept = kept - {u}
+        assert len(kept) == min(L + t + 1, k)
+        out.append(set(kept))
+    return out
+
+
+@pytest.mark.parametrize("N,d,seed", [(1, 4, 20), (33, 8, 21), (140, 16, 22)])
+def test_global_scores_match_library_softmax(N, d, seed):
+    Q, K, _ = _rand(N, d, seed)
+    np.testing.assert_allclose(global_scores(Q, K, 1 / math.sqrt(d)), _library_causal_weights(Q, K).sum(axis=0),
+                               rtol=1e-12)
+
+
+@pytest.mark.parametrize("L,T,heavy,recent,seed", [(30, 40, 6, 5, 0), (4, 50, 5, 3, 1), (25, 30, 7, 0, 2),
+                                                   (25, 30, 0, 6, 3), (10, 10, 20, 20, 4)])
+def test_fixed_scores_keep_top_heavy_by_brute_force(L, T, heavy, recent, seed):
+    # fixed scores (with deliberate ties): the cache is always the window plus the
+    # K_h best earlier positions
+    g = np.random.default_rng(seed)
+    N, d = L + T, 6
+    Q, K, V = (g.standard_normal((N, d)) for _ in range(3))
+    scores = g.integers(0, 6, size=N).astype(float) / 4
+    res = run_unit(Q, K, V, L, heavy, recent, fixed=scores)
+    assert _replay_sets(res, L, T, heavy + recent) == _brute_topk_sets(scores, L, T, heavy, recent)
+
+
+def test_fixed_decreasing_scores_is_sink_plus_window_attention():
+    # scores that fall with position keep the first K_h tokens forever: every
+    # output is attention over the sinks plus the window (torch SDPA, float64)
+    L, T, heavy, recent, d = 12, 30, 4, 5, 8
+    N = L + T
+    Q, K, V = _rand(N, d, 23)
+    res = run_unit(Q, K, V, L, heavy, recent, fixed=np.arange(N, 0, -1).astype(float))
+    mask = np.zeros((N, N), dtype=bool)
+    for i in range(N):
+        mask[i, : min(heavy, i + 1)] = True
+        mask[i, max(0, i - recent): i + 1] = True
+    np.testing.assert_allclose(res["out"], _sdpa_rows(Q, K, V, mask)[L:], rtol=1e-10, atol=1e-10)
+
+
+@pytest.mark.parametrize("L,T,heavy,recent,seed", [(20, 30, 5, 4, 30), (0, 40, 6, 6, 31), (35, 25, 8, 0, 32)])
+def test_global_run_follows_library_scores(L, T, heavy, recent, seed):
+    # the comparator ranks by the column sums of the whole sequence's causal
+    # softmax (scipy), and its cache is the brute-force top set of those scores
+    Q, K, V = _rand(L + T, 8, seed)
+    res = run_unit_global(Q, K, V, L, heavy, recent)
+    lib = _library_causal_weights(Q, K).sum(axis=0)
+    np.testing.assert_allclose(res["scores"], lib, rtol=1e-12)
+    assert _replay_sets(res, L, T, heavy + recent) == _brute_topk_sets(lib, L, T, heavy, recent)
