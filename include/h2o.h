@@ -150,14 +150,61 @@ h2o_status h2o_decode_step(h2o_cache* cache, const void* q, const void* k, const
 h2o_status h2o_cache_read(h2o_cache* cache, int32_t* pos, float* score, void* k_slots,
                           void* v_slots, int32_t* meta, void* stream);
 
-/* Copy the last prefill's per-token statistics to host memory (synchronises
+/* Copy the last h2o_prefill's per-token statistics to host memory (synchronises
  * `stream`).  Each pointer is host, nullable, [B, H, L] float32 with L the last
  * prompt_len:
  *   row_lse: log sum_j exp(scale*q_r.k_j) over j <= r, the natural log of the
  *            normaliser of prompt row r's causal softmax
  *   col_sum: c_j, the attention token j received from the prompt rows
- * Errors: H2O_ERR_INVALID_ARG, H2O_ERR_STATE (no prefill yet), H2O_ERR_HIP. */
+ * Errors: H2O_ERR_INVALID_ARG, H2O_ERR_STATE (no h2o_prefill yet, or an
+ * h2o_column_scores / h2o_prefill_scored call since), H2O_ERR_HIP. */
 h2o_status h2o_prefill_stats_read(h2o_cache* cache, float* row_lse, float* col_sum, void* stream);
+
+/* ---- Global-score comparator (Report §2.3 and its Figure 2(d): the greedy
+ * local score against a "global" one computed from the full attention of the
+ * whole sequence).  The three calls below run the same budgeted attention and
+ * the same keep/evict rule as h2o_prefill / h2o_decode_step, but rank tokens by
+ * scores the caller supplies and fixes in advance; nothing accumulates.  The
+ * global comparator is: h2o_column_scores over all N = L + T tokens, then
+ * h2o_prefill_scored with the first L scores, then h2o_decode_step_scored with
+ * score[i] at step i. */
+
+/* Column scores of a whole sequence: c_j = sum_{r >= j} a_rj with a the causal
+ * softmax of all n rows (the score H2O would give token j if every row of the
+ * sequence were known in advance).  Computed with the prefill's two passes.
+ *   q, k:   device, [B, H, n, d] in the cache dtype.
+ *   scores: device, [B, H, n] float32, written.
+ * Uses the cache's prefill scratch (n <= max_prompt) and leaves the cached
+ * entries untouched; afterwards h2o_prefill_stats_read reports H2O_ERR_STATE
+ * until the next h2o_prefill.  n == 0 does nothing (pointers may be NULL).
+ * Errors: H2O_ERR_INVALID_ARG (NULL or misaligned pointers, n < 0 or
+ * n > max_prompt), H2O_ERR_HIP. */
+h2o_status h2o_column_scores(h2o_cache* cache, const void* q, const void* k, int32_t n, float* scores,
+                             void* stream);
+
+/* Prefill by given scores: (re)initialise the cache from a prompt of
+ * `prompt_len` tokens exactly as h2o_prefill does (last K_r positions plus the
+ * K_h best of [0, prompt_len - K_r), equal scores ranked by position), but
+ * ranking by `scores` instead of the prompt's own column sums; the kept slots'
+ * scores are set to them.
+ *   k, v:   device, [B, H, prompt_len, d] in the cache dtype.
+ *   scores: device, [B, H, prompt_len] float32, finite and >= 0.
+ * No attention is computed; prompt_len may exceed max_prompt.  Afterwards
+ * h2o_prefill_stats_read reports H2O_ERR_STATE.  prompt_len == 0 gives an empty
+ * cache (pointers may be NULL).
+ * Errors: H2O_ERR_INVALID_ARG (NULL or misaligned pointers, prompt_len < 0),
+ * H2O_ERR_HIP. */
+h2o_status h2o_prefill_scored(h2o_cache* cache, const void* k, const void* v, int32_t prompt_len,
+                              const float* scores, void* stream);
+
+/* One decode step with fixed scores: attention and output exactly as
+ * h2o_decode_step, but no entry's score changes; the new token's score is
+ * new_score[unit] (device, [B, H] float32, finite and >= 0), and the victim is
+ * the candidate with the lowest score (lowest position on equal scores).
+ * Errors: as h2o_decode_step, and H2O_ERR_INVALID_ARG for a NULL or misaligned
+ * new_score. */
+h2o_status h2o_decode_step_scored(h2o_cache* cache, const void* q, const void* k, const void* v,
+                                  const float* new_score, float* out, int32_t* evicted, void* stream);
 
 /* Host-side state, no GPU call: entries cached per unit, next position, and the
  * last prompt length (-1 before the first prefill).  Pointers nullable. */

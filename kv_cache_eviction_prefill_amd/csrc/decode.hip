@@ -51,7 +51,8 @@ struct Layout {
 };
 
 // Score pass of one unit (whole block): every occupied slot adds its weight
-// exp2(x_j - M) / L with a Kahan-compensated fp32 sum; when the cache is full the
+// exp2(x_j - M) / L with a Kahan-compensated fp32 sum (with fixed scores nothing
+// is added and the new token's score is given); when the cache is full the
 // eviction candidates (pos <= i - K_r, and the new token when K_r = 0) compete on
 // the 64-bit key (score bits, pos) through a wave and LDS min, and the new
 // token's K/V, position and score overwrite the victim's slot.  pf_*: this
@@ -70,6 +71,7 @@ __device__ inline void score_pass(const DecodeArgs& a, int unit, float M, float 
   int32_t* ps = a.pos + static_cast<size_t>(unit) * a.kstride;
   const int cnt = a.count;
   const bool full = (cnt == a.k);
+  const bool accumulate = a.fixed_new == nullptr;  // else scores are fixed (global comparator)
 
   uint64_t best = kNoKey;
   int best_slot = -1;
@@ -95,13 +97,15 @@ __device__ inline void score_pass(const DecodeArgs& a, int unit, float M, float 
       cj = cp[j];
       pj = ps[j];
     }
-    const float w = fast_exp2(xj - M) * invL;
-    const float y = w - cj;  // Kahan-compensated add of this step's weight
-    const float t = sj + y;
-    cj = (t - sj) - y;
-    sj = t;
-    sc[j] = sj;
-    cp[j] = cj;
+    if (accumulate) {
+      const float w = fast_exp2(xj - M) * invL;
+      const float y = w - cj;  // Kahan-compensated add of this step's weight
+      const float t = sj + y;
+      cj = (t - sj) - y;
+      sj = t;
+      sc[j] = sj;
+      cp[j] = cj;
+    }
     if (full && pj <= a.cand_limit) {
       const uint64_t key = evict_key(sj, pj);
       if (key < best) {
@@ -110,7 +114,7 @@ __device__ inline void score_pass(const DecodeArgs& a, int unit, float M, float 
       }
     }
   }
-  const float w_new = fast_exp2(x_new - M) * invL;
+  const float w_new = accumulate ? fast_exp2(x_new - M) * invL : a.fixed_new[unit];
 
   int dst = cnt;  // cache not full: the new token takes the next free slot
   int32_t ev = -1;

@@ -25,6 +25,7 @@ struct h2o_cache {
   int32_t prompt_len;  // last prompt length, -1 before the first prefill
   int32_t lpad_cap;    // row capacity of the prefill scratch (multiple of 32)
   int32_t lpad_last;   // row stride of the last prefill's statistics
+  bool stats_valid;    // the prefill scratch holds the last h2o_prefill's statistics
   // device memory
   void* kslots;
   void* vslots;
@@ -271,6 +272,7 @@ h2o_status h2o_prefill(h2o_cache* c, const void* q, const void* k, const void* v
     if (e != hipSuccess) return hip_fail(e, "clear launch");
   } else {
     h2o::PrefillArgs a{};
+    a.stages = h2o::kStageScores | h2o::kStageSelect;
     a.q = q;
     a.k = k;
     a.v = v;
@@ -297,12 +299,93 @@ h2o_status h2o_prefill(h2o_cache* c, const void* q, const void* k, const void* v
   c->count = std::min(L, c->k);
   c->next_pos = L;
   c->prompt_len = L;
+  c->stats_valid = true;
   return H2O_OK;
 }
 
-h2o_status h2o_decode_step(h2o_cache* c, const void* q, const void* k, const void* v, float* out,
-                           int32_t* evicted, void* stream) {
+h2o_status h2o_column_scores(h2o_cache* c, const void* q, const void* k, int32_t n, float* scores, void* stream) {
   if (c == nullptr) return fail(H2O_ERR_INVALID_ARG, "cache is NULL");
+  if (n < 0) return fail(H2O_ERR_INVALID_ARG, "n must be >= 0");
+  if (n > c->p.max_prompt) return fail(H2O_ERR_INVALID_ARG, "n exceeds max_prompt");
+  if (n == 0) return H2O_OK;
+  if (q == nullptr || k == nullptr || scores == nullptr)
+    return fail(H2O_ERR_INVALID_ARG, "q, k and scores must be non-NULL");
+  if (!aligned16(q) || !aligned16(k)) return fail(H2O_ERR_INVALID_ARG, "q and k must be 16-byte aligned");
+  if ((reinterpret_cast<uintptr_t>(scores) & 3u) != 0)
+    return fail(H2O_ERR_INVALID_ARG, "scores must be 4-byte aligned");
+  DeviceGuard guard(c->device);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  h2o::PrefillArgs a{};
+  a.stages = h2o::kStageScores;
+  a.q = q;
+  a.k = k;
+  a.L = n;
+  a.Lpad = round32(n);
+  a.row_lse2 = c->row_lse2;
+  a.col_sum = c->col_sum;
+  a.scale = c->scale;
+  a.c2 = c->c2;
+  a.kcap = c->k;
+  a.kstride = c->kstride;
+  hipError_t e = h2o::launch_prefill(c->p.dtype, c->d, a, c->units, s);
+  if (e != hipSuccess) return hip_fail(e, "column score launch");
+  c->stats_valid = false;  // the prefill scratch now holds this sequence's statistics
+  e = hipMemcpy2DAsync(scores, static_cast<size_t>(n) * 4, c->col_sum, static_cast<size_t>(a.Lpad) * 4,
+                       static_cast<size_t>(n) * 4, c->units, hipMemcpyDeviceToDevice, s);
+  if (e != hipSuccess) return hip_fail(e, "copy column scores");
+  return H2O_OK;
+}
+
+h2o_status h2o_prefill_scored(h2o_cache* c, const void* k, const void* v, int32_t L, const float* scores,
+                              void* stream) {
+  if (c == nullptr) return fail(H2O_ERR_INVALID_ARG, "cache is NULL");
+  if (L < 0) return fail(H2O_ERR_INVALID_ARG, "prompt_len must be >= 0");
+  if (L > 0) {
+    if (k == nullptr || v == nullptr || scores == nullptr)
+      return fail(H2O_ERR_INVALID_ARG, "k, v and scores must be non-NULL");
+    if (!aligned16(k) || !aligned16(v)) return fail(H2O_ERR_INVALID_ARG, "k and v must be 16-byte aligned");
+    if ((reinterpret_cast<uintptr_t>(scores) & 3u) != 0)
+      return fail(H2O_ERR_INVALID_ARG, "scores must be 4-byte aligned");
+  }
+  DeviceGuard guard(c->device);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (L == 0) {
+    const hipError_t e = h2o::launch_clear(c->pos, c->score, c->comp, static_cast<size_t>(c->units) * c->kstride, s);
+    if (e != hipSuccess) return hip_fail(e, "clear launch");
+  } else {
+    h2o::PrefillArgs a{};
+    a.stages = h2o::kStageSelect;
+    a.k = k;
+    a.v = v;
+    a.L = L;
+    a.Lpad = round32(L);
+    a.scores_in = scores;
+    a.scores_stride = L;
+    a.kslots = c->kslots;
+    a.vslots = c->vslots;
+    a.score = c->score;
+    a.comp = c->comp;
+    a.pos = c->pos;
+    a.heavy = c->p.heavy_budget;
+    a.recent = c->p.recent_budget;
+    a.kcap = c->k;
+    a.kstride = c->kstride;
+    a.scale = c->scale;
+    a.c2 = c->c2;
+    const hipError_t e = h2o::launch_prefill(c->p.dtype, c->d, a, c->units, s);
+    if (e != hipSuccess) return hip_fail(e, "scored prefill launch");
+  }
+  c->count = std::min(L, c->k);
+  c->next_pos = L;
+  c->prompt_len = L;
+  c->stats_valid = false;
+  return H2O_OK;
+}
+
+namespace {
+
+h2o_status decode_common(h2o_cache* c, const void* q, const void* k, const void* v, const float* new_score,
+                         float* out, int32_t* evicted, void* stream) {
   if (q == nullptr || k == nullptr || v == nullptr || out == nullptr)
     return fail(H2O_ERR_INVALID_ARG, "q, k, v and out must be non-NULL");
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
@@ -331,6 +414,7 @@ h2o_status h2o_decode_step(h2o_cache* c, const void* q, const void* k, const voi
   a.new_pos = c->next_pos;
   a.cand_limit = c->next_pos - c->p.recent_budget;
   a.new_is_candidate = c->p.recent_budget == 0 ? 1 : 0;
+  a.fixed_new = new_score;
   a.nsplit = choose_nsplit(c, c->count, &a.split_len);
   a.c2 = c->c2;
   const hipError_t e = h2o::launch_decode(c->p.dtype, c->d, a, c->units, static_cast<hipStream_t>(stream));
@@ -338,6 +422,23 @@ h2o_status h2o_decode_step(h2o_cache* c, const void* q, const void* k, const voi
   if (c->count < c->k) ++c->count;
   ++c->next_pos;
   return H2O_OK;
+}
+
+}  // namespace
+
+h2o_status h2o_decode_step(h2o_cache* c, const void* q, const void* k, const void* v, float* out,
+                           int32_t* evicted, void* stream) {
+  if (c == nullptr) return fail(H2O_ERR_INVALID_ARG, "cache is NULL");
+  return decode_common(c, q, k, v, nullptr, out, evicted, stream);
+}
+
+h2o_status h2o_decode_step_scored(h2o_cache* c, const void* q, const void* k, const void* v,
+                                  const float* new_score, float* out, int32_t* evicted, void* stream) {
+  if (c == nullptr) return fail(H2O_ERR_INVALID_ARG, "cache is NULL");
+  if (new_score == nullptr) return fail(H2O_ERR_INVALID_ARG, "new_score must be non-NULL");
+  if ((reinterpret_cast<uintptr_t>(new_score) & 3u) != 0)
+    return fail(H2O_ERR_INVALID_ARG, "new_score must be 4-byte aligned");
+  return decode_common(c, q, k, v, new_score, out, evicted, stream);
 }
 
 h2o_status h2o_cache_read(h2o_cache* c, int32_t* pos, float* score, void* k_slots, void* v_slots, int32_t* meta,
@@ -369,6 +470,8 @@ h2o_status h2o_cache_read(h2o_cache* c, int32_t* pos, float* score, void* k_slot
 h2o_status h2o_prefill_stats_read(h2o_cache* c, float* row_lse, float* col_sum, void* stream) {
   if (c == nullptr) return fail(H2O_ERR_INVALID_ARG, "cache is NULL");
   if (c->prompt_len < 0) return fail(H2O_ERR_STATE, "no prefill yet");
+  if (!c->stats_valid)
+    return fail(H2O_ERR_STATE, "no statistics: the last call was h2o_prefill_scored or h2o_column_scores");
   DeviceGuard guard(c->device);
   hipError_t e = hipStreamSynchronize(static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "hipStreamSynchronize");

@@ -20,6 +20,7 @@ struct DecodeArgs {
   int32_t* evicted;  // [units] or nullptr
   float* part;       // split mode: [units, nsplit, 2 + d] partial (max, sum, o)
   float* logits;     // split mode: [units, k + 1] base-2 logits (new token at index k)
+  const float* fixed_new;  // [units] the new token's fixed score (scores do not accumulate), or nullptr
   int32_t k;           // slots per unit
   int32_t kstride;     // per-unit stride of score/comp/pos: k rounded up to 32 (128-byte rows)
   int32_t count;       // occupied slots before this step (slots 0..count-1)
@@ -33,8 +34,13 @@ struct DecodeArgs {
 
 hipError_t launch_decode(int dtype, int head_dim, const DecodeArgs& a, int units, hipStream_t s);
 
+// Prefill stages: the two score passes (row normalisers, column sums) and the
+// select + fill.
+enum PrefillStage : int32_t { kStageScores = 1, kStageSelect = 2 };
+
 // Prefill of every unit of a cache.
 struct PrefillArgs {
+  int32_t stages;     // PrefillStage bits
   const void* q;  // [units, L, d]
   const void* k;  // [units, L, d]
   const void* v;  // [units, L, d]
@@ -43,6 +49,8 @@ struct PrefillArgs {
   float* row_lse2;    // [units, Lpad] log2 sum_j exp2(c2 q_r.k_j) of each row; 0 past L
   float* col_sum;     // [units, Lpad] attention received by each prompt token
   float* out;         // [units, L, d] prompt attention output, or nullptr
+  const float* scores_in;  // [units, scores_stride] scores the select ranks by, or nullptr (col_sum)
+  int32_t scores_stride;
   void* kslots;       // [units, k, d]
   void* vslots;       // [units, k, d]
   float* score;       // [units, kstride]

@@ -660,7 +660,8 @@ __global__ __launch_bounds__(kThreads) void select_fill(PrefillArgs a) {
   const int unit = blockIdx.x;
   const int tid = threadIdx.x;
   const int L = a.L, kc = a.kcap;
-  const float* c = a.col_sum + static_cast<size_t>(unit) * a.Lpad;
+  const float* c = a.scores_in != nullptr ? a.scores_in + static_cast<size_t>(unit) * a.scores_stride
+                                          : a.col_sum + static_cast<size_t>(unit) * a.Lpad;
 
   int nkept;
   if (L <= kc) {
@@ -775,36 +776,40 @@ hipError_t launch_bf16(const PrefillArgs& a, int units, hipStream_t s) {
   const int nblk = (a.L + kBlockRows - 1) / kBlockRows;  // row blocks; a block takes a pair
   const int groups = (units + kXcds - 1) / kXcds;
   const dim3 grid(groups * kXcds * ((nblk + 1) / 2));
-  if (a.out != nullptr) {
-    const int nbo = (a.L + kOutRows - 1) / kOutRows;
-    const dim3 grid_o(groups * kXcds * ((nbo + 1) / 2));
-    hipLaunchKernelGGL((rowout_bf16<D>), grid_o, dim3(kThreads), 0, s, a, nbo, units);
-  } else {
-    hipLaunchKernelGGL((rowstats_bf16<D>), grid, dim3(kThreads), 0, s, a, nblk, units);
+  if (a.stages & kStageScores) {
+    if (a.out != nullptr) {
+      const int nbo = (a.L + kOutRows - 1) / kOutRows;
+      const dim3 grid_o(groups * kXcds * ((nbo + 1) / 2));
+      hipLaunchKernelGGL((rowout_bf16<D>), grid_o, dim3(kThreads), 0, s, a, nbo, units);
+    } else {
+      hipLaunchKernelGGL((rowstats_bf16<D>), grid, dim3(kThreads), 0, s, a, nblk, units);
+    }
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((colsum_bf16<D>), grid, dim3(kThreads), 0, s, a, nblk, units);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
   }
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((colsum_bf16<D>), grid, dim3(kThreads), 0, s, a, nblk, units);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  return launch_select<bf16_t, D>(a, units, s);
+  return (a.stages & kStageSelect) ? launch_select<bf16_t, D>(a, units, s) : hipSuccess;
 }
 
 template <int D>
 hipError_t launch_f32(const PrefillArgs& a, int units, hipStream_t s) {
   const int nblk = (a.L + 63) / 64;
-  hipLaunchKernelGGL((rowstats_f32<D>), dim3(units * nblk), dim3(64), 0, s, a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((colsum_f32<D>), dim3(units * nblk), dim3(64), 0, s, a);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  if (a.out != nullptr) {
-    hipLaunchKernelGGL((attnout_f32<D>), dim3(units * nblk), dim3(64), 0, s, a);
+  if (a.stages & kStageScores) {
+    hipLaunchKernelGGL((rowstats_f32<D>), dim3(units * nblk), dim3(64), 0, s, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((colsum_f32<D>), dim3(units * nblk), dim3(64), 0, s, a);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
+    if (a.out != nullptr) {
+      hipLaunchKernelGGL((attnout_f32<D>), dim3(units * nblk), dim3(64), 0, s, a);
+      e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
   }
-  return launch_select<float, D>(a, units, s);
+  return (a.stages & kStageSelect) ? launch_select<float, D>(a, units, s) : hipSuccess;
 }
 
 }  // namespace

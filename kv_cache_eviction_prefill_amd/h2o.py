@@ -51,6 +51,9 @@ _SIGNATURES = {
     "h2o_cache_read": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp]),
     "h2o_prefill_stats_read": (_i32, [_vp, _vp, _vp, _vp]),
     "h2o_cache_info": (_i32, [_vp, _p32, _p32, _p32]),
+    "h2o_column_scores": (_i32, [_vp, _vp, _vp, _i32, _vp, _vp]),
+    "h2o_prefill_scored": (_i32, [_vp, _vp, _vp, _i32, _vp, _vp]),
+    "h2o_decode_step_scored": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
     "h2o_status_str": (ctypes.c_char_p, [_i32]),
     "h2o_last_error": (ctypes.c_char_p, []),
 }
@@ -111,6 +114,18 @@ def h2o_prefill_stats_read(cache, row_lse, col_sum, stream):
 
 def h2o_cache_info(cache, count, next_pos, prompt_len):
     return load().h2o_cache_info(cache, count, next_pos, prompt_len)
+
+
+def h2o_column_scores(cache, q, k, n, scores, stream):
+    return load().h2o_column_scores(cache, q, k, n, scores, stream)
+
+
+def h2o_prefill_scored(cache, k, v, prompt_len, scores, stream):
+    return load().h2o_prefill_scored(cache, k, v, prompt_len, scores, stream)
+
+
+def h2o_decode_step_scored(cache, q, k, v, new_score, out, evicted, stream):
+    return load().h2o_decode_step_scored(cache, q, k, v, new_score, out, evicted, stream)
 
 
 def h2o_status_str(status):
@@ -207,6 +222,45 @@ class H2OCache:
             vs = (vs.astype(np.uint32) << 16).view(np.float32)
         assert pos.size == n
         return {"pos": pos, "score": score, "k": ks, "v": vs, "count": int(meta[0]), "next_pos": int(meta[1])}
+
+    # -- global-score comparator
+    def column_scores(self, q, k, out=None, stream=None):
+        """Column sums of the causal softmax of a whole sequence [B, H, n, d]:
+        float32 [B, H, n] (written into ``out`` when given)."""
+        n = q.shape[2]
+        shape = (self.B, self.H, n, self.d)
+        qp, kp = self._check_t(q, shape, self.tdtype, "q"), self._check_t(k, shape, self.tdtype, "k")
+        if out is None:
+            out = self.torch.empty((self.B, self.H, n), dtype=self.torch.float32, device=self.device)
+        op = self._check_t(out, (self.B, self.H, n), self.torch.float32, "out")
+        check(h2o_column_scores(self.handle, qp, kp, n, op, self._stream(stream)), "h2o_column_scores")
+        return out
+
+    def prefill_scored(self, k, v, scores, stream=None):
+        """Keep the prompt's recent window and best-scored tokens by ``scores`` [B, H, L]."""
+        L = k.shape[2]
+        shape = (self.B, self.H, L, self.d)
+        kp, vp = self._check_t(k, shape, self.tdtype, "k"), self._check_t(v, shape, self.tdtype, "v")
+        sp = self._check_t(scores, (self.B, self.H, L), self.torch.float32, "scores")
+        check(h2o_prefill_scored(self.handle, kp, vp, L, sp, self._stream(stream)), "h2o_prefill_scored")
+
+    def decode_step_scored(self, q, k, v, new_score, out=None, evicted=None, stream=None):
+        """A decode step with fixed scores; ``new_score``: float32 [B, H]."""
+        torch = self.torch
+        shape = (self.B, self.H, self.d)
+        qp = self._check_t(q, shape, self.tdtype, "q")
+        kp = self._check_t(k, shape, self.tdtype, "k")
+        vp = self._check_t(v, shape, self.tdtype, "v")
+        np_ = self._check_t(new_score, (self.B, self.H), torch.float32, "new_score")
+        if out is None:
+            out = torch.empty(shape, dtype=torch.float32, device=self.device)
+        op = self._check_t(out, shape, torch.float32, "out")
+        ep = None
+        if evicted is not None:
+            ep = self._check_t(evicted, (self.B, self.H), torch.int32, "evicted")
+        check(h2o_decode_step_scored(self.handle, qp, kp, vp, np_, op, ep, self._stream(stream)),
+              "h2o_decode_step_scored")
+        return out, evicted
 
     def prefill_stats(self, stream=None):
         L = self.info()[2]

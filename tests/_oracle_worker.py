@@ -13,7 +13,7 @@ from __future__ import annotations
 
 import numpy as np
 
-from oracle import ParityMismatch, run_unit
+from oracle import ParityMismatch, run_unit, run_unit_global
 
 OUT_ATOL = 2e-3
 SCORE_RTOL = 1e-4
@@ -31,16 +31,34 @@ def _rel(a, b):
 def check_unit(p: dict) -> dict:
     """``p``: Q, K, V [N, d] (float32, storage-rounded), L, heavy, recent, and the
     GPU's results for the unit: kept, evicted [T], out [T, d] (or sampled
-    steps), stats (row_lse, col_sum) or None, final (pos, score, k, v)."""
+    steps), stats (row_lse, col_sum) or None, final (pos, score, k, v).
+
+    ``p["mode"]``: "local" (H2O, the default), "global" (the global-score
+    comparator; ``p["gscores"]`` holds the GPU's column scores of the whole
+    sequence) or "fixed" (scores ``p["fixed"]`` given to both sides, so every
+    decision must agree exactly, with no near-tie adoption)."""
     tag = p["tag"]
+    mode = p.get("mode", "local")
     res = {"tag": tag, "ok": True, "msg": ""}
     try:
-        o = run_unit(p["Q"], p["K"], p["V"], p["L"], p["heavy"], p["recent"],
-                     replay_kept=p["kept"], replay_evicted=p["evicted"])
+        if mode == "global":
+            o = run_unit_global(p["Q"], p["K"], p["V"], p["L"], p["heavy"], p["recent"],
+                                replay_kept=p["kept"], replay_evicted=p["evicted"])
+        else:
+            o = run_unit(p["Q"], p["K"], p["V"], p["L"], p["heavy"], p["recent"],
+                         replay_kept=p["kept"], replay_evicted=p["evicted"],
+                         fixed=p["fixed"] if mode == "fixed" else None)
     except ParityMismatch as e:
         return {"tag": tag, "ok": False, "msg": f"decision mismatch: {e}"}
     res["ties"] = int(o["decode_ties_adopted"]) + int(o["prefill_tie_adopted"])
     msgs = []
+    if mode == "fixed" and res["ties"]:
+        msgs.append(f"{res['ties']} decisions differ under identical fixed scores")
+    if mode == "global":
+        e_g = float(np.max(_rel(p["gscores"], o["scores"])))
+        res["colsum_rel"] = e_g
+        if e_g > SCORE_RTOL:
+            msgs.append(f"global column score rel {e_g:.3g}")
     # prefill statistics
     st = p.get("stats")
     if st is not None and o["prefill"] is not None:

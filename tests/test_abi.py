@@ -16,7 +16,7 @@ def test_every_declared_symbol_is_exported():
     lib = H.load()
     names = H.declared_entry_points()
     assert {"h2o_cache_create", "h2o_cache_destroy", "h2o_prefill", "h2o_decode_step",
-            "h2o_cache_read"} <= set(names)
+            "h2o_cache_read", "h2o_column_scores", "h2o_prefill_scored", "h2o_decode_step_scored"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
         assert n in H._SIGNATURES, f"binding has no signature for {n}"
@@ -86,6 +86,9 @@ def test_null_and_state_checks_make_no_gpu_call():
     assert H.h2o_cache_read(None, None, None, None, None, None, None) == H.H2O_ERR_INVALID_ARG
     assert H.h2o_prefill_stats_read(None, None, None, None) == H.H2O_ERR_INVALID_ARG
     assert H.h2o_cache_info(None, None, None, None) == H.H2O_ERR_INVALID_ARG
+    assert H.h2o_column_scores(None, None, None, 4, None, None) == H.H2O_ERR_INVALID_ARG
+    assert H.h2o_prefill_scored(None, None, None, 4, None, None) == H.H2O_ERR_INVALID_ARG
+    assert H.h2o_decode_step_scored(None, None, None, None, None, None, None, None) == H.H2O_ERR_INVALID_ARG
     p = H.make_params(1, 1, 64, 2, 2, "f32")
     assert H.h2o_cache_create(ctypes.byref(p), -1, None) == H.H2O_ERR_INVALID_ARG
     out = ctypes.c_void_p(1234)
