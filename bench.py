@@ -35,10 +35,14 @@ BF16_MFMA_PEAK_TFLOPS = 2500.0
 MALL_BYTES = 256 * 2 ** 20
 
 
-def decode_bytes_per_unit(c: int, d: int, s: int) -> int:
+def decode_bytes_per_unit(c: int, d: int, s: int, fixed: bool = False) -> int:
     """Algorithmic HBM bytes of one decode step of one unit with c cached slots:
     K and V slot reads (2cds), score read+write (8c), position read (4c), the new
-    token's q/k/v reads (3ds), its K/V slot write (2ds), fp32 output (4d)."""
+    token's q/k/v reads (3ds), its K/V slot write (2ds), fp32 output (4d).  With
+    fixed scores (the global comparator) scores are only read (4c) and the new
+    token's score is read (4)."""
+    if fixed:
+        return c * (2 * d * s + 8) + d * (5 * s + 4) + 4
     return c * (2 * d * s + 12) + d * (5 * s + 4)
 
 
@@ -89,6 +93,9 @@ def parse():
     ap.add_argument("--layers", type=int, default=None, help="override the layer count (profiling runs)")
     ap.add_argument("--decode-steps", type=int, default=None, help="override decode steps (profiling runs)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--variant", choices=("h2o", "global"), default="h2o",
+                    help="h2o: the method; global: the global-score comparator (column scores of all "
+                         "prompt + generated tokens, then the same keep/evict rule with fixed scores)")
     ap.add_argument("--prefill-out", action="store_true",
                     help="prefill also writes the prompt's attention output (fp32 [B, H, L, d])")
     ap.add_argument("--cpu-units", type=int, default=96,
@@ -107,11 +114,11 @@ def _cpu_unit(args):
     """Worker: time the oracle on one unit (prefill + every decode step)."""
     import time as _t
 
-    from oracle import run_unit
+    from oracle import run_unit, run_unit_global
 
-    Q, K, V, L, kh, kr = args
+    Q, K, V, L, kh, kr, variant = args
     t0 = _t.perf_counter()
-    run_unit(Q, K, V, L, kh, kr)
+    (run_unit_global if variant == "global" else run_unit)(Q, K, V, L, kh, kr)
     return _t.perf_counter() - t0
 
 
@@ -159,15 +166,27 @@ def main():
     stream = torch.cuda.current_stream(dev)
     sp = stream.cuda_stream
 
+    glob = a.variant == "global"
+    if glob and a.prefill_out:
+        print("--prefill-out applies to the h2o variant only", file=sys.stderr)
+        sys.exit(2)
+    N = L + T
+
     # ---------------------------------------------------------------- inputs (untimed)
     t_gen = time.time()
-    pre, dec = [], []
+    pre, dec, seq, gsc = [], [], [], []
     for layer in range(NL):
         q, k, v = synth.torch_qkv(w, layer, 0, w.n_positions, dev)
-        pre.append(tuple(x[:, :, :L].contiguous() for x in (q, k, v)))
+        if glob:  # the comparator reads the whole sequence: column scores over q, k; prompt rows of k, v
+            seq.append((q, k, v))
+            gsc.append(torch.empty((B, H, N), dtype=torch.float32, device=dev))
+            pre.append(None)
+        else:
+            pre.append(tuple(x[:, :, :L].contiguous() for x in (q, k, v)))
         dec.append(tuple(x[:, :, L:].permute(2, 0, 1, 3).contiguous() for x in (q, k, v)))
         del q, k, v
-    caches = [H2OCache(B, H, d, w.heavy_budget, w.recent_budget, dtype=w.dtype, max_prompt=L) for _ in range(NL)]
+    caches = [H2OCache(B, H, d, w.heavy_budget, w.recent_budget, dtype=w.dtype, max_prompt=N if glob else L)
+              for _ in range(NL)]
     out = torch.empty((NL, B, H, d), dtype=torch.float32, device=dev)
     # the prompt attention output, when asked for: one buffer shared by the layers
     pout = torch.empty((B, H, L, d), dtype=torch.float32, device=dev) if a.prefill_out else None
@@ -178,27 +197,39 @@ def main():
 
     # raw pointers: the timed loop only marshals integers into the C entry points
     handles = [c.handle for c in caches]
-    pre_ptr = [tuple(x.data_ptr() for x in p) for p in pre]
+    pre_ptr = [tuple(x.data_ptr() for x in p) if p is not None else None for p in pre]
+    seq_ptr = [tuple(x.data_ptr() for x in p) for p in seq]
+    gsc_ptr = [g.data_ptr() for g in gsc]
     dec_ptr = [[tuple(x[t].data_ptr() for x in dq) for t in range(T)] for dq in dec]
     out_ptr = [out[l].data_ptr() for l in range(NL)]
     ev_ptr = [ev[l].data_ptr() for l in range(NL)]
     prefill_c, decode_c = lib.h2o_prefill, lib.h2o_decode_step
+    colsc_c, prefill_sc_c, decode_sc_c = lib.h2o_column_scores, lib.h2o_prefill_scored, lib.h2o_decode_step_scored
+
+    def _ok(st, where):
+        if st:
+            raise h2o.H2OError(st, where, h2o.h2o_last_error())
 
     def one_step(evs=None):
         if evs is not None:
             evs[0].record(stream)
         for l in range(NL):
-            st = prefill_c(handles[l], *pre_ptr[l], L, pout_ptr, sp)
-            if st:
-                raise h2o.H2OError(st, "h2o_prefill", h2o.h2o_last_error())
+            if glob:
+                qf, kf, vf = seq_ptr[l]
+                _ok(colsc_c(handles[l], qf, kf, N, gsc_ptr[l], sp), "h2o_column_scores")
+                _ok(prefill_sc_c(handles[l], kf, vf, L, N, gsc_ptr[l], sp), "h2o_prefill_scored")
+            else:
+                _ok(prefill_c(handles[l], *pre_ptr[l], L, pout_ptr, sp), "h2o_prefill")
         if evs is not None:
             evs[1].record(stream)
         for t in range(T):
             for l in range(NL):
                 qp, kp, vp = dec_ptr[l][t]
-                st = decode_c(handles[l], qp, kp, vp, out_ptr[l], ev_ptr[l], sp)
-                if st:
-                    raise h2o.H2OError(st, "h2o_decode_step", h2o.h2o_last_error())
+                if glob:
+                    _ok(decode_sc_c(handles[l], qp, kp, vp, gsc_ptr[l] + 4 * (L + t), N, out_ptr[l], ev_ptr[l], sp),
+                        "h2o_decode_step_scored")
+                else:
+                    _ok(decode_c(handles[l], qp, kp, vp, out_ptr[l], ev_ptr[l], sp), "h2o_decode_step")
         if evs is not None:
             evs[2].record(stream)
 
@@ -233,12 +264,16 @@ def main():
     tokens = B * T * K
     launches = NL * T * K
     # slots read by decode step t: the cached count before it, min(k, L + t)
-    dec_bytes_launch = B * H * sum(decode_bytes_per_unit(min(w.k, L + t), d, s) for t in range(T)) / T
+    dec_bytes_launch = B * H * sum(decode_bytes_per_unit(min(w.k, L + t), d, s, glob) for t in range(T)) / T
     avg_dec_s = t_dec / launches
     achieved = dec_bytes_launch / avg_dec_s / 1e9
     kv_cache_bytes = B * H * w.k * (2 * d * s + 12)
-    pf_flops = NL * B * H * prefill_flops_per_unit(L, d, a.prefill_out) * K
-    pf_bytes = NL * B * H * prefill_bytes_per_unit(L, w.k, d, s, a.prefill_out) * K
+    if glob:  # the two score passes run over all N tokens; the select reads the prompt's scores
+        pf_flops = NL * B * H * prefill_flops_per_unit(N, d) * K
+        pf_bytes = NL * B * H * (prefill_bytes_per_unit(N, w.k, d, s) + 8 * N) * K
+    else:
+        pf_flops = NL * B * H * prefill_flops_per_unit(L, d, a.prefill_out) * K
+        pf_bytes = NL * B * H * prefill_bytes_per_unit(L, w.k, d, s, a.prefill_out) * K
     res = {
         "metric": METRIC,
         "value": tokens / t_all,
@@ -255,9 +290,9 @@ def main():
         "config": {"workload": w.name, "layers": NL, "batch": B, "heads": H, "head_dim": d,
                    "prompt_len": L, "decode_steps": T, "heavy_budget": w.heavy_budget,
                    "recent_budget": w.recent_budget, "storage": w.dtype, "accumulate": "fp32",
-                   "prefill_out": bool(a.prefill_out)},
+                   "prefill_out": bool(a.prefill_out), "variant": a.variant},
         "roofline": {"kernel": f"decode_kernel<{w.dtype},{d}>", "bound": "hbm", "achieved": achieved,
-                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic(w.name) if a.layers is None else None,
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic(w.name) if a.layers is None and not glob else None,
                      "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
                      "bytes_per_launch": dec_bytes_launch, "avg_launch_us": 1e6 * avg_dec_s,
                      "launches": launches},
@@ -278,10 +313,13 @@ def main():
         picks = [(int(g.integers(NL)), int(g.integers(B)), int(g.integers(H))) for _ in range(a.cpu_units)]
         samples = []
         for (l, b, h) in picks:
-            qf = torch.cat([pre[l][0][b, h], dec[l][0][:, b, h]]).float().cpu().numpy()
-            kf = torch.cat([pre[l][1][b, h], dec[l][1][:, b, h]]).float().cpu().numpy()
-            vf = torch.cat([pre[l][2][b, h], dec[l][2][:, b, h]]).float().cpu().numpy()
-            samples.append((qf, kf, vf, L, w.heavy_budget, w.recent_budget))
+            if glob:
+                qf, kf, vf = (x[b, h].float().cpu().numpy() for x in seq[l])
+            else:
+                qf = torch.cat([pre[l][0][b, h], dec[l][0][:, b, h]]).float().cpu().numpy()
+                kf = torch.cat([pre[l][1][b, h], dec[l][1][:, b, h]]).float().cpu().numpy()
+                vf = torch.cat([pre[l][2][b, h], dec[l][2][:, b, h]]).float().cpu().numpy()
+            samples.append((qf, kf, vf, L, w.heavy_budget, w.recent_budget, a.variant))
         procs = min(len(os.sched_getaffinity(0)), 16, len(samples))
         os.environ.setdefault("OMP_NUM_THREADS", "1")
         os.environ.setdefault("OPENBLAS_NUM_THREADS", "1")

@@ -186,25 +186,30 @@ h2o_status h2o_column_scores(h2o_cache* cache, const void* q, const void* k, int
  * `prompt_len` tokens exactly as h2o_prefill does (last K_r positions plus the
  * K_h best of [0, prompt_len - K_r), equal scores ranked by position), but
  * ranking by `scores` instead of the prompt's own column sums; the kept slots'
- * scores are set to them.
- *   k, v:   device, [B, H, prompt_len, d] in the cache dtype.
- *   scores: device, [B, H, prompt_len] float32, finite and >= 0.
+ * scores are set to them.  The prompt is the first prompt_len rows of each
+ * unit's `seq_rows` rows (e.g. the whole sequence's K/V and column scores):
+ *   k, v:   device, [B, H, seq_rows, d] in the cache dtype.
+ *   scores: device, [B, H, seq_rows] float32, finite and >= 0 (the first
+ *           prompt_len of each unit are read).
  * No attention is computed; prompt_len may exceed max_prompt.  Afterwards
  * h2o_prefill_stats_read reports H2O_ERR_STATE.  prompt_len == 0 gives an empty
  * cache (pointers may be NULL).
- * Errors: H2O_ERR_INVALID_ARG (NULL or misaligned pointers, prompt_len < 0),
- * H2O_ERR_HIP. */
+ * Errors: H2O_ERR_INVALID_ARG (NULL or misaligned pointers, prompt_len < 0,
+ * seq_rows < prompt_len), H2O_ERR_HIP. */
 h2o_status h2o_prefill_scored(h2o_cache* cache, const void* k, const void* v, int32_t prompt_len,
-                              const float* scores, void* stream);
+                              int32_t seq_rows, const float* scores, void* stream);
 
 /* One decode step with fixed scores: attention and output exactly as
  * h2o_decode_step, but no entry's score changes; the new token's score is
- * new_score[unit] (device, [B, H] float32, finite and >= 0), and the victim is
- * the candidate with the lowest score (lowest position on equal scores).
+ * new_score[unit * score_stride] (device float32, finite and >= 0; stride 1 for
+ * a [B, H] array, n with the column scores of a [B, H, n] sequence offset to
+ * this step's position), and the victim is the candidate with the lowest score
+ * (lowest position on equal scores).
  * Errors: as h2o_decode_step, and H2O_ERR_INVALID_ARG for a NULL or misaligned
- * new_score. */
+ * new_score or score_stride < 1. */
 h2o_status h2o_decode_step_scored(h2o_cache* cache, const void* q, const void* k, const void* v,
-                                  const float* new_score, float* out, int32_t* evicted, void* stream);
+                                  const float* new_score, int32_t score_stride, float* out, int32_t* evicted,
+                                  void* stream);
 
 /* Host-side state, no GPU call: entries cached per unit, next position, and the
  * last prompt length (-1 before the first prefill).  Pointers nullable. */

@@ -114,7 +114,7 @@ __device__ inline void score_pass(const DecodeArgs& a, int unit, float M, float 
       }
     }
   }
-  const float w_new = accumulate ? fast_exp2(x_new - M) * invL : a.fixed_new[unit];
+  const float w_new = accumulate ? fast_exp2(x_new - M) * invL : a.fixed_new[static_cast<size_t>(unit) * a.fixed_stride];
 
   int dst = cnt;  // cache not full: the new token takes the next free slot
   int32_t ev = -1;

@@ -290,6 +290,7 @@ h2o_status h2o_prefill(h2o_cache* c, const void* q, const void* k, const void* v
     a.recent = c->p.recent_budget;
     a.kcap = c->k;
     a.kstride = c->kstride;
+    a.kv_rows = L;
     a.scale = c->scale;
     a.c2 = c->c2;
     const hipError_t e = h2o::launch_prefill(c->p.dtype, c->d, a, c->units, s);
@@ -336,10 +337,11 @@ h2o_status h2o_column_scores(h2o_cache* c, const void* q, const void* k, int32_t
   return H2O_OK;
 }
 
-h2o_status h2o_prefill_scored(h2o_cache* c, const void* k, const void* v, int32_t L, const float* scores,
-                              void* stream) {
+h2o_status h2o_prefill_scored(h2o_cache* c, const void* k, const void* v, int32_t L, int32_t seq_rows,
+                              const float* scores, void* stream) {
   if (c == nullptr) return fail(H2O_ERR_INVALID_ARG, "cache is NULL");
   if (L < 0) return fail(H2O_ERR_INVALID_ARG, "prompt_len must be >= 0");
+  if (seq_rows < L) return fail(H2O_ERR_INVALID_ARG, "seq_rows must be >= prompt_len");
   if (L > 0) {
     if (k == nullptr || v == nullptr || scores == nullptr)
       return fail(H2O_ERR_INVALID_ARG, "k, v and scores must be non-NULL");
@@ -360,7 +362,8 @@ h2o_status h2o_prefill_scored(h2o_cache* c, const void* k, const void* v, int32_
     a.L = L;
     a.Lpad = round32(L);
     a.scores_in = scores;
-    a.scores_stride = L;
+    a.scores_stride = seq_rows;
+    a.kv_rows = seq_rows;
     a.kslots = c->kslots;
     a.vslots = c->vslots;
     a.score = c->score;
@@ -385,7 +388,7 @@ h2o_status h2o_prefill_scored(h2o_cache* c, const void* k, const void* v, int32_
 namespace {
 
 h2o_status decode_common(h2o_cache* c, const void* q, const void* k, const void* v, const float* new_score,
-                         float* out, int32_t* evicted, void* stream) {
+                         int32_t score_stride, float* out, int32_t* evicted, void* stream) {
   if (q == nullptr || k == nullptr || v == nullptr || out == nullptr)
     return fail(H2O_ERR_INVALID_ARG, "q, k, v and out must be non-NULL");
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
@@ -415,6 +418,7 @@ h2o_status decode_common(h2o_cache* c, const void* q, const void* k, const void*
   a.cand_limit = c->next_pos - c->p.recent_budget;
   a.new_is_candidate = c->p.recent_budget == 0 ? 1 : 0;
   a.fixed_new = new_score;
+  a.fixed_stride = score_stride;
   a.nsplit = choose_nsplit(c, c->count, &a.split_len);
   a.c2 = c->c2;
   const hipError_t e = h2o::launch_decode(c->p.dtype, c->d, a, c->units, static_cast<hipStream_t>(stream));
@@ -429,16 +433,18 @@ h2o_status decode_common(h2o_cache* c, const void* q, const void* k, const void*
 h2o_status h2o_decode_step(h2o_cache* c, const void* q, const void* k, const void* v, float* out,
                            int32_t* evicted, void* stream) {
   if (c == nullptr) return fail(H2O_ERR_INVALID_ARG, "cache is NULL");
-  return decode_common(c, q, k, v, nullptr, out, evicted, stream);
+  return decode_common(c, q, k, v, nullptr, 1, out, evicted, stream);
 }
 
 h2o_status h2o_decode_step_scored(h2o_cache* c, const void* q, const void* k, const void* v,
-                                  const float* new_score, float* out, int32_t* evicted, void* stream) {
+                                  const float* new_score, int32_t score_stride, float* out, int32_t* evicted,
+                                  void* stream) {
   if (c == nullptr) return fail(H2O_ERR_INVALID_ARG, "cache is NULL");
   if (new_score == nullptr) return fail(H2O_ERR_INVALID_ARG, "new_score must be non-NULL");
   if ((reinterpret_cast<uintptr_t>(new_score) & 3u) != 0)
     return fail(H2O_ERR_INVALID_ARG, "new_score must be 4-byte aligned");
-  return decode_common(c, q, k, v, new_score, out, evicted, stream);
+  if (score_stride < 1) return fail(H2O_ERR_INVALID_ARG, "score_stride must be >= 1");
+  return decode_common(c, q, k, v, new_score, score_stride, out, evicted, stream);
 }
 
 h2o_status h2o_cache_read(h2o_cache* c, int32_t* pos, float* score, void* k_slots, void* v_slots, int32_t* meta,

@@ -20,7 +20,9 @@ struct DecodeArgs {
   int32_t* evicted;  // [units] or nullptr
   float* part;       // split mode: [units, nsplit, 2 + d] partial (max, sum, o)
   float* logits;     // split mode: [units, k + 1] base-2 logits (new token at index k)
-  const float* fixed_new;  // [units] the new token's fixed score (scores do not accumulate), or nullptr
+  const float* fixed_new;  // the new token's fixed score of unit u at fixed_new[u * fixed_stride]
+                           // (scores do not accumulate), or nullptr
+  int32_t fixed_stride;
   int32_t k;           // slots per unit
   int32_t kstride;     // per-unit stride of score/comp/pos: k rounded up to 32 (128-byte rows)
   int32_t count;       // occupied slots before this step (slots 0..count-1)
@@ -51,6 +53,7 @@ struct PrefillArgs {
   float* out;         // [units, L, d] prompt attention output, or nullptr
   const float* scores_in;  // [units, scores_stride] scores the select ranks by, or nullptr (col_sum)
   int32_t scores_stride;
+  int32_t kv_rows;    // rows per unit of k and v (>= L): the select gathers rows 0..L-1
   void* kslots;       // [units, k, d]
   void* vslots;       // [units, k, d]
   float* score;       // [units, kstride]

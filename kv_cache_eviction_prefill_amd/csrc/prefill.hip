@@ -743,8 +743,8 @@ __global__ __launch_bounds__(kThreads) void select_fill(PrefillArgs a) {
     }
     cp[s] = 0.f;
   }
-  const T* Ku = static_cast<const T*>(a.k) + static_cast<size_t>(unit) * L * D;
-  const T* Vu = static_cast<const T*>(a.v) + static_cast<size_t>(unit) * L * D;
+  const T* Ku = static_cast<const T*>(a.k) + static_cast<size_t>(unit) * a.kv_rows * D;
+  const T* Vu = static_cast<const T*>(a.v) + static_cast<size_t>(unit) * a.kv_rows * D;
   T* kd = static_cast<T*>(a.kslots) + static_cast<size_t>(unit) * kc * D;
   T* vd = static_cast<T*>(a.vslots) + static_cast<size_t>(unit) * kc * D;
   const int g = tid / LPR, r = tid % LPR;

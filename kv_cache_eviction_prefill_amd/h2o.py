@@ -52,8 +52,8 @@ _SIGNATURES = {
     "h2o_prefill_stats_read": (_i32, [_vp, _vp, _vp, _vp]),
     "h2o_cache_info": (_i32, [_vp, _p32, _p32, _p32]),
     "h2o_column_scores": (_i32, [_vp, _vp, _vp, _i32, _vp, _vp]),
-    "h2o_prefill_scored": (_i32, [_vp, _vp, _vp, _i32, _vp, _vp]),
-    "h2o_decode_step_scored": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
+    "h2o_prefill_scored": (_i32, [_vp, _vp, _vp, _i32, _i32, _vp, _vp]),
+    "h2o_decode_step_scored": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _vp]),
     "h2o_status_str": (ctypes.c_char_p, [_i32]),
     "h2o_last_error": (ctypes.c_char_p, []),
 }
@@ -120,12 +120,12 @@ def h2o_column_scores(cache, q, k, n, scores, stream):
     return load().h2o_column_scores(cache, q, k, n, scores, stream)
 
 
-def h2o_prefill_scored(cache, k, v, prompt_len, scores, stream):
-    return load().h2o_prefill_scored(cache, k, v, prompt_len, scores, stream)
+def h2o_prefill_scored(cache, k, v, prompt_len, seq_rows, scores, stream):
+    return load().h2o_prefill_scored(cache, k, v, prompt_len, seq_rows, scores, stream)
 
 
-def h2o_decode_step_scored(cache, q, k, v, new_score, out, evicted, stream):
-    return load().h2o_decode_step_scored(cache, q, k, v, new_score, out, evicted, stream)
+def h2o_decode_step_scored(cache, q, k, v, new_score, score_stride, out, evicted, stream):
+    return load().h2o_decode_step_scored(cache, q, k, v, new_score, score_stride, out, evicted, stream)
 
 
 def h2o_status_str(status):
@@ -236,29 +236,38 @@ class H2OCache:
         check(h2o_column_scores(self.handle, qp, kp, n, op, self._stream(stream)), "h2o_column_scores")
         return out
 
-    def prefill_scored(self, k, v, scores, stream=None):
-        """Keep the prompt's recent window and best-scored tokens by ``scores`` [B, H, L]."""
-        L = k.shape[2]
-        shape = (self.B, self.H, L, self.d)
+    def prefill_scored(self, k, v, scores, prompt_len=None, stream=None):
+        """Keep the prompt's recent window and best-scored tokens by ``scores``
+        [B, H, n]; ``k, v``: [B, H, n, d]; the prompt is their first ``prompt_len``
+        rows (all n by default)."""
+        n = k.shape[2]
+        L = n if prompt_len is None else prompt_len
+        shape = (self.B, self.H, n, self.d)
         kp, vp = self._check_t(k, shape, self.tdtype, "k"), self._check_t(v, shape, self.tdtype, "v")
-        sp = self._check_t(scores, (self.B, self.H, L), self.torch.float32, "scores")
-        check(h2o_prefill_scored(self.handle, kp, vp, L, sp, self._stream(stream)), "h2o_prefill_scored")
+        sp = self._check_t(scores, (self.B, self.H, n), self.torch.float32, "scores")
+        check(h2o_prefill_scored(self.handle, kp, vp, L, n, sp, self._stream(stream)), "h2o_prefill_scored")
 
     def decode_step_scored(self, q, k, v, new_score, out=None, evicted=None, stream=None):
-        """A decode step with fixed scores; ``new_score``: float32 [B, H]."""
+        """A decode step with fixed scores; ``new_score``: float32 [B, H] (any
+        strides along H and B that form one uniform unit stride, e.g. a column of
+        a [B, H, n] score tensor)."""
         torch = self.torch
         shape = (self.B, self.H, self.d)
         qp = self._check_t(q, shape, self.tdtype, "q")
         kp = self._check_t(k, shape, self.tdtype, "k")
         vp = self._check_t(v, shape, self.tdtype, "v")
-        np_ = self._check_t(new_score, (self.B, self.H), torch.float32, "new_score")
+        if (new_score.device != self.device or new_score.dtype != torch.float32
+                or tuple(new_score.shape) != (self.B, self.H)
+                or new_score.stride(0) != self.H * new_score.stride(1)):
+            raise ValueError("new_score: expected float32 [B, H] with one uniform unit stride on the cache device")
+        np_, stride = new_score.data_ptr(), new_score.stride(1)
         if out is None:
             out = torch.empty(shape, dtype=torch.float32, device=self.device)
         op = self._check_t(out, shape, torch.float32, "out")
         ep = None
         if evicted is not None:
             ep = self._check_t(evicted, (self.B, self.H), torch.int32, "evicted")
-        check(h2o_decode_step_scored(self.handle, qp, kp, vp, np_, op, ep, self._stream(stream)),
+        check(h2o_decode_step_scored(self.handle, qp, kp, vp, np_, stride, op, ep, self._stream(stream)),
               "h2o_decode_step_scored")
         return out, evicted
 

@@ -87,8 +87,8 @@ def test_null_and_state_checks_make_no_gpu_call():
     assert H.h2o_prefill_stats_read(None, None, None, None) == H.H2O_ERR_INVALID_ARG
     assert H.h2o_cache_info(None, None, None, None) == H.H2O_ERR_INVALID_ARG
     assert H.h2o_column_scores(None, None, None, 4, None, None) == H.H2O_ERR_INVALID_ARG
-    assert H.h2o_prefill_scored(None, None, None, 4, None, None) == H.H2O_ERR_INVALID_ARG
-    assert H.h2o_decode_step_scored(None, None, None, None, None, None, None, None) == H.H2O_ERR_INVALID_ARG
+    assert H.h2o_prefill_scored(None, None, None, 4, 4, None, None) == H.H2O_ERR_INVALID_ARG
+    assert H.h2o_decode_step_scored(None, None, None, None, None, 1, None, None, None) == H.H2O_ERR_INVALID_ARG
     p = H.make_params(1, 1, 64, 2, 2, "f32")
     assert H.h2o_cache_create(ctypes.byref(p), -1, None) == H.H2O_ERR_INVALID_ARG
     out = ctypes.c_void_p(1234)

@@ -14,7 +14,7 @@ pytestmark = pytest.mark.gpu
 if not torch.cuda.is_available():
     pytest.skip("no GPU", allow_module_level=True)
 
-from gpu_harness import check_payloads, log, unit_payload  # noqa: E402
+from gpu_harness import check_payloads, log, run_gpu, unit_payload  # noqa: E402
 from kv_cache_eviction_prefill_amd import H2OCache  # noqa: E402
 
 DEV = torch.device("cuda", 0)
@@ -35,14 +35,15 @@ def run_gpu_scored(q, k, v, L, heavy, recent, dtype, scores=None):
     if scores is None:
         scores = cache.column_scores(q, k)
         gs = scores.cpu().numpy()
-    cache.prefill_scored(k[:, :, :L].contiguous(), v[:, :, :L].contiguous(), scores[:, :, :L].contiguous())
+    # the prompt is read in place from the whole sequence's K/V and scores, and
+    # each step's score is a strided column of the [B, H, N] scores
+    cache.prefill_scored(k, v, scores, prompt_len=L)
     kept = cache.read()
     qd, kd, vd = (x[:, :, L:].permute(2, 0, 1, 3).contiguous() for x in (q, k, v))
-    sd = scores[:, :, L:].permute(2, 0, 1).contiguous()
     ev = torch.empty((T, B, H), dtype=torch.int32, device=DEV)
     outs = torch.empty((T, B, H, d), dtype=torch.float32, device=DEV)
     for t in range(T):
-        cache.decode_step_scored(qd[t], kd[t], vd[t], sd[t], outs[t], ev[t])
+        cache.decode_step_scored(qd[t], kd[t], vd[t], scores[:, :, L + t], outs[t], ev[t])
     final = cache.read()
     with pytest.raises(Exception):
         cache.prefill_stats()  # no statistics after a scored prefill
@@ -124,3 +125,33 @@ def test_global_comparator_end_to_end(d, L, T, heavy, recent, B, H):
     assert not bad, bad[:3]
     for r in results:
         assert "colsum_rel" in r and "out_err" in r, r
+
+
+@pytest.mark.parametrize("anchor,alpha", [("fixed", 3.0), ("fixed", 32.0), ("zipf", 40.0)])
+def test_comparator_quality_report(anchor, alpha):
+    # What the greedy local score loses against the global one, on the OPT-6.7B
+    # layer shape (512 units, 512 + 512, 20 % budget): each variant's decode
+    # outputs against full attention (a budget covering the whole sequence).  The
+    # workload's own anchors (alpha = 3) shift an anchor's logit by only
+    # alpha / sqrt(d) ~ 0.27, so its attention has no real heavy hitters; the
+    # stronger settings (fixed anchors at +2.8, Zipf-ranked strengths) do.  The
+    # numbers are a measurement of the method on synthetic inputs, logged, not a
+    # pass criterion; the test checks only that the full-budget run evicts nothing.
+    w = scaled(get("opt6.7b-layer-b16"), anchor=anchor, alpha=alpha)
+    L, T, kh, kr = w.prompt_len, w.decode_steps, w.heavy_budget, w.recent_budget
+    _, _, _, (q, k, v) = _inputs(w)
+    N = L + T
+    full = run_gpu(q, k, v, L, N // 2, N - N // 2, "bf16")
+    assert (full["evicted"] == -1).all()
+    ref = full["out"].astype(np.float64)
+    runs = {"h2o (local)": run_gpu(q, k, v, L, kh, kr, "bf16"),
+            "global": run_gpu_scored(q, k, v, L, kh, kr, "bf16"),
+            "recent window only": run_gpu(q, k, v, L, 0, kh + kr, "bf16"),
+            "heavy hitters only": run_gpu(q, k, v, L, kh + kr, 0, "bf16")}
+    for name, r in runs.items():
+        o = r["out"].astype(np.float64)
+        err = np.abs(o - ref)
+        rel = np.linalg.norm((o - ref).reshape(-1)) / np.linalg.norm(ref.reshape(-1))
+        log(f"comparator [{anchor} anchors, alpha {alpha:g}] {name}: k = {kh + kr} of {N}: "
+            f"mean |o - o_full| {err.mean():.4g}, max {err.max():.4g}, relative L2 {rel:.4g}")
+        assert np.isfinite(o).all()
