@@ -104,7 +104,41 @@ def prefill_output(Q: np.ndarray, K: np.ndarray, V: np.ndarray, scale: float) ->
     return A @ np.asarray(V, np.float64)
 
 
-def prefill_keep(c: np.ndarray, heavy: int, recent: int, prefer=None, tie_rtol: float = TIE_RTOL):
+@dataclass(frozen=True)
+class Pattern:
+    """A Sparse-Transformer attention pattern whose positions H2O keeps in
+    preference to its heavy hitters, the heavy hitters filling the rest of the
+    budget.  [Report §4.5 (Table 2): heavy hitters added to strided and fixed
+    sparse patterns]
+
+    * ``strided`` with period l: at step i the positions j with (i - j) mod l = 0
+      (every l-th token counted back from the query).
+    * ``fixed`` with period l and width c: the last c positions of every block of
+      l tokens (j mod l >= l - c), the same for every query.
+
+    READINGS: the pattern only orders the cache's own entries (an evicted token
+    never returns, so the pattern is honoured as far as the cache still holds it);
+    keep/evict rank by (protected, score, position), so a protected entry is
+    evicted only when every candidate is protected; the prefill ranks the prompt
+    as seen by the first generated token (i = L)."""
+
+    kind: str = "none"  # "none", "strided" or "fixed"
+    period: int = 1
+    width: int = 1
+
+    def protected(self, j: int, i: int) -> bool:
+        if self.kind == "strided":
+            return (i - j) % self.period == 0
+        if self.kind == "fixed":
+            return j % self.period >= self.period - self.width
+        return False
+
+
+NO_PATTERN = Pattern()
+
+
+def prefill_keep(c: np.ndarray, heavy: int, recent: int, prefer=None, tie_rtol: float = TIE_RTOL,
+                 pattern: Pattern = NO_PATTERN):
     """Positions kept after the prompt.  [Report §3.4, prefill rule]
 
     If the prompt fits the budget (L <= k = heavy + recent) every position is
@@ -113,7 +147,9 @@ def prefill_keep(c: np.ndarray, heavy: int, recent: int, prefer=None, tie_rtol: 
     [0, L - recent) so the two sets are disjoint and total k; the selection
     threshold is L > k (the pages' "prompt at least 2K" keeps everything at
     L = 2K under both readings); "best" is the reverse of the eviction order, so
-    on equal scores the higher position is kept.
+    on equal scores the higher position is kept.  With a ``pattern`` the
+    positions it protects (for the first generated token, i = L) rank above all
+    others.
 
     ``prefer`` (optional): another kept set.  If it differs from the oracle's only
     by positions whose scores lie within ``tie_rtol`` (relative) of the boundary
@@ -131,7 +167,8 @@ def prefill_keep(c: np.ndarray, heavy: int, recent: int, prefer=None, tie_rtol: 
         return kept, info
     pool = list(range(L - recent))
     recent_pos = list(range(L - recent, L))
-    best_first = sorted(pool, key=lambda j: (c[j], j), reverse=True)
+    prot = {j: pattern.protected(j, L) for j in pool}
+    best_first = sorted(pool, key=lambda j: (prot[j], c[j], j), reverse=True)
     heavy_set = best_first[:heavy]
     kept = sorted(heavy_set + recent_pos)
     if prefer is not None:
@@ -140,7 +177,8 @@ def prefill_keep(c: np.ndarray, heavy: int, recent: int, prefer=None, tie_rtol: 
             if heavy == 0:
                 raise ParityMismatch("no heavy hitters to choose, yet the kept sets differ")
             t = c[best_first[heavy - 1]]
-            band = {j for j in pool if abs(c[j] - t) <= tie_rtol * abs(t)}
+            pt = prot[best_first[heavy - 1]]
+            band = {j for j in pool if prot[j] == pt and abs(c[j] - t) <= tie_rtol * abs(t)}
             info["band"] = sorted(band)
             pset, kset = set(prefer), set(kept)
             ok = (len(prefer) == k and set(recent_pos) <= pset
@@ -172,6 +210,7 @@ class UnitCache:
     evicted_mass: float = 0.0
     rows: int = 0  # attention rows processed (prompt rows + decode steps)
     fixed: np.ndarray = None  # per-position scores fixed in advance (global comparator), or None
+    pattern: Pattern = NO_PATTERN  # sparse pattern kept in preference to heavy hitters
 
     def __post_init__(self):
         if self.K is None:
@@ -186,7 +225,8 @@ class UnitCache:
     # ------------------------------------------------------------------ prefill
     @classmethod
     def from_prompt(cls, Qp, Kp, Vp, heavy: int, recent: int, scale: float | None = None,
-                    prefer_kept=None, tie_rtol: float = TIE_RTOL, fixed=None):
+                    prefer_kept=None, tie_rtol: float = TIE_RTOL, fixed=None,
+                    pattern: Pattern = NO_PATTERN):
         """Prefill: score the prompt, keep per ``prefill_keep``, seed the scores
         of the kept entries with their column sums.  READING: prefill column sums
         seed the running scores (the decode steps keep adding to them).
@@ -197,14 +237,14 @@ class UnitCache:
         Qp, Kp, Vp = (np.asarray(x, np.float64) for x in (Qp, Kp, Vp))
         L, d = Kp.shape if Kp.ndim == 2 else (0, Qp.shape[-1])
         scale = default_scale(d) if scale is None else scale
-        cache = cls(heavy=heavy, recent=recent, scale=scale, d=d)
+        cache = cls(heavy=heavy, recent=recent, scale=scale, d=d, pattern=pattern)
         if fixed is not None:
             cache.fixed = np.asarray(fixed, np.float64)
         if L == 0:
             return cache, None, {"selected": False, "tie_adopted": False, "band": []}
         ps = prefill_scores(Qp, Kp, scale) if fixed is None else None
         c = ps.col_sum if fixed is None else cache.fixed[:L]
-        kept, info = prefill_keep(c, heavy, recent, prefer=prefer_kept, tie_rtol=tie_rtol)
+        kept, info = prefill_keep(c, heavy, recent, prefer=prefer_kept, tie_rtol=tie_rtol, pattern=pattern)
         kept = np.asarray(kept, np.int64)
         cache.pos = kept
         cache.K = Kp[kept].copy()
@@ -239,6 +279,8 @@ class UnitCache:
            READINGS: the pages' "oldest recent token leaves and each head evicts
            one heavy hitter" is one removal, not two (|S_i| = k and at most one
            eviction per step); the token leaving the window joins the candidates.
+           With a sparse ``pattern`` the candidates it protects at step i are
+           evicted only when every candidate is protected (see ``Pattern``).
 
         ``prefer_victim``: another side's decision for this step (a position, or
         -1 for no eviction).  It is adopted when it lies within ``tie_rtol``
@@ -268,10 +310,11 @@ class UnitCache:
             self.pos, self.K, self.V, self.score = G_pos, G_K, G_V, G_score
             return o, -1, info
         cand = np.nonzero(G_pos <= i - self.recent)[0]
-        u = min(cand, key=lambda t: (G_score[t], G_pos[t]))
+        prot = {t: self.pattern.protected(int(G_pos[t]), i) for t in cand}
+        u = min(cand, key=lambda t: (prot[t], G_score[t], G_pos[t]))
         if prefer_victim is not None and int(prefer_victim) != int(G_pos[u]):
             smin = G_score[u]
-            band = [t for t in cand if G_score[t] <= smin + tie_rtol * abs(smin)]
+            band = [t for t in cand if prot[t] == prot[u] and G_score[t] <= smin + tie_rtol * abs(smin)]
             info["band"] = [int(G_pos[t]) for t in band]
             hit = [t for t in band if int(G_pos[t]) == int(prefer_victim)]
             if not hit:
@@ -296,13 +339,14 @@ class UnitCache:
 # =============================================================================== driver
 def run_unit(Q, K, V, prompt_len: int, heavy: int, recent: int, scale: float | None = None,
              replay_kept=None, replay_evicted=None, tie_rtol: float = TIE_RTOL,
-             keep_weights: bool = False, fixed=None):
+             keep_weights: bool = False, fixed=None, pattern: Pattern = NO_PATTERN):
     """Prefill then decode one unit over positions 0..N-1 of ``Q, K, V`` ([N, d]).
 
     ``replay_kept`` / ``replay_evicted``: the other side's prefill kept set and
     per-step eviction log; they are adopted only at near-ties (see
     ``prefill_keep`` and ``UnitCache.step``).  ``fixed``: per-position scores
     [N] fixed in advance (see ``run_unit_global``); None for H2O itself.
+    ``pattern``: a sparse pattern kept in preference to heavy hitters.
 
     Returns a dict: prefill stats (or None), ``kept`` (sorted prefill kept set),
     ``out`` [T, d], ``evicted`` [T], the final ``cache`` and tie counters.
@@ -311,7 +355,8 @@ def run_unit(Q, K, V, prompt_len: int, heavy: int, recent: int, scale: float | N
     N, d = Q.shape
     L = prompt_len
     cache, ps, pinfo = UnitCache.from_prompt(Q[:L], K[:L], V[:L], heavy, recent, scale,
-                                             prefer_kept=replay_kept, tie_rtol=tie_rtol, fixed=fixed)
+                                             prefer_kept=replay_kept, tie_rtol=tie_rtol, fixed=fixed,
+                                             pattern=pattern)
     kept = [int(p) for p in cache.pos]
     T = N - L
     out = np.zeros((T, d))

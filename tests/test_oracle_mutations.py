@@ -15,18 +15,18 @@ import numpy as np
 import pytest
 import scipy.special
 
-from test_oracle_pins import (KEYS2, _brute_force_run, _brute_keep, _brute_topk_sets, _library_causal_weights,
-                              _replay_sets, _sdpa_rows)
+from test_oracle_pins import (KEYS2, _brute_force_run, _brute_keep, _brute_pattern_sets, _brute_topk_sets,
+                              _library_causal_weights, _replay_sets, _sdpa_rows)
 
 SRC = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "oracle", "h2o_oracle.py")
 
 MUTATIONS = {
     "ties evict the highest position": (
-        "u = min(cand, key=lambda t: (G_score[t], G_pos[t]))",
-        "u = min(cand, key=lambda t: (G_score[t], -G_pos[t]))"),
+        "u = min(cand, key=lambda t: (prot[t], G_score[t], G_pos[t]))",
+        "u = min(cand, key=lambda t: (prot[t], G_score[t], -G_pos[t]))"),
     "argmax instead of argmin": (
-        "u = min(cand, key=lambda t: (G_score[t], G_pos[t]))",
-        "u = max(cand, key=lambda t: (G_score[t], G_pos[t]))"),
+        "u = min(cand, key=lambda t: (prot[t], G_score[t], G_pos[t]))",
+        "u = max(cand, key=lambda t: (prot[t], G_score[t], G_pos[t]))"),
     "candidate bound off by one": (
         "cand = np.nonzero(G_pos <= i - self.recent)[0]",
         "cand = np.nonzero(G_pos < i - self.recent)[0]"),
@@ -40,11 +40,11 @@ MUTATIONS = {
         "G_score = np.concatenate([self.score, [0.0]]) + a",
         "G_score = np.concatenate([self.score, [a[-1]]])"),
     "prefill ties keep the lower position": (
-        "best_first = sorted(pool, key=lambda j: (c[j], j), reverse=True)",
-        "best_first = sorted(pool, key=lambda j: (c[j], -j), reverse=True)"),
+        "best_first = sorted(pool, key=lambda j: (prot[j], c[j], j), reverse=True)",
+        "best_first = sorted(pool, key=lambda j: (prot[j], c[j], -j), reverse=True)"),
     "prefill keeps the worst": (
-        "best_first = sorted(pool, key=lambda j: (c[j], j), reverse=True)",
-        "best_first = sorted(pool, key=lambda j: (c[j], j))"),
+        "best_first = sorted(pool, key=lambda j: (prot[j], c[j], j), reverse=True)",
+        "best_first = sorted(pool, key=lambda j: (prot[j], c[j], j))"),
     "scale 1/d": ("return 1.0 / np.sqrt(float(d))", "return 1.0 / float(d)"),
     "row sums instead of column sums": ("col_sum=A.sum(axis=0)", "col_sum=A.sum(axis=1)"),
     "transposed operands": ("x = scale * (K[: r + 1] @ Q[r])", "x = scale * (Q[: r + 1] @ K[r])"),
@@ -74,6 +74,18 @@ MUTATIONS = {
         "g = global_scores(Q, K, scale)",
         "g = np.concatenate([global_scores(Q[:max(prompt_len, 1)], K[:max(prompt_len, 1)], scale), "
         "np.zeros(len(Q) - max(prompt_len, 1))])"),
+    "protected entries evicted first": (
+        "u = min(cand, key=lambda t: (prot[t], G_score[t], G_pos[t]))",
+        "u = min(cand, key=lambda t: (not prot[t], G_score[t], G_pos[t]))"),
+    "pattern ignored at eviction": (
+        "u = min(cand, key=lambda t: (prot[t], G_score[t], G_pos[t]))",
+        "u = min(cand, key=lambda t: (G_score[t], G_pos[t]))"),
+    "prefill ignores the pattern": (
+        "best_first = sorted(pool, key=lambda j: (prot[j], c[j], j), reverse=True)",
+        "best_first = sorted(pool, key=lambda j: (c[j], j), reverse=True)"),
+    "strided offset off by one": ("return (i - j) % self.period == 0", "return (i - 1 - j) % self.period == 0"),
+    "fixed pattern takes the block heads": ("return j % self.period >= self.period - self.width",
+                                            "return j % self.period < self.width"),
     "evicted entries stay in the normaliser": (
         "a = softmax(x)\n        o = a @ G_V",
         "a = softmax(x)\n        a = a * (len(x) / (len(x) + self.evicted_mass))\n        o = a @ G_V"),
@@ -136,6 +148,14 @@ def _checks(m):
             res = m.run_unit(Q, K, V, L, h, r, fixed=sc)
             assert _replay_sets(res, L, T, h + r) == _brute_topk_sets(sc, L, T, h, r)
 
+    def sparse_pattern():
+        for (kind, per, wid) in [("strided", 5, 1), ("fixed", 8, 2), ("fixed", 6, 3)]:
+            for (L, T, h, r) in [(30, 40, 6, 5), (4, 50, 5, 3), (25, 30, 7, 0)]:
+                Q, K, V = (g.standard_normal((L + T, 6)) for _ in range(3))
+                sc = g.integers(0, 6, size=L + T).astype(float) / 4
+                res = m.run_unit(Q, K, V, L, h, r, fixed=sc, pattern=m.Pattern(kind, per, wid))
+                assert _replay_sets(res, L, T, h + r) == _brute_pattern_sets(sc, L, T, h, r, kind, per, wid)
+
     def sliding_window():
         N, L, R, d = 30, 9, 4, 6
         Q, K, V = (g.standard_normal((N, d)) for _ in range(3))
@@ -193,7 +213,7 @@ def _checks(m):
         assert len(c.pos) == 9
         assert abs(c.score.sum() - (c.rows - c.evicted_mass)) < 1e-9 * c.rows
 
-    return [full_attention, prefill_library, prefill_out, global_comparator, sliding_window, identical_keys, brute_force, keep_brute, mass]
+    return [full_attention, prefill_library, prefill_out, global_comparator, sparse_pattern, sliding_window, identical_keys, brute_force, keep_brute, mass]
 
 
 def test_unmutated_oracle_passes_every_check():

@@ -14,8 +14,8 @@ import scipy.special
 import torch
 from hypothesis import given, settings, strategies as st, HealthCheck
 
-from oracle import (ParityMismatch, UnitCache, global_scores, prefill_keep, prefill_output, prefill_scores, run_unit,
-                    run_unit_global)
+from oracle import (ParityMismatch, Pattern, UnitCache, global_scores, prefill_keep, prefill_output, prefill_scores,
+                    run_unit, run_unit_global)
 
 torch.set_default_dtype(torch.float64)
 
@@ -444,3 +444,87 @@ def test_global_run_follows_library_scores(L, T, heavy, recent, seed):
     lib = _library_causal_weights(Q, K).sum(axis=0)
     np.testing.assert_allclose(res["scores"], lib, rtol=1e-12)
     assert _replay_sets(res, L, T, heavy + recent) == _brute_topk_sets(lib, L, T, heavy, recent)
+
+
+# ----------------------------------------------------------------------------- sparse pattern + heavy hitters
+def _pattern_protects(kind, per, wid, j, i):
+    # strided: every per-th token counted back from the query; fixed: the last
+    # wid tokens of every block of per
+    if kind == "strided":
+        return (i - j) % per == 0
+    if kind == "fixed":
+        return j % per >= per - wid
+    return False
+
+
+def _brute_pattern_sets(scores, L, T, heavy, recent, kind, per, wid):
+    """Direct simulation with fixed scores, on plain sets: the prompt keeps its
+    window plus the heavy best by (protected, score, position); every step adds
+    the new token and, over budget, removes the lowest-scored unprotected
+    candidate (position <= i - recent), or the lowest-scored candidate when all
+    are protected."""
+    k = heavy + recent
+    if L <= k:
+        S = set(range(L))
+    else:
+        pool = range(L - recent)
+        best = sorted(pool, key=lambda j: (_pattern_protects(kind, per, wid, j, L), scores[j], j), reverse=True)
+        S = set(best[:heavy]) | set(range(L - recent, L))
+    out = []
+    for t in range(T):
+        i = L + t
+        S.add(i)
+        if len(S) > k:
+            cands = [j for j in S if j <= i - recent]
+            free = [j for j in cands if not _pattern_protects(kind, per, wid, j, i)]
+            S.remove(min(free or cands, key=lambda j: (scores[j], j)))
+        out.append(set(S))
+    return out
+
+
+@pytest.mark.parametrize("kind,per,wid", [("strided", 4, 1), ("strided", 7, 1), ("fixed", 8, 2), ("fixed", 5, 4)])
+@pytest.mark.parametrize("L,T,heavy,recent,seed", [(30, 40, 6, 5, 0), (4, 50, 5, 3, 1), (25, 30, 7, 0, 2),
+                                                   (25, 30, 0, 6, 3), (40, 60, 3, 2, 4)])
+def test_pattern_matches_set_simulation(kind, per, wid, L, T, heavy, recent, seed):
+    g = np.random.default_rng(seed)
+    N = L + T
+    Q, K, V = (g.standard_normal((N, 6)) for _ in range(3))
+    scores = g.integers(0, 6, size=N).astype(float) / 4
+    res = run_unit(Q, K, V, L, heavy, recent, fixed=scores, pattern=Pattern(kind, per, wid))
+    assert _replay_sets(res, L, T, heavy + recent) == _brute_pattern_sets(scores, L, T, heavy, recent, kind, per, wid)
+
+
+@pytest.mark.parametrize("pattern", [Pattern("fixed", 6, 6), Pattern("strided", 1, 1)])
+def test_pattern_protecting_everything_is_plain_h2o(pattern):
+    # a pattern that protects every position orders nothing: H2O's own choices
+    L, T, heavy, recent = 40, 60, 6, 5
+    Q, K, V = _rand(L + T, 8, 40)
+    a = run_unit(Q, K, V, L, heavy, recent, pattern=pattern)
+    b = run_unit(Q, K, V, L, heavy, recent)
+    assert a["kept"] == b["kept"] and a["evicted"].tolist() == b["evicted"].tolist()
+    np.testing.assert_array_equal(a["out"], b["out"])
+
+
+def test_fixed_pattern_fixed_scores_closed_form():
+    # a fixed pattern is the same for every query, so with fixed scores the cache
+    # is the window plus the K_h best earlier positions by (protected, score, pos)
+    L, T, heavy, recent, per, wid = 30, 50, 8, 4, 7, 2
+    g = np.random.default_rng(41)
+    N = L + T
+    Q, K, V = (g.standard_normal((N, 6)) for _ in range(3))
+    scores = g.integers(0, 5, size=N).astype(float)
+    res = run_unit(Q, K, V, L, heavy, recent, fixed=scores, pattern=Pattern("fixed", per, wid))
+    for t, S in enumerate(_replay_sets(res, L, T, heavy + recent)):
+        i = L + t
+        pool = range(i - recent + 1)
+        best = sorted(pool, key=lambda j: (j % per >= per - wid, scores[j], j), reverse=True)[:heavy]
+        assert S == set(best) | set(range(i - recent + 1, i + 1)), t
+
+
+def test_pattern_with_no_heavy_budget_is_sliding_window():
+    # K_h = 0: the only candidate is the token leaving the window, protected or not
+    L, T, recent = 20, 40, 6
+    Q, K, V = _rand(L + T, 8, 42)
+    for pat in (Pattern("strided", 3, 1), Pattern("fixed", 5, 2)):
+        res = run_unit(Q, K, V, L, 0, recent, pattern=pat)
+        assert res["evicted"].tolist() == [i - recent for i in range(L, L + T)]
