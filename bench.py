@@ -96,6 +96,8 @@ def parse():
     ap.add_argument("--variant", choices=("h2o", "global"), default="h2o",
                     help="h2o: the method; global: the global-score comparator (column scores of all "
                          "prompt + generated tokens, then the same keep/evict rule with fixed scores)")
+    ap.add_argument("--pattern", default="none",
+                    help="sparse pattern kept before heavy hitters: none, strided:PERIOD or fixed:PERIOD:WIDTH")
     ap.add_argument("--prefill-out", action="store_true",
                     help="prefill also writes the prompt's attention output (fp32 [B, H, L, d])")
     ap.add_argument("--cpu-units", type=int, default=96,
@@ -114,11 +116,14 @@ def _cpu_unit(args):
     """Worker: time the oracle on one unit (prefill + every decode step)."""
     import time as _t
 
-    from oracle import run_unit, run_unit_global
+    from oracle import Pattern, run_unit, run_unit_global
 
-    Q, K, V, L, kh, kr, variant = args
+    Q, K, V, L, kh, kr, variant, pattern = args
     t0 = _t.perf_counter()
-    (run_unit_global if variant == "global" else run_unit)(Q, K, V, L, kh, kr)
+    if variant == "global":
+        run_unit_global(Q, K, V, L, kh, kr)
+    else:
+        run_unit(Q, K, V, L, kh, kr, pattern=Pattern(*pattern))
     return _t.perf_counter() - t0
 
 
@@ -187,6 +192,10 @@ def main():
         del q, k, v
     caches = [H2OCache(B, H, d, w.heavy_budget, w.recent_budget, dtype=w.dtype, max_prompt=N if glob else L)
               for _ in range(NL)]
+    pat = a.pattern.split(":")
+    pattern = (pat[0], int(pat[1]) if len(pat) > 1 else 1, int(pat[2]) if len(pat) > 2 else 1)
+    for cch in caches:
+        cch.set_pattern(*pattern)
     out = torch.empty((NL, B, H, d), dtype=torch.float32, device=dev)
     # the prompt attention output, when asked for: one buffer shared by the layers
     pout = torch.empty((B, H, L, d), dtype=torch.float32, device=dev) if a.prefill_out else None
@@ -290,9 +299,9 @@ def main():
         "config": {"workload": w.name, "layers": NL, "batch": B, "heads": H, "head_dim": d,
                    "prompt_len": L, "decode_steps": T, "heavy_budget": w.heavy_budget,
                    "recent_budget": w.recent_budget, "storage": w.dtype, "accumulate": "fp32",
-                   "prefill_out": bool(a.prefill_out), "variant": a.variant},
+                   "prefill_out": bool(a.prefill_out), "variant": a.variant, "pattern": a.pattern},
         "roofline": {"kernel": f"decode_kernel<{w.dtype},{d}>", "bound": "hbm", "achieved": achieved,
-                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic(w.name) if a.layers is None and not glob else None,
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic(w.name) if a.layers is None and not glob and a.pattern == "none" else None,
                      "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
                      "bytes_per_launch": dec_bytes_launch, "avg_launch_us": 1e6 * avg_dec_s,
                      "launches": launches},
@@ -319,7 +328,7 @@ def main():
                 qf = torch.cat([pre[l][0][b, h], dec[l][0][:, b, h]]).float().cpu().numpy()
                 kf = torch.cat([pre[l][1][b, h], dec[l][1][:, b, h]]).float().cpu().numpy()
                 vf = torch.cat([pre[l][2][b, h], dec[l][2][:, b, h]]).float().cpu().numpy()
-            samples.append((qf, kf, vf, L, w.heavy_budget, w.recent_budget, a.variant))
+            samples.append((qf, kf, vf, L, w.heavy_budget, w.recent_budget, a.variant, pattern))
         procs = min(len(os.sched_getaffinity(0)), 16, len(samples))
         os.environ.setdefault("OMP_NUM_THREADS", "1")
         os.environ.setdefault("OPENBLAS_NUM_THREADS", "1")

@@ -211,6 +211,29 @@ h2o_status h2o_decode_step_scored(h2o_cache* cache, const void* q, const void* k
                                   const float* new_score, int32_t score_stride, float* out, int32_t* evicted,
                                   void* stream);
 
+/* ---- Heavy hitters added to a sparse attention pattern (Report §4.5, Table 2:
+ * strided and fixed Sparse-Transformer patterns, each improved by adding H2). */
+typedef enum {
+  H2O_PATTERN_NONE = 0,    /* plain H2O (the default) */
+  H2O_PATTERN_STRIDED = 1, /* at step i, the positions j with (i - j) mod period == 0 */
+  H2O_PATTERN_FIXED = 2    /* the last `width` positions of every block of `period`:
+                              j mod period >= period - width */
+} h2o_pattern;
+
+/* Keep a sparse pattern in preference to heavy hitters, for every later
+ * h2o_prefill / h2o_prefill_scored / h2o_decode_step / h2o_decode_step_scored
+ * call on this cache.  The budget and the recent window are unchanged; among
+ * the eviction candidates (and the prefill's heavy-hitter pool, judged for the
+ * first generated token i = prompt_len) the entries the pattern protects are
+ * kept first and the heavy hitters fill the rest: the victim is the lowest
+ * (protected, score, position), so a protected entry is evicted only when every
+ * candidate is protected.  An evicted token never returns, so the pattern is
+ * honoured as far as the cache still holds its positions.  width is ignored for
+ * H2O_PATTERN_STRIDED; H2O_PATTERN_NONE ignores both.  Host-side, no GPU call.
+ * Errors: H2O_ERR_INVALID_ARG (unknown kind, period < 1, width outside
+ * [1, period] for H2O_PATTERN_FIXED). */
+h2o_status h2o_cache_set_pattern(h2o_cache* cache, int32_t kind, int32_t period, int32_t width);
+
 /* Host-side state, no GPU call: entries cached per unit, next position, and the
  * last prompt length (-1 before the first prefill).  Pointers nullable. */
 h2o_status h2o_cache_info(const h2o_cache* cache, int32_t* count, int32_t* next_pos,

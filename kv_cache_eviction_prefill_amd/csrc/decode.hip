@@ -107,7 +107,7 @@ __device__ inline void score_pass(const DecodeArgs& a, int unit, float M, float 
       cp[j] = cj;
     }
     if (full && pj <= a.cand_limit) {
-      const uint64_t key = evict_key(sj, pj);
+      const uint64_t key = evict_key(sj, pj) | pattern_bit(a.pat_kind, a.pat_period, a.pat_width, pj, a.new_pos);
       if (key < best) {
         best = key;
         best_slot = j;
@@ -120,7 +120,8 @@ __device__ inline void score_pass(const DecodeArgs& a, int unit, float M, float 
   int32_t ev = -1;
   if (full) {
     if (a.new_is_candidate && tid == 0) {
-      const uint64_t key = evict_key(w_new, a.new_pos);
+      const uint64_t key = evict_key(w_new, a.new_pos) |
+                           pattern_bit(a.pat_kind, a.pat_period, a.pat_width, a.new_pos, a.new_pos);
       if (key < best) {
         best = key;
         best_slot = kNewSlot;

@@ -26,6 +26,7 @@ struct h2o_cache {
   int32_t lpad_cap;    // row capacity of the prefill scratch (multiple of 32)
   int32_t lpad_last;   // row stride of the last prefill's statistics
   bool stats_valid;    // the prefill scratch holds the last h2o_prefill's statistics
+  int32_t pat_kind, pat_period, pat_width;  // sparse pattern kept before heavy hitters
   // device memory
   void* kslots;
   void* vslots;
@@ -199,6 +200,9 @@ h2o_status h2o_cache_create(const h2o_params* params, int device, h2o_cache** ou
   c->k = params->heavy_budget + params->recent_budget;
   c->kstride = round32(c->k);
   c->units = params->batch * params->heads;
+  c->pat_kind = H2O_PATTERN_NONE;
+  c->pat_period = 1;
+  c->pat_width = 1;
   c->esize = params->dtype == H2O_F32 ? 4 : 2;
   c->scale = params->scale > 0.f ? params->scale : 1.f / std::sqrt(static_cast<float>(c->d));
   c->c2 = c->scale * kLog2e;
@@ -290,6 +294,9 @@ h2o_status h2o_prefill(h2o_cache* c, const void* q, const void* k, const void* v
     a.recent = c->p.recent_budget;
     a.kcap = c->k;
     a.kstride = c->kstride;
+    a.pat_kind = c->pat_kind;
+    a.pat_period = c->pat_period;
+    a.pat_width = c->pat_width;
     a.kv_rows = L;
     a.scale = c->scale;
     a.c2 = c->c2;
@@ -373,6 +380,9 @@ h2o_status h2o_prefill_scored(h2o_cache* c, const void* k, const void* v, int32_
     a.recent = c->p.recent_budget;
     a.kcap = c->k;
     a.kstride = c->kstride;
+    a.pat_kind = c->pat_kind;
+    a.pat_period = c->pat_period;
+    a.pat_width = c->pat_width;
     a.scale = c->scale;
     a.c2 = c->c2;
     const hipError_t e = h2o::launch_prefill(c->p.dtype, c->d, a, c->units, s);
@@ -419,6 +429,9 @@ h2o_status decode_common(h2o_cache* c, const void* q, const void* k, const void*
   a.new_is_candidate = c->p.recent_budget == 0 ? 1 : 0;
   a.fixed_new = new_score;
   a.fixed_stride = score_stride;
+  a.pat_kind = c->pat_kind;
+  a.pat_period = c->pat_period;
+  a.pat_width = c->pat_width;
   a.nsplit = choose_nsplit(c, c->count, &a.split_len);
   a.c2 = c->c2;
   const hipError_t e = h2o::launch_decode(c->p.dtype, c->d, a, c->units, static_cast<hipStream_t>(stream));
@@ -496,6 +509,24 @@ h2o_status h2o_prefill_stats_read(h2o_cache* c, float* row_lse, float* col_sum, 
     const size_t n = static_cast<size_t>(L) * c->units;
     for (size_t i = 0; i < n; ++i) row_lse[i] *= ln2;
   }
+  return H2O_OK;
+}
+
+h2o_status h2o_cache_set_pattern(h2o_cache* c, int32_t kind, int32_t period, int32_t width) {
+  if (c == nullptr) return fail(H2O_ERR_INVALID_ARG, "cache is NULL");
+  if (kind == H2O_PATTERN_NONE) {
+    c->pat_kind = kind;
+    c->pat_period = 1;
+    c->pat_width = 1;
+    return H2O_OK;
+  }
+  if (kind != H2O_PATTERN_STRIDED && kind != H2O_PATTERN_FIXED) return fail(H2O_ERR_INVALID_ARG, "unknown pattern");
+  if (period < 1) return fail(H2O_ERR_INVALID_ARG, "period must be >= 1");
+  if (kind == H2O_PATTERN_FIXED && (width < 1 || width > period))
+    return fail(H2O_ERR_INVALID_ARG, "width must be in [1, period]");
+  c->pat_kind = kind;
+  c->pat_period = period;
+  c->pat_width = kind == H2O_PATTERN_FIXED ? width : 1;
   return H2O_OK;
 }
 

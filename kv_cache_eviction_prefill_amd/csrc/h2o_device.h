@@ -116,6 +116,19 @@ __device__ inline uint64_t evict_key(float score, int32_t pos) {
   return (static_cast<uint64_t>(__float_as_uint(score)) << 32) | static_cast<uint32_t>(pos);
 }
 
+// Sparse attention pattern kept in preference to heavy hitters (strided: the
+// positions j with (i - j) mod period = 0 for the query at i; fixed: the last
+// `width` positions of every block of `period`).  Its entries get the top key
+// bit, so they order after every unprotected entry: score bits of non-negative
+// floats stay below 2^31 and never reach it.
+constexpr int kPatternNone = 0, kPatternStrided = 1, kPatternFixed = 2;
+__device__ inline uint64_t pattern_bit(int kind, int period, int width, int32_t j, int32_t i) {
+  bool p = false;
+  if (kind == kPatternStrided) p = (i - j) % period == 0;
+  else if (kind == kPatternFixed) p = j % period >= period - width;
+  return p ? (1ull << 63) : 0ull;
+}
+
 // Wave-uniform lexicographic minimum of (score bits, position) pairs: the
 // minimum score first, then the minimum position among the lanes holding it.
 __device__ inline uint64_t wave_min_key(uint64_t key) {

@@ -29,6 +29,7 @@ struct DecodeArgs {
   int32_t new_pos;     // position i of the new token
   int32_t cand_limit;  // positions <= cand_limit are eviction candidates (i - K_r)
   int32_t new_is_candidate;  // K_r == 0: the new token competes for eviction
+  int32_t pat_kind, pat_period, pat_width;  // sparse pattern kept before heavy hitters
   int32_t nsplit;      // blocks per unit (1: single-block path)
   int32_t split_len;   // slots per split block
   float c2;            // scale * log2(e)
@@ -54,6 +55,7 @@ struct PrefillArgs {
   const float* scores_in;  // [units, scores_stride] scores the select ranks by, or nullptr (col_sum)
   int32_t scores_stride;
   int32_t kv_rows;    // rows per unit of k and v (>= L): the select gathers rows 0..L-1
+  int32_t pat_kind, pat_period, pat_width;  // sparse pattern kept before heavy hitters (query i = L)
   void* kslots;       // [units, k, d]
   void* vslots;       // [units, k, d]
   float* score;       // [units, kstride]

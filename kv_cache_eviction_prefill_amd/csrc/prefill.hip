@@ -678,7 +678,7 @@ __global__ __launch_bounds__(kThreads) void select_fill(PrefillArgs a) {
         for (int t = tid; t < 256; t += kThreads) s_hist[t] = 0u;
         __syncthreads();
         for (int j = tid; j < pool; j += kThreads) {
-          const uint64_t key = evict_key(c[j], j);
+          const uint64_t key = evict_key(c[j], j) | pattern_bit(a.pat_kind, a.pat_period, a.pat_width, j, L);
           if ((key & mask) == prefix) atomicAdd(&s_hist[(key >> shift) & 255u], 1u);
         }
         __syncthreads();
@@ -708,7 +708,8 @@ __global__ __launch_bounds__(kThreads) void select_fill(PrefillArgs a) {
     for (int j0 = 0; j0 < L; j0 += kThreads) {
       const int j = j0 + tid;
       bool f;
-      if (j < pool) f = (a.heavy > 0) && (evict_key(c[j], j) >= thr);
+      if (j < pool)
+        f = (a.heavy > 0) && ((evict_key(c[j], j) | pattern_bit(a.pat_kind, a.pat_period, a.pat_width, j, L)) >= thr);
       else f = (j < L);
       const uint64_t bal = __ballot(f);
       const int lane = tid & (kWave - 1);

@@ -23,6 +23,7 @@ LIB_PATH = os.path.join(_PKG, "libh2o.so")
 HEADER_PATH = os.path.join(os.path.dirname(_PKG), "include", "h2o.h")
 
 H2O_F32, H2O_BF16 = 0, 1
+H2O_PATTERN_NONE, H2O_PATTERN_STRIDED, H2O_PATTERN_FIXED = 0, 1, 2
 STATUS = {0: "H2O_OK", 1: "H2O_ERR_INVALID_ARG", 2: "H2O_ERR_STATE", 3: "H2O_ERR_OOM",
           4: "H2O_ERR_HIP", 5: "H2O_ERR_UNSUPPORTED"}
 H2O_OK, H2O_ERR_INVALID_ARG, H2O_ERR_STATE, H2O_ERR_OOM, H2O_ERR_HIP, H2O_ERR_UNSUPPORTED = range(6)
@@ -52,6 +53,7 @@ _SIGNATURES = {
     "h2o_prefill_stats_read": (_i32, [_vp, _vp, _vp, _vp]),
     "h2o_cache_info": (_i32, [_vp, _p32, _p32, _p32]),
     "h2o_column_scores": (_i32, [_vp, _vp, _vp, _i32, _vp, _vp]),
+    "h2o_cache_set_pattern": (_i32, [_vp, _i32, _i32, _i32]),
     "h2o_prefill_scored": (_i32, [_vp, _vp, _vp, _i32, _i32, _vp, _vp]),
     "h2o_decode_step_scored": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _vp]),
     "h2o_status_str": (ctypes.c_char_p, [_i32]),
@@ -126,6 +128,10 @@ def h2o_prefill_scored(cache, k, v, prompt_len, seq_rows, scores, stream):
 
 def h2o_decode_step_scored(cache, q, k, v, new_score, score_stride, out, evicted, stream):
     return load().h2o_decode_step_scored(cache, q, k, v, new_score, score_stride, out, evicted, stream)
+
+
+def h2o_cache_set_pattern(cache, kind, period, width):
+    return load().h2o_cache_set_pattern(cache, kind, period, width)
 
 
 def h2o_status_str(status):
@@ -222,6 +228,12 @@ class H2OCache:
             vs = (vs.astype(np.uint32) << 16).view(np.float32)
         assert pos.size == n
         return {"pos": pos, "score": score, "k": ks, "v": vs, "count": int(meta[0]), "next_pos": int(meta[1])}
+
+    # -- sparse pattern kept before heavy hitters
+    def set_pattern(self, kind="none", period=1, width=1):
+        """``kind``: "none", "strided" or "fixed" (see ``h2o_cache_set_pattern``)."""
+        k = {"none": H2O_PATTERN_NONE, "strided": H2O_PATTERN_STRIDED, "fixed": H2O_PATTERN_FIXED}[kind]
+        check(h2o_cache_set_pattern(self.handle, k, period, width), "h2o_cache_set_pattern")
 
     # -- global-score comparator
     def column_scores(self, q, k, out=None, stream=None):

@@ -23,13 +23,16 @@ def widen(t: torch.Tensor) -> np.ndarray:
     return t.detach().to("cpu", torch.float32).numpy()
 
 
-def run_gpu(q, k, v, L, heavy, recent, dtype, collect_out=True, out_units=None, scale=0.0):
+def run_gpu(q, k, v, L, heavy, recent, dtype, collect_out=True, out_units=None, scale=0.0, pattern=None):
     """Prefill + decode on the GPU.  ``q, k, v``: device tensors [B, H, N, d] in the
-    storage dtype.  Returns host arrays: kept [B, H] lists, stats, evicted
-    [T, B, H], out [T, B, H, d] (or [T, n, d] for ``out_units``), final cache."""
+    storage dtype; ``pattern``: (kind, period, width) kept before heavy hitters,
+    or None.  Returns host arrays: kept [B, H] lists, stats, evicted [T, B, H],
+    out [T, B, H, d] (or [T, n, d] for ``out_units``), final cache."""
     B, H, N, d = q.shape
     T = N - L
     cache = H2OCache(B, H, d, heavy, recent, dtype=dtype, scale=scale, max_prompt=max(L, 1))
+    if pattern is not None:
+        cache.set_pattern(*pattern)
     qp, kp, vp = (x[:, :, :L].contiguous() for x in (q, k, v))
     cache.prefill(qp, kp, vp)
     after = cache.read()
@@ -55,6 +58,41 @@ def run_gpu(q, k, v, L, heavy, recent, dtype, collect_out=True, out_units=None, 
     torch.cuda.synchronize()
     res = {"kept": after, "stats": stats, "evicted": ev.cpu().numpy(), "final": final,
            "out": outs.cpu().numpy() if (collect_out or sel is not None) else None, "info": cache.info()}
+    cache.close()
+    return res
+
+
+def run_gpu_scored(q, k, v, L, heavy, recent, dtype, scores=None, pattern=None):
+    """Scored prefill + decode on the GPU.  ``scores``: device float32 [B, H, N]
+    fixed scores, or None to compute the global column scores of the whole
+    sequence first (the global comparator)."""
+    import pytest
+
+    B, H, N, d = q.shape
+    T = N - L
+    dev = q.device
+    cache = H2OCache(B, H, d, heavy, recent, dtype=dtype, max_prompt=N)
+    if pattern is not None:
+        cache.set_pattern(*pattern)
+    gs = None
+    if scores is None:
+        scores = cache.column_scores(q, k)
+        gs = scores.cpu().numpy()
+    # the prompt is read in place from the whole sequence's K/V and scores, and
+    # each step's score is a strided column of the [B, H, N] scores
+    cache.prefill_scored(k, v, scores, prompt_len=L)
+    kept = cache.read()
+    qd, kd, vd = (x[:, :, L:].permute(2, 0, 1, 3).contiguous() for x in (q, k, v))
+    ev = torch.empty((T, B, H), dtype=torch.int32, device=dev)
+    outs = torch.empty((T, B, H, d), dtype=torch.float32, device=dev)
+    for t in range(T):
+        cache.decode_step_scored(qd[t], kd[t], vd[t], scores[:, :, L + t], outs[t], ev[t])
+    final = cache.read()
+    with pytest.raises(Exception):
+        cache.prefill_stats()  # no statistics after a scored prefill
+    torch.cuda.synchronize()
+    res = {"kept": kept, "stats": None, "evicted": ev.cpu().numpy(), "final": final, "out": outs.cpu().numpy(),
+           "gscores": gs}
     cache.close()
     return res
 

@@ -87,6 +87,7 @@ def test_null_and_state_checks_make_no_gpu_call():
     assert H.h2o_prefill_stats_read(None, None, None, None) == H.H2O_ERR_INVALID_ARG
     assert H.h2o_cache_info(None, None, None, None) == H.H2O_ERR_INVALID_ARG
     assert H.h2o_column_scores(None, None, None, 4, None, None) == H.H2O_ERR_INVALID_ARG
+    assert H.h2o_cache_set_pattern(None, 1, 4, 1) == H.H2O_ERR_INVALID_ARG
     assert H.h2o_prefill_scored(None, None, None, 4, 4, None, None) == H.H2O_ERR_INVALID_ARG
     assert H.h2o_decode_step_scored(None, None, None, None, None, 1, None, None, None) == H.H2O_ERR_INVALID_ARG
     p = H.make_params(1, 1, 64, 2, 2, "f32")

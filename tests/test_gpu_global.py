@@ -14,7 +14,7 @@ pytestmark = pytest.mark.gpu
 if not torch.cuda.is_available():
     pytest.skip("no GPU", allow_module_level=True)
 
-from gpu_harness import check_payloads, log, run_gpu, unit_payload  # noqa: E402
+from gpu_harness import check_payloads, log, run_gpu, run_gpu_scored, unit_payload  # noqa: E402
 from kv_cache_eviction_prefill_amd import H2OCache  # noqa: E402
 
 DEV = torch.device("cuda", 0)
@@ -23,35 +23,6 @@ DEV = torch.device("cuda", 0)
 def _inputs(w):
     Q, K, V = synth.batch_qkv(w, 0)
     return Q, K, V, tuple(synth.to_torch(w, x, DEV) for x in (Q, K, V))
-
-
-def run_gpu_scored(q, k, v, L, heavy, recent, dtype, scores=None):
-    """Scored prefill + decode on the GPU.  ``scores``: device float32 [B, H, N]
-    fixed scores, or None to compute the global column scores first."""
-    B, H, N, d = q.shape
-    T = N - L
-    cache = H2OCache(B, H, d, heavy, recent, dtype=dtype, max_prompt=N)
-    gs = None
-    if scores is None:
-        scores = cache.column_scores(q, k)
-        gs = scores.cpu().numpy()
-    # the prompt is read in place from the whole sequence's K/V and scores, and
-    # each step's score is a strided column of the [B, H, N] scores
-    cache.prefill_scored(k, v, scores, prompt_len=L)
-    kept = cache.read()
-    qd, kd, vd = (x[:, :, L:].permute(2, 0, 1, 3).contiguous() for x in (q, k, v))
-    ev = torch.empty((T, B, H), dtype=torch.int32, device=DEV)
-    outs = torch.empty((T, B, H, d), dtype=torch.float32, device=DEV)
-    for t in range(T):
-        cache.decode_step_scored(qd[t], kd[t], vd[t], scores[:, :, L + t], outs[t], ev[t])
-    final = cache.read()
-    with pytest.raises(Exception):
-        cache.prefill_stats()  # no statistics after a scored prefill
-    torch.cuda.synchronize()
-    res = {"kept": kept, "stats": None, "evicted": ev.cpu().numpy(), "final": final, "out": outs.cpu().numpy(),
-           "gscores": gs}
-    cache.close()
-    return res
 
 
 @pytest.mark.parametrize("wl,d,N,B,H", [
