@@ -104,6 +104,61 @@ def prefill_output(Q: np.ndarray, K: np.ndarray, V: np.ndarray, scale: float) ->
     return A @ np.asarray(V, np.float64)
 
 
+# =============================================================================== position rolling
+def _round_bf16(x: np.ndarray) -> np.ndarray:
+    """Round float32 values to the nearest bfloat16 (ties to even), as float32."""
+    b = np.ascontiguousarray(x, np.float32).view(np.uint32)
+    b = (b + np.uint32(0x7FFF) + ((b >> np.uint32(16)) & np.uint32(1))) & np.uint32(0xFFFF0000)
+    return b.view(np.float32)
+
+
+@dataclass(frozen=True)
+class Rope:
+    """Rotary position embedding applied at positions inside the cache ("position
+    rolling"): the positions are the ranks of the attended entries, not their
+    positions in the text.  [Report §4.4, Q1: H2O with position rolling streams
+    4 million tokens]
+
+    READINGS (the pages name the technique only): rotary embedding over the pairs
+    (m, m + d/2) with frequencies theta_m = base^(-2m/d); at a decode step the
+    attended entries (the cached ones plus the new token) take positions
+    0, 1, ... in position order, so the new token sits at the last one and a
+    cached entry's rotation depends on how many entries lie between; the cache
+    keeps keys unrotated.  The prompt is attended before anything is evicted, so
+    its positions are its ranks.  The prompt's rotated queries and keys are the
+    operands of the score products and are rounded to the storage type
+    (``storage``: "bf16" or "f32"), each rotation computed in float32 from
+    float32 cosines and sines as x*c - y*s and x*s + y*c; decode rotations are
+    exact."""
+
+    base: float = 10000.0
+    storage: str = "f32"
+
+    def theta(self, d: int) -> np.ndarray:
+        return float(self.base) ** (-2.0 * np.arange(d // 2) / d)
+
+    def rotate(self, X: np.ndarray, pos) -> np.ndarray:
+        """Exact rotation of the rows of X [n, d] to positions ``pos`` [n]."""
+        X = np.asarray(X, np.float64)
+        h = X.shape[1] // 2
+        ang = np.asarray(pos, np.float64)[:, None] * self.theta(X.shape[1])[None, :]
+        c, s = np.cos(ang), np.sin(ang)
+        x, y = X[:, :h], X[:, h:]
+        return np.concatenate([x * c - y * s, x * s + y * c], axis=1)
+
+    def prompt(self, X: np.ndarray) -> np.ndarray:
+        """Rows of X [L, d] rotated to positions 0..L-1 in float32 and rounded to
+        the storage type (the prompt's score operands)."""
+        X32 = np.asarray(X, np.float32)
+        L, d = X32.shape
+        h = d // 2
+        ang = np.arange(L, dtype=np.float64)[:, None] * self.theta(d)[None, :]
+        c, s = np.cos(ang).astype(np.float32), np.sin(ang).astype(np.float32)
+        x, y = X32[:, :h], X32[:, h:]
+        out = np.concatenate([x * c - y * s, x * s + y * c], axis=1).astype(np.float32)
+        return (_round_bf16(out) if self.storage == "bf16" else out).astype(np.float64)
+
+
 @dataclass(frozen=True)
 class Pattern:
     """A Sparse-Transformer attention pattern whose positions H2O keeps in
@@ -211,6 +266,7 @@ class UnitCache:
     rows: int = 0  # attention rows processed (prompt rows + decode steps)
     fixed: np.ndarray = None  # per-position scores fixed in advance (global comparator), or None
     pattern: Pattern = NO_PATTERN  # sparse pattern kept in preference to heavy hitters
+    rope: Rope = None  # rotary embedding at positions inside the cache, or None
 
     def __post_init__(self):
         if self.K is None:
@@ -226,23 +282,28 @@ class UnitCache:
     @classmethod
     def from_prompt(cls, Qp, Kp, Vp, heavy: int, recent: int, scale: float | None = None,
                     prefer_kept=None, tie_rtol: float = TIE_RTOL, fixed=None,
-                    pattern: Pattern = NO_PATTERN):
+                    pattern: Pattern = NO_PATTERN, rope: Rope = None):
         """Prefill: score the prompt, keep per ``prefill_keep``, seed the scores
         of the kept entries with their column sums.  READING: prefill column sums
         seed the running scores (the decode steps keep adding to them).
 
         ``fixed``: scores for every position of the sequence, fixed in advance
         (the global comparator).  The prompt is then ranked by ``fixed[:L]``
-        instead of its own column sums, and decode steps add nothing."""
+        instead of its own column sums, and decode steps add nothing.  ``rope``:
+        the prompt is scored on its rotated (and storage-rounded) queries and
+        keys; the cache keeps the keys unrotated."""
         Qp, Kp, Vp = (np.asarray(x, np.float64) for x in (Qp, Kp, Vp))
         L, d = Kp.shape if Kp.ndim == 2 else (0, Qp.shape[-1])
         scale = default_scale(d) if scale is None else scale
-        cache = cls(heavy=heavy, recent=recent, scale=scale, d=d, pattern=pattern)
+        cache = cls(heavy=heavy, recent=recent, scale=scale, d=d, pattern=pattern, rope=rope)
         if fixed is not None:
             cache.fixed = np.asarray(fixed, np.float64)
         if L == 0:
             return cache, None, {"selected": False, "tie_adopted": False, "band": []}
-        ps = prefill_scores(Qp, Kp, scale) if fixed is None else None
+        if fixed is None:
+            ps = prefill_scores(Qp, Kp, scale) if rope is None else prefill_scores(rope.prompt(Qp), rope.prompt(Kp), scale)
+        else:
+            ps = None
         c = ps.col_sum if fixed is None else cache.fixed[:L]
         kept, info = prefill_keep(c, heavy, recent, prefer=prefer_kept, tie_rtol=tie_rtol, pattern=pattern)
         kept = np.asarray(kept, np.int64)
@@ -294,7 +355,15 @@ class UnitCache:
         G_pos = np.concatenate([self.pos, [i]])
         G_K = np.vstack([self.K, np.asarray(k_new, np.float64)[None]])
         G_V = np.vstack([self.V, np.asarray(v_new, np.float64)[None]])
-        x = self.scale * (G_K @ q)
+        if self.rope is None:
+            x = self.scale * (G_K @ q)
+        else:
+            # position rolling: the attended entries sit at their ranks 0..|G|-1
+            # in position order; the new token (the latest) at |G| - 1
+            rank = np.empty(len(G_pos), np.int64)
+            rank[np.argsort(G_pos, kind="stable")] = np.arange(len(G_pos))
+            qr = self.rope.rotate(q[None], [len(G_pos) - 1])[0]
+            x = self.scale * (self.rope.rotate(G_K, rank) @ qr)
         a = softmax(x)
         o = a @ G_V
         if self.fixed is None:
@@ -339,7 +408,7 @@ class UnitCache:
 # =============================================================================== driver
 def run_unit(Q, K, V, prompt_len: int, heavy: int, recent: int, scale: float | None = None,
              replay_kept=None, replay_evicted=None, tie_rtol: float = TIE_RTOL,
-             keep_weights: bool = False, fixed=None, pattern: Pattern = NO_PATTERN):
+             keep_weights: bool = False, fixed=None, pattern: Pattern = NO_PATTERN, rope: Rope = None):
     """Prefill then decode one unit over positions 0..N-1 of ``Q, K, V`` ([N, d]).
 
     ``replay_kept`` / ``replay_evicted``: the other side's prefill kept set and
@@ -347,6 +416,7 @@ def run_unit(Q, K, V, prompt_len: int, heavy: int, recent: int, scale: float | N
     ``prefill_keep`` and ``UnitCache.step``).  ``fixed``: per-position scores
     [N] fixed in advance (see ``run_unit_global``); None for H2O itself.
     ``pattern``: a sparse pattern kept in preference to heavy hitters.
+    ``rope``: rotary embedding at positions inside the cache (position rolling).
 
     Returns a dict: prefill stats (or None), ``kept`` (sorted prefill kept set),
     ``out`` [T, d], ``evicted`` [T], the final ``cache`` and tie counters.
@@ -356,7 +426,7 @@ def run_unit(Q, K, V, prompt_len: int, heavy: int, recent: int, scale: float | N
     L = prompt_len
     cache, ps, pinfo = UnitCache.from_prompt(Q[:L], K[:L], V[:L], heavy, recent, scale,
                                              prefer_kept=replay_kept, tie_rtol=tie_rtol, fixed=fixed,
-                                             pattern=pattern)
+                                             pattern=pattern, rope=rope)
     kept = [int(p) for p in cache.pos]
     T = N - L
     out = np.zeros((T, d))
@@ -389,7 +459,7 @@ def global_scores(Q, K, scale: float) -> np.ndarray:
 
 
 def run_unit_global(Q, K, V, prompt_len: int, heavy: int, recent: int, scale: float | None = None,
-                    replay_kept=None, replay_evicted=None, tie_rtol: float = TIE_RTOL):
+                    replay_kept=None, replay_evicted=None, tie_rtol: float = TIE_RTOL, rope: Rope = None):
     """The global comparator: the same prefill keep and decode eviction rule as
     ``run_unit``, but every token's score is its global score (``global_scores``
     over all N rows), fixed in advance; decode steps accumulate nothing.  The
@@ -400,8 +470,8 @@ def run_unit_global(Q, K, V, prompt_len: int, heavy: int, recent: int, scale: fl
     differs.  Returns ``run_unit``'s dict plus ``scores`` (the global scores)."""
     Q, K, V = (np.asarray(x, np.float64) for x in (Q, K, V))
     scale = default_scale(Q.shape[1]) if scale is None else scale
-    g = global_scores(Q, K, scale)
+    g = global_scores(Q, K, scale) if rope is None else global_scores(rope.prompt(Q), rope.prompt(K), scale)
     res = run_unit(Q, K, V, prompt_len, heavy, recent, scale, replay_kept=replay_kept,
-                   replay_evicted=replay_evicted, tie_rtol=tie_rtol, fixed=g)
+                   replay_evicted=replay_evicted, tie_rtol=tie_rtol, fixed=g, rope=rope)
     res["scores"] = g
     return res

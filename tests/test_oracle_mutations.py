@@ -86,6 +86,16 @@ MUTATIONS = {
     "strided offset off by one": ("return (i - j) % self.period == 0", "return (i - 1 - j) % self.period == 0"),
     "fixed pattern takes the block heads": ("return j % self.period >= self.period - self.width",
                                             "return j % self.period < self.width"),
+    "rolling uses text positions": (
+        'rank[np.argsort(G_pos, kind="stable")] = np.arange(len(G_pos))',
+        "rank[:] = G_pos - G_pos.max() + len(G_pos) - 1"),
+    "rotation sign flipped": ("return np.concatenate([x * c - y * s, x * s + y * c], axis=1)\n",
+                              "return np.concatenate([x * c + y * s, -x * s + y * c], axis=1)\n"),
+    "new token one position late": ("qr = self.rope.rotate(q[None], [len(G_pos) - 1])[0]",
+                                    "qr = self.rope.rotate(q[None], [len(G_pos)])[0]"),
+    "prompt scored unrotated": ("prefill_scores(rope.prompt(Qp), rope.prompt(Kp), scale)",
+                                "prefill_scores(Qp, Kp, scale)"),
+    "rope frequencies halved": ("** (-2.0 * np.arange(d // 2) / d)", "** (-1.0 * np.arange(d // 2) / d)"),
     "evicted entries stay in the normaliser": (
         "a = softmax(x)\n        o = a @ G_V",
         "a = softmax(x)\n        a = a * (len(x) / (len(x) + self.evicted_mass))\n        o = a @ G_V"),
@@ -156,6 +166,32 @@ def _checks(m):
                 res = m.run_unit(Q, K, V, L, h, r, fixed=sc, pattern=m.Pattern(kind, per, wid))
                 assert _replay_sets(res, L, T, h + r) == _brute_pattern_sets(sc, L, T, h, r, kind, per, wid)
 
+    def rolling():
+        from test_oracle_pins import _complex_rope
+        N, d, base = 40, 8, 30.0
+        Q, K, V = (g.standard_normal((N, d)) for _ in range(3))
+        res = m.run_unit(Q, K, V, 10, 40, 40, rope=m.Rope(base))  # nothing evicted
+        ref = _sdpa_rows(_complex_rope(Q, np.arange(N), base), _complex_rope(K, np.arange(N), base), V,
+                         np.tril(np.ones((N, N), dtype=bool)))
+        np.testing.assert_allclose(res["out"], ref[10:], rtol=1e-10, atol=1e-10)
+        lib = _library_causal_weights(_complex_rope(Q[:10], np.arange(10), base),
+                                      _complex_rope(K[:10], np.arange(10), base)).sum(axis=0)
+        np.testing.assert_allclose(res["prefill"].col_sum, lib, rtol=2e-5)
+        L, T, h, r = 30, 40, 6, 5
+        Q, K, V = (g.standard_normal((L + T, d)) for _ in range(3))
+        sc = g.permutation(L + T).astype(float)
+        res = m.run_unit(Q, K, V, L, h, r, fixed=sc, rope=m.Rope(base))
+        sets = _brute_topk_sets(sc, L, T, h, r)
+        prev = set(res["kept"])
+        for t in range(T):
+            i = L + t
+            G = sorted(prev | {i})
+            x = np.array([(_complex_rope(K[j][None], [rk], base) @
+                           _complex_rope(Q[i][None], [len(G) - 1], base).T).item() for rk, j in enumerate(G)])
+            o = scipy.special.softmax(x / math.sqrt(d)) @ V[G]
+            np.testing.assert_allclose(res["out"][t], o, rtol=1e-10, atol=1e-10)
+            prev = sets[t]
+
     def sliding_window():
         N, L, R, d = 30, 9, 4, 6
         Q, K, V = (g.standard_normal((N, d)) for _ in range(3))
@@ -213,7 +249,7 @@ def _checks(m):
         assert len(c.pos) == 9
         assert abs(c.score.sum() - (c.rows - c.evicted_mass)) < 1e-9 * c.rows
 
-    return [full_attention, prefill_library, prefill_out, global_comparator, sparse_pattern, sliding_window, identical_keys, brute_force, keep_brute, mass]
+    return [full_attention, prefill_library, prefill_out, global_comparator, sparse_pattern, rolling, sliding_window, identical_keys, brute_force, keep_brute, mass]
 
 
 def test_unmutated_oracle_passes_every_check():

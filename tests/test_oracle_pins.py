@@ -14,8 +14,8 @@ import scipy.special
 import torch
 from hypothesis import given, settings, strategies as st, HealthCheck
 
-from oracle import (ParityMismatch, Pattern, UnitCache, global_scores, prefill_keep, prefill_output, prefill_scores,
-                    run_unit, run_unit_global)
+from oracle import (ParityMismatch, Pattern, Rope, UnitCache, global_scores, prefill_keep, prefill_output,
+                    prefill_scores, run_unit, run_unit_global)
 
 torch.set_default_dtype(torch.float64)
 
@@ -528,3 +528,109 @@ def test_pattern_with_no_heavy_budget_is_sliding_window():
     for pat in (Pattern("strided", 3, 1), Pattern("fixed", 5, 2)):
         res = run_unit(Q, K, V, L, 0, recent, pattern=pat)
         assert res["evicted"].tolist() == [i - recent for i in range(L, L + T)]
+
+
+# ----------------------------------------------------------------------------- position rolling (rotary embedding)
+def _complex_rope(X, pos, base=10000.0):
+    """Rotary embedding written as complex multiplication: the pair (x_m, x_{m+d/2})
+    is the complex number x_m + i x_{m+d/2}, turned by pos * base^(-2m/d) radians."""
+    X = np.asarray(X, np.float64)
+    h = X.shape[1] // 2
+    z = X[:, :h] + 1j * X[:, h:]
+    w = np.exp(1j * np.outer(np.asarray(pos, np.float64), base ** (-np.arange(0, X.shape[1], 2) / X.shape[1])))
+    r = z * w
+    return np.concatenate([r.real, r.imag], axis=1)
+
+
+def test_rope_rotation_matches_complex_multiplication():
+    g = np.random.default_rng(50)
+    X = g.standard_normal((9, 16))
+    pos = np.array([0, 1, 2, 7, 100, 1000, 4095, 12, 3])
+    np.testing.assert_allclose(Rope(500.0).rotate(X, pos), _complex_rope(X, pos, 500.0), rtol=1e-12, atol=1e-12)
+
+
+def test_rope_scores_depend_on_position_gaps_only():
+    g = np.random.default_rng(51)
+    q, k = g.standard_normal((1, 32)), g.standard_normal((1, 32))
+    r = Rope()
+    base = (r.rotate(q, [40]) @ r.rotate(k, [17]).T).item()
+    for t in (-17, 5, 900):
+        assert abs((r.rotate(q, [40 + t]) @ r.rotate(k, [17 + t]).T).item() - base) < 1e-10
+
+
+def test_bf16_rounding_matches_torch():
+    g = np.random.default_rng(52)
+    x = np.concatenate([g.standard_normal(1000).astype(np.float32),
+                        np.array([1 + 2 ** -8, 1 + 3 * 2 ** -8, -(1 + 2 ** -8), 1 + 2 ** -9], np.float32)])
+    from oracle.h2o_oracle import _round_bf16
+    ref = torch.from_numpy(x).to(torch.bfloat16).to(torch.float32).numpy()
+    assert np.array_equal(_round_bf16(x), ref)
+
+
+@pytest.mark.parametrize("storage", ["f32", "bf16"])
+def test_rope_prompt_operands(storage):
+    # the prompt's rotated operands: the exact rotation, rounded (float32, then bf16)
+    g = np.random.default_rng(53)
+    X = g.standard_normal((300, 64)).astype(np.float32)
+    got = Rope(10000.0, storage).prompt(X)
+    exact = _complex_rope(X, np.arange(300))
+    tol = 2 ** -8 if storage == "bf16" else 1e-6
+    assert np.all(np.abs(got - exact) <= tol * np.abs(exact) + 1e-6)
+    if storage == "bf16":
+        assert np.array_equal(got.astype(np.float32), torch.from_numpy(got.astype(np.float32)).to(
+            torch.bfloat16).float().numpy())
+
+
+@pytest.mark.parametrize("L,T,heavy,recent", [(12, 20, 40, 40), (0, 25, 30, 30)])
+def test_rope_full_budget_is_rope_attention(L, T, heavy, recent):
+    # nothing is evicted, so ranks are text positions: torch SDPA on q, k rotated
+    # to their own positions (complex formulation)
+    N, d = L + T, 8
+    Q, K, V = _rand(N, d, 54)
+    res = run_unit(Q, K, V, L, heavy, recent, rope=Rope(100.0))
+    ref = _sdpa_rows(_complex_rope(Q, np.arange(N), 100.0), _complex_rope(K, np.arange(N), 100.0), V,
+                     np.tril(np.ones((N, N), dtype=bool)))
+    np.testing.assert_allclose(res["out"], ref[L:], rtol=1e-10, atol=1e-10)
+
+
+def test_rope_sliding_window_is_rope_band_attention():
+    # K_h = 0 keeps a contiguous window, so rank gaps equal position gaps
+    L, T, recent, d = 10, 30, 5, 8
+    N = L + T
+    Q, K, V = _rand(N, d, 55)
+    res = run_unit(Q, K, V, L, 0, recent, rope=Rope(50.0))
+    band = np.zeros((N, N), dtype=bool)
+    for i in range(N):
+        band[i, max(0, i - recent): i + 1] = True
+    ref = _sdpa_rows(_complex_rope(Q, np.arange(N), 50.0), _complex_rope(K, np.arange(N), 50.0), V, band)
+    np.testing.assert_allclose(res["out"], ref[L:], rtol=1e-10, atol=1e-10)
+
+
+@pytest.mark.parametrize("L,T,heavy,recent", [(30, 40, 6, 5), (20, 30, 5, 0)])
+def test_rope_rolling_with_heavy_hitters_by_enumeration(L, T, heavy, recent):
+    # fixed scores fix every step's attended set (window + best earlier positions);
+    # the entries sit at their index in the sorted position list, the new token
+    # last; logits from the complex formulation, softmax from scipy
+    N, d, base = L + T, 8, 30.0
+    g = np.random.default_rng(56 + recent)
+    Q, K, V = (g.standard_normal((N, d)) for _ in range(3))
+    scores = g.permutation(N).astype(float)
+    res = run_unit(Q, K, V, L, heavy, recent, fixed=scores, rope=Rope(base))
+    sets = _brute_topk_sets(scores, L, T, heavy, recent)
+    prev = set(res["kept"])
+    for t in range(T):
+        i = L + t
+        G = sorted(prev | {i})
+        x = np.array([(_complex_rope(K[j][None], [r], base) @ _complex_rope(Q[i][None], [len(G) - 1], base).T).item()
+                      for r, j in enumerate(G)]) / math.sqrt(d)
+        o = scipy.special.softmax(x) @ V[G]
+        np.testing.assert_allclose(res["out"][t], o, rtol=1e-10, atol=1e-10)
+        prev = sets[t]
+
+
+def test_rope_prompt_column_sums_match_library():
+    L, d = 64, 16
+    Q, K, _ = _rand(L, d, 57)
+    res = run_unit(Q, K, K, L, 8, 8, rope=Rope(10000.0, "f32"))
+    lib = _library_causal_weights(_complex_rope(Q, np.arange(L)), _complex_rope(K, np.arange(L))).sum(axis=0)
+    np.testing.assert_allclose(res["prefill"].col_sum, lib, rtol=2e-5)
