@@ -96,6 +96,8 @@ def parse():
     ap.add_argument("--variant", choices=("h2o", "global"), default="h2o",
                     help="h2o: the method; global: the global-score comparator (column scores of all "
                          "prompt + generated tokens, then the same keep/evict rule with fixed scores)")
+    ap.add_argument("--rope", type=float, default=0.0,
+                    help="> 0: rotary embedding at positions inside the cache (position rolling) with this base")
     ap.add_argument("--pattern", default="none",
                     help="sparse pattern kept before heavy hitters: none, strided:PERIOD or fixed:PERIOD:WIDTH")
     ap.add_argument("--prefill-out", action="store_true",
@@ -116,14 +118,15 @@ def _cpu_unit(args):
     """Worker: time the oracle on one unit (prefill + every decode step)."""
     import time as _t
 
-    from oracle import Pattern, run_unit, run_unit_global
+    from oracle import Pattern, Rope, run_unit, run_unit_global
 
-    Q, K, V, L, kh, kr, variant, pattern = args
+    Q, K, V, L, kh, kr, variant, pattern, rope = args
+    rope = Rope(*rope) if rope else None
     t0 = _t.perf_counter()
     if variant == "global":
-        run_unit_global(Q, K, V, L, kh, kr)
+        run_unit_global(Q, K, V, L, kh, kr, rope=rope)
     else:
-        run_unit(Q, K, V, L, kh, kr, pattern=Pattern(*pattern))
+        run_unit(Q, K, V, L, kh, kr, pattern=Pattern(*pattern), rope=rope)
     return _t.perf_counter() - t0
 
 
@@ -190,8 +193,8 @@ def main():
             pre.append(tuple(x[:, :, :L].contiguous() for x in (q, k, v)))
         dec.append(tuple(x[:, :, L:].permute(2, 0, 1, 3).contiguous() for x in (q, k, v)))
         del q, k, v
-    caches = [H2OCache(B, H, d, w.heavy_budget, w.recent_budget, dtype=w.dtype, max_prompt=N if glob else L)
-              for _ in range(NL)]
+    caches = [H2OCache(B, H, d, w.heavy_budget, w.recent_budget, dtype=w.dtype, max_prompt=N if glob else L,
+                       rope_base=a.rope) for _ in range(NL)]
     pat = a.pattern.split(":")
     pattern = (pat[0], int(pat[1]) if len(pat) > 1 else 1, int(pat[2]) if len(pat) > 2 else 1)
     for cch in caches:
@@ -299,9 +302,11 @@ def main():
         "config": {"workload": w.name, "layers": NL, "batch": B, "heads": H, "head_dim": d,
                    "prompt_len": L, "decode_steps": T, "heavy_budget": w.heavy_budget,
                    "recent_budget": w.recent_budget, "storage": w.dtype, "accumulate": "fp32",
-                   "prefill_out": bool(a.prefill_out), "variant": a.variant, "pattern": a.pattern},
+                   "prefill_out": bool(a.prefill_out), "variant": a.variant, "pattern": a.pattern,
+                   "rope_base": a.rope},
         "roofline": {"kernel": f"decode_kernel<{w.dtype},{d}>", "bound": "hbm", "achieved": achieved,
-                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic(w.name) if a.layers is None and not glob and a.pattern == "none" else None,
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": (measured_traffic(w.name)
+                                 if a.layers is None and not glob and a.pattern == "none" and not a.rope else None),
                      "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
                      "bytes_per_launch": dec_bytes_launch, "avg_launch_us": 1e6 * avg_dec_s,
                      "launches": launches},
@@ -328,7 +333,8 @@ def main():
                 qf = torch.cat([pre[l][0][b, h], dec[l][0][:, b, h]]).float().cpu().numpy()
                 kf = torch.cat([pre[l][1][b, h], dec[l][1][:, b, h]]).float().cpu().numpy()
                 vf = torch.cat([pre[l][2][b, h], dec[l][2][:, b, h]]).float().cpu().numpy()
-            samples.append((qf, kf, vf, L, w.heavy_budget, w.recent_budget, a.variant, pattern))
+            samples.append((qf, kf, vf, L, w.heavy_budget, w.recent_budget, a.variant, pattern,
+                            (a.rope, w.dtype) if a.rope else None))
         procs = min(len(os.sched_getaffinity(0)), 16, len(samples))
         os.environ.setdefault("OMP_NUM_THREADS", "1")
         os.environ.setdefault("OPENBLAS_NUM_THREADS", "1")

@@ -74,7 +74,22 @@ typedef struct {
   int32_t dtype;         /* h2o_dtype */
   float scale;           /* logit scale; <= 0 selects 1/sqrt(head_dim) */
   int32_t max_prompt;    /* >= 0: longest prompt h2o_prefill will accept */
+  float rope_base;       /* > 0: rotary position embedding at positions inside
+                            the cache, frequencies rope_base^(-2m/d); 0: none */
 } h2o_params;
+/* Position rolling (Report §4.4, Q1: H2O with position rolling streams 4 million
+ * tokens).  With rope_base > 0 the caller passes unrotated queries and keys and
+ * the cache keeps keys unrotated; the library rotates them (pairs (m, m + d/2),
+ * angle p * rope_base^(-2m/d)) to positions *inside the cache*: at a decode step
+ * the attended entries (the cached ones and the new token) take the positions
+ * 0, 1, ... in order of their text positions, the new token the last one, so a
+ * logit depends on how many entries lie between query and key rather than on
+ * their distance in the text.  The prompt, attended before anything is
+ * evicted, is rotated to its own positions 0..L-1; its rotated queries and keys
+ * are rounded to the cache dtype (the operands of the score products), each
+ * computed in float32 as x*c - y*s and x*s + y*c from float32 cosines and sines
+ * of double-precision angles.  Decode rotations are done in float32 without
+ * rounding.  rope_base must be finite and >= 0. */
 /* The budget is k = K_h + K_r >= 1 (Report §3.1: k < n cached tokens).
  * B*H*max(k, max_prompt) must stay below 2^31, and one unit's prompt matrix,
  * max_prompt*d*sizeof(dtype), below 2^32 bytes. */

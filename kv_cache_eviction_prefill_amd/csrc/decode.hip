@@ -62,7 +62,7 @@ template <typename T, int D, int NP, bool kPfX>
 __device__ inline void score_pass(const DecodeArgs& a, int unit, float M, float invL, const float* lg, float x_new,
                                   const float (&pf_s)[NP], const float (&pf_c)[NP], const int32_t (&pf_p)[NP],
                                   const float (&pf_x)[NP], const uint4* s_knew, const uint4* s_vnew,
-                                  uint64_t* s_key, int* s_slot) {
+                                  uint64_t* s_key, int* s_slot, int* s_vrank) {
   using Lay = Layout<T, D>;
   constexpr int EPL = Lay::EPL, LPR = Lay::LPR;
   const int tid = threadIdx.x, g = tid / LPR, r = tid % LPR;
@@ -133,7 +133,10 @@ __device__ inline void score_pass(const DecodeArgs& a, int unit, float M, float 
     uint64_t bm = s_key[0];
 #pragma unroll
     for (int w = 1; w < kThreads / kWave; ++w) bm = s_key[w] < bm ? s_key[w] : bm;
-    if (best == bm) *s_slot = best_slot;  // keys are unique: exactly one owner
+    if (best == bm) {  // keys are unique: exactly one owner
+      *s_slot = best_slot;
+      if (a.rank != nullptr && best_slot >= 0) *s_vrank = a.rank[static_cast<size_t>(unit) * a.kstride + best_slot];
+    }
     __syncthreads();
     ev = static_cast<int32_t>(static_cast<uint32_t>(bm & 0xffffffffu));
     dst = *s_slot == kNewSlot ? -1 : *s_slot;
@@ -151,12 +154,61 @@ __device__ inline void score_pass(const DecodeArgs& a, int unit, float M, float 
       st16(vd + r * EPL, s_vnew[r]);
     }
   }
+  if (a.rank != nullptr) {  // position rolling: keep every slot's place among the cached entries
+    int32_t* rk = a.rank + static_cast<size_t>(unit) * a.kstride;
+    if (!full) {
+      if (tid == 0) rk[cnt] = cnt;  // the new token is the latest entry
+    } else if (dst >= 0) {
+      const int rv = *s_vrank;  // entries after the victim move down one place
+      for (int j = tid; j < cnt; j += kThreads) {
+        if (j == dst) continue;
+        const int32_t rj = rk[j];
+        if (rj > rv) rk[j] = rj - 1;
+      }
+      if (tid == 0) rk[dst] = a.k - 1;
+    }
+  }
   if (tid == 0 && a.evicted != nullptr) a.evicted[unit] = ev;
 }
 
+// Rotary embedding at positions inside the cache: a cached entry at place r
+// and the new token at place `count` give the logit k . R(-(r - count)) q, so the
+// query is turned per slot.  Each lane holds EPL elements of one half of the
+// pairs (m, m + d/2); its partner lane (lane ^ LPR/2) holds the other half.
+template <typename T, int D>
+struct RopeLane {
+  static constexpr int EPL = Layout<T, D>::EPL, LPR = Layout<T, D>::LPR;
+  float qp[EPL];       // the partner lane's query elements
+  float hi[EPL], lo[EPL];  // theta_m / (2 pi) of this lane's pairs, split
+  float sgn;           // +1 on the first half of the pairs, -1 on the second
+  __device__ void init(const DecodeArgs& a, const float (&qf)[EPL], int r) {
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) {
+      qp[e] = __shfl_xor(qf[e], LPR / 2, kWave);
+      const int m = (r % (LPR / 2)) * EPL + e;
+      hi[e] = a.rope_th[2 * m];
+      lo[e] = a.rope_th[2 * m + 1];
+    }
+    sgn = r < LPR / 2 ? 1.f : -1.f;
+  }
+  // q turned by -(rank gap) n: q c + sgn * q' s with (c, s) of the angle n theta_m
+  __device__ void turn(const float (&qf)[EPL], int n, float (&qr)[EPL]) const {
+    const float dn = static_cast<float>(n);
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) {
+      float t = dn * hi[e];  // exact: hi has at most 11 significant bits, |n| < 2^14
+      t -= rintf(t);
+      t = fmaf(dn, lo[e], t);
+      t -= rintf(t);  // fraction of a turn
+      const float c = __builtin_amdgcn_cosf(t), s = __builtin_amdgcn_sinf(t);
+      qr[e] = fmaf(qf[e], c, sgn * qp[e] * s);
+    }
+  }
+};
+
 // 8 waves per SIMD: all blocks of a 2048-unit launch are resident at once.
-template <typename T, int D, bool SPLIT>
-__global__ __launch_bounds__(kThreads, 8) void decode_kernel(DecodeArgs a) {
+template <typename T, int D, bool SPLIT, bool ROPE>
+__global__ __launch_bounds__(kThreads, ROPE ? 4 : 8) void decode_kernel(DecodeArgs a) {
   using Lay = Layout<T, D>;
   constexpr int EPL = Lay::EPL, LPR = Lay::LPR, NG = Lay::NG;
   extern __shared__ float s_logit[];  // single-block path: [k + 1], new token at index k
@@ -164,7 +216,7 @@ __global__ __launch_bounds__(kThreads, 8) void decode_kernel(DecodeArgs a) {
   __shared__ float s_o[NG][D];
   __shared__ uint64_t s_key[kThreads / kWave];
   __shared__ uint4 s_knew[LPR], s_vnew[LPR];
-  __shared__ int s_slot;
+  __shared__ int s_slot, s_vrank;
 
   const int tid = threadIdx.x;
   const int g = tid / LPR, r = tid % LPR;
@@ -185,6 +237,9 @@ __global__ __launch_bounds__(kThreads, 8) void decode_kernel(DecodeArgs a) {
 
   float qf[EPL];
   Elem<T>::unpack(ld16(qn + r * EPL), qf);
+  RopeLane<T, D> rope;
+  const int32_t* rkb = ROPE ? a.rank + static_cast<size_t>(unit) * a.kstride : nullptr;
+  if constexpr (ROPE) rope.init(a, qf, r);
   // The new token's rows are loaded once: group 0 attends to them and parks them
   // in LDS for the overwrite at the end.
   uint4 kn_raw = make_uint4(0u, 0u, 0u, 0u), vn_raw = make_uint4(0u, 0u, 0u, 0u);
@@ -235,11 +290,13 @@ __global__ __launch_bounds__(kThreads, 8) void decode_kernel(DecodeArgs a) {
 
   for (int base = s0 + g; base < s1; base += NG * kUnroll) {
     uint4 kr[kUnroll], vr[kUnroll];
+    int32_t rkj[kUnroll];
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
       const int j = min(base + u * NG, s1 - 1);
       kr[u] = ld16_stream(kb + static_cast<size_t>(j) * D + r * EPL);
       vr[u] = ld16_stream(vb + static_cast<size_t>(j) * D + r * EPL);
+      if constexpr (ROPE) rkj[u] = rkb[j];
     }
     float x[kUnroll];
     float mx = m;
@@ -248,8 +305,15 @@ __global__ __launch_bounds__(kThreads, 8) void decode_kernel(DecodeArgs a) {
       float kf[EPL];
       Elem<T>::unpack(kr[u], kf);
       float dot = 0.f;
+      if constexpr (ROPE) {
+        float qr[EPL];
+        rope.turn(qf, rkj[u] - a.count, qr);
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) dot = fmaf(qf[e], kf[e], dot);
+        for (int e = 0; e < EPL; ++e) dot = fmaf(qr[e], kf[e], dot);
+      } else {
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) dot = fmaf(qf[e], kf[e], dot);
+      }
       dot = group_sum<LPR>(dot);
       x[u] = (base + u * NG < s1) ? dot * a.c2 : -INFINITY;
       mx = fmaxf(mx, x[u]);
@@ -310,7 +374,7 @@ __global__ __launch_bounds__(kThreads, 8) void decode_kernel(DecodeArgs a) {
   } else {
     if (tid < D) a.out[static_cast<size_t>(unit) * D + tid] = acc / Ls;
     score_pass<T, D, kPrefetch, false>(a, unit, M, 1.f / Ls, s_logit, s_logit[a.k], pf_s, pf_c, pf_p, pf_s, s_knew,
-                                       s_vnew, s_key, &s_slot);
+                                       s_vnew, s_key, &s_slot, &s_vrank);
   }
 }
 
@@ -325,7 +389,7 @@ __global__ __launch_bounds__(kThreads) void decode_finish(DecodeArgs a) {
   __shared__ float s_pm[kMaxSplitBlocks], s_pl[kMaxSplitBlocks];
   __shared__ uint64_t s_key[kThreads / kWave];
   __shared__ uint4 s_knew[LPR], s_vnew[LPR];
-  __shared__ int s_slot;
+  __shared__ int s_slot, s_vrank;
   const int tid = threadIdx.x, unit = blockIdx.x;
   const float* sc = a.score + static_cast<size_t>(unit) * a.kstride;
   const float* cp = a.comp + static_cast<size_t>(unit) * a.kstride;
@@ -373,16 +437,16 @@ __global__ __launch_bounds__(kThreads) void decode_finish(DecodeArgs a) {
   }
   if (tid < D) a.out[static_cast<size_t>(unit) * D + tid] = og / Lg;
   score_pass<T, D, NP, true>(a, unit, Mg, 1.f / Lg, lg, x_new, pf_s, pf_c, pf_p, pf_x, s_knew, s_vnew, s_key,
-                             &s_slot);
+                             &s_slot, &s_vrank);
 }
 
-template <typename T, int D>
+template <typename T, int D, bool ROPE>
 hipError_t launch_typed(const DecodeArgs& a, int units, hipStream_t s) {
   if (a.nsplit == 1) {
     const size_t shm = static_cast<size_t>(a.k + 1) * sizeof(float);
-    hipLaunchKernelGGL((decode_kernel<T, D, false>), dim3(units), dim3(kThreads), shm, s, a);
+    hipLaunchKernelGGL((decode_kernel<T, D, false, ROPE>), dim3(units), dim3(kThreads), shm, s, a);
   } else {
-    hipLaunchKernelGGL((decode_kernel<T, D, true>), dim3(units * a.nsplit), dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL((decode_kernel<T, D, true, ROPE>), dim3(units * a.nsplit), dim3(kThreads), 0, s, a);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((decode_finish<T, D>), dim3(units), dim3(kThreads), 0, s, a);
@@ -393,10 +457,15 @@ hipError_t launch_typed(const DecodeArgs& a, int units, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_decode(int dtype, int head_dim, const DecodeArgs& a, int units, hipStream_t s) {
-  if (dtype == 0) {
-    return head_dim == 64 ? launch_typed<float, 64>(a, units, s) : launch_typed<float, 128>(a, units, s);
+  if (a.rank != nullptr) {
+    if (dtype == 0)
+      return head_dim == 64 ? launch_typed<float, 64, true>(a, units, s) : launch_typed<float, 128, true>(a, units, s);
+    return head_dim == 64 ? launch_typed<bf16_t, 64, true>(a, units, s) : launch_typed<bf16_t, 128, true>(a, units, s);
   }
-  return head_dim == 64 ? launch_typed<bf16_t, 64>(a, units, s) : launch_typed<bf16_t, 128>(a, units, s);
+  if (dtype == 0) {
+    return head_dim == 64 ? launch_typed<float, 64, false>(a, units, s) : launch_typed<float, 128, false>(a, units, s);
+  }
+  return head_dim == 64 ? launch_typed<bf16_t, 64, false>(a, units, s) : launch_typed<bf16_t, 128, false>(a, units, s);
 }
 
 }  // namespace h2o

@@ -9,6 +9,7 @@
 #include <cstdint>
 #include <cstring>
 #include <string>
+#include <vector>
 
 #include "h2o.h"
 #include "launch.h"
@@ -38,6 +39,12 @@ struct h2o_cache {
   int32_t max_split;
   float* row_lse2;
   float* col_sum;
+  // position rolling (rope_base > 0), else null
+  int32_t* rank;   // [units, kstride] position of each slot among the cached entries
+  void* qrot;      // [units, lpad_cap, d] the prompt's rotated queries (cache dtype)
+  void* krot;      // [units, lpad_cap, d] the prompt's rotated keys
+  float* rope_cs;  // [lpad_cap, d/2] (cos, sin) of position p * theta_m
+  float* rope_th;  // [d/2] (hi, lo): theta_m / (2 pi) split so that n * hi is exact
 };
 
 namespace {
@@ -85,7 +92,7 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 int32_t round32(int32_t n) { return (n + 31) / 32 * 32; }
 
 struct Sizes {
-  size_t kv, meta, split, prefill, total;
+  size_t kv, meta, split, prefill, rope, total;
   int32_t max_split, lpad;
 };
 
@@ -101,6 +108,7 @@ h2o_status check_params(const h2o_params* p, Sizes* sz) {
   if (p->dtype != H2O_F32 && p->dtype != H2O_BF16) return fail(H2O_ERR_INVALID_ARG, "unknown dtype");
   if (!std::isfinite(p->scale)) return fail(H2O_ERR_INVALID_ARG, "scale must be finite");
   if (p->max_prompt < 0) return fail(H2O_ERR_INVALID_ARG, "max_prompt must be >= 0");
+  if (!std::isfinite(p->rope_base) || p->rope_base < 0.f) return fail(H2O_ERR_INVALID_ARG, "rope_base must be >= 0");
   const int64_t units = static_cast<int64_t>(p->batch) * p->heads;
   const int64_t rows = std::max<int64_t>(k, round32(std::min<int32_t>(p->max_prompt, INT32_MAX - 31)));
   if (units * rows >= (int64_t{1} << 31) || units * kMaxSplit >= (int64_t{1} << 31))
@@ -121,16 +129,57 @@ h2o_status check_params(const h2o_params* p, Sizes* sz) {
                     : 0;
     sz->lpad = round32(p->max_prompt);
     sz->prefill = 2 * u * static_cast<size_t>(sz->lpad) * 4;
-    sz->total = sz->kv + sz->meta + sz->split + sz->prefill;
+    // position rolling: slot ranks, the prompt's rotated q/k, cos/sin per prompt
+    // position and pair, per-pair frequencies (two floats)
+    sz->rope = p->rope_base > 0.f ? u * static_cast<size_t>(round32(static_cast<int32_t>(k))) * 4 +
+                                        2 * u * static_cast<size_t>(sz->lpad) * d * es +
+                                        static_cast<size_t>(sz->lpad) * (d / 2) * 8 + (d / 2) * 8
+                                  : 0;
+    sz->total = sz->kv + sz->meta + sz->split + sz->prefill + sz->rope;
   }
   return H2O_OK;
 }
 
 void free_all(h2o_cache* c) {
   void* ptrs[] = {c->kslots, c->vslots, c->score, c->comp, c->pos, c->part, c->logits,
-                  c->row_lse2, c->col_sum};
+                  c->row_lse2, c->col_sum, c->rank, c->qrot, c->krot, c->rope_cs, c->rope_th};
   for (void* q : ptrs)
     if (q != nullptr) (void)hipFree(q);
+}
+
+// Rotary tables, in double precision on the host: (cos, sin) of p * theta_m for
+// every prompt position p and pair m (rounded to float), and theta_m / (2 pi)
+// split as hi + lo with hi holding 10 significant bits, so that n * hi is exact
+// in float for |n| < 2^14 (any rank gap) and the decode angle n * theta keeps its
+// fraction of a turn to about 1e-7.
+hipError_t upload_rope_tables(h2o_cache* c, float base) {
+  const int h = c->d / 2;
+  std::vector<float> cs(static_cast<size_t>(c->lpad_cap) * h * 2), th(static_cast<size_t>(h) * 2);
+  for (int m = 0; m < h; ++m) {
+    const double theta = std::pow(static_cast<double>(base), -2.0 * m / c->d);
+    for (int p = 0; p < c->lpad_cap; ++p) {
+      cs[(static_cast<size_t>(p) * h + m) * 2] = static_cast<float>(std::cos(p * theta));
+      cs[(static_cast<size_t>(p) * h + m) * 2 + 1] = static_cast<float>(std::sin(p * theta));
+    }
+    const double rev = theta / (2.0 * 3.14159265358979323846);
+    int ex = 0;
+    std::frexp(rev, &ex);
+    const double hi = std::ldexp(std::nearbyint(std::ldexp(rev, 10 - ex)), ex - 10);
+    th[static_cast<size_t>(m) * 2] = static_cast<float>(hi);
+    th[static_cast<size_t>(m) * 2 + 1] = static_cast<float>(rev - hi);
+  }
+  hipError_t e = hipSuccess;
+  if (!cs.empty()) e = hipMemcpy(c->rope_cs, cs.data(), cs.size() * 4, hipMemcpyHostToDevice);
+  if (e == hipSuccess) e = hipMemcpy(c->rope_th, th.data(), th.size() * 4, hipMemcpyHostToDevice);
+  return e;
+}
+
+// The prompt's queries and keys rotated to positions 0..n-1 into the cache's
+// scratch (n <= max_prompt).
+hipError_t rotate_prompt(h2o_cache* c, const void* q, const void* k, int32_t n, hipStream_t s) {
+  hipError_t e = h2o::launch_rope_prompt(c->p.dtype, c->d, q, c->qrot, n, c->units, c->rope_cs, s);
+  if (e == hipSuccess) e = h2o::launch_rope_prompt(c->p.dtype, c->d, k, c->krot, n, c->units, c->rope_cs, s);
+  return e;
 }
 
 int choose_nsplit(const h2o_cache* c, int32_t count, int32_t* split_len) {
@@ -214,6 +263,7 @@ h2o_status h2o_cache_create(const h2o_params* params, int device, h2o_cache** ou
   c->max_split = sz.max_split;
 
   const size_t u = c->units, kk = c->k, d = c->d;
+  const bool rope = params->rope_base > 0.f;
   struct Alloc {
     void** p;
     size_t bytes;
@@ -227,6 +277,11 @@ h2o_status h2o_cache_create(const h2o_params* params, int device, h2o_cache** ou
       {reinterpret_cast<void**>(&c->logits), c->max_split > 1 ? u * (kk + 1) * 4 : 0},
       {reinterpret_cast<void**>(&c->row_lse2), u * c->lpad_cap * 4},
       {reinterpret_cast<void**>(&c->col_sum), u * c->lpad_cap * 4},
+      {reinterpret_cast<void**>(&c->rank), rope ? u * c->kstride * 4 : 0},
+      {&c->qrot, rope ? u * c->lpad_cap * d * c->esize : 0},
+      {&c->krot, rope ? u * c->lpad_cap * d * c->esize : 0},
+      {reinterpret_cast<void**>(&c->rope_cs), rope ? static_cast<size_t>(c->lpad_cap) * (d / 2) * 8 : 0},
+      {reinterpret_cast<void**>(&c->rope_th), rope ? (d / 2) * 8 : 0},
   };
   for (const Alloc& a : allocs) {
     if (a.bytes == 0) continue;
@@ -238,6 +293,7 @@ h2o_status h2o_cache_create(const h2o_params* params, int device, h2o_cache** ou
     }
   }
   hipError_t e = h2o::launch_clear(c->pos, c->score, c->comp, u * c->kstride, nullptr);
+  if (e == hipSuccess && rope) e = upload_rope_tables(c, params->rope_base);
   if (e == hipSuccess) e = hipDeviceSynchronize();
   if (e != hipSuccess) {
     free_all(c);
@@ -280,8 +336,16 @@ h2o_status h2o_prefill(h2o_cache* c, const void* q, const void* k, const void* v
     a.q = q;
     a.k = k;
     a.v = v;
+    a.kcache = k;
+    a.rank = c->rank;
     a.L = L;
     a.Lpad = round32(L);
+    if (c->rank != nullptr) {  // position rolling: score the prompt on its rotated q/k
+      const hipError_t er = rotate_prompt(c, q, k, L, s);
+      if (er != hipSuccess) return hip_fail(er, "rotary embedding launch");
+      a.q = c->qrot;
+      a.k = c->krot;
+    }
     a.row_lse2 = c->row_lse2;
     a.col_sum = c->col_sum;
     a.out = out;
@@ -328,6 +392,12 @@ h2o_status h2o_column_scores(h2o_cache* c, const void* q, const void* k, int32_t
   a.q = q;
   a.k = k;
   a.L = n;
+  if (c->rank != nullptr) {  // position rolling: the sequence's own positions
+    const hipError_t er = rotate_prompt(c, q, k, n, s);
+    if (er != hipSuccess) return hip_fail(er, "rotary embedding launch");
+    a.q = c->qrot;
+    a.k = c->krot;
+  }
   a.Lpad = round32(n);
   a.row_lse2 = c->row_lse2;
   a.col_sum = c->col_sum;
@@ -365,6 +435,8 @@ h2o_status h2o_prefill_scored(h2o_cache* c, const void* k, const void* v, int32_
     h2o::PrefillArgs a{};
     a.stages = h2o::kStageSelect;
     a.k = k;
+    a.kcache = k;
+    a.rank = c->rank;
     a.v = v;
     a.L = L;
     a.Lpad = round32(L);
@@ -432,6 +504,8 @@ h2o_status decode_common(h2o_cache* c, const void* q, const void* k, const void*
   a.pat_kind = c->pat_kind;
   a.pat_period = c->pat_period;
   a.pat_width = c->pat_width;
+  a.rank = c->rank;
+  a.rope_th = c->rope_th;
   a.nsplit = choose_nsplit(c, c->count, &a.split_len);
   a.c2 = c->c2;
   const hipError_t e = h2o::launch_decode(c->p.dtype, c->d, a, c->units, static_cast<hipStream_t>(stream));

@@ -30,6 +30,8 @@ struct DecodeArgs {
   int32_t cand_limit;  // positions <= cand_limit are eviction candidates (i - K_r)
   int32_t new_is_candidate;  // K_r == 0: the new token competes for eviction
   int32_t pat_kind, pat_period, pat_width;  // sparse pattern kept before heavy hitters
+  int32_t* rank;       // position rolling: [units, kstride] slot positions inside the cache, or nullptr
+  const float* rope_th;  // [d/2] (hi, lo) theta_m / (2 pi), when rank != nullptr
   int32_t nsplit;      // blocks per unit (1: single-block path)
   int32_t split_len;   // slots per split block
   float c2;            // scale * log2(e)
@@ -55,6 +57,8 @@ struct PrefillArgs {
   const float* scores_in;  // [units, scores_stride] scores the select ranks by, or nullptr (col_sum)
   int32_t scores_stride;
   int32_t kv_rows;    // rows per unit of k and v (>= L): the select gathers rows 0..L-1
+  const void* kcache;  // [units, kv_rows, d] the key rows the select stores (k unless k holds rotated keys)
+  int32_t* rank;       // position rolling: [units, kstride] slot positions inside the cache, or nullptr
   int32_t pat_kind, pat_period, pat_width;  // sparse pattern kept before heavy hitters (query i = L)
   void* kslots;       // [units, k, d]
   void* vslots;       // [units, k, d]
@@ -70,6 +74,11 @@ struct PrefillArgs {
 };
 
 hipError_t launch_prefill(int dtype, int head_dim, const PrefillArgs& a, int units, hipStream_t s);
+
+// Rotary embedding of a prompt: rows r of x [units, L, d] rotated to position r
+// into y (same layout), from the (cos, sin) table [>= L, d/2].
+hipError_t launch_rope_prompt(int dtype, int head_dim, const void* x, void* y, int32_t L, int units,
+                              const float* cs, hipStream_t s);
 
 // Mark every slot empty (pos = -1, score = comp = 0).
 hipError_t launch_clear(int32_t* pos, float* score, float* comp, size_t n, hipStream_t s);

@@ -733,6 +733,7 @@ __global__ __launch_bounds__(kThreads) void select_fill(PrefillArgs a) {
   float* sc = a.score + static_cast<size_t>(unit) * a.kstride;
   float* cp = a.comp + static_cast<size_t>(unit) * a.kstride;
   int32_t* ps = a.pos + static_cast<size_t>(unit) * a.kstride;
+  int32_t* rk = a.rank != nullptr ? a.rank + static_cast<size_t>(unit) * a.kstride : nullptr;
   for (int s = tid; s < kc; s += kThreads) {
     if (s < nkept) {
       const int j = s_kept[s];
@@ -743,8 +744,9 @@ __global__ __launch_bounds__(kThreads) void select_fill(PrefillArgs a) {
       sc[s] = 0.f;
     }
     cp[s] = 0.f;
+    if (rk != nullptr) rk[s] = s < nkept ? s : 0;  // slots are filled in position order
   }
-  const T* Ku = static_cast<const T*>(a.k) + static_cast<size_t>(unit) * a.kv_rows * D;
+  const T* Ku = static_cast<const T*>(a.kcache) + static_cast<size_t>(unit) * a.kv_rows * D;
   const T* Vu = static_cast<const T*>(a.v) + static_cast<size_t>(unit) * a.kv_rows * D;
   T* kd = static_cast<T*>(a.kslots) + static_cast<size_t>(unit) * kc * D;
   T* vd = static_cast<T*>(a.vslots) + static_cast<size_t>(unit) * kc * D;
@@ -754,6 +756,34 @@ __global__ __launch_bounds__(kThreads) void select_fill(PrefillArgs a) {
     st16(kd + static_cast<size_t>(s) * D + r * EPL, ld16(Ku + static_cast<size_t>(j) * D + r * EPL));
     st16(vd + static_cast<size_t>(s) * D + r * EPL, ld16(Vu + static_cast<size_t>(j) * D + r * EPL));
   }
+}
+
+// ------------------------------------------------------------------ rotary embedding of the prompt
+// One thread per (row, pair m): (x, y) = (x_m, x_{m+d/2}) of row r becomes
+// (x c - y s, x s + y c) with (c, s) the table's entry for (r, m), each product
+// and sum rounded separately, the result rounded to the storage type.
+__device__ inline float to_f32(float x) { return x; }
+__device__ inline float to_f32(bf16_t x) { return __uint_as_float(static_cast<uint32_t>(x.bits) << 16); }
+template <typename T>
+__device__ inline T from_f32(float x);
+template <>
+__device__ inline float from_f32<float>(float x) { return x; }
+template <>
+__device__ inline bf16_t from_f32<bf16_t>(float x) {  // round to nearest even
+  return bf16_t{__builtin_bit_cast(uint16_t, static_cast<__bf16>(x))};
+}
+
+template <typename T, int D>
+__global__ __launch_bounds__(256) void rope_prompt(const T* x, T* y, int L, size_t pairs, const float2* cs) {
+  constexpr int H = D / 2;
+  const size_t t = blockIdx.x * static_cast<size_t>(256) + threadIdx.x;
+  if (t >= pairs) return;
+  const size_t row = t / H;  // unit * L + r
+  const int m = static_cast<int>(t % H), r = static_cast<int>(row % L);
+  const float2 w = cs[static_cast<size_t>(r) * H + m];
+  const float a = to_f32(x[row * D + m]), b = to_f32(x[row * D + m + H]);
+  y[row * D + m] = from_f32<T>(__fsub_rn(__fmul_rn(a, w.x), __fmul_rn(b, w.y)));
+  y[row * D + m + H] = from_f32<T>(__fadd_rn(__fmul_rn(a, w.y), __fmul_rn(b, w.x)));
 }
 
 __global__ void clear_kernel(int32_t* pos, float* score, float* comp, size_t n) {
@@ -818,6 +848,30 @@ hipError_t launch_f32(const PrefillArgs& a, int units, hipStream_t s) {
 hipError_t launch_prefill(int dtype, int head_dim, const PrefillArgs& a, int units, hipStream_t s) {
   if (dtype == 0) return head_dim == 64 ? launch_f32<64>(a, units, s) : launch_f32<128>(a, units, s);
   return head_dim == 64 ? launch_bf16<64>(a, units, s) : launch_bf16<128>(a, units, s);
+}
+
+hipError_t launch_rope_prompt(int dtype, int head_dim, const void* x, void* y, int32_t L, int units,
+                              const float* cs, hipStream_t s) {
+  const size_t pairs = static_cast<size_t>(units) * L * (head_dim / 2);
+  if (pairs == 0) return hipSuccess;
+  const dim3 grid(static_cast<unsigned>((pairs + 255) / 256));
+  const float2* t = reinterpret_cast<const float2*>(cs);
+  if (dtype == 0) {
+    if (head_dim == 64)
+      hipLaunchKernelGGL((rope_prompt<float, 64>), grid, dim3(256), 0, s, static_cast<const float*>(x),
+                         static_cast<float*>(y), L, pairs, t);
+    else
+      hipLaunchKernelGGL((rope_prompt<float, 128>), grid, dim3(256), 0, s, static_cast<const float*>(x),
+                         static_cast<float*>(y), L, pairs, t);
+  } else {
+    if (head_dim == 64)
+      hipLaunchKernelGGL((rope_prompt<bf16_t, 64>), grid, dim3(256), 0, s, static_cast<const bf16_t*>(x),
+                         static_cast<bf16_t*>(y), L, pairs, t);
+    else
+      hipLaunchKernelGGL((rope_prompt<bf16_t, 128>), grid, dim3(256), 0, s, static_cast<const bf16_t*>(x),
+                         static_cast<bf16_t*>(y), L, pairs, t);
+  }
+  return hipGetLastError();
 }
 
 hipError_t launch_clear(int32_t* pos, float* score, float* comp, size_t n, hipStream_t s) {

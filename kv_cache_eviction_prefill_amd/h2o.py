@@ -32,7 +32,8 @@ H2O_OK, H2O_ERR_INVALID_ARG, H2O_ERR_STATE, H2O_ERR_OOM, H2O_ERR_HIP, H2O_ERR_UN
 class h2o_params(ctypes.Structure):
     _fields_ = [("batch", ctypes.c_int32), ("heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
                 ("heavy_budget", ctypes.c_int32), ("recent_budget", ctypes.c_int32),
-                ("dtype", ctypes.c_int32), ("scale", ctypes.c_float), ("max_prompt", ctypes.c_int32)]
+                ("dtype", ctypes.c_int32), ("scale", ctypes.c_float), ("max_prompt", ctypes.c_int32),
+                ("rope_base", ctypes.c_float)]
 
 
 class H2OError(RuntimeError):
@@ -147,9 +148,10 @@ def check(status: int, where: str) -> None:
         raise H2OError(status, where, h2o_last_error())
 
 
-def make_params(batch, heads, head_dim, heavy, recent, dtype="bf16", scale=0.0, max_prompt=0) -> h2o_params:
+def make_params(batch, heads, head_dim, heavy, recent, dtype="bf16", scale=0.0, max_prompt=0,
+                rope_base=0.0) -> h2o_params:
     dt = {"f32": H2O_F32, "bf16": H2O_BF16}[dtype] if isinstance(dtype, str) else int(dtype)
-    return h2o_params(batch, heads, head_dim, heavy, recent, dt, float(scale), max_prompt)
+    return h2o_params(batch, heads, head_dim, heavy, recent, dt, float(scale), max_prompt, float(rope_base))
 
 
 def _np_ptr(a) -> int | None:
@@ -161,11 +163,11 @@ class H2OCache:
     """One budgeted cache (one attention layer) on one GPU."""
 
     def __init__(self, batch, heads, head_dim, heavy, recent, dtype="bf16", scale=0.0, max_prompt=0,
-                 device=None):
+                 device=None, rope_base=0.0):
         import torch
 
         self.torch = torch
-        self.params = make_params(batch, heads, head_dim, heavy, recent, dtype, scale, max_prompt)
+        self.params = make_params(batch, heads, head_dim, heavy, recent, dtype, scale, max_prompt, rope_base)
         self.dtype = dtype
         self.tdtype = torch.float32 if dtype == "f32" else torch.bfloat16
         self.B, self.H, self.d = batch, heads, head_dim

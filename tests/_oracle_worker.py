@@ -13,7 +13,7 @@ from __future__ import annotations
 
 import numpy as np
 
-from oracle import NO_PATTERN, ParityMismatch, Pattern, run_unit, run_unit_global
+from oracle import NO_PATTERN, ParityMismatch, Pattern, Rope, run_unit, run_unit_global
 
 OUT_ATOL = 2e-3
 SCORE_RTOL = 1e-4
@@ -37,19 +37,22 @@ def check_unit(p: dict) -> dict:
     comparator; ``p["gscores"]`` holds the GPU's column scores of the whole
     sequence) or "fixed" (scores ``p["fixed"]`` given to both sides, so every
     decision must agree exactly, with no near-tie adoption).  ``p["pattern"]``:
-    (kind, period, width) of a sparse pattern kept before heavy hitters."""
+    (kind, period, width) of a sparse pattern kept before heavy hitters;
+    ``p["rope"]``: (base, storage) of the rotary embedding at positions inside
+    the cache."""
     tag = p["tag"]
     mode = p.get("mode", "local")
     pattern = Pattern(*p["pattern"]) if p.get("pattern") else NO_PATTERN
+    rope = Rope(*p["rope"]) if p.get("rope") else None
     res = {"tag": tag, "ok": True, "msg": ""}
     try:
         if mode == "global":
             o = run_unit_global(p["Q"], p["K"], p["V"], p["L"], p["heavy"], p["recent"],
-                                replay_kept=p["kept"], replay_evicted=p["evicted"])
+                                replay_kept=p["kept"], replay_evicted=p["evicted"], rope=rope)
         else:
             o = run_unit(p["Q"], p["K"], p["V"], p["L"], p["heavy"], p["recent"],
                          replay_kept=p["kept"], replay_evicted=p["evicted"],
-                         fixed=p["fixed"] if mode == "fixed" else None, pattern=pattern)
+                         fixed=p["fixed"] if mode == "fixed" else None, pattern=pattern, rope=rope)
     except ParityMismatch as e:
         return {"tag": tag, "ok": False, "msg": f"decision mismatch: {e}"}
     res["ties"] = int(o["decode_ties_adopted"]) + int(o["prefill_tie_adopted"])

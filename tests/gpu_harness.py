@@ -23,14 +23,16 @@ def widen(t: torch.Tensor) -> np.ndarray:
     return t.detach().to("cpu", torch.float32).numpy()
 
 
-def run_gpu(q, k, v, L, heavy, recent, dtype, collect_out=True, out_units=None, scale=0.0, pattern=None):
+def run_gpu(q, k, v, L, heavy, recent, dtype, collect_out=True, out_units=None, scale=0.0, pattern=None,
+            rope_base=0.0):
     """Prefill + decode on the GPU.  ``q, k, v``: device tensors [B, H, N, d] in the
     storage dtype; ``pattern``: (kind, period, width) kept before heavy hitters,
-    or None.  Returns host arrays: kept [B, H] lists, stats, evicted [T, B, H],
+    or None; ``rope_base`` > 0: rotary embedding at positions inside the cache.
+    Returns host arrays: kept [B, H] lists, stats, evicted [T, B, H],
     out [T, B, H, d] (or [T, n, d] for ``out_units``), final cache."""
     B, H, N, d = q.shape
     T = N - L
-    cache = H2OCache(B, H, d, heavy, recent, dtype=dtype, scale=scale, max_prompt=max(L, 1))
+    cache = H2OCache(B, H, d, heavy, recent, dtype=dtype, scale=scale, max_prompt=max(L, 1), rope_base=rope_base)
     if pattern is not None:
         cache.set_pattern(*pattern)
     qp, kp, vp = (x[:, :, :L].contiguous() for x in (q, k, v))
@@ -62,7 +64,7 @@ def run_gpu(q, k, v, L, heavy, recent, dtype, collect_out=True, out_units=None, 
     return res
 
 
-def run_gpu_scored(q, k, v, L, heavy, recent, dtype, scores=None, pattern=None):
+def run_gpu_scored(q, k, v, L, heavy, recent, dtype, scores=None, pattern=None, rope_base=0.0):
     """Scored prefill + decode on the GPU.  ``scores``: device float32 [B, H, N]
     fixed scores, or None to compute the global column scores of the whole
     sequence first (the global comparator)."""
@@ -71,7 +73,7 @@ def run_gpu_scored(q, k, v, L, heavy, recent, dtype, scores=None, pattern=None):
     B, H, N, d = q.shape
     T = N - L
     dev = q.device
-    cache = H2OCache(B, H, d, heavy, recent, dtype=dtype, max_prompt=N)
+    cache = H2OCache(B, H, d, heavy, recent, dtype=dtype, max_prompt=N, rope_base=rope_base)
     if pattern is not None:
         cache.set_pattern(*pattern)
     gs = None

@@ -30,10 +30,11 @@ def test_status_strings():
 
 
 def _bytes(**kw):
-    base = dict(batch=2, heads=3, head_dim=128, heavy=4, recent=4, dtype="bf16", scale=0.0, max_prompt=64)
+    base = dict(batch=2, heads=3, head_dim=128, heavy=4, recent=4, dtype="bf16", scale=0.0, max_prompt=64,
+                rope_base=0.0)
     base.update(kw)
     p = H.make_params(base["batch"], base["heads"], base["head_dim"], base["heavy"], base["recent"],
-                      base["dtype"], base["scale"], base["max_prompt"])
+                      base["dtype"], base["scale"], base["max_prompt"], base["rope_base"])
     kv, tot = ctypes.c_size_t(), ctypes.c_size_t()
     st = H.h2o_cache_bytes(ctypes.byref(p), ctypes.byref(kv), ctypes.byref(tot))
     return st, kv.value, tot.value
@@ -45,6 +46,8 @@ def _bytes(**kw):
     (dict(heavy=0, recent=0), H.H2O_ERR_INVALID_ARG), (dict(heavy=-1), H.H2O_ERR_INVALID_ARG),
     (dict(heavy=10000, recent=5000), H.H2O_ERR_UNSUPPORTED), (dict(dtype=7), H.H2O_ERR_INVALID_ARG),
     (dict(scale=float("nan")), H.H2O_ERR_INVALID_ARG), (dict(max_prompt=-1), H.H2O_ERR_INVALID_ARG),
+    (dict(rope_base=-1.0), H.H2O_ERR_INVALID_ARG), (dict(rope_base=float("inf")), H.H2O_ERR_INVALID_ARG),
+    (dict(rope_base=10000.0), H.H2O_OK),
     (dict(batch=1 << 16, heads=1 << 10, max_prompt=4096), H.H2O_ERR_INVALID_ARG),
     # one unit's [max_prompt, d] bf16 prompt matrix must stay below 2^32 bytes
     (dict(batch=1, heads=1, max_prompt=1 << 24), H.H2O_ERR_INVALID_ARG),
@@ -65,6 +68,10 @@ def test_cache_bytes_accounting():
     assert tot == kv + 6 * 32 * 12 + (6 * 64 * 130 * 4 + 6 * 9 * 4) + 2 * 6 * 64 * 4
     st, kv32, _ = _bytes(dtype="f32")
     assert kv32 == 2 * kv
+    # position rolling adds slot ranks, the prompt's rotated q/k and the rotary tables
+    st, _, tot_r = _bytes(batch=2, heads=3, head_dim=128, heavy=4, recent=4, dtype="bf16", max_prompt=64,
+                          rope_base=10000.0)
+    assert st == 0 and tot_r == tot + 6 * 32 * 4 + 2 * 6 * 64 * 128 * 2 + 64 * 64 * 8 + 64 * 8
 
 
 def test_kv_size_matches_reported_example():
