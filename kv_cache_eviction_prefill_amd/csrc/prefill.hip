@@ -759,9 +759,10 @@ __global__ __launch_bounds__(kThreads) void select_fill(PrefillArgs a) {
 }
 
 // ------------------------------------------------------------------ rotary embedding of the prompt
-// One thread per (row, pair m): (x, y) = (x_m, x_{m+d/2}) of row r becomes
-// (x c - y s, x s + y c) with (c, s) the table's entry for (r, m), each product
-// and sum rounded separately, the result rounded to the storage type.
+// One thread per (row, run of E pairs): the 16-byte chunk holding x_m .. x_{m+E-1}
+// and the one holding x_{m+d/2} ..; each pair (x, y) becomes (x c - y s, x s + y c)
+// with (c, s) the table's entry for (r, m), each product and sum rounded
+// separately, the result rounded to the storage type.
 __device__ inline float to_f32(float x) { return x; }
 __device__ inline float to_f32(bf16_t x) { return __uint_as_float(static_cast<uint32_t>(x.bits) << 16); }
 template <typename T>
@@ -774,16 +775,28 @@ __device__ inline bf16_t from_f32<bf16_t>(float x) {  // round to nearest even
 }
 
 template <typename T, int D>
-__global__ __launch_bounds__(256) void rope_prompt(const T* x, T* y, int L, size_t pairs, const float2* cs) {
-  constexpr int H = D / 2;
+__global__ __launch_bounds__(256) void rope_prompt(const T* x, T* y, int L, size_t runs, const float2* cs) {
+  constexpr int H = D / 2, E = 16 / static_cast<int>(sizeof(T)), RPR = H / E;  // pairs per run, runs per row
   const size_t t = blockIdx.x * static_cast<size_t>(256) + threadIdx.x;
-  if (t >= pairs) return;
-  const size_t row = t / H;  // unit * L + r
-  const int m = static_cast<int>(t % H), r = static_cast<int>(row % L);
-  const float2 w = cs[static_cast<size_t>(r) * H + m];
-  const float a = to_f32(x[row * D + m]), b = to_f32(x[row * D + m + H]);
-  y[row * D + m] = from_f32<T>(__fsub_rn(__fmul_rn(a, w.x), __fmul_rn(b, w.y)));
-  y[row * D + m + H] = from_f32<T>(__fadd_rn(__fmul_rn(a, w.y), __fmul_rn(b, w.x)));
+  if (t >= runs) return;
+  const size_t row = t / RPR;  // unit * L + r
+  const int m0 = static_cast<int>(t % RPR) * E, r = static_cast<int>(row % L);
+  union Chunk {
+    uint4 u;
+    T e[E];
+  } a, b, oa, ob;
+  a.u = ld16(x + row * D + m0);
+  b.u = ld16(x + row * D + m0 + H);
+  const float2* w = cs + static_cast<size_t>(r) * H + m0;
+#pragma unroll
+  for (int i = 0; i < E; ++i) {
+    const float2 cw = w[i];
+    const float xa = to_f32(a.e[i]), yb = to_f32(b.e[i]);
+    oa.e[i] = from_f32<T>(__fsub_rn(__fmul_rn(xa, cw.x), __fmul_rn(yb, cw.y)));
+    ob.e[i] = from_f32<T>(__fadd_rn(__fmul_rn(xa, cw.y), __fmul_rn(yb, cw.x)));
+  }
+  st16(y + row * D + m0, oa.u);
+  st16(y + row * D + m0 + H, ob.u);
 }
 
 __global__ void clear_kernel(int32_t* pos, float* score, float* comp, size_t n) {
@@ -852,24 +865,25 @@ hipError_t launch_prefill(int dtype, int head_dim, const PrefillArgs& a, int uni
 
 hipError_t launch_rope_prompt(int dtype, int head_dim, const void* x, void* y, int32_t L, int units,
                               const float* cs, hipStream_t s) {
-  const size_t pairs = static_cast<size_t>(units) * L * (head_dim / 2);
-  if (pairs == 0) return hipSuccess;
-  const dim3 grid(static_cast<unsigned>((pairs + 255) / 256));
+  // one thread per 16 bytes of the first half of a row
+  const size_t runs = static_cast<size_t>(units) * L * (head_dim / 2) / (dtype == 0 ? 4 : 8);
+  if (runs == 0) return hipSuccess;
+  const dim3 grid(static_cast<unsigned>((runs + 255) / 256));
   const float2* t = reinterpret_cast<const float2*>(cs);
   if (dtype == 0) {
     if (head_dim == 64)
       hipLaunchKernelGGL((rope_prompt<float, 64>), grid, dim3(256), 0, s, static_cast<const float*>(x),
-                         static_cast<float*>(y), L, pairs, t);
+                         static_cast<float*>(y), L, runs, t);
     else
       hipLaunchKernelGGL((rope_prompt<float, 128>), grid, dim3(256), 0, s, static_cast<const float*>(x),
-                         static_cast<float*>(y), L, pairs, t);
+                         static_cast<float*>(y), L, runs, t);
   } else {
     if (head_dim == 64)
       hipLaunchKernelGGL((rope_prompt<bf16_t, 64>), grid, dim3(256), 0, s, static_cast<const bf16_t*>(x),
-                         static_cast<bf16_t*>(y), L, pairs, t);
+                         static_cast<bf16_t*>(y), L, runs, t);
     else
       hipLaunchKernelGGL((rope_prompt<bf16_t, 128>), grid, dim3(256), 0, s, static_cast<const bf16_t*>(x),
-                         static_cast<bf16_t*>(y), L, pairs, t);
+                         static_cast<bf16_t*>(y), L, runs, t);
   }
   return hipGetLastError();
 }
