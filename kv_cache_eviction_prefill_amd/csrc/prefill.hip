@@ -43,6 +43,14 @@ constexpr uint64_t kNoKey = ~0ull;
 
 __device__ inline bf16x8 ld_bf16x8(const bf16_t* p) { return __builtin_bit_cast(bf16x8, ld16(p)); }
 
+// The lane's index within its wave, read afresh (the asm is not hoisted out of
+// the branch that uses it).
+__device__ inline int lane_id_here() {
+  int id;
+  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(id));
+  return id;
+}
+
 // ------------------------------------------------------------------ bf16 MFMA passes
 // Each of a block's 4 waves owns 64 rows (pass 1: queries, pass 2: keys) as two
 // 32-row subtiles whose operand stays in registers.  The other operand streams
@@ -302,7 +310,8 @@ __global__ __launch_bounds__(kThreads, 4) void rowstats_bf16(PrefillArgs a, int 
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
           if (k0 + kTile - 1 > qw + 32 * s) {  // diagonal tile: keys after the query leave the row
-            const int rel = qw + 32 * s + fr - k0 - 4 * (lane >> 5);
+            const int ln = lane_id_here();  // re-read here: keeping it live across the loop spills
+            const int rel = qw + 32 * s + (ln & 31) - k0 - 4 * (ln >> 5);
 #pragma unroll
             for (int i = 0; i < 16; ++i) acc[s][i] = (8 * (i >> 2) + (i & 3)) <= rel ? acc[s][i] : -INFINITY;
           }
@@ -646,7 +655,9 @@ __global__ __launch_bounds__(64) void colsum_f32(PrefillArgs a) {
 }
 
 // ------------------------------------------------------------------ select + fill
-template <typename T, int D>
+// PAT: a sparse pattern is set (its bit joins the key; a template flag, so the
+// plain rule pays nothing for it).
+template <typename T, int D, bool PAT>
 __global__ __launch_bounds__(kThreads) void select_fill(PrefillArgs a) {
   constexpr int EPL = Elem<T>::kPer16B;
   constexpr int LPR = D / EPL;
@@ -678,7 +689,8 @@ __global__ __launch_bounds__(kThreads) void select_fill(PrefillArgs a) {
         for (int t = tid; t < 256; t += kThreads) s_hist[t] = 0u;
         __syncthreads();
         for (int j = tid; j < pool; j += kThreads) {
-          const uint64_t key = evict_key(c[j], j) | pattern_bit(a.pat_kind, a.pat_period, a.pat_width, j, L);
+          const uint64_t key = PAT ? evict_key(c[j], j) | pattern_bit(a.pat_kind, a.pat_period, a.pat_width, j, L)
+                                   : evict_key(c[j], j);
           if ((key & mask) == prefix) atomicAdd(&s_hist[(key >> shift) & 255u], 1u);
         }
         __syncthreads();
@@ -709,7 +721,9 @@ __global__ __launch_bounds__(kThreads) void select_fill(PrefillArgs a) {
       const int j = j0 + tid;
       bool f;
       if (j < pool)
-        f = (a.heavy > 0) && ((evict_key(c[j], j) | pattern_bit(a.pat_kind, a.pat_period, a.pat_width, j, L)) >= thr);
+        f = (a.heavy > 0) &&
+            ((PAT ? evict_key(c[j], j) | pattern_bit(a.pat_kind, a.pat_period, a.pat_width, j, L) : evict_key(c[j], j)) >=
+             thr);
       else f = (j < L);
       const uint64_t bal = __ballot(f);
       const int lane = tid & (kWave - 1);
@@ -810,8 +824,11 @@ __global__ void clear_kernel(int32_t* pos, float* score, float* comp, size_t n) 
 
 template <typename T, int D>
 hipError_t launch_select(const PrefillArgs& a, int units, hipStream_t s) {
-  hipLaunchKernelGGL((select_fill<T, D>), dim3(units), dim3(kThreads),
-                     static_cast<size_t>(a.kcap) * sizeof(int), s, a);
+  const size_t shm = static_cast<size_t>(a.kcap) * sizeof(int);
+  if (a.pat_kind != kPatternNone)
+    hipLaunchKernelGGL((select_fill<T, D, true>), dim3(units), dim3(kThreads), shm, s, a);
+  else
+    hipLaunchKernelGGL((select_fill<T, D, false>), dim3(units), dim3(kThreads), shm, s, a);
   return hipGetLastError();
 }
 
