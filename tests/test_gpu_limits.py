@@ -1,0 +1,64 @@
+"""The library's limits on the GPU against the oracle (needs an MI355X): the
+largest budget (k = 12288 slots) on the split path and on the single-block
+path, and head_dim 64 at the benchmark's full launch shape.  Inputs come from
+the device-side generator; the oracle reads the sampled units' inputs back from
+those tensors and runs each unit in full."""
+import numpy as np
+import pytest
+import torch
+
+from workload import get, scaled, synth
+
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():
+    pytest.skip("no GPU", allow_module_level=True)
+
+from gpu_harness import check_payloads, log, run_gpu, unit_payload  # noqa: E402
+
+DEV = torch.device("cuda", 0)
+K_MAX = 12288
+
+
+def _run(w, units, T):
+    L = w.prompt_len
+    q, k, v = synth.torch_qkv(w, 0, 0, L + T, DEV)
+    log(f"case {w.name}: B={w.batch} H={w.heads} d={w.head_dim} L={L} T={T} k={w.k}; {len(units)} sampled units")
+    g = run_gpu(q, k, v, L, w.heavy_budget, w.recent_budget, w.dtype, out_units=units)
+    payloads = []
+    for n, (b, h) in enumerate(units):
+        Q, K, V = (x[b, h].to(torch.float32).cpu().numpy() for x in (q, k, v))
+        payloads.append(unit_payload(g, b, h, Q, K, V, L, w.heavy_budget, w.recent_budget, out_index=n,
+                                     tag=f"{w.name}/b{b}h{h}"))
+    del q, k, v
+    torch.cuda.empty_cache()
+    results, bad = check_payloads(payloads)
+    assert not bad, bad[:3]
+    for r in results:
+        assert "score_rel" in r and "out_err" in r and "colsum_rel" in r, r
+    # the budget holds exactly
+    assert ((g["final"]["pos"] >= 0).sum(-1) == min(L + T, w.k)).all()
+    return g
+
+
+def test_largest_budget_split_path():
+    # 2 units: each unit's 12288 slots are spread over 64 blocks, the finish launch
+    # loads most of its metadata inside the loop
+    w = scaled(get("llama7b-stream-4m"), batch=1, heads=2, prompt_len=12400, decode_steps=24,
+               heavy_budget=K_MAX // 2, recent_budget=K_MAX // 2, n_anchors=64)
+    _run(w, [(0, 0), (0, 1)], 24)
+
+
+def test_largest_budget_single_block_path():
+    # 512 units (one block per unit): 48 KB of logits in LDS per block
+    w = scaled(get("opt6.7b-32L-b64"), layers=1, batch=4, heads=128, head_dim=64, prompt_len=12300,
+               decode_steps=8, heavy_budget=K_MAX // 2, recent_budget=K_MAX // 2, n_anchors=64)
+    _run(w, [(0, 3), (3, 100)], 8)
+
+
+def test_head_dim_64_at_full_shape():
+    # the benchmark's 2048 units and 2048-token prompt, head_dim 64
+    w = scaled(get("opt6.7b-32L-b64"), layers=1, head_dim=64, decode_steps=96)
+    rng = np.random.default_rng(64)
+    idx = rng.choice(w.batch * w.heads, size=6, replace=False)
+    _run(w, [(int(i) // w.heads, int(i) % w.heads) for i in sorted(idx)], 96)
