@@ -39,7 +39,7 @@ def check_unit(p: dict) -> dict:
     decision must agree exactly, with no near-tie adoption).  ``p["pattern"]``:
     (kind, period, width) of a sparse pattern kept before heavy hitters;
     ``p["rope"]``: (base, storage) of the rotary embedding at positions inside
-    the cache."""
+    the cache; ``p["scale"]``: the logit scale when not 1/sqrt(d)."""
     tag = p["tag"]
     mode = p.get("mode", "local")
     pattern = Pattern(*p["pattern"]) if p.get("pattern") else NO_PATTERN
@@ -47,10 +47,10 @@ def check_unit(p: dict) -> dict:
     res = {"tag": tag, "ok": True, "msg": ""}
     try:
         if mode == "global":
-            o = run_unit_global(p["Q"], p["K"], p["V"], p["L"], p["heavy"], p["recent"],
+            o = run_unit_global(p["Q"], p["K"], p["V"], p["L"], p["heavy"], p["recent"], p.get("scale"),
                                 replay_kept=p["kept"], replay_evicted=p["evicted"], rope=rope)
         else:
-            o = run_unit(p["Q"], p["K"], p["V"], p["L"], p["heavy"], p["recent"],
+            o = run_unit(p["Q"], p["K"], p["V"], p["L"], p["heavy"], p["recent"], p.get("scale"),
                          replay_kept=p["kept"], replay_evicted=p["evicted"],
                          fixed=p["fixed"] if mode == "fixed" else None, pattern=pattern, rope=rope)
     except ParityMismatch as e:

@@ -118,3 +118,35 @@ def test_opt67b_layer_b16_full():
     g = run_gpu(q, k, v, w.prompt_len, w.heavy_budget, w.recent_budget, w.dtype)
     res = _check_all(w, Q, K, V, g)
     log(f"{w.name}: near-ties adopted {sum(r.get('ties', 0) for r in res)}")
+
+
+def test_custom_scale_matches_oracle():
+    # a caller-chosen logit scale instead of 1/sqrt(d), both dtypes
+    for wl, d, scale in (("tiny-fp32", 64, 0.05), ("opt6.7b-layer-b16", 128, 0.2)):
+        w = scaled(get(wl), batch=2, heads=2, head_dim=d, prompt_len=150, decode_steps=60, heavy_budget=20,
+                   recent_budget=10, n_anchors=3)
+        Q, K, V, (q, k, v) = _numpy_inputs(w)
+        log(f"case custom scale {scale} {w.dtype} d={d}")
+        g = run_gpu(q, k, v, w.prompt_len, 20, 10, w.dtype, scale=scale)
+        payloads = []
+        for b in range(w.batch):
+            for h in range(w.heads):
+                pl = unit_payload(g, b, h, Q[b, h], K[b, h], V[b, h], w.prompt_len, 20, 10)
+                pl["scale"] = scale
+                payloads.append(pl)
+        results, bad = check_payloads(payloads)
+        assert not bad, bad[:3]
+
+
+@pytest.mark.parametrize("d,L,T,heavy,recent,B,H", [
+    (128, 300, 100, 30, 12, 2, 2),   # fp32 caches beyond the tiny workload
+    (64, 97, 140, 0, 16, 1, 3),      # fp32 sliding window, ragged prompt
+    (128, 700, 40, 150, 150, 1, 2),  # fp32 split path
+])
+def test_fp32_shapes(d, L, T, heavy, recent, B, H):
+    w = scaled(get("tiny-fp32"), batch=B, heads=H, head_dim=d, prompt_len=L, decode_steps=T,
+               heavy_budget=heavy, recent_budget=recent, n_anchors=max(1, (L + T) // 50))
+    log(f"case fp32 d={d} L={L} T={T} K_h={heavy} K_r={recent} B={B} H={H}")
+    Q, K, V, (q, k, v) = _numpy_inputs(w)
+    g = run_gpu(q, k, v, L, heavy, recent, "f32")
+    _check_all(w, Q, K, V, g)
