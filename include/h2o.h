@@ -119,7 +119,9 @@ h2o_status h2o_cache_destroy(h2o_cache* cache);
  *   out:     device, nullable, [B, H, prompt_len, d] float32: when non-NULL it
  *            receives the prompt's own attention output o_r = sum_{j<=r} a_rj v_j
  *            (every prompt row attends fully; eviction starts after the prompt).
- *            bf16 caches form it from bf16-rounded weights a_rj.
+ *            bf16 caches round the softmax terms to bf16 before the product
+ *            with V and normalise in float32 afterwards.  Asking for it leaves
+ *            the cache and the statistics bit-identical to a call without it.
  * For each unit: every prompt row r attends causally (positions 0..r, itself
  * included) with a = softmax(scale * q_r . k_j); token j's score is the total
  * attention it receives, c_j = sum_{r >= j} a_rj (Report §2.3, §3.3).  If
