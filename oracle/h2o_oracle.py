@@ -36,6 +36,7 @@ scale = 1/sqrt(d), and scores never decay.
 """
 from __future__ import annotations
 
+from collections import defaultdict
 from dataclasses import dataclass, field
 
 import numpy as np
@@ -379,7 +380,10 @@ class UnitCache:
             self.pos, self.K, self.V, self.score = G_pos, G_K, G_V, G_score
             return o, -1, info
         cand = np.nonzero(G_pos <= i - self.recent)[0]
-        prot = {t: self.pattern.protected(int(G_pos[t]), i) for t in cand}
+        if self.pattern.kind == "none":
+            prot = defaultdict(bool)  # nothing is protected
+        else:
+            prot = {t: self.pattern.protected(int(G_pos[t]), i) for t in cand}
         u = min(cand, key=lambda t: (prot[t], G_score[t], G_pos[t]))
         if prefer_victim is not None and int(prefer_victim) != int(G_pos[u]):
             smin = G_score[u]

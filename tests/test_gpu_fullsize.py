@@ -104,3 +104,11 @@ def test_llama7b_stream_split_path():
     # the first eviction happens at step k - L = 1536
     w = get("llama7b-stream-4m")
     _run_sampled(w, 0, _sample(w, 4, 7), T=6000)
+
+
+def test_llama7b_stream_deep_replay():
+    # the stream well past its first evictions: 30,000 steps (28,464 of them
+    # evicting) replayed in full by the oracle for two heads, so the compensated
+    # scores and every eviction are checked far into the stream
+    w = get("llama7b-stream-4m")
+    _run_sampled(w, 0, [(0, 5), (0, 26)], T=30000)
