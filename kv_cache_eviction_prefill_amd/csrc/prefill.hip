@@ -655,6 +655,63 @@ __global__ __launch_bounds__(64) void colsum_f32(PrefillArgs a) {
 }
 
 // ------------------------------------------------------------------ select + fill
+// Per unit (one block): when the prompt is longer than the budget, the K_h
+// largest keys of the heavy-hitter pool [0, L - K_r) are found by a radix
+// select and kept with the recent window, in position order; then the kept K/V
+// rows, positions and scores are written into the slots.
+
+// Selection key of prompt position j (score bits, position; the pattern bit on top).
+template <bool PAT>
+__device__ inline uint64_t key_of(const PrefillArgs& a, const float* c, int j, int L) {
+  return PAT ? evict_key(c[j], j) | pattern_bit(a.pat_kind, a.pat_period, a.pat_width, j, L) : evict_key(c[j], j);
+}
+
+__device__ inline uint32_t wave_or_u32(uint32_t v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v |= static_cast<uint32_t>(__shfl_xor(static_cast<int>(v), o, kWave));
+  return v;
+}
+__device__ inline uint32_t wave_and_u32(uint32_t v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v &= static_cast<uint32_t>(__shfl_xor(static_cast<int>(v), o, kWave));
+  return v;
+}
+
+// The bin of a 256-bin histogram (one bin per thread of the 256-thread block)
+// that holds the need-th largest element, counting from the top bin: on return
+// *digit is that bin, *need the element's rank inside it and *cnt the bin's
+// count (the same in every thread).  A block-wide scan of the counts from the top.
+__device__ inline void pick_bin(const unsigned* hist, int need_in, int* digit, int* need, int* cnt,
+                                uint32_t* s_red, int* s_pick) {
+  static_assert(kThreads == 256, "one bin per thread");
+  const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
+  const int b = 255 - tid;
+  const uint32_t h = hist[b];
+  uint32_t x = h;
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const uint32_t y = static_cast<uint32_t>(__shfl_up(static_cast<int>(x), o, kWave));
+    if (lane >= o) x += y;
+  }
+  if (lane == kWave - 1) s_red[wave] = x;
+  __syncthreads();
+  uint32_t base = 0u;
+#pragma unroll
+  for (int w = 0; w < kThreads / kWave; ++w) base += w < wave ? s_red[w] : 0u;
+  const uint32_t incl = base + x, excl = incl - h;
+  const uint32_t nd = static_cast<uint32_t>(need_in);
+  if (excl < nd && nd <= incl) {
+    s_pick[0] = b;
+    s_pick[1] = static_cast<int>(nd - excl);
+    s_pick[2] = static_cast<int>(h);
+  }
+  __syncthreads();
+  *digit = s_pick[0];
+  *need = s_pick[1];
+  *cnt = s_pick[2];
+  __syncthreads();  // s_red and s_pick are reused
+}
+
 // PAT: a sparse pattern is set (its bit joins the key; a template flag, so the
 // plain rule pays nothing for it).
 template <typename T, int D, bool PAT>
@@ -664,8 +721,8 @@ __global__ __launch_bounds__(kThreads) void select_fill(PrefillArgs a) {
   constexpr int NG = kThreads / LPR;
   extern __shared__ int s_kept[];  // [kcap] kept positions in slot order
   __shared__ unsigned s_hist[256];
-  __shared__ uint64_t s_prefix;
-  __shared__ int s_need;
+  __shared__ uint32_t s_red[2 * (kThreads / kWave)];
+  __shared__ int s_pick[3];
   __shared__ int s_wsum[kThreads / kWave];
 
   const int unit = blockIdx.x;
@@ -682,38 +739,82 @@ __global__ __launch_bounds__(kThreads) void select_fill(PrefillArgs a) {
     const int pool = L - a.recent;  // heavy-hitter candidates: [0, L - K_r)
     uint64_t thr = kNoKey;
     if (a.heavy > 0) {
-      // MSB-first radix select of the heavy-th largest key among the pool
-      uint64_t prefix = 0, mask = 0;
-      int need = a.heavy;
-      for (int shift = 56; shift >= 0; shift -= 8) {
-        for (int t = tid; t < 256; t += kThreads) s_hist[t] = 0u;
-        __syncthreads();
-        for (int j = tid; j < pool; j += kThreads) {
-          const uint64_t key = PAT ? evict_key(c[j], j) | pattern_bit(a.pat_kind, a.pat_period, a.pat_width, j, L)
-                                   : evict_key(c[j], j);
-          if ((key & mask) == prefix) atomicAdd(&s_hist[(key >> shift) & 255u], 1u);
-        }
-        __syncthreads();
-        if (tid == 0) {
-          int cum = 0, dsel = 0;
-          for (int dd = 255; dd >= 0; --dd) {
-            const int h = static_cast<int>(s_hist[dd]);
-            if (cum + h >= need) {
-              dsel = dd;
-              break;
-            }
-            cum += h;
-          }
-          s_prefix = prefix | (static_cast<uint64_t>(dsel) << shift);
-          s_need = need - cum;
-        }
-        __syncthreads();
-        prefix = s_prefix;
-        need = s_need;
-        mask |= static_cast<uint64_t>(255u) << shift;
-        __syncthreads();
+      // The heavy-th largest key of the pool, high word (score bits) first: the
+      // bits every pool key shares are skipped, the rest is a radix select over
+      // 8-bit digits from the top; the low word (position) is only needed when
+      // the threshold score is tied across the boundary.
+      const int wave = tid / kWave, lane = tid % kWave;
+      uint32_t hor = 0u, hand = ~0u;
+      for (int j = tid; j < pool; j += kThreads) {
+        const uint32_t h = static_cast<uint32_t>(key_of<PAT>(a, c, j, L) >> 32);
+        hor |= h;
+        hand &= h;
       }
-      thr = prefix;  // exactly `heavy` pool keys are >= thr (keys are unique)
+      hor = wave_or_u32(hor);
+      hand = wave_and_u32(hand);
+      if (lane == 0) {
+        s_red[wave] = hor;
+        s_red[kThreads / kWave + wave] = hand;
+      }
+      __syncthreads();
+      hor = s_red[0];
+      hand = s_red[kThreads / kWave];
+#pragma unroll
+      for (int w = 1; w < kThreads / kWave; ++w) {
+        hor |= s_red[w];
+        hand &= s_red[kThreads / kWave + w];
+      }
+      const uint32_t diff = hor ^ hand;
+      int need = a.heavy;
+      uint32_t H = hand;  // all pool keys share their high word when diff == 0
+      int cnt_eq = pool;
+      if (diff != 0u) {
+        // bits above `top` are common (2u << 31 wraps to 0: then there are none)
+        const int top = 31 - __clz(diff);
+        uint32_t above = ~((2u << top) - 1u);
+        uint32_t prefix = hand & above;
+        for (int hi_bit = top; hi_bit >= 0; hi_bit -= 8) {
+          const int lo_bit = max(hi_bit - 7, 0);
+          const uint32_t wmask = (2u << (hi_bit - lo_bit)) - 1u;
+          s_hist[tid] = 0u;
+          __syncthreads();
+          for (int j = tid; j < pool; j += kThreads) {
+            const uint32_t h = static_cast<uint32_t>(key_of<PAT>(a, c, j, L) >> 32);
+            if ((h & above) == prefix) atomicAdd(&s_hist[(h >> lo_bit) & wmask], 1u);
+          }
+          __syncthreads();
+          int digit, cnt;
+          pick_bin(s_hist, need, &digit, &need, &cnt, s_red, s_pick);
+          prefix |= static_cast<uint32_t>(digit) << lo_bit;
+          above |= wmask << lo_bit;
+          cnt_eq = cnt;
+        }
+        H = prefix;
+      }
+      if (need == cnt_eq) {
+        thr = static_cast<uint64_t>(H) << 32;  // every key with this high word is kept
+      } else {
+        // the need largest positions among the keys whose high word is H
+        const int top = 31 - __clz(static_cast<uint32_t>(max(pool - 1, 1)));
+        uint32_t prefix = 0u, above = ~((2u << top) - 1u);
+        for (int hi_bit = top; hi_bit >= 0; hi_bit -= 8) {
+          const int lo_bit = max(hi_bit - 7, 0);
+          const uint32_t wmask = (2u << (hi_bit - lo_bit)) - 1u;
+          s_hist[tid] = 0u;
+          __syncthreads();
+          for (int j = tid; j < pool; j += kThreads) {
+            const uint32_t h = static_cast<uint32_t>(key_of<PAT>(a, c, j, L) >> 32);
+            const uint32_t p = static_cast<uint32_t>(j);
+            if (h == H && (p & above) == prefix) atomicAdd(&s_hist[(p >> lo_bit) & wmask], 1u);
+          }
+          __syncthreads();
+          int digit, cnt;
+          pick_bin(s_hist, need, &digit, &need, &cnt, s_red, s_pick);
+          prefix |= static_cast<uint32_t>(digit) << lo_bit;
+          above |= wmask << lo_bit;
+        }
+        thr = (static_cast<uint64_t>(H) << 32) | prefix;
+      }
     }
     // compaction in position order: heavy hitters first, then the recent window
     int base_slot = 0;
@@ -721,9 +822,7 @@ __global__ __launch_bounds__(kThreads) void select_fill(PrefillArgs a) {
       const int j = j0 + tid;
       bool f;
       if (j < pool)
-        f = (a.heavy > 0) &&
-            ((PAT ? evict_key(c[j], j) | pattern_bit(a.pat_kind, a.pat_period, a.pat_width, j, L) : evict_key(c[j], j)) >=
-             thr);
+        f = (a.heavy > 0) && key_of<PAT>(a, c, j, L) >= thr;
       else f = (j < L);
       const uint64_t bal = __ballot(f);
       const int lane = tid & (kWave - 1);
@@ -764,11 +863,27 @@ __global__ __launch_bounds__(kThreads) void select_fill(PrefillArgs a) {
   const T* Vu = static_cast<const T*>(a.v) + static_cast<size_t>(unit) * a.kv_rows * D;
   T* kd = static_cast<T*>(a.kslots) + static_cast<size_t>(unit) * kc * D;
   T* vd = static_cast<T*>(a.vslots) + static_cast<size_t>(unit) * kc * D;
+  // the kept rows: each row group moves kGather rows of K and V per round, all
+  // loads issued before the first store
+  constexpr int kGather = 4;
   const int g = tid / LPR, r = tid % LPR;
-  for (int s = g; s < nkept; s += NG) {
-    const int j = s_kept[s];
-    st16(kd + static_cast<size_t>(s) * D + r * EPL, ld16(Ku + static_cast<size_t>(j) * D + r * EPL));
-    st16(vd + static_cast<size_t>(s) * D + r * EPL, ld16(Vu + static_cast<size_t>(j) * D + r * EPL));
+  for (int s0 = g; s0 < nkept; s0 += NG * kGather) {
+    uint4 kr[kGather], vr[kGather];
+#pragma unroll
+    for (int u = 0; u < kGather; ++u) {
+      const int s = min(s0 + u * NG, nkept - 1);
+      const int j = s_kept[s];
+      kr[u] = ld16_stream(Ku + static_cast<size_t>(j) * D + r * EPL);
+      vr[u] = ld16_stream(Vu + static_cast<size_t>(j) * D + r * EPL);
+    }
+#pragma unroll
+    for (int u = 0; u < kGather; ++u) {
+      const int s = s0 + u * NG;
+      if (s < nkept) {
+        st16(kd + static_cast<size_t>(s) * D + r * EPL, kr[u]);
+        st16(vd + static_cast<size_t>(s) * D + r * EPL, vr[u]);
+      }
+    }
   }
 }
 
