@@ -39,7 +39,8 @@ constexpr int kPrefetch = 2;  // score-pass slots per thread whose metadata is l
 constexpr uint64_t kNoKey = ~0ull;
 constexpr int kNewSlot = -2;
 constexpr int kMaxSplitBlocks = 64;  // most blocks one unit's slots are split over
-constexpr int kFinishPrefetch = 8;   // slots per thread whose metadata the finish launch loads first
+constexpr int kFinishThreads = 512;  // threads of a finish block (one block per unit)
+constexpr int kFinishPrefetch = 4;   // slots per thread whose metadata the finish launch loads first
 
 template <typename T, int D>
 struct Layout {
@@ -58,7 +59,7 @@ struct Layout {
 // token's K/V, position and score overwrite the victim's slot.  pf_*: this
 // thread's first NP slots' metadata, loaded early by the caller; lg: the unit's
 // logits, the new token's at index k; s_knew/s_vnew: its K/V rows, in LDS.
-template <typename T, int D, int NP, bool kPfX>
+template <typename T, int D, int NP, bool kPfX, int NT = kThreads>
 __device__ inline void score_pass(const DecodeArgs& a, int unit, float M, float invL, const float* lg, float x_new,
                                   const float (&pf_s)[NP], const float (&pf_c)[NP], const int32_t (&pf_p)[NP],
                                   const float (&pf_x)[NP], const uint4* s_knew, const uint4* s_vnew,
@@ -75,7 +76,7 @@ __device__ inline void score_pass(const DecodeArgs& a, int unit, float M, float 
 
   uint64_t best = kNoKey;
   int best_slot = -1;
-  for (int i = 0, j = tid; j < cnt; ++i, j += kThreads) {
+  for (int i = 0, j = tid; j < cnt; ++i, j += NT) {
     float xj, sj, cj;
     int32_t pj;
     if (i < NP) {
@@ -132,7 +133,7 @@ __device__ inline void score_pass(const DecodeArgs& a, int unit, float M, float 
     __syncthreads();
     uint64_t bm = s_key[0];
 #pragma unroll
-    for (int w = 1; w < kThreads / kWave; ++w) bm = s_key[w] < bm ? s_key[w] : bm;
+    for (int w = 1; w < NT / kWave; ++w) bm = s_key[w] < bm ? s_key[w] : bm;
     if (best == bm) {  // keys are unique: exactly one owner
       *s_slot = best_slot;
       if (a.rank != nullptr && best_slot >= 0) *s_vrank = a.rank[static_cast<size_t>(unit) * a.kstride + best_slot];
@@ -142,7 +143,7 @@ __device__ inline void score_pass(const DecodeArgs& a, int unit, float M, float 
     dst = *s_slot == kNewSlot ? -1 : *s_slot;
   }
   if (dst >= 0) {
-    if (tid == dst % kThreads) {  // the thread that last wrote this slot's score
+    if (tid == dst % NT) {  // the thread that last wrote this slot's score
       sc[dst] = w_new;
       cp[dst] = 0.f;
       ps[dst] = a.new_pos;
@@ -160,7 +161,7 @@ __device__ inline void score_pass(const DecodeArgs& a, int unit, float M, float 
       if (tid == 0) rk[cnt] = cnt;  // the new token is the latest entry
     } else if (dst >= 0) {
       const int rv = *s_vrank;  // entries after the victim move down one place
-      for (int j = tid; j < cnt; j += kThreads) {
+      for (int j = tid; j < cnt; j += NT) {
         if (j == dst) continue;
         const int32_t rj = rk[j];
         if (rj > rv) rk[j] = rj - 1;
@@ -382,12 +383,13 @@ __global__ __launch_bounds__(kThreads, ROPE ? 4 : 8) void decode_kernel(DecodeAr
 // partials of the first launch into the output and runs the score pass over the
 // logits it wrote.
 template <typename T, int D>
-__global__ __launch_bounds__(kThreads) void decode_finish(DecodeArgs a) {
+__global__ __launch_bounds__(kFinishThreads) void decode_finish(DecodeArgs a) {
   using Lay = Layout<T, D>;
   constexpr int EPL = Lay::EPL, LPR = Lay::LPR;
+  constexpr int NT = kFinishThreads;
   constexpr int NP = kFinishPrefetch;
   __shared__ float s_pm[kMaxSplitBlocks], s_pl[kMaxSplitBlocks];
-  __shared__ uint64_t s_key[kThreads / kWave];
+  __shared__ uint64_t s_key[NT / kWave];
   __shared__ uint4 s_knew[LPR], s_vnew[LPR];
   __shared__ int s_slot, s_vrank;
   const int tid = threadIdx.x, unit = blockIdx.x;
@@ -403,7 +405,7 @@ __global__ __launch_bounds__(kThreads) void decode_finish(DecodeArgs a) {
   int32_t pf_p[NP];
 #pragma unroll
   for (int i = 0; i < NP; ++i) {
-    const int j = tid + i * kThreads;
+    const int j = tid + i * NT;
     const bool ok = j < a.count;
     pf_x[i] = ok ? lg[j] : 0.f;
     pf_s[i] = ok ? sc[j] : 0.f;
@@ -436,7 +438,7 @@ __global__ __launch_bounds__(kThreads) void decode_finish(DecodeArgs a) {
     }
   }
   if (tid < D) a.out[static_cast<size_t>(unit) * D + tid] = og / Lg;
-  score_pass<T, D, NP, true>(a, unit, Mg, 1.f / Lg, lg, x_new, pf_s, pf_c, pf_p, pf_x, s_knew, s_vnew, s_key,
+  score_pass<T, D, NP, true, NT>(a, unit, Mg, 1.f / Lg, lg, x_new, pf_s, pf_c, pf_p, pf_x, s_knew, s_vnew, s_key,
                              &s_slot, &s_vrank);
 }
 
@@ -449,7 +451,7 @@ hipError_t launch_typed(const DecodeArgs& a, int units, hipStream_t s) {
     hipLaunchKernelGGL((decode_kernel<T, D, true, ROPE>), dim3(units * a.nsplit), dim3(kThreads), 0, s, a);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((decode_finish<T, D>), dim3(units), dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL((decode_finish<T, D>), dim3(units), dim3(kFinishThreads), 0, s, a);
   }
   return hipGetLastError();
 }
