@@ -19,10 +19,12 @@
 //      (rowout instead, when the caller asks for the prompt's own attention
 //                 output o_r = sum_j a_rj v_j: the same normalisers and the output
 //                 from one sweep over K and V)
-//   3. select_fill: per unit, a radix select on the 64-bit key (score bits,
-//                 position) finds the K_h-th best heavy-hitter candidate, a
-//                 ballot/popcount compaction assigns slots in position order,
-//                 and the kept K/V rows, positions and scores are written.
+//   3. select_fill: per unit, a radix select finds the K_h-th best heavy-hitter
+//                 candidate under the (score, position) order - over the score
+//                 bits that differ, then over positions only when the boundary
+//                 score is tied - a ballot/popcount compaction assigns slots in
+//                 position order, and the kept K/V rows, positions and scores
+//                 are written.
 //
 // Cost model of the MFMA passes on gfx950 (measured): per 32x32 logit tile the
 // MFMAs take 8 x 32 cycles, and the exponentials alone (one v_exp per logit, at
