@@ -179,30 +179,56 @@ __device__ inline void score_pass(const DecodeArgs& a, int unit, float M, float 
 template <typename T, int D>
 struct RopeLane {
   static constexpr int EPL = Layout<T, D>::EPL, LPR = Layout<T, D>::LPR;
+  // With 16 lanes per row the partner lane (lane ^ 8) sits in the same DPP row:
+  // each lane then evaluates the angles of only half of its pairs and takes the
+  // other half from its partner, which needs the same (cos, sin) values.
+  static constexpr bool kShare = LPR == 16;
+  static constexpr int NA = kShare ? EPL / 2 : EPL;  // angles this lane evaluates
   float qp[EPL];       // the partner lane's query elements
-  float hi[EPL], lo[EPL];  // theta_m / (2 pi) of this lane's pairs, split
+  float hi[NA], lo[NA];  // theta_m / (2 pi) of the pairs this lane evaluates, split
   float sgn;           // +1 on the first half of the pairs, -1 on the second
   __device__ void init(const DecodeArgs& a, const float (&qf)[EPL], int r) {
+    const bool second = r >= LPR / 2;
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) {
-      qp[e] = __shfl_xor(qf[e], LPR / 2, kWave);
-      const int m = (r % (LPR / 2)) * EPL + e;
-      hi[e] = a.rope_th[2 * m];
-      lo[e] = a.rope_th[2 * m + 1];
+    for (int e = 0; e < EPL; ++e) qp[e] = __shfl_xor(qf[e], LPR / 2, kWave);
+#pragma unroll
+    for (int i = 0; i < NA; ++i) {
+      // shared: the first-half lane evaluates pairs e < EPL/2, its partner the rest
+      const int m = (r % (LPR / 2)) * EPL + (kShare && second ? EPL / 2 : 0) + i;
+      hi[i] = a.rope_th[2 * m];
+      lo[i] = a.rope_th[2 * m + 1];
     }
-    sgn = r < LPR / 2 ? 1.f : -1.f;
+    sgn = second ? -1.f : 1.f;
   }
   // q turned by -(rank gap) n: q c + sgn * q' s with (c, s) of the angle n theta_m
   __device__ void turn(const float (&qf)[EPL], int n, float (&qr)[EPL]) const {
     const float dn = static_cast<float>(n);
+    float c[NA], s[NA];
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) {
-      float t = dn * hi[e];  // exact: hi has at most 11 significant bits, |n| < 2^14
+    for (int i = 0; i < NA; ++i) {
+      float t = dn * hi[i];  // exact: hi has at most 11 significant bits, |n| < 2^14
       t -= rintf(t);
-      t = fmaf(dn, lo[e], t);
+      t = fmaf(dn, lo[i], t);
       t -= rintf(t);  // fraction of a turn
-      const float c = __builtin_amdgcn_cosf(t), s = __builtin_amdgcn_sinf(t);
-      qr[e] = fmaf(qf[e], c, sgn * qp[e] * s);
+      c[i] = __builtin_amdgcn_cosf(t);
+      s[i] = __builtin_amdgcn_sinf(t);
+    }
+    if constexpr (kShare) {
+      // pairs e < EPL/2: the first-half lanes' own values, copied into the
+      // second-half lanes (banks 2, 3 of the row); pairs e >= EPL/2: the other way
+#pragma unroll
+      for (int i = 0; i < NA; ++i) {
+        const int ci = __float_as_int(c[i]), si = __float_as_int(s[i]);
+        const float c_lo = __int_as_float(__builtin_amdgcn_update_dpp(ci, ci, kDppRowRor8, 0xF, 0xC, false));
+        const float s_lo = __int_as_float(__builtin_amdgcn_update_dpp(si, si, kDppRowRor8, 0xF, 0xC, false));
+        const float c_hi = __int_as_float(__builtin_amdgcn_update_dpp(ci, ci, kDppRowRor8, 0xF, 0x3, false));
+        const float s_hi = __int_as_float(__builtin_amdgcn_update_dpp(si, si, kDppRowRor8, 0xF, 0x3, false));
+        qr[i] = fmaf(qf[i], c_lo, sgn * qp[i] * s_lo);
+        qr[i + NA] = fmaf(qf[i + NA], c_hi, sgn * qp[i + NA] * s_hi);
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) qr[e] = fmaf(qf[e], c[e], sgn * qp[e] * s[e]);
     }
   }
 };
