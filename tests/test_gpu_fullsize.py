@@ -107,8 +107,8 @@ def test_llama7b_stream_split_path():
 
 
 def test_llama7b_stream_deep_replay():
-    # the stream well past its first evictions: 30,000 steps (28,464 of them
-    # evicting) replayed in full by the oracle for two heads, so the compensated
+    # the stream well past its first evictions: 100,000 steps (98,464 of them
+    # evicting) replayed in full by the oracle for four heads, so the compensated
     # scores and every eviction are checked far into the stream
     w = get("llama7b-stream-4m")
-    _run_sampled(w, 0, [(0, 5), (0, 26)], T=30000)
+    _run_sampled(w, 0, [(0, 5), (0, 12), (0, 19), (0, 26)], T=100000)
