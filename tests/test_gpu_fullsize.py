@@ -80,16 +80,19 @@ def _run_sampled(w, layer, units, T=None, check_props=True):
     return g, results
 
 
-@pytest.mark.parametrize("layer", [0, 31])
+@pytest.mark.parametrize("layer", [0, 15, 31])
 def test_opt67b_32layer_b64_full_shape(layer):
-    # the benchmark's launch configuration: 2048 units, prompt 2048, 1024 decode steps, k = 410
+    # the benchmark's launch configuration: 2048 units, prompt 2048, 1024 decode
+    # steps, k = 410; 32 sampled units on each of three layers
     w = get("opt6.7b-32L-b64")
-    _run_sampled(w, layer, _sample(w, 12, layer))
+    _run_sampled(w, layer, _sample(w, 32, layer))
 
 
-def test_opt30b_b128_4pct_full_shape():
-    w = get("opt30b-b128-4pct")
-    _run_sampled(w, 0, _sample(w, 10, 4))
+@pytest.mark.parametrize("budget", ["4pct", "10pct", "20pct"])
+def test_opt30b_b128_full_shape(budget):
+    # 7,168 units, prompt 1024, 1024 decode steps, k = 42 / 104 / 206
+    w = get(f"opt30b-b128-{budget}")
+    _run_sampled(w, 0, _sample(w, 16, int(budget[:-3])))
 
 
 def test_opt30b_b128_100pct_is_full_attention():
