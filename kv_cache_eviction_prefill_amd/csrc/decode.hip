@@ -34,6 +34,13 @@ namespace h2o {
 namespace {
 
 constexpr int kThreads = 256;
+// Small budgets (k <= kSmallK) over many units run 128-thread blocks: the row
+// groups of a 256-thread block would each hold only a few slots, and twice as
+// many units are in flight per CU (k = 42 over 7,168 units: 40 -> 34 us per
+// launch).  With few units the larger blocks stay faster.
+constexpr int kSmallThreads = 128;
+constexpr int kSmallK = 128;
+constexpr int kSmallKUnits = 1024;
 constexpr int kUnroll = 2;    // slots in flight per row group (K and V each)
 constexpr int kPrefetch = 2;  // score-pass slots per thread whose metadata is loaded up front
 constexpr uint64_t kNoKey = ~0ull;
@@ -42,11 +49,11 @@ constexpr int kMaxSplitBlocks = 64;  // most blocks one unit's slots are split o
 constexpr int kFinishThreads = 512;  // threads of a finish block (one block per unit)
 constexpr int kFinishPrefetch = 4;   // slots per thread whose metadata the finish launch loads first
 
-template <typename T, int D>
+template <typename T, int D, int NT = kThreads>
 struct Layout {
   static constexpr int EPL = Elem<T>::kPer16B;  // elements per lane
   static constexpr int LPR = D / EPL;           // lanes per K/V row
-  static constexpr int NG = kThreads / LPR;     // row groups per block
+  static constexpr int NG = NT / LPR;           // row groups per block
   static_assert((LPR & (LPR - 1)) == 0 && LPR <= kWave, "row must map to a power-of-two lane group");
   static_assert(LPR >= kUnroll, "one lane per in-flight slot stores its logit");
 };
@@ -234,14 +241,15 @@ struct RopeLane {
 };
 
 // 8 waves per SIMD: all blocks of a 2048-unit launch are resident at once.
-template <typename T, int D, bool SPLIT, bool ROPE>
-__global__ __launch_bounds__(kThreads, ROPE ? 4 : 8) void decode_kernel(DecodeArgs a) {
-  using Lay = Layout<T, D>;
+template <typename T, int D, bool SPLIT, bool ROPE, int NT = kThreads>
+__global__ __launch_bounds__(NT, ROPE ? 4 : 8) void decode_kernel(DecodeArgs a) {
+  using Lay = Layout<T, D, NT>;
+  static_assert(NT >= D, "one thread per output column in the merge");
   constexpr int EPL = Lay::EPL, LPR = Lay::LPR, NG = Lay::NG;
   extern __shared__ float s_logit[];  // single-block path: [k + 1], new token at index k
   __shared__ float s_m[NG], s_l[NG];
   __shared__ float s_o[NG][D];
-  __shared__ uint64_t s_key[kThreads / kWave];
+  __shared__ uint64_t s_key[NT / kWave];
   __shared__ uint4 s_knew[LPR], s_vnew[LPR];
   __shared__ int s_slot, s_vrank;
 
@@ -283,7 +291,7 @@ __global__ __launch_bounds__(kThreads, ROPE ? 4 : 8) void decode_kernel(DecodeAr
   if (!SPLIT) {
 #pragma unroll
     for (int i = 0; i < kPrefetch; ++i) {
-      const int j = tid + i * kThreads;
+      const int j = tid + i * NT;
       const bool ok = j < a.count;
       pf_s[i] = ok ? sc[j] : 0.f;
       pf_c[i] = ok ? cp[j] : 0.f;
@@ -400,7 +408,7 @@ __global__ __launch_bounds__(kThreads, ROPE ? 4 : 8) void decode_kernel(DecodeAr
     if (tid < D) pp[2 + tid] = acc;
   } else {
     if (tid < D) a.out[static_cast<size_t>(unit) * D + tid] = acc / Ls;
-    score_pass<T, D, kPrefetch, false>(a, unit, M, 1.f / Ls, s_logit, s_logit[a.k], pf_s, pf_c, pf_p, pf_s, s_knew,
+    score_pass<T, D, kPrefetch, false, NT>(a, unit, M, 1.f / Ls, s_logit, s_logit[a.k], pf_s, pf_c, pf_p, pf_s, s_knew,
                                        s_vnew, s_key, &s_slot, &s_vrank);
   }
 }
@@ -472,7 +480,11 @@ template <typename T, int D, bool ROPE>
 hipError_t launch_typed(const DecodeArgs& a, int units, hipStream_t s) {
   if (a.nsplit == 1) {
     const size_t shm = static_cast<size_t>(a.k + 1) * sizeof(float);
-    hipLaunchKernelGGL((decode_kernel<T, D, false, ROPE>), dim3(units), dim3(kThreads), shm, s, a);
+    if (a.k <= kSmallK && units >= kSmallKUnits)  // small budgets: more units in flight per CU
+      hipLaunchKernelGGL((decode_kernel<T, D, false, ROPE, kSmallThreads>), dim3(units), dim3(kSmallThreads), shm, s,
+                         a);
+    else
+      hipLaunchKernelGGL((decode_kernel<T, D, false, ROPE>), dim3(units), dim3(kThreads), shm, s, a);
   } else {
     hipLaunchKernelGGL((decode_kernel<T, D, true, ROPE>), dim3(units * a.nsplit), dim3(kThreads), 0, s, a);
     const hipError_t e = hipGetLastError();

@@ -1,6 +1,7 @@
 """The library's limits on the GPU against the oracle (needs an MI355X): the
 largest budget (k = 12288 slots) on the split path and on the single-block
-path, and head_dim 64 at the benchmark's full launch shape.  Inputs come from
+path, head_dim 64 at the benchmark's full launch shape, and small budgets over
+many units (the 128-thread decode blocks) for both storage types and head sizes.  Inputs come from
 the device-side generator; the oracle reads the sampled units' inputs back from
 those tensors and runs each unit in full."""
 import numpy as np
@@ -62,3 +63,16 @@ def test_head_dim_64_at_full_shape():
     rng = np.random.default_rng(64)
     idx = rng.choice(w.batch * w.heads, size=6, replace=False)
     _run(w, [(int(i) // w.heads, int(i) % w.heads) for i in sorted(idx)], 96)
+
+
+@pytest.mark.parametrize("base,d", [("opt6.7b-layer-b16", 128), ("opt6.7b-layer-b16", 64), ("tiny-fp32", 64),
+                                    ("tiny-fp32", 128)])
+def test_small_budget_many_units(base, d):
+    # 1,024 units with k = 32 and 1,024 units with k = 128 (the largest budget on
+    # the 128-thread blocks), prompt longer than the budget
+    for heavy, recent in ((20, 12), (64, 64)):
+        w = scaled(get(base), layers=1, batch=32, heads=32, head_dim=d, prompt_len=300, decode_steps=40,
+                   heavy_budget=heavy, recent_budget=recent, n_anchors=6)
+        rng = np.random.default_rng(d + heavy)
+        idx = rng.choice(w.batch * w.heads, size=4, replace=False)
+        _run(w, [(int(i) // w.heads, int(i) % w.heads) for i in sorted(idx)], 40)
