@@ -76,3 +76,39 @@ def test_small_budget_many_units(base, d):
         rng = np.random.default_rng(d + heavy)
         idx = rng.choice(w.batch * w.heads, size=4, replace=False)
         _run(w, [(int(i) // w.heads, int(i) % w.heads) for i in sorted(idx)], 40)
+
+
+@pytest.mark.parametrize("variant", ["rope", "pattern", "fixed"])
+def test_small_budget_blocks_with_variants(variant):
+    # the 128-thread decode blocks (k <= 128 over >= 1024 units) with position
+    # rolling, with a sparse pattern and with fixed scores
+    from gpu_harness import run_gpu_scored
+
+    L, T, heavy, recent = 200, 30, 24, 16
+    w = scaled(get("opt6.7b-layer-b16"), layers=1, batch=32, heads=32, prompt_len=L, decode_steps=T,
+               heavy_budget=heavy, recent_budget=recent, n_anchors=5)
+    q, k, v = synth.torch_qkv(w, 0, 0, L + T, DEV)
+    units = [(1, 3), (17, 30)]
+    extra, fixed = {}, None
+    if variant == "rope":
+        g = run_gpu(q, k, v, L, heavy, recent, "bf16", out_units=units, rope_base=10000.0)
+        extra = {"rope": (10000.0, "bf16")}
+    elif variant == "pattern":
+        g = run_gpu(q, k, v, L, heavy, recent, "bf16", out_units=units, pattern=("strided", 8, 1))
+        extra = {"pattern": ("strided", 8, 1)}
+    else:
+        fixed = (np.random.default_rng(5).integers(0, 64, size=(w.batch, w.heads, L + T)) / 16).astype(np.float32)
+        g = run_gpu_scored(q, k, v, L, heavy, recent, "bf16", torch.from_numpy(fixed).to(DEV))
+    log(f"case small-budget blocks with {variant}: 1024 units, k={heavy + recent}")
+    payloads = []
+    for n, (b, h) in enumerate(units):
+        Q, K, V = (x[b, h].to(torch.float32).cpu().numpy() for x in (q, k, v))
+        pl = unit_payload(g, b, h, Q, K, V, L, heavy, recent, out_index=None if fixed is not None else n)
+        pl.update(extra)
+        if fixed is not None:
+            pl.update(mode="fixed", fixed=fixed[b, h].astype(np.float64))
+        payloads.append(pl)
+    results, bad = check_payloads(payloads)
+    assert not bad, bad[:3]
+    for r in results:
+        assert "score_rel" in r and "out_err" in r, r
