@@ -112,3 +112,13 @@ def test_small_budget_blocks_with_variants(variant):
     assert not bad, bad[:3]
     for r in results:
         assert "score_rel" in r and "out_err" in r, r
+
+
+def test_small_budget_blocks_cache_filling():
+    # 1,024 units on the 128-thread blocks with a prompt shorter than the budget:
+    # the cache fills during decode (new tokens take free slots), then evicts
+    w = scaled(get("opt6.7b-layer-b16"), layers=1, batch=32, heads=32, prompt_len=50, decode_steps=120,
+               heavy_budget=64, recent_budget=64, n_anchors=4)
+    g = _run(w, [(0, 0), (13, 7), (31, 31)], 120)
+    ev = g["evicted"]
+    assert (ev[: 128 - 50] == -1).all() and (ev[128 - 50:] >= 0).all()
