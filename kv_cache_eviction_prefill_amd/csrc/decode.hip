@@ -148,12 +148,38 @@ __device__ inline void score_pass(const DecodeArgs& a, int unit, float M, float 
     uint64_t bm = s_key[0];
 #pragma unroll
     for (int w = 1; w < NT / kWave; ++w) bm = s_key[w] < bm ? s_key[w] : bm;
+    ev = static_cast<int32_t>(static_cast<uint32_t>(bm & 0xffffffffu));
+    if (a.rank == nullptr) {
+      // the wave holding the minimum writes the new token over the victim (its
+      // owner lane last wrote that slot's score): no second block barrier
+      const uint64_t own = __ballot(best == bm);
+      if (own != 0) {
+        const int ol = __ffsll(static_cast<unsigned long long>(own)) - 1;
+        const int vs = __builtin_amdgcn_readlane(best_slot, ol);
+        if (vs >= 0) {
+          const int lane = tid & (kWave - 1);
+          if (lane == ol) {
+            sc[vs] = w_new;
+            cp[vs] = 0.f;
+            ps[vs] = a.new_pos;
+          }
+          if (lane < LPR) {
+            T* kd = static_cast<T*>(a.kslots) + (static_cast<size_t>(unit) * a.k + vs) * D;
+            T* vd = static_cast<T*>(a.vslots) + (static_cast<size_t>(unit) * a.k + vs) * D;
+            st16(kd + r * EPL, s_knew[r]);
+            st16(vd + r * EPL, s_vnew[r]);
+          }
+        }
+      }
+      if (tid == 0 && a.evicted != nullptr) a.evicted[unit] = ev;
+      return;
+    }
+    // position rolling: every thread needs the victim's place among the entries
     if (best == bm) {  // keys are unique: exactly one owner
       *s_slot = best_slot;
-      if (a.rank != nullptr && best_slot >= 0) *s_vrank = a.rank[static_cast<size_t>(unit) * a.kstride + best_slot];
+      if (best_slot >= 0) *s_vrank = a.rank[static_cast<size_t>(unit) * a.kstride + best_slot];
     }
     __syncthreads();
-    ev = static_cast<int32_t>(static_cast<uint32_t>(bm & 0xffffffffu));
     dst = *s_slot == kNewSlot ? -1 : *s_slot;
   }
   if (dst >= 0) {
