@@ -12,6 +12,17 @@ from kv_cache_eviction_prefill_amd import h2o as H
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
 
+@pytest.fixture(scope="module", autouse=True)
+def built_library():
+    """The in-tree library, compiled here (hipcc cross-compiles for gfx950 without
+    a GPU) when nothing has been built yet."""
+    if not os.path.exists(H.LIB_PATH):
+        from kv_cache_eviction_prefill_amd import build
+
+        build.build()
+    return H.load()
+
+
 def test_every_declared_symbol_is_exported():
     lib = H.load()
     names = H.declared_entry_points()
