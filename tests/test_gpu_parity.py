@@ -150,3 +150,64 @@ def test_fp32_shapes(d, L, T, heavy, recent, B, H):
     Q, K, V, (q, k, v) = _numpy_inputs(w)
     g = run_gpu(q, k, v, L, heavy, recent, "f32")
     _check_all(w, Q, K, V, g)
+
+
+def test_interleaved_caches_are_independent():
+    # three caches with different shapes and paths (single-block bf16, split-path
+    # bf16 with a pattern, fp32) driven step by step in turn on one stream and on
+    # a second stream: each ends bit-identical to a run of that cache alone, so no
+    # state is shared between caches and nothing depends on the call order
+    from kv_cache_eviction_prefill_amd import H2OCache
+
+    specs = [
+        (scaled(get("opt6.7b-layer-b16"), batch=2, heads=4, prompt_len=300, decode_steps=40, heavy_budget=30,
+                recent_budget=30), None),
+        (scaled(get("opt6.7b-layer-b16"), batch=1, heads=2, prompt_len=700, decode_steps=40, heavy_budget=150,
+                recent_budget=150), ("strided", 8, 1)),
+        (scaled(get("tiny-fp32"), batch=2, heads=3, prompt_len=100, decode_steps=40, heavy_budget=12,
+                recent_budget=8), None),
+    ]
+    inputs = []
+    for w, pat in specs:
+        _, _, _, (q, k, v) = _numpy_inputs(w)
+        inputs.append((w, pat, q, k, v))
+    alone = [run_gpu(q, k, v, w.prompt_len, w.heavy_budget, w.recent_budget, w.dtype, pattern=pat)
+             for w, pat, q, k, v in inputs]
+
+    side = torch.cuda.Stream()
+    caches, outs, evs = [], [], []
+    for n, (w, pat, q, k, v) in enumerate(inputs):
+        c = H2OCache(w.batch, w.heads, w.head_dim, w.heavy_budget, w.recent_budget, dtype=w.dtype,
+                     max_prompt=w.prompt_len)
+        if pat is not None:
+            c.set_pattern(*pat)
+        L = w.prompt_len
+        c.prefill(*(x[:, :, :L].contiguous() for x in (q, k, v)))
+        caches.append(c)
+        outs.append([])
+        evs.append([])
+    T = specs[0][0].decode_steps
+    for t in range(T):
+        for n, (w, pat, q, k, v) in enumerate(inputs):
+            L = w.prompt_len
+            st = side if (t + n) % 2 else torch.cuda.current_stream()
+            qd, kd, vd = (x[:, :, L + t].contiguous() for x in (q, k, v))
+            ev = torch.empty((w.batch, w.heads), dtype=torch.int32, device=q.device)
+            # the side stream waits for the inputs made on the current stream
+            st.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(st):
+                o, _ = caches[n].decode_step(qd, kd, vd, evicted=ev, stream=st)
+            torch.cuda.current_stream().wait_stream(st)
+            outs[n].append(o)
+            evs[n].append(ev)
+    torch.cuda.synchronize()
+    for n, (w, pat, q, k, v) in enumerate(inputs):
+        ref = alone[n]
+        out = torch.stack(outs[n]).cpu().numpy()
+        ev = torch.stack(evs[n]).cpu().numpy()
+        fin = caches[n].read()
+        caches[n].close()
+        assert np.array_equal(out.view(np.uint32), ref["out"].view(np.uint32)), n
+        assert np.array_equal(ev, ref["evicted"]), n
+        assert np.array_equal(fin["pos"], ref["final"]["pos"]), n
+        assert np.array_equal(fin["score"].view(np.uint32), ref["final"]["score"].view(np.uint32)), n
