@@ -10,7 +10,8 @@
 // token.
 //
 // Work mapping (gfx950, wave64, 256 threads per block; 128 for small budgets
-// over many units):
+// over many units; one wave per unit for bf16 d=128 at larger budgets over many
+// units):
 //   * A K/V row of d elements is 16 bytes per lane over LPR lanes (bf16 d=128:
 //     16 lanes), so one wave-wide load instruction moves 4 whole rows (1 KiB),
 //     fully coalesced.  The block's 16 row groups walk the unit's slots with
@@ -29,6 +30,8 @@
 //     launch boundary orders the two: no block waits for another and no
 //     device-scope fence is needed (on gfx950 each such fence writes back and
 //     invalidates the whole L2 of its XCD).
+#include <type_traits>
+
 #include "h2o_device.h"
 #include "launch.h"
 
@@ -49,6 +52,13 @@ constexpr int kUnroll = 2;    // slots in flight per row group (K and V each)
 // 9.3 -> 8.8 us per launch; equal or better at every budget measured).
 constexpr int kFewUnits = 1024;
 constexpr int kUnrollFew = 4;
+// bf16 d=128 over many units at budgets above kSmallK runs one wave per unit,
+// its 4 row groups with 8 slots in flight each: twice the bytes in flight per
+// wave, and the merge and score pass involve no other wave (2048 units: k = 410
+// 74 -> 70 us per launch, k = 2048 368 -> 335 us; 7168 units, k = 2048:
+// 1310 -> 1276 us).  At k <= kSmallK or with few units it is slower.
+constexpr int kWaveThreads = 64;
+constexpr int kWaveUnroll = 8;
 constexpr int kPrefetch = 2;  // score-pass slots per thread whose metadata is loaded up front
 constexpr uint64_t kNoKey = ~0ull;
 constexpr int kNewSlot = -2;
@@ -273,11 +283,14 @@ struct RopeLane {
   }
 };
 
-// 8 waves per SIMD: all blocks of a 2048-unit launch are resident at once.
+// 8 waves per SIMD: all blocks of a 2048-unit launch are resident at once.  A
+// one-wave block keeps its 8 slots per group in flight with up to 256 registers.
 template <typename T, int D, bool SPLIT, bool ROPE, int NT = kThreads, int UN = kUnroll>
-__global__ __launch_bounds__(NT, ROPE || UN > kUnroll ? 4 : 8) void decode_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(NT, NT == kWaveThreads ? 2 : (ROPE || UN > kUnroll ? 4 : 8)) void decode_kernel(
+    DecodeArgs a) {
   using Lay = Layout<T, D, NT>;
-  static_assert(NT >= D, "one thread per output column in the merge");
+  constexpr int NP = NT >= kThreads ? kPrefetch : 512 / NT;  // score-pass slots prefetched per thread
+  constexpr int NC = (D + NT - 1) / NT;                       // output columns per thread in the merge
   static_assert(Lay::LPR >= UN, "one lane per in-flight slot stores its logit");
   constexpr int EPL = Lay::EPL, LPR = Lay::LPR, NG = Lay::NG;
   extern __shared__ float s_logit[];  // single-block path: [k + 1], new token at index k
@@ -320,11 +333,11 @@ __global__ __launch_bounds__(NT, ROPE || UN > kUnroll ? 4 : 8) void decode_kerne
   }
   // Score-pass metadata of this thread's first slots: loaded now, it arrives
   // under the K/V stream instead of after it.
-  float pf_s[kPrefetch], pf_c[kPrefetch];
-  int32_t pf_p[kPrefetch];
+  float pf_s[NP], pf_c[NP];
+  int32_t pf_p[NP];
   if (!SPLIT) {
 #pragma unroll
-    for (int i = 0; i < kPrefetch; ++i) {
+    for (int i = 0; i < NP; ++i) {
       const int j = tid + i * NT;
       const bool ok = j < a.count;
       pf_s[i] = ok ? sc[j] : 0.f;
@@ -425,12 +438,16 @@ __global__ __launch_bounds__(NT, ROPE || UN > kUnroll ? 4 : 8) void decode_kerne
   float M = -INFINITY;
 #pragma unroll 8
   for (int t = 0; t < NG; ++t) M = fmaxf(M, s_m[t]);
-  float Ls = 0.f, acc = 0.f;
+  float Ls = 0.f, acc[NC];
+#pragma unroll
+  for (int c = 0; c < NC; ++c) acc[c] = 0.f;
 #pragma unroll 8
   for (int t = 0; t < NG; ++t) {
     const float wt = fast_exp2(s_m[t] - M);
     Ls = fmaf(s_l[t], wt, Ls);
-    if (tid < D) acc = fmaf(s_o[t][tid], wt, acc);
+#pragma unroll
+    for (int c = 0; c < NC; ++c)
+      if (tid + c * NT < D) acc[c] = fmaf(s_o[t][tid + c * NT], wt, acc[c]);
   }
 
   if constexpr (SPLIT) {
@@ -439,11 +456,15 @@ __global__ __launch_bounds__(NT, ROPE || UN > kUnroll ? 4 : 8) void decode_kerne
       pp[0] = M;
       pp[1] = Ls;
     }
-    if (tid < D) pp[2 + tid] = acc;
+#pragma unroll
+    for (int c = 0; c < NC; ++c)
+      if (tid + c * NT < D) pp[2 + tid + c * NT] = acc[c];
   } else {
-    if (tid < D) a.out[static_cast<size_t>(unit) * D + tid] = acc / Ls;
-    score_pass<T, D, kPrefetch, false, NT>(a, unit, M, 1.f / Ls, s_logit, s_logit[a.k], pf_s, pf_c, pf_p, pf_s, s_knew,
-                                       s_vnew, s_key, &s_slot, &s_vrank);
+#pragma unroll
+    for (int c = 0; c < NC; ++c)
+      if (tid + c * NT < D) a.out[static_cast<size_t>(unit) * D + tid + c * NT] = acc[c] / Ls;
+    score_pass<T, D, NP, false, NT>(a, unit, M, 1.f / Ls, s_logit, s_logit[a.k], pf_s, pf_c, pf_p, pf_s, s_knew,
+                                    s_vnew, s_key, &s_slot, &s_vrank);
   }
 }
 
@@ -514,6 +535,13 @@ template <typename T, int D, bool ROPE>
 hipError_t launch_typed(const DecodeArgs& a, int units, hipStream_t s) {
   if (a.nsplit == 1) {
     const size_t shm = static_cast<size_t>(a.k + 1) * sizeof(float);
+    if constexpr (std::is_same<T, bf16_t>::value && D == 128 && !ROPE) {
+      if (units >= kFewUnits && a.k > kSmallK) {  // many units, larger budgets: one wave per unit
+        hipLaunchKernelGGL((decode_kernel<T, D, false, ROPE, kWaveThreads, kWaveUnroll>), dim3(units),
+                           dim3(kWaveThreads), shm, s, a);
+        return hipGetLastError();
+      }
+    }
     if (units < kFewUnits)  // few units: 4 slots in flight per row group
       hipLaunchKernelGGL((decode_kernel<T, D, false, ROPE, kThreads, kUnrollFew>), dim3(units), dim3(kThreads), shm,
                          s, a);

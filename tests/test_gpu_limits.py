@@ -1,7 +1,8 @@
 """The library's limits on the GPU against the oracle (needs an MI355X): the
 largest budget (k = 12288 slots) on the split path and on the single-block
-path, head_dim 64 at the benchmark's full launch shape, and small budgets over
-many units (the 128-thread decode blocks) for both storage types and head sizes.  Inputs come from
+path, head_dim 64 at the benchmark's full launch shape, small budgets over
+many units (the 128-thread decode blocks) for both storage types and head sizes,
+and larger bf16 budgets over many units (the one-wave decode blocks).  Inputs come from
 the device-side generator; the oracle reads the sampled units' inputs back from
 those tensors and runs each unit in full."""
 import numpy as np
@@ -122,3 +123,60 @@ def test_small_budget_blocks_cache_filling():
     g = _run(w, [(0, 0), (13, 7), (31, 31)], 120)
     ev = g["evicted"]
     assert (ev[: 128 - 50] == -1).all() and (ev[128 - 50:] >= 0).all()
+
+
+@pytest.mark.parametrize("heavy,recent", [(65, 64), (150, 150)])
+def test_one_wave_blocks(heavy, recent):
+    # bf16 d=128, 1,024 units with k = 129 (the smallest budget on the one-wave
+    # blocks) and k = 300 (slots not a multiple of the 32 in flight per wave)
+    w = scaled(get("opt6.7b-layer-b16"), layers=1, batch=32, heads=32, prompt_len=420, decode_steps=40,
+               heavy_budget=heavy, recent_budget=recent, n_anchors=6)
+    rng = np.random.default_rng(heavy + recent)
+    idx = rng.choice(w.batch * w.heads, size=4, replace=False)
+    _run(w, [(int(i) // w.heads, int(i) % w.heads) for i in sorted(idx)], 40)
+
+
+@pytest.mark.parametrize("variant", ["rope", "pattern", "fixed"])
+def test_one_wave_blocks_with_variants(variant):
+    # 1,024 bf16 units at k = 160: the pattern and fixed-score variants run on the
+    # one-wave blocks, position rolling on the 256-thread blocks
+    from gpu_harness import run_gpu_scored
+
+    L, T, heavy, recent = 330, 30, 90, 70
+    w = scaled(get("opt6.7b-layer-b16"), layers=1, batch=32, heads=32, prompt_len=L, decode_steps=T,
+               heavy_budget=heavy, recent_budget=recent, n_anchors=5)
+    q, k, v = synth.torch_qkv(w, 0, 0, L + T, DEV)
+    units = [(2, 5), (30, 17)]
+    extra, fixed = {}, None
+    if variant == "rope":
+        g = run_gpu(q, k, v, L, heavy, recent, "bf16", out_units=units, rope_base=10000.0)
+        extra = {"rope": (10000.0, "bf16")}
+    elif variant == "pattern":
+        g = run_gpu(q, k, v, L, heavy, recent, "bf16", out_units=units, pattern=("fixed", 16, 2))
+        extra = {"pattern": ("fixed", 16, 2)}
+    else:
+        fixed = (np.random.default_rng(6).integers(0, 64, size=(w.batch, w.heads, L + T)) / 16).astype(np.float32)
+        g = run_gpu_scored(q, k, v, L, heavy, recent, "bf16", torch.from_numpy(fixed).to(DEV))
+    log(f"case one-wave blocks with {variant}: 1024 units, k={heavy + recent}")
+    payloads = []
+    for n, (b, h) in enumerate(units):
+        Q, K, V = (x[b, h].to(torch.float32).cpu().numpy() for x in (q, k, v))
+        pl = unit_payload(g, b, h, Q, K, V, L, heavy, recent, out_index=None if fixed is not None else n)
+        pl.update(extra)
+        if fixed is not None:
+            pl.update(mode="fixed", fixed=fixed[b, h].astype(np.float64))
+        payloads.append(pl)
+    results, bad = check_payloads(payloads)
+    assert not bad, bad[:3]
+    for r in results:
+        assert "score_rel" in r and "out_err" in r, r
+
+
+def test_one_wave_blocks_cache_filling():
+    # 1,024 bf16 units on the one-wave blocks with a prompt shorter than the
+    # budget: new tokens take free slots until the cache is full, then evict
+    w = scaled(get("opt6.7b-layer-b16"), layers=1, batch=32, heads=32, prompt_len=100, decode_steps=140,
+               heavy_budget=100, recent_budget=100, n_anchors=4)
+    g = _run(w, [(0, 0), (9, 21), (31, 31)], 140)
+    ev = g["evicted"]
+    assert (ev[: 200 - 100] == -1).all() and (ev[200 - 100:] >= 0).all()
