@@ -28,7 +28,10 @@
  *     dense row-major, 16-byte aligned, and owned by the caller; they must stay
  *     valid until the stream has passed the call.
  *   - stream: a hipStream_t on the cache's device, or NULL for the null stream.
- *     Calls are asynchronous unless stated otherwise.
+ *     Calls are asynchronous unless stated otherwise.  Each call makes the
+ *     cache's device current for its duration and restores the caller's device
+ *     on return; if the device cannot be made current the call returns
+ *     H2O_ERR_HIP before any other work.
  *   - Return codes only: nothing throws across the ABI and nothing exits the
  *     process.  Argument and state checks run before any GPU work; when one
  *     fails the cache is left unchanged.  A fault inside an already-queued kernel

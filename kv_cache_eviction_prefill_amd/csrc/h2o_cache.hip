@@ -71,21 +71,30 @@ h2o_status hip_fail(hipError_t e, const char* what) {
   return e == hipErrorOutOfMemory ? H2O_ERR_OOM : H2O_ERR_HIP;
 }
 
+// Makes the cache's device current for one call and restores the caller's on
+// exit; ok() is false when the device could not be made current, and the call
+// then fails before touching any memory.
 class DeviceGuard {
  public:
   explicit DeviceGuard(int dev) {
-    if (hipGetDevice(&prev_) == hipSuccess && prev_ != dev) {
-      changed_ = hipSetDevice(dev) == hipSuccess;
+    ok_ = hipGetDevice(&prev_) == hipSuccess;
+    if (ok_ && prev_ != dev) {
+      ok_ = hipSetDevice(dev) == hipSuccess;
+      changed_ = ok_;
     }
   }
   ~DeviceGuard() {
     if (changed_) (void)hipSetDevice(prev_);
   }
+  bool ok() const { return ok_; }
 
  private:
   int prev_ = -1;
+  bool ok_ = false;
   bool changed_ = false;
 };
+
+h2o_status device_fail() { return fail(H2O_ERR_HIP, "could not make the cache's device current"); }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -241,6 +250,7 @@ h2o_status h2o_cache_create(const h2o_params* params, int device, h2o_cache** ou
     if (dev >= n) return fail(H2O_ERR_INVALID_ARG, "device index out of range");
   }
   DeviceGuard guard(dev);
+  if (!guard.ok()) return device_fail();
   h2o_cache* c = new (std::nothrow) h2o_cache{};
   if (c == nullptr) return fail(H2O_ERR_OOM, "host allocation failed");
   c->p = *params;
@@ -307,7 +317,7 @@ h2o_status h2o_cache_create(const h2o_params* params, int device, h2o_cache** ou
 h2o_status h2o_cache_destroy(h2o_cache* c) {
   if (c == nullptr) return H2O_OK;
   DeviceGuard guard(c->device);
-  const hipError_t e = hipDeviceSynchronize();
+  const hipError_t e = guard.ok() ? hipDeviceSynchronize() : hipErrorInvalidDevice;
   free_all(c);
   delete c;
   if (e != hipSuccess) return hip_fail(e, "hipDeviceSynchronize before free");
@@ -326,6 +336,7 @@ h2o_status h2o_prefill(h2o_cache* c, const void* q, const void* k, const void* v
     if (out != nullptr && !aligned16(out)) return fail(H2O_ERR_INVALID_ARG, "out must be 16-byte aligned");
   }
   DeviceGuard guard(c->device);
+  if (!guard.ok()) return device_fail();
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (L == 0) {
     const hipError_t e = h2o::launch_clear(c->pos, c->score, c->comp, static_cast<size_t>(c->units) * c->kstride, s);
@@ -386,6 +397,7 @@ h2o_status h2o_column_scores(h2o_cache* c, const void* q, const void* k, int32_t
   if ((reinterpret_cast<uintptr_t>(scores) & 3u) != 0)
     return fail(H2O_ERR_INVALID_ARG, "scores must be 4-byte aligned");
   DeviceGuard guard(c->device);
+  if (!guard.ok()) return device_fail();
   hipStream_t s = static_cast<hipStream_t>(stream);
   h2o::PrefillArgs a{};
   a.stages = h2o::kStageScores;
@@ -427,6 +439,7 @@ h2o_status h2o_prefill_scored(h2o_cache* c, const void* k, const void* v, int32_
       return fail(H2O_ERR_INVALID_ARG, "scores must be 4-byte aligned");
   }
   DeviceGuard guard(c->device);
+  if (!guard.ok()) return device_fail();
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (L == 0) {
     const hipError_t e = h2o::launch_clear(c->pos, c->score, c->comp, static_cast<size_t>(c->units) * c->kstride, s);
@@ -480,6 +493,7 @@ h2o_status decode_common(h2o_cache* c, const void* q, const void* k, const void*
   if (c->prompt_len < 0) return fail(H2O_ERR_STATE, "decode before prefill");
   if (c->next_pos == INT32_MAX) return fail(H2O_ERR_STATE, "position counter would overflow int32");
   DeviceGuard guard(c->device);
+  if (!guard.ok()) return device_fail();
   h2o::DecodeArgs a{};
   a.q = q;
   a.knew = k;
@@ -538,6 +552,7 @@ h2o_status h2o_cache_read(h2o_cache* c, int32_t* pos, float* score, void* k_slot
                           void* stream) {
   if (c == nullptr) return fail(H2O_ERR_INVALID_ARG, "cache is NULL");
   DeviceGuard guard(c->device);
+  if (!guard.ok()) return device_fail();
   hipError_t e = hipStreamSynchronize(static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "hipStreamSynchronize");
   const size_t n = static_cast<size_t>(c->units) * c->k;
@@ -566,6 +581,7 @@ h2o_status h2o_prefill_stats_read(h2o_cache* c, float* row_lse, float* col_sum, 
   if (!c->stats_valid)
     return fail(H2O_ERR_STATE, "no statistics: the last call was h2o_prefill_scored or h2o_column_scores");
   DeviceGuard guard(c->device);
+  if (!guard.ok()) return device_fail();
   hipError_t e = hipStreamSynchronize(static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "hipStreamSynchronize");
   const int32_t L = c->prompt_len;
