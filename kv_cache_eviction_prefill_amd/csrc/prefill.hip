@@ -457,12 +457,35 @@ __device__ inline i16x4 lds_tr16(uint32_t addr) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(static_cast<uintptr_t>(addr)));
 }
 
-// Byte offset, inside a swizzled tile, of 16-bit element `col` of tile row `key`.
+// V tiles have a placement of their own: chunk c of tile row r sits at chunk
+// c ^ v_swz(r).  A transposing read takes, per half-wave, 4 consecutive key
+// rows (r = 4j .. 4j+3) times 4 chunks of one 64-byte column block; v_swz sends
+// those 4 rows to 4 different 64-byte quarters of the 256 bytes the LDS banks
+// serve per cycle (d = 128: a row spans all 256 bytes, the quarter is bits 2-3
+// of the chunk; d = 64: a row spans half of them, the quarter is the row's
+// parity and bit 2 of the chunk), and the 4 chunks of a row fill its quarter,
+// so the read is free of bank conflicts.  The placement repeats every 16 rows,
+// so one source offset per lane serves every load of a tile.
 template <int D>
-__device__ inline uint32_t tile_elem_offset(int key, int col) {
+__device__ inline int v_swz(int r) {
+  if constexpr (D == 128) return ((r & 3) << 2) | ((r >> 2) & 3);
+  else return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
+}
+
+template <int D>
+__device__ inline int tile_voff_v() {
+  using T = Tile<D>;
+  const int o = threadIdx.x * 16;
+  const int r = o / T::kRowBytes, p = (o % T::kRowBytes) / 16;
+  return r * T::kRowBytes + ((p ^ v_swz<D>(r)) * 16);
+}
+
+// Byte offset, inside a V tile, of 16-bit element `col` of tile row `key`.
+template <int D>
+__device__ inline uint32_t v_elem_offset(int key, int col) {
   using T = Tile<D>;
   const int byte = 2 * col;
-  return key * T::kRowBytes + ((((byte >> 4) ^ (key & T::kSwz))) << 4) + (byte & 15);
+  return key * T::kRowBytes + (((byte >> 4) ^ v_swz<D>(key)) << 4) + (byte & 15);
 }
 
 template <int D>
@@ -483,7 +506,7 @@ __global__ __launch_bounds__(kThreads, 3) void rowout_bf16(PrefillArgs a, int nb
   float* out = a.out + static_cast<size_t>(unit) * L * D;
   const __amdgpu_buffer_rsrc_t rk = make_rsrc(Ku, static_cast<uint32_t>(L) * T::kRowBytes);
   const __amdgpu_buffer_rsrc_t rv = make_rsrc(Vu, static_cast<uint32_t>(L) * T::kRowBytes);
-  const int voff = tile_voff<D>();
+  const int voff = tile_voff<D>(), voffv = tile_voff_v<D>();
   const uint32_t xo = frag_offset<D>(lane);
   // this lane's role as a source of the transposing read: key row 4(g/2) + j
   // (+ 8 for the second read, + 16 for the second 16-key block), d columns
@@ -500,10 +523,10 @@ __global__ __launch_bounds__(kThreads, 3) void rowout_bf16(PrefillArgs a, int nb
     bf16x8 bq[D / 16];
     row_frag<D>(Qu, qw + fr, L, lane, bq);
     tile_async(rk, voff, 0, sK[0], T::kRowBytes, T::kLoads);
-    tile_async(rv, voff, 0, sV[0], T::kRowBytes, T::kLoads);
+    tile_async(rv, voffv, 0, sV[0], T::kRowBytes, T::kLoads);
     if (ntile > 1) {
       tile_async(rk, voff, kTile, sK[1], T::kRowBytes, T::kLoads);
-      tile_async(rv, voff, kTile, sV[1], T::kRowBytes, T::kLoads);
+      tile_async(rv, voffv, kTile, sV[1], T::kRowBytes, T::kLoads);
     }
 #pragma unroll
     for (int kk = 0; kk < D / 16; ++kk) asm volatile("" : "+v"(bq[kk]));
@@ -517,7 +540,7 @@ __global__ __launch_bounds__(kThreads, 3) void rowout_bf16(PrefillArgs a, int nb
       tile_barrier();
       if (t + 2 < ntile) {
         tile_async(rk, voff, (t + 2) * kTile, sK[(t + 2) % kBufs], T::kRowBytes, T::kLoads);
-        tile_async(rv, voff, (t + 2) * kTile, sV[(t + 2) % kBufs], T::kRowBytes, T::kLoads);
+        tile_async(rv, voffv, (t + 2) * kTile, sV[(t + 2) % kBufs], T::kRowBytes, T::kLoads);
       }
       const int k0 = t * kTile;
       if (qw < L && k0 <= qw + 31) {
@@ -550,8 +573,8 @@ __global__ __launch_bounds__(kThreads, 3) void rowout_bf16(PrefillArgs a, int nb
         for (int db = 0; db < NDB; ++db) {
 #pragma unroll
           for (int kb = 0; kb < 2; ++kb) {
-            const i16x4 lo = lds_tr16(vt + tile_elem_offset<D>(tkey + 16 * kb, tcol + 32 * db));
-            const i16x4 hi = lds_tr16(vt + tile_elem_offset<D>(tkey + 16 * kb + 8, tcol + 32 * db));
+            const i16x4 lo = lds_tr16(vt + v_elem_offset<D>(tkey + 16 * kb, tcol + 32 * db));
+            const i16x4 hi = lds_tr16(vt + v_elem_offset<D>(tkey + 16 * kb + 8, tcol + 32 * db));
             const bf16x8 av = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
             o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pw[kb], o[db], 0, 0, 0);
           }
