@@ -24,8 +24,9 @@
 //     fp32 sum; eviction candidates compete on a 64-bit key (score bits, pos),
 //     which orders by score then position exactly; a wave/LDS min picks the
 //     victim, whose slot the new token's K/V, position and score overwrite.
-//   * Split path (few units): nsplit blocks per unit each stream a slice of the
-//     slots and write (max, sum, o) partials and their logits; a second launch,
+//   * Split path (few units): nsplit blocks per unit (one-wave blocks for short
+//     bf16 d=128 slices) each stream a slice of the slots and write (max, sum,
+//     o) partials and their logits; a second launch,
 //     one block per unit, merges the partials and runs the score pass.  The
 //     launch boundary orders the two: no block waits for another and no
 //     device-scope fence is needed (on gfx950 each such fence writes back and
@@ -59,6 +60,11 @@ constexpr int kUnrollFew = 4;
 // 1310 -> 1276 us).  At k <= kSmallK or with few units it is slower.
 constexpr int kWaveThreads = 64;
 constexpr int kWaveUnroll = 8;
+// The split path's partial blocks for bf16 d=128 are one-wave blocks too when
+// each block's slice of slots is short (32 units x 2048 slots, with the finish
+// launch, per step: slices of 64 slots 16.0 -> 15.1 us, of 128 16.6 -> 16.4 us;
+// with slices of 256 the 256-thread blocks stay faster, 19.4 against 21.1 us).
+constexpr int kWaveSplitLen = 128;
 constexpr int kPrefetch = 2;  // score-pass slots per thread whose metadata is loaded up front
 constexpr uint64_t kNoKey = ~0ull;
 constexpr int kNewSlot = -2;
@@ -551,7 +557,13 @@ hipError_t launch_typed(const DecodeArgs& a, int units, hipStream_t s) {
     else
       hipLaunchKernelGGL((decode_kernel<T, D, false, ROPE>), dim3(units), dim3(kThreads), shm, s, a);
   } else {
-    hipLaunchKernelGGL((decode_kernel<T, D, true, ROPE>), dim3(units * a.nsplit), dim3(kThreads), 0, s, a);
+    bool wave_blocks = false;
+    if constexpr (std::is_same<T, bf16_t>::value && D == 128 && !ROPE) wave_blocks = a.split_len <= kWaveSplitLen;
+    if (wave_blocks)
+      hipLaunchKernelGGL((decode_kernel<T, D, true, ROPE, kWaveThreads, kWaveUnroll>), dim3(units * a.nsplit),
+                         dim3(kWaveThreads), 0, s, a);
+    else
+      hipLaunchKernelGGL((decode_kernel<T, D, true, ROPE>), dim3(units * a.nsplit), dim3(kThreads), 0, s, a);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((decode_finish<T, D>), dim3(units), dim3(kFinishThreads), 0, s, a);

@@ -2,7 +2,8 @@
 largest budget (k = 12288 slots) on the split path and on the single-block
 path, head_dim 64 at the benchmark's full launch shape, small budgets over
 many units (the 128-thread decode blocks) for both storage types and head sizes,
-and larger bf16 budgets over many units (the one-wave decode blocks).  Inputs come from
+larger bf16 budgets over many units (the one-wave decode blocks) and short split
+slices (the one-wave partial blocks).  Inputs come from
 the device-side generator; the oracle reads the sampled units' inputs back from
 those tensors and runs each unit in full."""
 import numpy as np
@@ -180,3 +181,17 @@ def test_one_wave_blocks_cache_filling():
     g = _run(w, [(0, 0), (9, 21), (31, 31)], 140)
     ev = g["evicted"]
     assert (ev[: 200 - 100] == -1).all() and (ev[200 - 100:] >= 0).all()
+
+
+@pytest.mark.parametrize("batch,heads,L,T,heavy,recent", [
+    (1, 8, 1500, 40, 512, 512),   # 8 units: 16 slices of 64 slots per unit
+    (1, 8, 700, 60, 512, 512),    # the cache fills during decode: 10 slices of 70-76 slots
+    (4, 64, 600, 30, 256, 256),   # 256 units: 4 slices of 128 slots, the longest on one-wave blocks
+])
+def test_one_wave_split_blocks(batch, heads, L, T, heavy, recent):
+    # the split path's partial blocks for bf16 d=128 with short slices run one wave each
+    w = scaled(get("opt6.7b-layer-b16"), layers=1, batch=batch, heads=heads, prompt_len=L, decode_steps=T,
+               heavy_budget=heavy, recent_budget=recent, n_anchors=6)
+    rng = np.random.default_rng(L + heads)
+    idx = rng.choice(w.batch * w.heads, size=2, replace=False)
+    _run(w, [(int(i) // w.heads, int(i) % w.heads) for i in sorted(idx)], T)
