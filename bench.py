@@ -334,7 +334,7 @@ def main():
                 kf = torch.cat([pre[l][1][b, h], dec[l][1][:, b, h]]).float().cpu().numpy()
                 vf = torch.cat([pre[l][2][b, h], dec[l][2][:, b, h]]).float().cpu().numpy()
             samples.append((qf, kf, vf, L, w.heavy_budget, w.recent_budget, a.variant, pattern,
-                            (a.rope, w.dtype) if a.rope else None))
+                            (a.rope,) if a.rope else None))
         procs = min(len(os.sched_getaffinity(0)), 16, len(samples))
         os.environ.setdefault("OMP_NUM_THREADS", "1")
         os.environ.setdefault("OPENBLAS_NUM_THREADS", "1")

@@ -106,13 +106,6 @@ def prefill_output(Q: np.ndarray, K: np.ndarray, V: np.ndarray, scale: float) ->
 
 
 # =============================================================================== position rolling
-def _round_bf16(x: np.ndarray) -> np.ndarray:
-    """Round float32 values to the nearest bfloat16 (ties to even), as float32."""
-    b = np.ascontiguousarray(x, np.float32).view(np.uint32)
-    b = (b + np.uint32(0x7FFF) + ((b >> np.uint32(16)) & np.uint32(1))) & np.uint32(0xFFFF0000)
-    return b.view(np.float32)
-
-
 @dataclass(frozen=True)
 class Rope:
     """Rotary position embedding applied at positions inside the cache ("position
@@ -126,20 +119,17 @@ class Rope:
     0, 1, ... in position order, so the new token sits at the last one and a
     cached entry's rotation depends on how many entries lie between; the cache
     keeps keys unrotated.  The prompt is attended before anything is evicted, so
-    its positions are its ranks.  The prompt's rotated queries and keys are the
-    operands of the score products and are rounded to the storage type
-    (``storage``: "bf16" or "f32"), each rotation computed in float32 from
-    float32 cosines and sines as x*c - y*s and x*s + y*c; decode rotations are
-    exact."""
+    its positions are its ranks.  Every rotation here is exact (float64), for the
+    prompt's score operands as for the decode steps."""
 
     base: float = 10000.0
-    storage: str = "f32"
 
     def theta(self, d: int) -> np.ndarray:
         return float(self.base) ** (-2.0 * np.arange(d // 2) / d)
 
     def rotate(self, X: np.ndarray, pos) -> np.ndarray:
-        """Exact rotation of the rows of X [n, d] to positions ``pos`` [n]."""
+        """Exact rotation of the rows of X [n, d] to positions ``pos`` [n]: each
+        pair (x_m, x_{m+d/2}) turns by the angle pos * theta_m."""
         X = np.asarray(X, np.float64)
         h = X.shape[1] // 2
         ang = np.asarray(pos, np.float64)[:, None] * self.theta(X.shape[1])[None, :]
@@ -148,16 +138,10 @@ class Rope:
         return np.concatenate([x * c - y * s, x * s + y * c], axis=1)
 
     def prompt(self, X: np.ndarray) -> np.ndarray:
-        """Rows of X [L, d] rotated to positions 0..L-1 in float32 and rounded to
-        the storage type (the prompt's score operands)."""
-        X32 = np.asarray(X, np.float32)
-        L, d = X32.shape
-        h = d // 2
-        ang = np.arange(L, dtype=np.float64)[:, None] * self.theta(d)[None, :]
-        c, s = np.cos(ang).astype(np.float32), np.sin(ang).astype(np.float32)
-        x, y = X32[:, :h], X32[:, h:]
-        out = np.concatenate([x * c - y * s, x * s + y * c], axis=1).astype(np.float32)
-        return (_round_bf16(out) if self.storage == "bf16" else out).astype(np.float64)
+        """Rows of X [L, d] rotated to their own positions 0..L-1 (the prompt's
+        score operands), exactly."""
+        X = np.asarray(X, np.float64)
+        return self.rotate(X, np.arange(X.shape[0]))
 
 
 @dataclass(frozen=True)
@@ -291,8 +275,8 @@ class UnitCache:
         ``fixed``: scores for every position of the sequence, fixed in advance
         (the global comparator).  The prompt is then ranked by ``fixed[:L]``
         instead of its own column sums, and decode steps add nothing.  ``rope``:
-        the prompt is scored on its rotated (and storage-rounded) queries and
-        keys; the cache keeps the keys unrotated."""
+        the prompt is scored on its rotated queries and keys; the cache keeps
+        the keys unrotated."""
         Qp, Kp, Vp = (np.asarray(x, np.float64) for x in (Qp, Kp, Vp))
         L, d = Kp.shape if Kp.ndim == 2 else (0, Qp.shape[-1])
         scale = default_scale(d) if scale is None else scale

@@ -38,7 +38,7 @@ def check_unit(p: dict) -> dict:
     sequence) or "fixed" (scores ``p["fixed"]`` given to both sides, so every
     decision must agree exactly, with no near-tie adoption).  ``p["pattern"]``:
     (kind, period, width) of a sparse pattern kept before heavy hitters;
-    ``p["rope"]``: (base, storage) of the rotary embedding at positions inside
+    ``p["rope"]``: (base,) of the rotary embedding at positions inside
     the cache; ``p["scale"]``: the logit scale when not 1/sqrt(d)."""
     tag = p["tag"]
     mode = p.get("mode", "local")

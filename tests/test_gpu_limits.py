@@ -94,7 +94,7 @@ def test_small_budget_blocks_with_variants(variant):
     extra, fixed = {}, None
     if variant == "rope":
         g = run_gpu(q, k, v, L, heavy, recent, "bf16", out_units=units, rope_base=10000.0)
-        extra = {"rope": (10000.0, "bf16")}
+        extra = {"rope": (10000.0,)}
     elif variant == "pattern":
         g = run_gpu(q, k, v, L, heavy, recent, "bf16", out_units=units, pattern=("strided", 8, 1))
         extra = {"pattern": ("strided", 8, 1)}
@@ -151,7 +151,7 @@ def test_one_wave_blocks_with_variants(variant):
     extra, fixed = {}, None
     if variant == "rope":
         g = run_gpu(q, k, v, L, heavy, recent, "bf16", out_units=units, rope_base=10000.0)
-        extra = {"rope": (10000.0, "bf16")}
+        extra = {"rope": (10000.0,)}
     elif variant == "pattern":
         g = run_gpu(q, k, v, L, heavy, recent, "bf16", out_units=units, pattern=("fixed", 16, 2))
         extra = {"pattern": ("fixed", 16, 2)}

@@ -28,7 +28,7 @@ def _check(g, w, Q, K, V, base, **extra):
     for b in range(w.batch):
         for h in range(w.heads):
             pl = unit_payload(g, b, h, Q[b, h], K[b, h], V[b, h], w.prompt_len, w.heavy_budget, w.recent_budget)
-            pl.update(rope=(base, w.dtype), **{k: (v[b, h] if isinstance(v, np.ndarray) else v)
+            pl.update(rope=(base,), **{k: (v[b, h] if isinstance(v, np.ndarray) else v)
                                                 for k, v in extra.items()})
             payloads.append(pl)
     results, bad = check_payloads(payloads)

@@ -91,6 +91,12 @@ MUTATIONS = {
         "rank[:] = G_pos - G_pos.max() + len(G_pos) - 1"),
     "rotation sign flipped": ("return np.concatenate([x * c - y * s, x * s + y * c], axis=1)\n",
                               "return np.concatenate([x * c + y * s, -x * s + y * c], axis=1)\n"),
+    "rotation pairs adjacent elements": ("x, y = X[:, :h], X[:, h:]", "x, y = X[:, 0::2], X[:, 1::2]"),
+    "prompt rotated to reversed positions": ("return self.rotate(X, np.arange(X.shape[0]))",
+                                             "return self.rotate(X, np.arange(X.shape[0])[::-1])"),
+    "prompt rotation order swapped": ("return self.rotate(X, np.arange(X.shape[0]))",
+                                      "return np.roll(self.rotate(np.roll(X, X.shape[1] // 2, axis=1), "
+                                      "np.arange(X.shape[0])), X.shape[1] // 2, axis=1)"),
     "new token one position late": ("qr = self.rope.rotate(q[None], [len(G_pos) - 1])[0]",
                                     "qr = self.rope.rotate(q[None], [len(G_pos)])[0]"),
     "prompt scored unrotated": ("prefill_scores(rope.prompt(Qp), rope.prompt(Kp), scale)",
@@ -176,7 +182,9 @@ def _checks(m):
         np.testing.assert_allclose(res["out"], ref[10:], rtol=1e-10, atol=1e-10)
         lib = _library_causal_weights(_complex_rope(Q[:10], np.arange(10), base),
                                       _complex_rope(K[:10], np.arange(10), base)).sum(axis=0)
-        np.testing.assert_allclose(res["prefill"].col_sum, lib, rtol=2e-5)
+        np.testing.assert_allclose(res["prefill"].col_sum, lib, rtol=1e-10)
+        np.testing.assert_allclose(m.Rope(base).prompt(Q), _complex_rope(Q, np.arange(N), base), rtol=1e-12,
+                                   atol=1e-12)
         L, T, h, r = 30, 40, 6, 5
         Q, K, V = (g.standard_normal((L + T, d)) for _ in range(3))
         sc = g.permutation(L + T).astype(float)

@@ -558,27 +558,12 @@ def test_rope_scores_depend_on_position_gaps_only():
         assert abs((r.rotate(q, [40 + t]) @ r.rotate(k, [17 + t]).T).item() - base) < 1e-10
 
 
-def test_bf16_rounding_matches_torch():
-    g = np.random.default_rng(52)
-    x = np.concatenate([g.standard_normal(1000).astype(np.float32),
-                        np.array([1 + 2 ** -8, 1 + 3 * 2 ** -8, -(1 + 2 ** -8), 1 + 2 ** -9], np.float32)])
-    from oracle.h2o_oracle import _round_bf16
-    ref = torch.from_numpy(x).to(torch.bfloat16).to(torch.float32).numpy()
-    assert np.array_equal(_round_bf16(x), ref)
-
-
-@pytest.mark.parametrize("storage", ["f32", "bf16"])
-def test_rope_prompt_operands(storage):
-    # the prompt's rotated operands: the exact rotation, rounded (float32, then bf16)
+def test_rope_prompt_operands():
+    # the prompt's rotated operands are the exact rotation to positions 0..L-1
     g = np.random.default_rng(53)
     X = g.standard_normal((300, 64)).astype(np.float32)
-    got = Rope(10000.0, storage).prompt(X)
-    exact = _complex_rope(X, np.arange(300))
-    tol = 2 ** -8 if storage == "bf16" else 1e-6
-    assert np.all(np.abs(got - exact) <= tol * np.abs(exact) + 1e-6)
-    if storage == "bf16":
-        assert np.array_equal(got.astype(np.float32), torch.from_numpy(got.astype(np.float32)).to(
-            torch.bfloat16).float().numpy())
+    got = Rope(10000.0).prompt(X)
+    np.testing.assert_allclose(got, _complex_rope(X, np.arange(300)), rtol=1e-12, atol=1e-12)
 
 
 @pytest.mark.parametrize("L,T,heavy,recent", [(12, 20, 40, 40), (0, 25, 30, 30)])
@@ -631,6 +616,6 @@ def test_rope_rolling_with_heavy_hitters_by_enumeration(L, T, heavy, recent):
 def test_rope_prompt_column_sums_match_library():
     L, d = 64, 16
     Q, K, _ = _rand(L, d, 57)
-    res = run_unit(Q, K, K, L, 8, 8, rope=Rope(10000.0, "f32"))
+    res = run_unit(Q, K, K, L, 8, 8, rope=Rope(10000.0))
     lib = _library_causal_weights(_complex_rope(Q, np.arange(L)), _complex_rope(K, np.arange(L))).sum(axis=0)
-    np.testing.assert_allclose(res["prefill"].col_sum, lib, rtol=2e-5)
+    np.testing.assert_allclose(res["prefill"].col_sum, lib, rtol=1e-10)
