@@ -88,11 +88,14 @@ typedef struct {
  * 0, 1, ... in order of their text positions, the new token the last one, so a
  * logit depends on how many entries lie between query and key rather than on
  * their distance in the text.  The prompt, attended before anything is
- * evicted, is rotated to its own positions 0..L-1; its rotated queries and keys
- * are rounded to the cache dtype (the operands of the score products), each
- * computed in float32 as x*c - y*s and x*s + y*c from float32 cosines and sines
- * of double-precision angles.  Decode rotations are done in float32 without
- * rounding.  rope_base must be finite and >= 0. */
+ * evicted, is rotated to its own positions 0..L-1: each rotated value is
+ * computed in float32 (x*c - y*s, x*s + y*c from float32 cosines and sines of
+ * double-precision angles) and, for bf16 caches, carried into the score
+ * products as two bf16 parts hi = bf16(v), lo = bf16(v - hi) (three products
+ * per pair of operands), so the prompt's scores follow the exact rotation to
+ * fp32-level error.  The prompt is rotated chunk by chunk of units into a
+ * scratch area of at most 512 MiB (or 8 units, if larger).  Decode rotations
+ * are done in float32 without rounding.  rope_base must be finite and >= 0. */
 /* The budget is k = K_h + K_r >= 1 (Report §3.1: k < n cached tokens).
  * B*H*max(k, max_prompt) must stay below 2^31, and one unit's prompt matrix,
  * max_prompt*d*sizeof(dtype), below 2^32 bytes. */
@@ -162,7 +165,9 @@ h2o_status h2o_decode_step(h2o_cache* cache, const void* q, const void* k, const
 /* Copy the cache contents to host memory; synchronises `stream` first and
  * reports any earlier asynchronous fault.  Every pointer is host and nullable.
  *   pos:     [B, H, k] int32, the position held by each slot, -1 for empty slots
- *   score:   [B, H, k] float32, the accumulated score of each slot
+ *   score:   [B, H, k] float32, the accumulated score of each slot: the
+ *            device keeps it as a Kahan pair (sum s, compensation c), and the
+ *            value written here is s - c rounded to float32
  *   k_slots, v_slots: [B, H, k, d] in the cache dtype
  *   meta:    int32[2] = {entries cached per unit, next position}
  * Slot order within a unit carries no meaning; compare by position.

@@ -41,8 +41,9 @@ struct h2o_cache {
   float* col_sum;
   // position rolling (rope_base > 0), else null
   int32_t* rank;   // [units, kstride] position of each slot among the cached entries
-  void* qrot;      // [units, lpad_cap, d] the prompt's rotated queries (cache dtype)
-  void* krot;      // [units, lpad_cap, d] the prompt's rotated keys
+  int32_t rope_units;  // units whose prompt is rotated and scored per pass
+  void* rope_ops;  // the rotated prompt of rope_units units: fp32 q, k [rope_units, lpad_cap, d] each;
+                   // bf16 q hi, q lo, k hi, k lo [rope_units, lpad_cap, d] each
   float* rope_cs;  // [lpad_cap, d/2] (cos, sin) of position p * theta_m
   float* rope_th;  // [d/2] (hi, lo): theta_m / (2 pi) split so that n * hi is exact
 };
@@ -58,6 +59,10 @@ constexpr int32_t kSplitUnits = 512;
 constexpr int32_t kMaxSplit = 64;
 constexpr int32_t kMinSlotsPerSplit = 64;
 constexpr float kLog2e = 1.4426950408889634f;
+// Position rolling rotates the prompt into scratch chunk by chunk of units; the
+// chunk is sized so the scratch stays under this many bytes (and at least 8
+// units: one per XCD).
+constexpr size_t kRopeScratchBytes = size_t{512} << 20;
 
 thread_local std::string g_err;
 
@@ -102,7 +107,7 @@ int32_t round32(int32_t n) { return (n + 31) / 32 * 32; }
 
 struct Sizes {
   size_t kv, meta, split, prefill, rope, total;
-  int32_t max_split, lpad;
+  int32_t max_split, lpad, rope_units;
 };
 
 h2o_status check_params(const h2o_params* p, Sizes* sz) {
@@ -138,10 +143,15 @@ h2o_status check_params(const h2o_params* p, Sizes* sz) {
                     : 0;
     sz->lpad = round32(p->max_prompt);
     sz->prefill = 2 * u * static_cast<size_t>(sz->lpad) * 4;
-    // position rolling: slot ranks, the prompt's rotated q/k, cos/sin per prompt
-    // position and pair, per-pair frequencies (two floats)
+    // position rolling: slot ranks, the rotated prompt of a chunk of units (8
+    // bytes per element: fp32 q and k, or bf16 hi and lo of each), cos/sin per
+    // prompt position and pair, per-pair frequencies (two floats)
+    const size_t per_unit = static_cast<size_t>(sz->lpad) * d * 8;
+    sz->rope_units = per_unit == 0 ? static_cast<int32_t>(units)
+                                   : static_cast<int32_t>(std::min<size_t>(
+                                         u, std::max<size_t>(8, kRopeScratchBytes / per_unit)));
     sz->rope = p->rope_base > 0.f ? u * static_cast<size_t>(round32(static_cast<int32_t>(k))) * 4 +
-                                        2 * u * static_cast<size_t>(sz->lpad) * d * es +
+                                        static_cast<size_t>(sz->rope_units) * per_unit +
                                         static_cast<size_t>(sz->lpad) * (d / 2) * 8 + (d / 2) * 8
                                   : 0;
     sz->total = sz->kv + sz->meta + sz->split + sz->prefill + sz->rope;
@@ -151,7 +161,7 @@ h2o_status check_params(const h2o_params* p, Sizes* sz) {
 
 void free_all(h2o_cache* c) {
   void* ptrs[] = {c->kslots, c->vslots, c->score, c->comp, c->pos, c->part, c->logits,
-                  c->row_lse2, c->col_sum, c->rank, c->qrot, c->krot, c->rope_cs, c->rope_th};
+                  c->row_lse2, c->col_sum, c->rank, c->rope_ops, c->rope_cs, c->rope_th};
   for (void* q : ptrs)
     if (q != nullptr) (void)hipFree(q);
 }
@@ -183,12 +193,45 @@ hipError_t upload_rope_tables(h2o_cache* c, float base) {
   return e;
 }
 
-// The prompt's queries and keys rotated to positions 0..n-1 into the cache's
-// scratch (n <= max_prompt).
-hipError_t rotate_prompt(h2o_cache* c, const void* q, const void* k, int32_t n, hipStream_t s) {
-  hipError_t e = h2o::launch_rope_prompt(c->p.dtype, c->d, q, c->qrot, n, c->units, c->rope_cs, s);
-  if (e == hipSuccess) e = h2o::launch_rope_prompt(c->p.dtype, c->d, k, c->krot, n, c->units, c->rope_cs, s);
-  return e;
+// The prompt's score passes (row normalisers, column sums and, when a.out is
+// set, the prompt's own output) over rows 0..a.L-1 of q and k.  With position
+// rolling the prompt is first rotated to positions 0..L-1, a chunk of units at a
+// time, into the cache's scratch (bf16: as hi and lo parts), and each chunk is
+// scored from there.
+hipError_t score_prompt(h2o_cache* c, h2o::PrefillArgs a, hipStream_t s) {
+  a.stages = h2o::kStageScores;
+  if (c->rank == nullptr) return h2o::launch_prefill(c->p.dtype, c->d, a, c->units, s);
+  const size_t elems = static_cast<size_t>(a.L) * c->d;  // elements per unit of q, k, v and out
+  const size_t cap = static_cast<size_t>(c->rope_units) * c->lpad_cap * c->d;  // elements per scratch array
+  char* ops = static_cast<char*>(c->rope_ops);
+  const bool bf16 = c->p.dtype == H2O_BF16;
+  // bf16: q hi, q lo, k hi, k lo; fp32: q, k
+  void* qh = ops;
+  void* ql = bf16 ? ops + cap * 2 : nullptr;
+  void* kh = ops + cap * 4;
+  void* kl = bf16 ? ops + cap * 6 : nullptr;
+  const char* q = static_cast<const char*>(a.q);
+  const char* k = static_cast<const char*>(a.k);
+  for (int32_t u0 = 0; u0 < c->units; u0 += c->rope_units) {
+    const int32_t nu = std::min(c->rope_units, c->units - u0);
+    const size_t off = static_cast<size_t>(u0) * elems;
+    hipError_t e = h2o::launch_rope_prompt(c->p.dtype, c->d, q + off * c->esize, qh, ql, a.L, nu, c->rope_cs, s);
+    if (e == hipSuccess)
+      e = h2o::launch_rope_prompt(c->p.dtype, c->d, k + off * c->esize, kh, kl, a.L, nu, c->rope_cs, s);
+    if (e != hipSuccess) return e;
+    h2o::PrefillArgs b = a;
+    b.q = qh;
+    b.k = kh;
+    b.q_lo = ql;
+    b.k_lo = kl;
+    b.v = a.v != nullptr ? static_cast<const char*>(a.v) + off * c->esize : nullptr;
+    b.out = a.out != nullptr ? a.out + off : nullptr;
+    b.row_lse2 = a.row_lse2 + static_cast<size_t>(u0) * a.Lpad;
+    b.col_sum = a.col_sum + static_cast<size_t>(u0) * a.Lpad;
+    e = h2o::launch_prefill(c->p.dtype, c->d, b, nu, s);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 int choose_nsplit(const h2o_cache* c, int32_t count, int32_t* split_len) {
@@ -271,6 +314,7 @@ h2o_status h2o_cache_create(const h2o_params* params, int device, h2o_cache** ou
   c->lpad_cap = sz.lpad;
   c->lpad_last = 0;
   c->max_split = sz.max_split;
+  c->rope_units = sz.rope_units;
 
   const size_t u = c->units, kk = c->k, d = c->d;
   const bool rope = params->rope_base > 0.f;
@@ -288,8 +332,7 @@ h2o_status h2o_cache_create(const h2o_params* params, int device, h2o_cache** ou
       {reinterpret_cast<void**>(&c->row_lse2), u * c->lpad_cap * 4},
       {reinterpret_cast<void**>(&c->col_sum), u * c->lpad_cap * 4},
       {reinterpret_cast<void**>(&c->rank), rope ? u * c->kstride * 4 : 0},
-      {&c->qrot, rope ? u * c->lpad_cap * d * c->esize : 0},
-      {&c->krot, rope ? u * c->lpad_cap * d * c->esize : 0},
+      {&c->rope_ops, rope ? static_cast<size_t>(c->rope_units) * c->lpad_cap * d * 8 : 0},
       {reinterpret_cast<void**>(&c->rope_cs), rope ? static_cast<size_t>(c->lpad_cap) * (d / 2) * 8 : 0},
       {reinterpret_cast<void**>(&c->rope_th), rope ? (d / 2) * 8 : 0},
   };
@@ -351,12 +394,6 @@ h2o_status h2o_prefill(h2o_cache* c, const void* q, const void* k, const void* v
     a.rank = c->rank;
     a.L = L;
     a.Lpad = round32(L);
-    if (c->rank != nullptr) {  // position rolling: score the prompt on its rotated q/k
-      const hipError_t er = rotate_prompt(c, q, k, L, s);
-      if (er != hipSuccess) return hip_fail(er, "rotary embedding launch");
-      a.q = c->qrot;
-      a.k = c->krot;
-    }
     a.row_lse2 = c->row_lse2;
     a.col_sum = c->col_sum;
     a.out = out;
@@ -375,7 +412,14 @@ h2o_status h2o_prefill(h2o_cache* c, const void* q, const void* k, const void* v
     a.kv_rows = L;
     a.scale = c->scale;
     a.c2 = c->c2;
-    const hipError_t e = h2o::launch_prefill(c->p.dtype, c->d, a, c->units, s);
+    hipError_t e;
+    if (c->rank != nullptr) {  // position rolling: the prompt is scored on its rotated q/k
+      e = score_prompt(c, a, s);
+      a.stages = h2o::kStageSelect;
+      if (e == hipSuccess) e = h2o::launch_prefill(c->p.dtype, c->d, a, c->units, s);
+    } else {
+      e = h2o::launch_prefill(c->p.dtype, c->d, a, c->units, s);
+    }
     if (e != hipSuccess) return hip_fail(e, "prefill launch");
     c->lpad_last = a.Lpad;
   }
@@ -404,12 +448,6 @@ h2o_status h2o_column_scores(h2o_cache* c, const void* q, const void* k, int32_t
   a.q = q;
   a.k = k;
   a.L = n;
-  if (c->rank != nullptr) {  // position rolling: the sequence's own positions
-    const hipError_t er = rotate_prompt(c, q, k, n, s);
-    if (er != hipSuccess) return hip_fail(er, "rotary embedding launch");
-    a.q = c->qrot;
-    a.k = c->krot;
-  }
   a.Lpad = round32(n);
   a.row_lse2 = c->row_lse2;
   a.col_sum = c->col_sum;
@@ -417,7 +455,7 @@ h2o_status h2o_column_scores(h2o_cache* c, const void* q, const void* k, int32_t
   a.c2 = c->c2;
   a.kcap = c->k;
   a.kstride = c->kstride;
-  hipError_t e = h2o::launch_prefill(c->p.dtype, c->d, a, c->units, s);
+  hipError_t e = score_prompt(c, a, s);  // position rolling: at the sequence's own positions
   if (e != hipSuccess) return hip_fail(e, "column score launch");
   c->stats_valid = false;  // the prefill scratch now holds this sequence's statistics
   e = hipMemcpy2DAsync(scores, static_cast<size_t>(n) * 4, c->col_sum, static_cast<size_t>(a.Lpad) * 4,
@@ -560,9 +598,16 @@ h2o_status h2o_cache_read(h2o_cache* c, int32_t* pos, float* score, void* k_slot
   if (pos != nullptr &&
       (e = hipMemcpy2D(pos, row, c->pos, pitch, row, c->units, hipMemcpyDeviceToHost)) != hipSuccess)
     return hip_fail(e, "copy pos");
-  if (score != nullptr &&
-      (e = hipMemcpy2D(score, row, c->score, pitch, row, c->units, hipMemcpyDeviceToHost)) != hipSuccess)
-    return hip_fail(e, "copy score");
+  if (score != nullptr) {
+    // the Kahan pair (running sum s, compensation c) folded into one value: the
+    // sum of the added weights is s - c
+    std::vector<float> comp(n);
+    if ((e = hipMemcpy2D(score, row, c->score, pitch, row, c->units, hipMemcpyDeviceToHost)) != hipSuccess ||
+        (e = hipMemcpy2D(comp.data(), row, c->comp, pitch, row, c->units, hipMemcpyDeviceToHost)) != hipSuccess)
+      return hip_fail(e, "copy score");
+    for (size_t i = 0; i < n; ++i)
+      score[i] = static_cast<float>(static_cast<double>(score[i]) - static_cast<double>(comp[i]));
+  }
   const size_t kvb = n * c->d * c->esize;
   if (k_slots != nullptr && (e = hipMemcpy(k_slots, c->kslots, kvb, hipMemcpyDeviceToHost)) != hipSuccess)
     return hip_fail(e, "copy k slots");

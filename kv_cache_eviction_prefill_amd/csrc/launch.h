@@ -49,6 +49,8 @@ struct PrefillArgs {
   const void* q;  // [units, L, d]
   const void* k;  // [units, L, d]
   const void* v;  // [units, L, d]
+  const void* q_lo;  // bf16 position rolling: [units, L, d] lo parts of the rotated q (q holds the hi
+  const void* k_lo;  // parts), likewise for k; nullptr otherwise
   int32_t L;
   int32_t Lpad;       // stride of the per-row scratch arrays (multiple of 32, >= L)
   float* row_lse2;    // [units, Lpad] log2 sum_j exp2(c2 q_r.k_j) of each row; 0 past L
@@ -76,8 +78,10 @@ struct PrefillArgs {
 hipError_t launch_prefill(int dtype, int head_dim, const PrefillArgs& a, int units, hipStream_t s);
 
 // Rotary embedding of a prompt: rows r of x [units, L, d] rotated to position r
-// into y (same layout), from the (cos, sin) table [>= L, d/2].
-hipError_t launch_rope_prompt(int dtype, int head_dim, const void* x, void* y, int32_t L, int units,
+// into y (same layout), from the (cos, sin) table [>= L, d/2].  bf16: y receives
+// bf16(v) and y_lo bf16(v - bf16(v)) of each rotated value v; fp32: y receives v
+// and y_lo is unused.
+hipError_t launch_rope_prompt(int dtype, int head_dim, const void* x, void* y, void* y_lo, int32_t L, int units,
                               const float* cs, hipStream_t s);
 
 // Mark every slot empty (pos = -1, score = comp = 0).

@@ -32,6 +32,7 @@
 // and one add on the common path.  Overlap of the matrix cores with the VALU
 // needs several waves per SIMD: registers are kept to 128 (4 waves per SIMD).
 #include <cmath>
+#include <type_traits>
 
 #include "h2o_device.h"
 #include "launch.h"
@@ -64,10 +65,23 @@ __device__ inline int lane_id_here() {
 // XCD (blocks are dealt to the 8 XCDs round-robin) and walk the streamed tiles in
 // the same order (pass 1 upwards from key 0, pass 2 downwards from the last
 // query), so each tile is fetched once into that XCD's L2 and shared.
-constexpr int kBlockRows = 256;
-constexpr int kWaveRows = 64;
 constexpr int kXcds = 8;
 constexpr int kBufs = 3;
+
+// Operands of the score products.  Plain: the bf16 inputs, two 32-row subtiles
+// per wave.  Split (position rolling): a rotated row is no longer a bf16 value,
+// so it arrives as two bf16 rows hi = bf16(x), lo = bf16(x - hi) (x to about
+// 2^-17 relative) and every logit takes three products hi.hi + hi.lo + lo.hi
+// (lo.lo, below 2^-16 of each term, is left out); the wave keeps hi and lo of
+// one 32-row subtile in the registers two subtiles take otherwise, and each
+// streamed tile carries its hi rows, then its lo rows.
+template <bool SPLIT>
+struct Pass {
+  static constexpr int NS = SPLIT ? 1 : 2;  // 32-row subtiles per wave
+  static constexpr int NA = SPLIT ? 2 : 1;  // bf16 arrays per operand (hi, lo)
+  static constexpr int kWaveRows = 32 * NS;
+  static constexpr int kBlockRows = 4 * kWaveRows;
+};
 
 template <int D>
 struct Tile {
@@ -175,10 +189,10 @@ __device__ inline void row_frag(const bf16_t* base, int row, int L, int lane, bf
 // Wait here (once per row block) for the register operand, so the compiler leaves
 // no wait for it inside the tile loop, where it would also wait for the tiles in
 // flight.
-template <int D>
-__device__ inline void settle(bf16x8 (&f)[2][D / 16]) {
+template <int D, int NS>
+__device__ inline void settle(bf16x8 (&f)[NS][D / 16]) {
 #pragma unroll
-  for (int s = 0; s < 2; ++s)
+  for (int s = 0; s < NS; ++s)
 #pragma unroll
     for (int kk = 0; kk < D / 16; ++kk) asm volatile("" : "+v"(f[s][kk]));
 }
@@ -204,6 +218,23 @@ __device__ inline void tile_mfma(uint32_t fb, const bf16x8 (&b)[2][D / 16], floa
     __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
   }
   __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+}
+
+// Split operands: the S tile of one 32-row subtile (register hi `bh`, lo `bl`)
+// against the LDS tile whose hi rows are at `fb` and lo rows at `fbl`:
+// hi.hi in one accumulator, hi.lo + lo.hi in another (3 x D/16 MFMAs).
+template <int D>
+__device__ inline floatx16 tile_mfma_split(uint32_t fb, uint32_t fbl, const bf16x8 (&bh)[D / 16],
+                                           const bf16x8 (&bl)[D / 16]) {
+  floatx16 a0 = {}, a1 = {};
+#pragma unroll
+  for (int kk = 0; kk < D / 16; ++kk) {
+    const bf16x8 th = tile_frag_kk(fb, kk), tl = tile_frag_kk(fbl, kk);
+    a0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(th, bh[kk], a0, 0, 0, 0);
+    a1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(th, bl[kk], a1, 0, 0, 0);
+    a1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tl, bh[kk], a1, 0, 0, 0);
+  }
+  return a0 + a1;
 }
 
 // exp2(v_i * c + b) for the 16 logits of a lane, and their sum as four
@@ -269,48 +300,68 @@ __device__ inline float row_update(const floatx16& s, float c2, int lane, float&
 // kept by row_update against a lazily moved offset: the common tile costs one
 // fma, one exp and one add per logit.  The pass with the attention output runs
 // the same per-query arithmetic, so both give the same normalisers bit for bit.
-template <int D>
-__global__ __launch_bounds__(kThreads, 4) void rowstats_bf16(PrefillArgs a, int nblk, int units) {
+template <int D, bool SPLIT>
+__global__ __launch_bounds__(kThreads, SPLIT ? 3 : 4) void rowstats_bf16(PrefillArgs a, int nblk, int units) {
   using T = Tile<D>;
-  __shared__ __align__(256) unsigned char sK[kBufs][T::kBytes];
+  using P = Pass<SPLIT>;
+  constexpr int NS = P::NS, NA = P::NA;
+  __shared__ __align__(256) unsigned char sK[kBufs][NA * T::kBytes];
   const int npair = (nblk + 1) / 2;
   int unit, pb;
   if (!block_coords(npair, units, &unit, &pb)) return;
   const int L = a.L;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave), lane = threadIdx.x % kWave;
   const int fr = lane & 31;
-  const bf16_t* Qu = static_cast<const bf16_t*>(a.q) + static_cast<size_t>(unit) * L * D;
-  const bf16_t* Ku = static_cast<const bf16_t*>(a.k) + static_cast<size_t>(unit) * L * D;
+  const size_t uoff = static_cast<size_t>(unit) * L * D;
+  const bf16_t* Qu = static_cast<const bf16_t*>(a.q) + uoff;
+  const bf16_t* Ku = static_cast<const bf16_t*>(a.k) + uoff;
   const __amdgpu_buffer_rsrc_t rk = make_rsrc(Ku, static_cast<uint32_t>(L) * T::kRowBytes);
+  // split operands: the lo rows of q and k (unused otherwise)
+  const bf16_t* Ql = SPLIT ? static_cast<const bf16_t*>(a.q_lo) + uoff : Qu;
+  const __amdgpu_buffer_rsrc_t rkl =
+      SPLIT ? make_rsrc(static_cast<const bf16_t*>(a.k_lo) + uoff, static_cast<uint32_t>(L) * T::kRowBytes) : rk;
   const int voff = tile_voff<D>();
   const uint32_t xo = frag_offset<D>(lane);
   for (int h = 0; h < 2; ++h) {
     const int blk = h == 0 ? nblk - 1 - pb : pb;
     if (h == 1 && blk == nblk - 1 - pb) break;  // odd count: the middle block is alone
-    const int qb = blk * kBlockRows;
-    const int qw = qb + wave * kWaveRows;
-    const int ntile = (min(qb + kBlockRows, L) - 1) / kTile + 1;
+    const int qb = blk * P::kBlockRows;
+    const int qw = qb + wave * P::kWaveRows;
+    const int ntile = (min(qb + P::kBlockRows, L) - 1) / kTile + 1;
     if (h == 1) tile_barrier();  // the first row block's tiles are no longer read
-    bf16x8 bq[2][D / 16];
+    bf16x8 bq[NS][D / 16], bql[NS][D / 16];
 #pragma unroll
-    for (int s = 0; s < 2; ++s) row_frag<D>(Qu, qw + 32 * s + fr, L, lane, bq[s]);
-    tile_async(rk, voff, 0, sK[0], T::kRowBytes, T::kLoads);
-    if (ntile > 1) tile_async(rk, voff, kTile, sK[1], T::kRowBytes, T::kLoads);
-    settle<D>(bq);
-    float m[2] = {-1e30f, -1e30f}, l[2] = {0.f, 0.f};
+    for (int s = 0; s < NS; ++s) row_frag<D>(Qu, qw + 32 * s + fr, L, lane, bq[s]);
+    if constexpr (SPLIT) row_frag<D>(Ql, qw + fr, L, lane, bql[0]);
+    // the key rows t*32.. (hi, then lo when split) into buffer `buf`
+    auto issue = [&](int t, int buf) {
+      tile_async(rk, voff, t * kTile, sK[buf], T::kRowBytes, T::kLoads);
+      if constexpr (SPLIT) tile_async(rkl, voff, t * kTile, sK[buf] + T::kBytes, T::kRowBytes, T::kLoads);
+    };
+    issue(0, 0);
+    if (ntile > 1) issue(1, 1);
+    settle<D, NS>(bq);
+    if constexpr (SPLIT) settle<D, NS>(bql);
+    float m[NS], l[NS];
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      m[s] = -1e30f;
+      l[s] = 0.f;
+    }
     for (int t = 0; t < ntile; ++t) {
-      if (t + 1 < ntile) wait_vm<T::kLoads>();  // this tile landed; the next may be in flight
+      if (t + 1 < ntile) wait_vm<NA * T::kLoads>();  // this tile landed; the next may be in flight
       else wait_vm<0>();
       tile_barrier();
-      if (t + 2 < ntile) tile_async(rk, voff, (t + 2) * kTile, sK[(t + 2) % kBufs], T::kRowBytes, T::kLoads);
+      if (t + 2 < ntile) issue(t + 2, (t + 2) % kBufs);
       const int k0 = t * kTile;
-      if (qw < L && k0 <= qw + kWaveRows - 1) {
+      if (qw < L && k0 <= qw + P::kWaveRows - 1) {
         uint32_t fb = lds_addr(sK[t % kBufs]) + xo;
         asm volatile("" : "+v"(fb));  // keep the per-step offsets inside the loop
-        floatx16 acc[2];
-        tile_mfma<D>(fb, bq, acc);
+        floatx16 acc[NS];
+        if constexpr (SPLIT) acc[0] = tile_mfma_split<D>(fb, fb + T::kBytes, bq[0], bql[0]);
+        else tile_mfma<D>(fb, bq, acc);
 #pragma unroll
-        for (int s = 0; s < 2; ++s) {
+        for (int s = 0; s < NS; ++s) {
           if (k0 + kTile - 1 > qw + 32 * s) {  // diagonal tile: keys after the query leave the row
             const int ln = lane_id_here();  // re-read here: keeping it live across the loop spills
             const int rel = qw + 32 * s + (ln & 31) - k0 - 4 * (ln >> 5);
@@ -325,7 +376,7 @@ __global__ __launch_bounds__(kThreads, 4) void rowstats_bf16(PrefillArgs a, int 
     }
     // lanes l and l+32 hold the same queries over different key rows
 #pragma unroll
-    for (int s = 0; s < 2; ++s) {
+    for (int s = 0; s < NS; ++s) {
       const float lt = l[s] + __shfl_xor(l[s], 32, kWave);
       const int q = qw + 32 * s + lane;
       // rows L..Lpad-1 get 0 so pass 2 reads finite normalisers for its masked rows
@@ -338,11 +389,13 @@ __global__ __launch_bounds__(kThreads, 4) void rowstats_bf16(PrefillArgs a, int 
 // Pass 2: S = Q K^T per 32x32 tile, so a lane holds 16 query rows of one key
 // column; c_j accumulates exp2(S c2 - lse2_r) over the rows r >= j.  Query tiles
 // are walked from the last one down.  Each tile buffer carries the tile's 32 row
-// normalisers after its 32 rows (brought by lanes 0..7 of wave 0).
-template <int D>
-__global__ __launch_bounds__(kThreads, 4) void colsum_bf16(PrefillArgs a, int nblk, int units) {
+// normalisers after its rows (brought by lanes 0..7 of wave 0).
+template <int D, bool SPLIT>
+__global__ __launch_bounds__(kThreads, SPLIT ? 3 : 4) void colsum_bf16(PrefillArgs a, int nblk, int units) {
   using T = Tile<D>;
-  constexpr int kBufBytes = T::kBytes + 256;  // tile, normalisers, padding to 256 bytes
+  using P = Pass<SPLIT>;
+  constexpr int NS = P::NS, NA = P::NA;
+  constexpr int kBufBytes = NA * T::kBytes + 256;  // tile rows, normalisers, padding to 256 bytes
   __shared__ __align__(256) unsigned char sQ[kBufs][kBufBytes];
   const int npair = (nblk + 1) / 2;
   int unit, pb;
@@ -350,53 +403,63 @@ __global__ __launch_bounds__(kThreads, 4) void colsum_bf16(PrefillArgs a, int nb
   const int L = a.L;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave), lane = threadIdx.x % kWave;
   const int fr = lane & 31;
-  const bf16_t* Qu = static_cast<const bf16_t*>(a.q) + static_cast<size_t>(unit) * L * D;
-  const bf16_t* Ku = static_cast<const bf16_t*>(a.k) + static_cast<size_t>(unit) * L * D;
+  const size_t uoff = static_cast<size_t>(unit) * L * D;
+  const bf16_t* Qu = static_cast<const bf16_t*>(a.q) + uoff;
+  const bf16_t* Ku = static_cast<const bf16_t*>(a.k) + uoff;
   const float* lse = a.row_lse2 + static_cast<size_t>(unit) * a.Lpad;
   const __amdgpu_buffer_rsrc_t rq = make_rsrc(Qu, static_cast<uint32_t>(L) * T::kRowBytes);
   const __amdgpu_buffer_rsrc_t rl = make_rsrc(lse, static_cast<uint32_t>(a.Lpad) * 4);
+  // split operands: the lo rows of q and k (unused otherwise)
+  const bf16_t* Kl = SPLIT ? static_cast<const bf16_t*>(a.k_lo) + uoff : Ku;
+  const __amdgpu_buffer_rsrc_t rql =
+      SPLIT ? make_rsrc(static_cast<const bf16_t*>(a.q_lo) + uoff, static_cast<uint32_t>(L) * T::kRowBytes) : rq;
   const int voff = tile_voff<D>();  // for lanes 0..7 of wave 0 this is lane * 16
   const uint32_t xo = frag_offset<D>(lane);
   const bool lse_lane = wave == 0 && lane < 8;
   for (int h = 0; h < 2; ++h) {
     const int blk = h == 0 ? pb : nblk - 1 - pb;
     if (h == 1 && blk == pb) break;
-    const int kb = blk * kBlockRows;
-    const int kw = kb + wave * kWaveRows;
+    const int kb = blk * P::kBlockRows;
+    const int kw = kb + wave * P::kWaveRows;
     const int t0 = kb / kTile, tn = (L - 1) / kTile;
     if (h == 1) tile_barrier();
-    bf16x8 bk[2][D / 16];
+    bf16x8 bk[NS][D / 16], bkl[NS][D / 16];
 #pragma unroll
-    for (int s = 0; s < 2; ++s) row_frag<D>(Ku, kw + 32 * s + fr, L, lane, bk[s]);
-    // the tile of query rows t*32.. and its normalisers into buffer `buf`
-#define H2O_COLSUM_ISSUE(t, buf)                                             \
-  do {                                                                       \
-    tile_async(rq, voff, (t) * kTile, sQ[buf], T::kRowBytes, T::kLoads);     \
-    if (lse_lane) lse_async(rl, voff, (t) * kTile, sQ[buf] + T::kBytes);     \
-  } while (0)
-    H2O_COLSUM_ISSUE(tn, 0);
-    if (tn > t0) H2O_COLSUM_ISSUE(tn - 1, 1);
-    settle<D>(bk);
-    float cs[2] = {0.f, 0.f};
+    for (int s = 0; s < NS; ++s) row_frag<D>(Ku, kw + 32 * s + fr, L, lane, bk[s]);
+    if constexpr (SPLIT) row_frag<D>(Kl, kw + fr, L, lane, bkl[0]);
+    // the query rows t*32.. (hi, then lo when split) and their normalisers into buffer `buf`
+    auto issue = [&](int t, int buf) {
+      tile_async(rq, voff, t * kTile, sQ[buf], T::kRowBytes, T::kLoads);
+      if constexpr (SPLIT) tile_async(rql, voff, t * kTile, sQ[buf] + T::kBytes, T::kRowBytes, T::kLoads);
+      if (lse_lane) lse_async(rl, voff, t * kTile, sQ[buf] + NA * T::kBytes);
+    };
+    issue(tn, 0);
+    if (tn > t0) issue(tn - 1, 1);
+    settle<D, NS>(bk);
+    if constexpr (SPLIT) settle<D, NS>(bkl);
+    float cs[NS];
+#pragma unroll
+    for (int s = 0; s < NS; ++s) cs[s] = 0.f;
     for (int t = tn; t >= t0; --t) {
       const int it = tn - t;
       if (t == t0) wait_vm<0>();
-      else if (wave == 0) wait_vm<T::kLoads + 1>();  // wave 0 also brings the normalisers
-      else wait_vm<T::kLoads>();
+      else if (wave == 0) wait_vm<NA * T::kLoads + 1>();  // wave 0 also brings the normalisers
+      else wait_vm<NA * T::kLoads>();
       tile_barrier();
-      if (t - 2 >= t0) H2O_COLSUM_ISSUE(t - 2, (it + 2) % kBufs);
+      if (t - 2 >= t0) issue(t - 2, (it + 2) % kBufs);
       const int q0 = t * kTile;
       if (kw < L && q0 + kTile - 1 >= kw) {
         const uint32_t tile = lds_addr(sQ[it % kBufs]);
         uint32_t fb = tile + xo;
         asm volatile("" : "+v"(fb));
-        floatx16 acc[2];
-        tile_mfma<D>(fb, bk, acc);
-        if (q0 < kw + kWaveRows || q0 + kTile > L) {  // diagonal or ragged last tile
+        floatx16 acc[NS];
+        if constexpr (SPLIT) acc[0] = tile_mfma_split<D>(fb, fb + T::kBytes, bk[0], bkl[0]);
+        else tile_mfma<D>(fb, bk, acc);
+        if (q0 < kw + P::kWaveRows || q0 + kTile > L) {  // diagonal or ragged last tile
           // rows above the key and rows past L leave the column: logit -> -inf
           const int h4 = 4 * (lane >> 5);
 #pragma unroll
-          for (int s = 0; s < 2; ++s) {
+          for (int s = 0; s < NS; ++s) {
             const int lo = kw + 32 * s + fr - q0 - h4, hi = L - q0 - h4;
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
@@ -407,9 +470,9 @@ __global__ __launch_bounds__(kThreads, 4) void colsum_bf16(PrefillArgs a, int nb
         }
         // the 16 rows of this lane sit in 4 runs of 4 consecutive rows: one float4
         // of normalisers per run
-        const uint32_t lrow = tile + T::kBytes + 16 * (lane >> 5);
+        const uint32_t lrow = tile + NA * T::kBytes + 16 * (lane >> 5);
 #pragma unroll
-        for (int s = 0; s < 2; ++s) {
+        for (int s = 0; s < NS; ++s) {
           float part[4];
 #pragma unroll
           for (int g = 0; g < 4; ++g) {
@@ -424,9 +487,8 @@ __global__ __launch_bounds__(kThreads, 4) void colsum_bf16(PrefillArgs a, int nb
         }
       }
     }
-#undef H2O_COLSUM_ISSUE
 #pragma unroll
-    for (int s = 0; s < 2; ++s) {
+    for (int s = 0; s < NS; ++s) {
       const float c = cs[s] + __shfl_xor(cs[s], 32, kWave);
       const int key = kw + 32 * s + lane;
       if (lane < 32 && key < L) a.col_sum[static_cast<size_t>(unit) * a.Lpad + key] = c;
@@ -488,11 +550,26 @@ __device__ inline uint32_t v_elem_offset(int key, int col) {
   return key * T::kRowBytes + (((byte >> 4) ^ v_swz<D>(key)) << 4) + (byte & 15);
 }
 
-template <int D>
-__global__ __launch_bounds__(kThreads, 3) void rowout_bf16(PrefillArgs a, int nblk, int units) {
+// The terms p >= 0 of a lane's 16 keys as two bf16 B operands each: hi = p with
+// its low 16 mantissa bits cleared (a bf16 value), lo = bf16(p - hi) (p - hi is
+// exact in fp32), so hi + lo is p to 2^-16 relative.  A single bf16 operand
+// would carry 2^-9 of each term into the output (about 3e-3 absolute where a
+// few keys hold the row's weight).
+__device__ inline void split_terms(const floatx16& p, bf16x8 (&hi)[2], bf16x8 (&lo)[2]) {
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const uint32_t hb = __float_as_uint(p[i]) & 0xffff0000u;
+    hi[i >> 3][i & 7] = __builtin_bit_cast(__bf16, static_cast<uint16_t>(hb >> 16));
+    lo[i >> 3][i & 7] = static_cast<__bf16>(p[i] - __uint_as_float(hb));
+  }
+}
+
+template <int D, bool SPLIT>
+__global__ __launch_bounds__(kThreads, SPLIT ? 2 : 3) void rowout_bf16(PrefillArgs a, int nblk, int units) {
   using T = Tile<D>;
+  constexpr int NA = Pass<SPLIT>::NA;
   constexpr int NDB = D / 32;  // 32-wide column blocks of the output
-  __shared__ __align__(256) unsigned char sK[kBufs][T::kBytes];
+  __shared__ __align__(256) unsigned char sK[kBufs][NA * T::kBytes];
   __shared__ __align__(256) unsigned char sV[kBufs][T::kBytes];
   const int npair = (nblk + 1) / 2;
   int unit, pb;
@@ -500,12 +577,17 @@ __global__ __launch_bounds__(kThreads, 3) void rowout_bf16(PrefillArgs a, int nb
   const int L = a.L;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave), lane = threadIdx.x % kWave;
   const int fr = lane & 31, hh = lane >> 5;
-  const bf16_t* Qu = static_cast<const bf16_t*>(a.q) + static_cast<size_t>(unit) * L * D;
-  const bf16_t* Ku = static_cast<const bf16_t*>(a.k) + static_cast<size_t>(unit) * L * D;
-  const bf16_t* Vu = static_cast<const bf16_t*>(a.v) + static_cast<size_t>(unit) * L * D;
-  float* out = a.out + static_cast<size_t>(unit) * L * D;
+  const size_t uoff = static_cast<size_t>(unit) * L * D;
+  const bf16_t* Qu = static_cast<const bf16_t*>(a.q) + uoff;
+  const bf16_t* Ku = static_cast<const bf16_t*>(a.k) + uoff;
+  const bf16_t* Vu = static_cast<const bf16_t*>(a.v) + uoff;
+  float* out = a.out + uoff;
   const __amdgpu_buffer_rsrc_t rk = make_rsrc(Ku, static_cast<uint32_t>(L) * T::kRowBytes);
   const __amdgpu_buffer_rsrc_t rv = make_rsrc(Vu, static_cast<uint32_t>(L) * T::kRowBytes);
+  // split operands: the lo rows of q and k (unused otherwise)
+  const bf16_t* Ql = SPLIT ? static_cast<const bf16_t*>(a.q_lo) + uoff : Qu;
+  const __amdgpu_buffer_rsrc_t rkl =
+      SPLIT ? make_rsrc(static_cast<const bf16_t*>(a.k_lo) + uoff, static_cast<uint32_t>(L) * T::kRowBytes) : rk;
   const int voff = tile_voff<D>(), voffv = tile_voff_v<D>();
   const uint32_t xo = frag_offset<D>(lane);
   // this lane's role as a source of the transposing read: key row 4(g/2) + j
@@ -520,36 +602,41 @@ __global__ __launch_bounds__(kThreads, 3) void rowout_bf16(PrefillArgs a, int nb
     const int qw = blk * kOutRows + wave * 32;
     const int ntile = (min(blk * kOutRows + kOutRows, L) - 1) / kTile + 1;
     if (h == 1) tile_barrier();
-    bf16x8 bq[D / 16];
-    row_frag<D>(Qu, qw + fr, L, lane, bq);
-    tile_async(rk, voff, 0, sK[0], T::kRowBytes, T::kLoads);
-    tile_async(rv, voffv, 0, sV[0], T::kRowBytes, T::kLoads);
-    if (ntile > 1) {
-      tile_async(rk, voff, kTile, sK[1], T::kRowBytes, T::kLoads);
-      tile_async(rv, voffv, kTile, sV[1], T::kRowBytes, T::kLoads);
-    }
-#pragma unroll
-    for (int kk = 0; kk < D / 16; ++kk) asm volatile("" : "+v"(bq[kk]));
+    bf16x8 bq[1][D / 16], bql[1][D / 16];
+    row_frag<D>(Qu, qw + fr, L, lane, bq[0]);
+    if constexpr (SPLIT) row_frag<D>(Ql, qw + fr, L, lane, bql[0]);
+    // K rows t*32.. (hi, then lo when split) and V rows t*32.. into buffer `buf`
+    auto issue = [&](int t, int buf) {
+      tile_async(rk, voff, t * kTile, sK[buf], T::kRowBytes, T::kLoads);
+      if constexpr (SPLIT) tile_async(rkl, voff, t * kTile, sK[buf] + T::kBytes, T::kRowBytes, T::kLoads);
+      tile_async(rv, voffv, t * kTile, sV[buf], T::kRowBytes, T::kLoads);
+    };
+    issue(0, 0);
+    if (ntile > 1) issue(1, 1);
+    settle<D, 1>(bq);
+    if constexpr (SPLIT) settle<D, 1>(bql);
     floatx16 o[NDB];
 #pragma unroll
     for (int db = 0; db < NDB; ++db) o[db] = floatx16{};
     float m = -1e30f, l = 0.f;
     for (int t = 0; t < ntile; ++t) {
-      if (t + 1 < ntile) wait_vm<2 * T::kLoads>();  // K and V of this tile landed
+      if (t + 1 < ntile) wait_vm<(NA + 1) * T::kLoads>();  // K and V of this tile landed
       else wait_vm<0>();
       tile_barrier();
-      if (t + 2 < ntile) {
-        tile_async(rk, voff, (t + 2) * kTile, sK[(t + 2) % kBufs], T::kRowBytes, T::kLoads);
-        tile_async(rv, voffv, (t + 2) * kTile, sV[(t + 2) % kBufs], T::kRowBytes, T::kLoads);
-      }
+      if (t + 2 < ntile) issue(t + 2, (t + 2) % kBufs);
       const int k0 = t * kTile;
       if (qw < L && k0 <= qw + 31) {
         uint32_t fb = lds_addr(sK[t % kBufs]) + xo;
         asm volatile("" : "+v"(fb));
-        floatx16 sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tile_frag_kk(fb, 0), bq[0], floatx16{}, 0, 0, 0);
+        floatx16 sacc;
+        if constexpr (SPLIT) {
+          sacc = tile_mfma_split<D>(fb, fb + T::kBytes, bq[0], bql[0]);
+        } else {
+          sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tile_frag_kk(fb, 0), bq[0][0], floatx16{}, 0, 0, 0);
 #pragma unroll
-        for (int kk = 1; kk < D / 16; ++kk)
-          sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tile_frag_kk(fb, kk), bq[kk], sacc, 0, 0, 0);
+          for (int kk = 1; kk < D / 16; ++kk)
+            sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tile_frag_kk(fb, kk), bq[0][kk], sacc, 0, 0, 0);
+        }
         if (k0 + kTile - 1 > qw) {  // diagonal tile: keys after the query get weight 0
           const int rel = qw + fr - k0 - 4 * hh;
 #pragma unroll
@@ -564,9 +651,8 @@ __global__ __launch_bounds__(kThreads, 3) void rowout_bf16(PrefillArgs a, int nb
 #pragma unroll
             for (int i = 0; i < 16; ++i) o[db][i] *= r;
         }
-        bf16x8 pw[2];  // terms of keys 16kb.. as the B operand, kb = 0, 1
-#pragma unroll
-        for (int i = 0; i < 16; ++i) pw[i >> 3][i & 7] = static_cast<__bf16>(p[i]);
+        bf16x8 pw[2], pl[2];  // terms of keys 16kb.. as B operands (hi, lo), kb = 0, 1
+        split_terms(p, pw, pl);
         uint32_t vt = lds_addr(sV[t % kBufs]);
         asm volatile("" : "+v"(vt));
 #pragma unroll
@@ -577,6 +663,7 @@ __global__ __launch_bounds__(kThreads, 3) void rowout_bf16(PrefillArgs a, int nb
             const i16x4 hi = lds_tr16(vt + v_elem_offset<D>(tkey + 16 * kb + 8, tcol + 32 * db));
             const bf16x8 av = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
             o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pw[kb], o[db], 0, 0, 0);
+            o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pl[kb], o[db], 0, 0, 0);
           }
         }
       }
@@ -915,22 +1002,17 @@ __global__ __launch_bounds__(kThreads) void select_fill(PrefillArgs a) {
 // ------------------------------------------------------------------ rotary embedding of the prompt
 // One thread per (row, run of E pairs): the 16-byte chunk holding x_m .. x_{m+E-1}
 // and the one holding x_{m+d/2} ..; each pair (x, y) becomes (x c - y s, x s + y c)
-// with (c, s) the table's entry for (r, m), each product and sum rounded
-// separately, the result rounded to the storage type.
+// in fp32, with (c, s) the table's entry for (r, m).  fp32 storage keeps the
+// result; bf16 storage writes it as hi = bf16(v) into y and lo = bf16(v - hi)
+// into y_lo (the score passes' split operands).
 __device__ inline float to_f32(float x) { return x; }
 __device__ inline float to_f32(bf16_t x) { return __uint_as_float(static_cast<uint32_t>(x.bits) << 16); }
-template <typename T>
-__device__ inline T from_f32(float x);
-template <>
-__device__ inline float from_f32<float>(float x) { return x; }
-template <>
-__device__ inline bf16_t from_f32<bf16_t>(float x) {  // round to nearest even
-  return bf16_t{__builtin_bit_cast(uint16_t, static_cast<__bf16>(x))};
-}
+__device__ inline bf16_t bf16_rne(float x) { return bf16_t{__builtin_bit_cast(uint16_t, static_cast<__bf16>(x))}; }
 
 template <typename T, int D>
-__global__ __launch_bounds__(256) void rope_prompt(const T* x, T* y, int L, size_t runs, const float2* cs) {
+__global__ __launch_bounds__(256) void rope_prompt(const T* x, T* y, T* y_lo, int L, size_t runs, const float2* cs) {
   constexpr int H = D / 2, E = 16 / static_cast<int>(sizeof(T)), RPR = H / E;  // pairs per run, runs per row
+  constexpr bool kSplit = !std::is_same<T, float>::value;
   const size_t t = blockIdx.x * static_cast<size_t>(256) + threadIdx.x;
   if (t >= runs) return;
   const size_t row = t / RPR;  // unit * L + r
@@ -938,7 +1020,7 @@ __global__ __launch_bounds__(256) void rope_prompt(const T* x, T* y, int L, size
   union Chunk {
     uint4 u;
     T e[E];
-  } a, b, oa, ob;
+  } a, b, oa, ob, la, lb;
   a.u = ld16(x + row * D + m0);
   b.u = ld16(x + row * D + m0 + H);
   const float2* w = cs + static_cast<size_t>(r) * H + m0;
@@ -946,11 +1028,24 @@ __global__ __launch_bounds__(256) void rope_prompt(const T* x, T* y, int L, size
   for (int i = 0; i < E; ++i) {
     const float2 cw = w[i];
     const float xa = to_f32(a.e[i]), yb = to_f32(b.e[i]);
-    oa.e[i] = from_f32<T>(__fsub_rn(__fmul_rn(xa, cw.x), __fmul_rn(yb, cw.y)));
-    ob.e[i] = from_f32<T>(__fadd_rn(__fmul_rn(xa, cw.y), __fmul_rn(yb, cw.x)));
+    const float va = __fsub_rn(__fmul_rn(xa, cw.x), __fmul_rn(yb, cw.y));
+    const float vb = __fadd_rn(__fmul_rn(xa, cw.y), __fmul_rn(yb, cw.x));
+    if constexpr (kSplit) {
+      oa.e[i] = bf16_rne(va);
+      ob.e[i] = bf16_rne(vb);
+      la.e[i] = bf16_rne(va - to_f32(oa.e[i]));
+      lb.e[i] = bf16_rne(vb - to_f32(ob.e[i]));
+    } else {
+      oa.e[i] = va;
+      ob.e[i] = vb;
+    }
   }
   st16(y + row * D + m0, oa.u);
   st16(y + row * D + m0 + H, ob.u);
+  if constexpr (kSplit) {
+    st16(y_lo + row * D + m0, la.u);
+    st16(y_lo + row * D + m0 + H, lb.u);
+  }
 }
 
 __global__ void clear_kernel(int32_t* pos, float* score, float* comp, size_t n) {
@@ -972,23 +1067,29 @@ hipError_t launch_select(const PrefillArgs& a, int units, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <int D>
-hipError_t launch_bf16(const PrefillArgs& a, int units, hipStream_t s) {
-  const int nblk = (a.L + kBlockRows - 1) / kBlockRows;  // row blocks; a block takes a pair
+template <int D, bool SPLIT>
+hipError_t launch_bf16_scores(const PrefillArgs& a, int units, hipStream_t s) {
+  const int nblk = (a.L + Pass<SPLIT>::kBlockRows - 1) / Pass<SPLIT>::kBlockRows;  // a block takes a pair
   const int groups = (units + kXcds - 1) / kXcds;
   const dim3 grid(groups * kXcds * ((nblk + 1) / 2));
+  if (a.out != nullptr) {
+    const int nbo = (a.L + kOutRows - 1) / kOutRows;
+    const dim3 grid_o(groups * kXcds * ((nbo + 1) / 2));
+    hipLaunchKernelGGL((rowout_bf16<D, SPLIT>), grid_o, dim3(kThreads), 0, s, a, nbo, units);
+  } else {
+    hipLaunchKernelGGL((rowstats_bf16<D, SPLIT>), grid, dim3(kThreads), 0, s, a, nblk, units);
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((colsum_bf16<D, SPLIT>), grid, dim3(kThreads), 0, s, a, nblk, units);
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_bf16(const PrefillArgs& a, int units, hipStream_t s) {
   if (a.stages & kStageScores) {
-    if (a.out != nullptr) {
-      const int nbo = (a.L + kOutRows - 1) / kOutRows;
-      const dim3 grid_o(groups * kXcds * ((nbo + 1) / 2));
-      hipLaunchKernelGGL((rowout_bf16<D>), grid_o, dim3(kThreads), 0, s, a, nbo, units);
-    } else {
-      hipLaunchKernelGGL((rowstats_bf16<D>), grid, dim3(kThreads), 0, s, a, nblk, units);
-    }
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((colsum_bf16<D>), grid, dim3(kThreads), 0, s, a, nblk, units);
-    e = hipGetLastError();
+    const hipError_t e = a.q_lo != nullptr ? launch_bf16_scores<D, true>(a, units, s)
+                                           : launch_bf16_scores<D, false>(a, units, s);
     if (e != hipSuccess) return e;
   }
   return (a.stages & kStageSelect) ? launch_select<bf16_t, D>(a, units, s) : hipSuccess;
@@ -1020,7 +1121,7 @@ hipError_t launch_prefill(int dtype, int head_dim, const PrefillArgs& a, int uni
   return head_dim == 64 ? launch_bf16<64>(a, units, s) : launch_bf16<128>(a, units, s);
 }
 
-hipError_t launch_rope_prompt(int dtype, int head_dim, const void* x, void* y, int32_t L, int units,
+hipError_t launch_rope_prompt(int dtype, int head_dim, const void* x, void* y, void* y_lo, int32_t L, int units,
                               const float* cs, hipStream_t s) {
   // one thread per 16 bytes of the first half of a row
   const size_t runs = static_cast<size_t>(units) * L * (head_dim / 2) / (dtype == 0 ? 4 : 8);
@@ -1030,17 +1131,17 @@ hipError_t launch_rope_prompt(int dtype, int head_dim, const void* x, void* y, i
   if (dtype == 0) {
     if (head_dim == 64)
       hipLaunchKernelGGL((rope_prompt<float, 64>), grid, dim3(256), 0, s, static_cast<const float*>(x),
-                         static_cast<float*>(y), L, runs, t);
+                         static_cast<float*>(y), nullptr, L, runs, t);
     else
       hipLaunchKernelGGL((rope_prompt<float, 128>), grid, dim3(256), 0, s, static_cast<const float*>(x),
-                         static_cast<float*>(y), L, runs, t);
+                         static_cast<float*>(y), nullptr, L, runs, t);
   } else {
     if (head_dim == 64)
       hipLaunchKernelGGL((rope_prompt<bf16_t, 64>), grid, dim3(256), 0, s, static_cast<const bf16_t*>(x),
-                         static_cast<bf16_t*>(y), L, runs, t);
+                         static_cast<bf16_t*>(y), static_cast<bf16_t*>(y_lo), L, runs, t);
     else
       hipLaunchKernelGGL((rope_prompt<bf16_t, 128>), grid, dim3(256), 0, s, static_cast<const bf16_t*>(x),
-                         static_cast<bf16_t*>(y), L, runs, t);
+                         static_cast<bf16_t*>(y), static_cast<bf16_t*>(y_lo), L, runs, t);
   }
   return hipGetLastError();
 }
