@@ -207,6 +207,27 @@ h2o_status h2o_prefill_stats_read(h2o_cache* cache, float* row_lse, float* col_s
 h2o_status h2o_column_scores(h2o_cache* cache, const void* q, const void* k, int32_t n, float* scores,
                              void* stream);
 
+/* h2o_column_scores for callers that cannot allocate device memory (code under
+ * HIP graph capture, serving loops that forbid hipMalloc): the same column
+ * scores of a whole sequence, with no cache object.  Its scratch (each row's
+ * softmax normaliser and the column sums, batch*heads*round32(n)*8 bytes, at
+ * most 16 MiB) is a file-scope device array of the library rather than an
+ * allocation; the call allocates nothing, host or device, after the first call
+ * on a device (which looks the array up).
+ *   params: batch, heads, head_dim, dtype and scale are used (budgets and
+ *           max_prompt are ignored); rope_base must be 0.
+ *   q, k:   device, [B, H, n, d] in params->dtype, on the current device.
+ *   scores: device, [B, H, n] float32, written (stream-ordered).
+ * Every call on one GPU shares that GPU's array: calls that overlap on one GPU
+ * (on different streams or threads) race and must be serialised by the caller.
+ * The array keeps the last call's contents; no call reads a value it has not
+ * first written, so nothing needs clearing.  n == 0 does nothing.
+ * Errors: H2O_ERR_INVALID_ARG (NULL params or pointers, misaligned pointers,
+ * n < 0, or the scratch limit exceeded), H2O_ERR_UNSUPPORTED (head_dim not 64
+ * or 128, rope_base != 0), H2O_ERR_HIP. */
+h2o_status h2o_column_scores_noalloc(const h2o_params* params, const void* q, const void* k, int32_t n,
+                                     float* scores, void* stream);
+
 /* Prefill by given scores: (re)initialise the cache from a prompt of
  * `prompt_len` tokens exactly as h2o_prefill does (last K_r positions plus the
  * K_h best of [0, prompt_len - K_r), equal scores ranked by position), but

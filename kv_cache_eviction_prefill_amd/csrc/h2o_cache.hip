@@ -8,6 +8,7 @@
 #include <cmath>
 #include <cstdint>
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -248,6 +249,33 @@ int choose_nsplit(const h2o_cache* c, int32_t count, int32_t* split_len) {
   return (count + *split_len - 1) / *split_len;  // every split holds >= 1 slot
 }
 
+// Scratch of h2o_column_scores_noalloc: a file-scope device array instead of
+// an allocation (the prompt's row normalisers and column sums, [units, Lpad]
+// float32 each).  Every GPU that loads the library holds its own copy until
+// the process ends; host code reaches it only through the address
+// hipGetSymbolAddress returns on that device.
+constexpr size_t kStaticScratchBytes = size_t{16} << 20;
+__device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// This device's copy of `scratch` (looked up on the first call per device,
+// with the device current).
+hipError_t static_scratch(int dev, void** ptr) {
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return hipSuccess;
+}
+
 }  // namespace
 
 extern "C" {
@@ -460,6 +488,55 @@ h2o_status h2o_column_scores(h2o_cache* c, const void* q, const void* k, int32_t
   c->stats_valid = false;  // the prefill scratch now holds this sequence's statistics
   e = hipMemcpy2DAsync(scores, static_cast<size_t>(n) * 4, c->col_sum, static_cast<size_t>(a.Lpad) * 4,
                        static_cast<size_t>(n) * 4, c->units, hipMemcpyDeviceToDevice, s);
+  if (e != hipSuccess) return hip_fail(e, "copy column scores");
+  return H2O_OK;
+}
+
+h2o_status h2o_column_scores_noalloc(const h2o_params* p, const void* q, const void* k, int32_t n, float* scores,
+                                     void* stream) {
+  if (p == nullptr) return fail(H2O_ERR_INVALID_ARG, "params is NULL");
+  if (p->batch < 1 || p->heads < 1) return fail(H2O_ERR_INVALID_ARG, "batch and heads must be >= 1");
+  if (p->head_dim != 64 && p->head_dim != 128) return fail(H2O_ERR_UNSUPPORTED, "head_dim must be 64 or 128");
+  if (p->dtype != H2O_F32 && p->dtype != H2O_BF16) return fail(H2O_ERR_INVALID_ARG, "unknown dtype");
+  if (!std::isfinite(p->scale)) return fail(H2O_ERR_INVALID_ARG, "scale must be finite");
+  if (p->rope_base != 0.f) return fail(H2O_ERR_UNSUPPORTED, "position rolling needs a cache (h2o_column_scores)");
+  if (n < 0) return fail(H2O_ERR_INVALID_ARG, "n must be >= 0");
+  if (n == 0) return H2O_OK;
+  if (q == nullptr || k == nullptr || scores == nullptr)
+    return fail(H2O_ERR_INVALID_ARG, "q, k and scores must be non-NULL");
+  if (!aligned16(q) || !aligned16(k)) return fail(H2O_ERR_INVALID_ARG, "q and k must be 16-byte aligned");
+  if ((reinterpret_cast<uintptr_t>(scores) & 3u) != 0)
+    return fail(H2O_ERR_INVALID_ARG, "scores must be 4-byte aligned");
+  const int64_t units = static_cast<int64_t>(p->batch) * p->heads;
+  const int64_t lpad = round32(std::min<int32_t>(n, INT32_MAX - 31));
+  const int64_t esize = p->dtype == H2O_F32 ? 4 : 2;
+  if (lpad * p->head_dim * esize >= (int64_t{1} << 32))
+    return fail(H2O_ERR_INVALID_ARG, "n * head_dim * element size must stay below 2^32 bytes");
+  if (units * lpad * 8 > static_cast<int64_t>(kStaticScratchBytes))
+    return fail(H2O_ERR_INVALID_ARG, "batch * heads * n (rounded up to 32) * 8 bytes exceeds the 16 MiB static scratch");
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  void* base = nullptr;
+  e = static_scratch(dev, &base);
+  if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const float scale = p->scale > 0.f ? p->scale : 1.f / std::sqrt(static_cast<float>(p->head_dim));
+  h2o::PrefillArgs a{};
+  a.stages = h2o::kStageScores;
+  a.q = q;
+  a.k = k;
+  a.L = n;
+  a.Lpad = static_cast<int32_t>(lpad);
+  // every value of the scratch that a pass reads, an earlier pass of this call writes
+  a.row_lse2 = static_cast<float*>(base);
+  a.col_sum = static_cast<float*>(base) + units * lpad;
+  a.scale = scale;
+  a.c2 = scale * kLog2e;
+  e = h2o::launch_prefill(p->dtype, p->head_dim, a, static_cast<int>(units), s);
+  if (e != hipSuccess) return hip_fail(e, "column score launch");
+  e = hipMemcpy2DAsync(scores, static_cast<size_t>(n) * 4, a.col_sum, static_cast<size_t>(lpad) * 4,
+                       static_cast<size_t>(n) * 4, static_cast<size_t>(units), hipMemcpyDeviceToDevice, s);
   if (e != hipSuccess) return hip_fail(e, "copy column scores");
   return H2O_OK;
 }

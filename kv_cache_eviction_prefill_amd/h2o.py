@@ -54,6 +54,7 @@ _SIGNATURES = {
     "h2o_prefill_stats_read": (_i32, [_vp, _vp, _vp, _vp]),
     "h2o_cache_info": (_i32, [_vp, _p32, _p32, _p32]),
     "h2o_column_scores": (_i32, [_vp, _vp, _vp, _i32, _vp, _vp]),
+    "h2o_column_scores_noalloc": (_i32, [ctypes.POINTER(h2o_params), _vp, _vp, _i32, _vp, _vp]),
     "h2o_cache_set_pattern": (_i32, [_vp, _i32, _i32, _i32]),
     "h2o_prefill_scored": (_i32, [_vp, _vp, _vp, _i32, _i32, _vp, _vp]),
     "h2o_decode_step_scored": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _vp]),
@@ -121,6 +122,10 @@ def h2o_cache_info(cache, count, next_pos, prompt_len):
 
 def h2o_column_scores(cache, q, k, n, scores, stream):
     return load().h2o_column_scores(cache, q, k, n, scores, stream)
+
+
+def h2o_column_scores_noalloc(params, q, k, n, scores, stream):
+    return load().h2o_column_scores_noalloc(params, q, k, n, scores, stream)
 
 
 def h2o_prefill_scored(cache, k, v, prompt_len, seq_rows, scores, stream):
