@@ -102,10 +102,16 @@ def parse():
                     help="sparse pattern kept before heavy hitters: none, strided:PERIOD or fixed:PERIOD:WIDTH")
     ap.add_argument("--prefill-out", action="store_true",
                     help="prefill also writes the prompt's attention output (fp32 [B, H, L, d])")
+    ap.add_argument("--no-parity", action="store_true",
+                    help="skip the untimed re-run that records the sampled units' results for the oracle")
+    ap.add_argument("--cpu-max-steps", type=int, default=20000,
+                    help="the CPU leg (and its parity re-run) covers at most this many decode steps per unit, "
+                         "extrapolated linearly to the whole decode (the 4 M-token stream)")
     ap.add_argument("--cpu-units", type=int, default=96,
                     help="units in the CPU-oracle sample (about 15 s of CPU work at this shape)")
     ap.add_argument("--copy-calibration", action="store_true",
-                    help="also run a plain 1 GiB device copy (calibrates HBM byte counters)")
+                    help="accepted for older profiling commands: the 1 GiB copy and read that calibrate the "
+                         "HBM byte counters and give the measured bandwidth ceilings now always run")
     return ap.parse_args()
 
 
@@ -115,39 +121,150 @@ def _warm(_):
 
 
 def _cpu_unit(args):
-    """Worker: time the oracle on one unit (prefill + every decode step)."""
+    """Worker: the oracle on one unit (prefill + every decode step), timed; then,
+    when the GPU's results for the unit are given, their comparison (the oracle
+    adopts the GPU's decision only at near-ties, as in the parity tests)."""
     import time as _t
 
-    from oracle import Pattern, Rope, run_unit, run_unit_global
+    import numpy as _np
 
-    Q, K, V, L, kh, kr, variant, pattern, rope = args
+    from oracle import ParityMismatch, Pattern, Rope, run_unit, run_unit_global
+
+    Q, K, V, L, kh, kr, variant, pattern, rope, gpu = args
     rope = Rope(*rope) if rope else None
+    replay = {} if gpu is None else {"replay_kept": gpu["kept"], "replay_evicted": gpu["evicted"]}
     t0 = _t.perf_counter()
-    if variant == "global":
-        run_unit_global(Q, K, V, L, kh, kr, rope=rope)
-    else:
-        run_unit(Q, K, V, L, kh, kr, pattern=Pattern(*pattern), rope=rope)
-    return _t.perf_counter() - t0
+    try:
+        if variant == "global":
+            res = run_unit_global(Q, K, V, L, kh, kr, rope=rope, **replay)
+        else:
+            res = run_unit(Q, K, V, L, kh, kr, pattern=Pattern(*pattern), rope=rope, **replay)
+    except ParityMismatch as e:
+        return _t.perf_counter() - t0, {"ok": False, "msg": f"decision mismatch: {e}"}
+    dt = _t.perf_counter() - t0
+    if gpu is None:
+        return dt, None
+    out_err = float(_np.max(_np.abs(gpu["out"] - res["out"]))) if len(res["out"]) else 0.0
+    pos, score, _, _ = res["cache"].snapshot()
+    gp, gs = gpu["pos"], gpu["score"]
+    valid = gp >= 0
+    order = _np.argsort(gp[valid])
+    same_pos = _np.array_equal(gp[valid][order], pos)
+    score_rel = float(_np.max(_np.abs(gs[valid][order] - score) / score)) if same_pos and len(pos) else 0.0
+    ok = same_pos and out_err <= 2e-3 and score_rel <= 1e-4
+    return dt, {"ok": ok, "out_err": out_err, "score_rel": score_rel, "same_positions": same_pos,
+                "ties": int(res["decode_ties_adopted"]) + int(res["prefill_tie_adopted"])}
 
 
-def cpu_baseline(w, samples, procs):
+def host_info(procs):
+    """What the CPU baseline ran on: CPU model, core counts, library versions."""
+    import platform
+
+    import numpy as np
+
+    model = platform.processor() or "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    blas = "unknown"
+    try:
+        cfg = np.show_config(mode="dicts")
+        b = cfg.get("Build Dependencies", {}).get("blas", {})
+        blas = f"{b.get('name', '?')} {b.get('version', '')}".strip()
+    except Exception:  # noqa: BLE001 - older numpy: no dict form
+        pass
+    import torch
+
+    return {"cpu_model": model, "cores_visible": len(os.sched_getaffinity(0)), "cores_used": procs,
+            "core_cap": "at most 16 worker processes: the GPU host's CPU share per GPU",
+            "python": platform.python_version(), "numpy": np.__version__, "blas": blas,
+            "torch": torch.__version__, "hip": getattr(torch.version, "hip", None)}
+
+
+def cpu_baseline(w, samples, procs, steps_run):
     import multiprocessing as mp
 
     ctx = mp.get_context("spawn")
-    with ctx.Pool(procs) as pool:
+    pool = ctx.Pool(procs)
+    try:
         pool.map(_warm, range(procs), chunksize=1)  # start every worker before timing
         t0 = time.perf_counter()
-        per_unit = pool.map(_cpu_unit, samples, chunksize=1)
+        results = pool.map(_cpu_unit, samples, chunksize=1)
         wall = time.perf_counter() - t0
+    finally:
+        # close + join lets the workers exit on their own (terminate() would
+        # signal them, which profilers that trap signals report as aborts)
+        pool.close()
+        pool.join()
+    per_unit = [r[0] for r in results]
     units_total = w.layers * w.batch * w.heads
     # units are independent and equally sized: whole-job time = mean unit time x units / cores
-    job_seconds = (sum(per_unit) / len(per_unit)) * units_total / procs
-    return {"value": w.batch * w.decode_steps / job_seconds, "unit": "tokens/s", "cores": procs,
+    # (x the decode steps not run, for a decode longer than the sample covers: the
+    # cost per step is flat once the cache is full)
+    stretch = w.decode_steps / steps_run
+    job_seconds = (sum(per_unit) / len(per_unit)) * stretch * units_total / procs
+    part = (f"the first {steps_run} of {w.decode_steps} decode steps, extrapolated linearly"
+            if steps_run < w.decode_steps else f"{w.decode_steps} decode steps")
+    base = {"value": w.batch * w.decode_steps / job_seconds, "unit": "tokens/s", "cores": procs,
             "kind": "oracle",
             "sample": f"{len(samples)} of {units_total} (layer, batch, head) units, each a full prefill of "
-                      f"{w.prompt_len} tokens plus {w.decode_steps} decode steps (float64 NumPy, one unit per "
+                      f"{w.prompt_len} tokens plus {part} (float64 NumPy, one unit per "
                       f"process, {procs} processes); mean {sum(per_unit) / len(per_unit):.3f} s per unit, "
-                      f"whole job extrapolated to {job_seconds:.0f} s; sample wall {wall:.2f} s"}
+                      f"whole job extrapolated to {job_seconds:.0f} s; sample wall {wall:.2f} s",
+            "host": host_info(procs)}
+    checks = [r[1] for r in results if r[1] is not None]
+    parity = None
+    if checks:
+        bad = [c for c in checks if not c["ok"]]
+        parity = {"units": len(checks), "ok": not bad,
+                  "max_out_err": max((c.get("out_err", 0.0) for c in checks), default=0.0),
+                  "max_score_rel": max((c.get("score_rel", 0.0) for c in checks), default=0.0),
+                  "near_ties_adopted": sum(c.get("ties", 0) for c in checks),
+                  "failures": [c.get("msg", c) for c in bad[:3]],
+                  "what": "the sampled units' decode outputs at every step (2e-3 abs), final positions "
+                          "(exact) and final scores (1e-4 rel) against the oracle, from an untimed "
+                          "run of the same launch sequence after the timed steps"}
+    return base, parity
+
+
+def ceilings(torch, dev, lib, sp):
+    """Measured HBM ceilings on this GPU, best of 5 timed with events: the
+    library's streaming-read probe over 4 GiB (reads only) and a 1 GiB
+    device-to-device copy (read + write)."""
+    src = torch.empty(1 << 28, dtype=torch.float32, device=dev).fill_(1.0)
+    dst = torch.empty_like(src)
+    big = torch.ones(1 << 30, dtype=torch.float32, device=dev)
+    sink = torch.zeros(4, dtype=torch.int32, device=dev)
+
+    def probe():
+        st = lib.h2o_probe_read(big.data_ptr(), big.numel() * 4, sink.data_ptr(), sp)
+        if st:
+            raise RuntimeError(f"h2o_probe_read failed with status {st}")
+
+    out = {}
+    for name, fn, nbytes in (("read", probe, big.numel() * 4),
+                             ("copy", lambda: dst.copy_(src), 2 * src.numel() * 4)):
+        fn()
+        best = None
+        for _ in range(5):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            e1.synchronize()
+            t = e0.elapsed_time(e1) / 1e3
+            best = t if best is None else min(best, t)
+        out[f"{name}_GBps"] = nbytes / best / 1e9
+    torch.cuda.synchronize()
+    del src, dst, big, sink
+    out["note"] = ("read: h2o_probe_read over 4 GiB (a plain stream of 16-byte non-temporal loads); "
+                   "copy: torch's 1 GiB device copy (read + write bytes), which also calibrates the rocprofv3 "
+                   "byte counters")
+    return out
 
 
 def main():
@@ -183,16 +300,25 @@ def main():
     # ---------------------------------------------------------------- inputs (untimed)
     t_gen = time.time()
     pre, dec, seq, gsc = [], [], [], []
+    tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    gen_chunk = 1 << 18  # decode positions generated per call (the 4 M-token stream in 16 pieces)
     for layer in range(NL):
-        q, k, v = synth.torch_qkv(w, layer, 0, w.n_positions, dev)
         if glob:  # the comparator reads the whole sequence: column scores over q, k; prompt rows of k, v
+            q, k, v = synth.torch_qkv(w, layer, 0, N, dev)
             seq.append((q, k, v))
             gsc.append(torch.empty((B, H, N), dtype=torch.float32, device=dev))
             pre.append(None)
-        else:
-            pre.append(tuple(x[:, :, :L].contiguous() for x in (q, k, v)))
-        dec.append(tuple(x[:, :, L:].permute(2, 0, 1, 3).contiguous() for x in (q, k, v)))
-        del q, k, v
+            dec.append(tuple(x[:, :, L:].permute(2, 0, 1, 3).contiguous() for x in (q, k, v)))
+            del q, k, v
+            continue
+        pre.append(synth.torch_qkv(w, layer, 0, L, dev))
+        dq = tuple(torch.empty((T, B, H, d), dtype=tdt, device=dev) for _ in range(3))
+        for c0 in range(0, T, gen_chunk):
+            c1 = min(T, c0 + gen_chunk)
+            for x, y in zip(dq, synth.torch_qkv(w, layer, L + c0, L + c1, dev)):
+                x[c0:c1] = y.permute(2, 0, 1, 3)
+            del y
+        dec.append(dq)
     caches = [H2OCache(B, H, d, w.heavy_budget, w.recent_budget, dtype=w.dtype, max_prompt=N if glob else L,
                        rope_base=a.rope) for _ in range(NL)]
     pat = a.pattern.split(":")
@@ -212,10 +338,15 @@ def main():
     pre_ptr = [tuple(x.data_ptr() for x in p) if p is not None else None for p in pre]
     seq_ptr = [tuple(x.data_ptr() for x in p) for p in seq]
     gsc_ptr = [g.data_ptr() for g in gsc]
-    dec_ptr = [[tuple(x[t].data_ptr() for x in dq) for t in range(T)] for dq in dec]
+    tok = B * H * d * s  # bytes of one step's q, k or v; decode inputs are [T, B, H, d]
+    dec_base = [tuple(x.data_ptr() for x in dq) for dq in dec]
     out_ptr = [out[l].data_ptr() for l in range(NL)]
     ev_ptr = [ev[l].data_ptr() for l in range(NL)]
-    prefill_c, decode_c = lib.h2o_prefill, lib.h2o_decode_step
+    prefill_c, decode_c, steps_c = lib.h2o_prefill, lib.h2o_decode_step, lib.h2o_decode_steps
+    # one layer: the whole decode is one h2o_decode_steps call (each step's evicted
+    # positions kept in a [T, B, H] log, the last step's output in `out`)
+    use_steps = NL == 1 and not glob
+    ev_log = torch.empty((T, B, H), dtype=torch.int32, device=dev) if use_steps else None
     colsc_c, prefill_sc_c, decode_sc_c = lib.h2o_column_scores, lib.h2o_prefill_scored, lib.h2o_decode_step_scored
 
     def _ok(st, where):
@@ -234,9 +365,14 @@ def main():
                 _ok(prefill_c(handles[l], *pre_ptr[l], L, pout_ptr, sp), "h2o_prefill")
         if evs is not None:
             evs[1].record(stream)
+        if use_steps:
+            _ok(steps_c(handles[0], *dec_base[0], T, out_ptr[0], 0, ev_log.data_ptr(), sp), "h2o_decode_steps")
+            if evs is not None:
+                evs[2].record(stream)
+            return
         for t in range(T):
             for l in range(NL):
-                qp, kp, vp = dec_ptr[l][t]
+                qp, kp, vp = (x + t * tok for x in dec_base[l])
                 if glob:
                     _ok(decode_sc_c(handles[l], qp, kp, vp, gsc_ptr[l] + 4 * (L + t), N, out_ptr[l], ev_ptr[l], sp),
                         "h2o_decode_step_scored")
@@ -245,12 +381,7 @@ def main():
         if evs is not None:
             evs[2].record(stream)
 
-    if a.copy_calibration:  # plain copy of known size for counter calibration
-        src = torch.empty(1 << 28, dtype=torch.float32, device=dev).fill_(1.0)
-        dst = torch.empty_like(src)
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
+    ceil = ceilings(torch, dev, lib, sp)  # untimed: bandwidth references and the counters' calibration copy
 
     for _ in range(a.warmup):
         one_step()
@@ -270,7 +401,7 @@ def main():
     # sanity: the caches hold min(k, L + T) entries and advanced by T
     cnt, nxt, pl = caches[0].info()
     assert (cnt, nxt, pl) == (min(L + T, w.k), L + T, L), (cnt, nxt, pl)
-    assert bool((ev >= -1).all())
+    assert bool((ev >= -1).all()) and (ev_log is None or bool((ev_log >= -1).all()))
 
     K = a.steps
     tokens = B * T * K
@@ -309,7 +440,8 @@ def main():
                                  if a.layers is None and not glob and a.pattern == "none" and not a.rope else None),
                      "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
                      "bytes_per_launch": dec_bytes_launch, "avg_launch_us": 1e6 * avg_dec_s,
-                     "launches": launches},
+                     "launches": launches, "measured_ceilings": ceil,
+                     "frac_of_measured_read": achieved / ceil["read_GBps"]},
         "decode": {"tokens_per_s": tokens / t_dec, "ms_per_token_step": 1e3 * t_dec / (T * K),
                    "GBps": achieved, "hbm_frac": achieved / HBM_PEAK_GBS,
                    # a cache that fits the 256 MB Infinity Cache is read from there, not HBM:
@@ -322,25 +454,75 @@ def main():
         "timing": {"wall_s": wall, "event_s": t_all, "input_gen_s": gen_s},
     }
 
+    def verify_pass(picks):
+        """Untimed re-run of one step in the same launch sequence, recording for
+        the sampled units the prefill's kept positions, every step's eviction and
+        output, and the final positions and scores."""
+        by_layer = {}
+        for i, (l, b, h) in enumerate(picks):
+            by_layer.setdefault(l, []).append((i, b * H + h))
+        sel = {l: (torch.tensor([i for i, _ in v], device=dev), torch.tensor([u for _, u in v], device=dev))
+               for l, v in by_layer.items()}
+        outs = torch.empty((Tc, len(picks), d), dtype=torch.float32, device=dev)
+        vlog = torch.empty((Tc, NL, B, H), dtype=torch.int32, device=dev)
+        for l in range(NL):
+            if glob:
+                qf, kf, vf = seq_ptr[l]
+                _ok(colsc_c(handles[l], qf, kf, N, gsc_ptr[l], sp), "h2o_column_scores")
+                _ok(prefill_sc_c(handles[l], kf, vf, L, N, gsc_ptr[l], sp), "h2o_prefill_scored")
+            else:
+                _ok(prefill_c(handles[l], *pre_ptr[l], L, pout_ptr, sp), "h2o_prefill")
+        kept = {}
+        pos = np.empty((B, H, w.k), np.int32)
+        for l in by_layer:
+            _ok(lib.h2o_cache_read(handles[l], pos.ctypes.data, None, None, None, None, sp), "h2o_cache_read")
+            kept[l] = pos.copy()
+        for t in range(Tc):
+            for l in range(NL):
+                qp, kp, vp = (x + t * tok for x in dec_base[l])
+                ep = vlog[t, l].data_ptr()
+                if glob:
+                    _ok(decode_sc_c(handles[l], qp, kp, vp, gsc_ptr[l] + 4 * (L + t), N, out_ptr[l], ep, sp),
+                        "h2o_decode_step_scored")
+                else:
+                    _ok(decode_c(handles[l], qp, kp, vp, out_ptr[l], ep, sp), "h2o_decode_step")
+                if l in sel:
+                    outs[t].index_copy_(0, sel[l][0], out[l].view(B * H, d).index_select(0, sel[l][1]))
+        final = {}
+        score = np.empty((B, H, w.k), np.float32)
+        for l in by_layer:
+            _ok(lib.h2o_cache_read(handles[l], pos.ctypes.data, score.ctypes.data, None, None, None, sp),
+                "h2o_cache_read")
+            final[l] = (pos.copy(), score.copy())
+        outs_h, ev_h = outs.cpu().numpy(), vlog.cpu().numpy()
+        res_units = []
+        for i, (l, b, h) in enumerate(picks):
+            kp_ = kept[l][b, h]
+            res_units.append({"kept": sorted(int(x) for x in kp_[kp_ >= 0]),
+                              "evicted": ev_h[:, l, b, h].astype(np.int64), "out": outs_h[:, i].astype(np.float64),
+                              "pos": final[l][0][b, h], "score": final[l][1][b, h].astype(np.float64)})
+        return res_units
+
+    Tc = T if glob else min(T, a.cpu_max_steps)  # decode steps the CPU leg and its parity re-run cover
     if not a.no_cpu_baseline:
         g = np.random.default_rng(7)
         picks = [(int(g.integers(NL)), int(g.integers(B)), int(g.integers(H))) for _ in range(a.cpu_units)]
+        gpu_units = verify_pass(picks) if not a.no_parity else [None] * len(picks)
         samples = []
-        for (l, b, h) in picks:
+        for n_pick, (l, b, h) in enumerate(picks):
             if glob:
                 qf, kf, vf = (x[b, h].float().cpu().numpy() for x in seq[l])
             else:
-                qf = torch.cat([pre[l][0][b, h], dec[l][0][:, b, h]]).float().cpu().numpy()
-                kf = torch.cat([pre[l][1][b, h], dec[l][1][:, b, h]]).float().cpu().numpy()
-                vf = torch.cat([pre[l][2][b, h], dec[l][2][:, b, h]]).float().cpu().numpy()
+                qf, kf, vf = (torch.cat([pre[l][i][b, h], dec[l][i][:Tc, b, h]]).float().cpu().numpy()
+                              for i in range(3))
             samples.append((qf, kf, vf, L, w.heavy_budget, w.recent_budget, a.variant, pattern,
-                            (a.rope,) if a.rope else None))
+                            (a.rope,) if a.rope else None, gpu_units[n_pick]))
         procs = min(len(os.sched_getaffinity(0)), 16, len(samples))
         os.environ.setdefault("OMP_NUM_THREADS", "1")
         os.environ.setdefault("OPENBLAS_NUM_THREADS", "1")
-        res["cpu_baseline"] = cpu_baseline(w, samples, procs)
+        res["cpu_baseline"], res["parity"] = cpu_baseline(w, samples, procs, Tc)
     else:
-        res["cpu_baseline"] = None
+        res["cpu_baseline"], res["parity"] = None, None
 
     for cch in caches:
         cch.close()

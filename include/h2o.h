@@ -162,6 +162,25 @@ h2o_status h2o_prefill(h2o_cache* cache, const void* q, const void* k, const voi
 h2o_status h2o_decode_step(h2o_cache* cache, const void* q, const void* k, const void* v,
                            float* out, int32_t* evicted, void* stream);
 
+/* Several decode steps whose tokens are all known in advance: a known text
+ * streamed through the cache (the Report §4.4 Q1 streaming evaluation reads a
+ * book token by token), or one layer of a model run chunk by chunk over such a
+ * text.  Exactly `steps` h2o_decode_step calls, step t taking token t, with
+ * bit-identical results.
+ *   q, k, v: device, [steps, B, H, d] in the cache dtype.
+ *   out:     device, float32: step t writes its [B, H, d] output at
+ *            out + t * out_step (elements; a multiple of 4); out_step == 0
+ *            leaves the last step's output.
+ *   evicted: device, [steps, B, H] int32, nullable: each step's evicted
+ *            position (as h2o_decode_step).
+ * steps == 0 does nothing.  Arguments and state are checked once, before the
+ * first step.
+ * Errors: as h2o_decode_step; H2O_ERR_INVALID_ARG also for steps < 0 or a
+ * negative or misaligned out_step; H2O_ERR_STATE when the position counter
+ * would pass INT32_MAX within the steps. */
+h2o_status h2o_decode_steps(h2o_cache* cache, const void* q, const void* k, const void* v, int32_t steps,
+                            float* out, int64_t out_step, int32_t* evicted, void* stream);
+
 /* Copy the cache contents to host memory; synchronises `stream` first and
  * reports any earlier asynchronous fault.  Every pointer is host and nullable.
  *   pos:     [B, H, k] int32, the position held by each slot, -1 for empty slots
@@ -290,6 +309,16 @@ const char* h2o_status_str(h2o_status status);
 
 /* Detail of the last error returned on the calling thread ("" if none). */
 const char* h2o_last_error(void);
+
+/* Measurement aid, not part of the method: read `bytes` of device memory at
+ * `buf` once, as a plain stream (16-byte non-temporal loads, 8 in flight per
+ * lane, 16 blocks of 256 threads per compute unit, each block on contiguous
+ * 32 KiB runs), on `stream`.  Timing it gives the streaming-read bandwidth the GPU sustains,
+ * the practical ceiling for the decode kernel.  `sink` (device, 4 bytes) is
+ * written with probability 2^-32 only (it keeps the loads alive).
+ * Errors: H2O_ERR_INVALID_ARG (NULL pointers, buf or bytes not a multiple of
+ * 16), H2O_ERR_HIP. */
+h2o_status h2o_probe_read(const void* buf, size_t bytes, uint32_t* sink, void* stream);
 
 #ifdef __cplusplus
 }

@@ -597,18 +597,10 @@ h2o_status h2o_prefill_scored(h2o_cache* c, const void* k, const void* v, int32_
 
 namespace {
 
-h2o_status decode_common(h2o_cache* c, const void* q, const void* k, const void* v, const float* new_score,
-                         int32_t score_stride, float* out, int32_t* evicted, void* stream) {
-  if (q == nullptr || k == nullptr || v == nullptr || out == nullptr)
-    return fail(H2O_ERR_INVALID_ARG, "q, k, v and out must be non-NULL");
-  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
-    return fail(H2O_ERR_INVALID_ARG, "q, k, v and out must be 16-byte aligned");
-  if (evicted != nullptr && (reinterpret_cast<uintptr_t>(evicted) & 3u) != 0)
-    return fail(H2O_ERR_INVALID_ARG, "evicted must be 4-byte aligned");
-  if (c->prompt_len < 0) return fail(H2O_ERR_STATE, "decode before prefill");
-  if (c->next_pos == INT32_MAX) return fail(H2O_ERR_STATE, "position counter would overflow int32");
-  DeviceGuard guard(c->device);
-  if (!guard.ok()) return device_fail();
+// One decode step of every unit: the launch and the host-side step counters.
+// The caller has validated the arguments and made the cache's device current.
+hipError_t decode_launch(h2o_cache* c, const void* q, const void* k, const void* v, const float* new_score,
+                         int32_t score_stride, float* out, int32_t* evicted, hipStream_t stream) {
   h2o::DecodeArgs a{};
   a.q = q;
   a.knew = k;
@@ -637,10 +629,28 @@ h2o_status decode_common(h2o_cache* c, const void* q, const void* k, const void*
   a.rope_th = c->rope_th;
   a.nsplit = choose_nsplit(c, c->count, &a.split_len);
   a.c2 = c->c2;
-  const hipError_t e = h2o::launch_decode(c->p.dtype, c->d, a, c->units, static_cast<hipStream_t>(stream));
-  if (e != hipSuccess) return hip_fail(e, "decode launch");
+  const hipError_t e = h2o::launch_decode(c->p.dtype, c->d, a, c->units, stream);
+  if (e != hipSuccess) return e;
   if (c->count < c->k) ++c->count;
   ++c->next_pos;
+  return hipSuccess;
+}
+
+h2o_status decode_common(h2o_cache* c, const void* q, const void* k, const void* v, const float* new_score,
+                         int32_t score_stride, float* out, int32_t* evicted, void* stream) {
+  if (q == nullptr || k == nullptr || v == nullptr || out == nullptr)
+    return fail(H2O_ERR_INVALID_ARG, "q, k, v and out must be non-NULL");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
+    return fail(H2O_ERR_INVALID_ARG, "q, k, v and out must be 16-byte aligned");
+  if (evicted != nullptr && (reinterpret_cast<uintptr_t>(evicted) & 3u) != 0)
+    return fail(H2O_ERR_INVALID_ARG, "evicted must be 4-byte aligned");
+  if (c->prompt_len < 0) return fail(H2O_ERR_STATE, "decode before prefill");
+  if (c->next_pos == INT32_MAX) return fail(H2O_ERR_STATE, "position counter would overflow int32");
+  DeviceGuard guard(c->device);
+  if (!guard.ok()) return device_fail();
+  const hipError_t e = decode_launch(c, q, k, v, new_score, score_stride, out, evicted,
+                                     static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "decode launch");
   return H2O_OK;
 }
 
@@ -650,6 +660,36 @@ h2o_status h2o_decode_step(h2o_cache* c, const void* q, const void* k, const voi
                            int32_t* evicted, void* stream) {
   if (c == nullptr) return fail(H2O_ERR_INVALID_ARG, "cache is NULL");
   return decode_common(c, q, k, v, nullptr, 1, out, evicted, stream);
+}
+
+h2o_status h2o_decode_steps(h2o_cache* c, const void* q, const void* k, const void* v, int32_t steps, float* out,
+                            int64_t out_step, int32_t* evicted, void* stream) {
+  if (c == nullptr) return fail(H2O_ERR_INVALID_ARG, "cache is NULL");
+  if (steps < 0) return fail(H2O_ERR_INVALID_ARG, "steps must be >= 0");
+  if (out_step < 0 || (out_step & 3) != 0) return fail(H2O_ERR_INVALID_ARG, "out_step must be >= 0 and a multiple of 4");
+  if (steps == 0) return H2O_OK;
+  if (q == nullptr || k == nullptr || v == nullptr || out == nullptr)
+    return fail(H2O_ERR_INVALID_ARG, "q, k, v and out must be non-NULL");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
+    return fail(H2O_ERR_INVALID_ARG, "q, k, v and out must be 16-byte aligned");
+  if (evicted != nullptr && (reinterpret_cast<uintptr_t>(evicted) & 3u) != 0)
+    return fail(H2O_ERR_INVALID_ARG, "evicted must be 4-byte aligned");
+  if (c->prompt_len < 0) return fail(H2O_ERR_STATE, "decode before prefill");
+  if (static_cast<int64_t>(c->next_pos) + steps > INT32_MAX)
+    return fail(H2O_ERR_STATE, "position counter would overflow int32");
+  DeviceGuard guard(c->device);
+  if (!guard.ok()) return device_fail();
+  const size_t tok = static_cast<size_t>(c->units) * c->d * c->esize;  // bytes of one step's q, k or v
+  const size_t units = static_cast<size_t>(c->units);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  for (int32_t t = 0; t < steps; ++t) {
+    const size_t off = static_cast<size_t>(t) * tok;
+    const hipError_t e = decode_launch(c, static_cast<const char*>(q) + off, static_cast<const char*>(k) + off,
+                                       static_cast<const char*>(v) + off, nullptr, 1, out + t * out_step,
+                                       evicted != nullptr ? evicted + t * units : nullptr, s);
+    if (e != hipSuccess) return hip_fail(e, "decode launch");
+  }
+  return H2O_OK;
 }
 
 h2o_status h2o_decode_step_scored(h2o_cache* c, const void* q, const void* k, const void* v,

@@ -50,6 +50,7 @@ _SIGNATURES = {
     "h2o_cache_destroy": (_i32, [_vp]),
     "h2o_prefill": (_i32, [_vp, _vp, _vp, _vp, _i32, _vp, _vp]),
     "h2o_decode_step": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp]),
+    "h2o_decode_steps": (_i32, [_vp, _vp, _vp, _vp, _i32, _vp, ctypes.c_int64, _vp, _vp]),
     "h2o_cache_read": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp]),
     "h2o_prefill_stats_read": (_i32, [_vp, _vp, _vp, _vp]),
     "h2o_cache_info": (_i32, [_vp, _p32, _p32, _p32]),
@@ -58,6 +59,7 @@ _SIGNATURES = {
     "h2o_cache_set_pattern": (_i32, [_vp, _i32, _i32, _i32]),
     "h2o_prefill_scored": (_i32, [_vp, _vp, _vp, _i32, _i32, _vp, _vp]),
     "h2o_decode_step_scored": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _vp]),
+    "h2o_probe_read": (_i32, [_vp, ctypes.c_size_t, _vp, _vp]),
     "h2o_status_str": (ctypes.c_char_p, [_i32]),
     "h2o_last_error": (ctypes.c_char_p, []),
 }
@@ -108,6 +110,10 @@ def h2o_decode_step(cache, q, k, v, out, evicted, stream):
     return load().h2o_decode_step(cache, q, k, v, out, evicted, stream)
 
 
+def h2o_decode_steps(cache, q, k, v, steps, out, out_step, evicted, stream):
+    return load().h2o_decode_steps(cache, q, k, v, steps, out, out_step, evicted, stream)
+
+
 def h2o_cache_read(cache, pos, score, k_slots, v_slots, meta, stream):
     return load().h2o_cache_read(cache, pos, score, k_slots, v_slots, meta, stream)
 
@@ -122,6 +128,10 @@ def h2o_cache_info(cache, count, next_pos, prompt_len):
 
 def h2o_column_scores(cache, q, k, n, scores, stream):
     return load().h2o_column_scores(cache, q, k, n, scores, stream)
+
+
+def h2o_probe_read(buf, nbytes, sink, stream):
+    return load().h2o_probe_read(buf, nbytes, sink, stream)
 
 
 def h2o_column_scores_noalloc(params, q, k, n, scores, stream):
@@ -217,6 +227,25 @@ class H2OCache:
         if evicted is not None:
             ep = self._check_t(evicted, (self.B, self.H), torch.int32, "evicted")
         check(h2o_decode_step(self.handle, qp, kp, vp, op, ep, self._stream(stream)), "h2o_decode_step")
+        return out, evicted
+
+    def decode_steps(self, q, k, v, out=None, evicted=None, keep_all=True, stream=None):
+        """``q, k, v``: [T, B, H, d], token t of step t.  ``out``: float32
+        [T, B, H, d] (every step's output) or, with ``keep_all=False``,
+        [B, H, d] (the last step's); ``evicted``: optional int32 [T, B, H]."""
+        torch = self.torch
+        T = q.shape[0]
+        shape = (T, self.B, self.H, self.d)
+        qp = self._check_t(q, shape, self.tdtype, "q")
+        kp = self._check_t(k, shape, self.tdtype, "k")
+        vp = self._check_t(v, shape, self.tdtype, "v")
+        oshape = shape if keep_all else shape[1:]
+        if out is None:
+            out = torch.empty(oshape, dtype=torch.float32, device=self.device)
+        op = self._check_t(out, oshape, torch.float32, "out")
+        ep = self._check_t(evicted, shape[:3], torch.int32, "evicted") if evicted is not None else None
+        step = self.B * self.H * self.d if keep_all else 0
+        check(h2o_decode_steps(self.handle, qp, kp, vp, T, op, step, ep, self._stream(stream)), "h2o_decode_steps")
         return out, evicted
 
     def read(self, stream=None):

@@ -107,6 +107,7 @@ def test_null_and_state_checks_make_no_gpu_call():
     assert H.h2o_cache_destroy(None) == H.H2O_OK
     assert H.h2o_prefill(None, None, None, None, 0, None, None) == H.H2O_ERR_INVALID_ARG
     assert H.h2o_decode_step(None, None, None, None, None, None, None) == H.H2O_ERR_INVALID_ARG
+    assert H.h2o_decode_steps(None, None, None, None, 1, None, 0, None, None) == H.H2O_ERR_INVALID_ARG
     assert H.h2o_cache_read(None, None, None, None, None, None, None) == H.H2O_ERR_INVALID_ARG
     assert H.h2o_prefill_stats_read(None, None, None, None) == H.H2O_ERR_INVALID_ARG
     assert H.h2o_cache_info(None, None, None, None) == H.H2O_ERR_INVALID_ARG

@@ -1,0 +1,97 @@
+"""h2o_decode_steps (several decode steps whose tokens are known in advance) through
+the C ABI (needs an MI355X): bit-identical to the same number of h2o_decode_step
+calls, on every decode path (small budgets, the split path for few units, the
+one-wave blocks, position rolling, a sparse pattern), outputs of every step
+kept or only the last, and its argument checks."""
+import numpy as np
+import pytest
+import torch
+
+from workload import get, scaled, synth
+
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():
+    pytest.skip("no GPU", allow_module_level=True)
+
+from gpu_harness import log  # noqa: E402
+from kv_cache_eviction_prefill_amd import H2OCache, h2o  # noqa: E402
+
+DEV = torch.device("cuda", 0)
+
+
+def _cache(w, q, k, v, L, rope, pattern):
+    c = H2OCache(w.batch, w.heads, w.head_dim, w.heavy_budget, w.recent_budget, dtype=w.dtype, max_prompt=L,
+                 rope_base=rope)
+    if pattern is not None:
+        c.set_pattern(*pattern)
+    c.prefill(*(x[:, :, :L].contiguous() for x in (q, k, v)))
+    return c
+
+
+def _same(a, b, what):
+    a, b = np.asarray(a), np.asarray(b)
+    assert a.shape == b.shape and np.array_equal(a.view(np.uint8), b.view(np.uint8)), what
+
+
+@pytest.mark.parametrize("wl,B,H,d,L,T,heavy,recent,rope,pattern", [
+    ("opt6.7b-layer-b16", 2, 4, 128, 100, 150, 20, 20, 0.0, None),        # single block per unit
+    ("opt6.7b-layer-b16", 1, 4, 128, 400, 200, 150, 150, 0.0, None),      # split path (few units, k = 300)
+    ("opt6.7b-layer-b16", 8, 128, 128, 300, 40, 100, 100, 0.0, None),     # one-wave blocks (1024 units, k > 128)
+    ("opt6.7b-layer-b16", 2, 3, 128, 120, 100, 30, 10, 10000.0, None),    # position rolling
+    ("opt6.7b-layer-b16", 2, 3, 64, 120, 100, 30, 10, 0.0, ("strided", 8, 1)),  # sparse pattern
+    ("tiny-fp32", 1, 2, 64, 256, 64, 26, 26, 0.0, None),                  # fp32 storage
+])
+def test_steps_match_single_steps(wl, B, H, d, L, T, heavy, recent, rope, pattern):
+    w = scaled(get(wl), batch=B, heads=H, head_dim=d, prompt_len=L, decode_steps=T, heavy_budget=heavy,
+               recent_budget=recent, n_anchors=max(1, (L + T) // 50))
+    log(f"case steps {w.dtype} B={B} H={H} d={d} L={L} T={T} k={heavy}+{recent} rope={rope} pattern={pattern}")
+    q, k, v = synth.torch_qkv(w, 0, 0, L + T, DEV)
+    qd, kd, vd = (x[:, :, L:].permute(2, 0, 1, 3).contiguous() for x in (q, k, v))
+    one = _cache(w, q, k, v, L, rope, pattern)
+    o1 = torch.empty((T, B, H, d), dtype=torch.float32, device=DEV)
+    e1 = torch.empty((T, B, H), dtype=torch.int32, device=DEV)
+    for t in range(T):
+        one.decode_step(qd[t], kd[t], vd[t], o1[t], e1[t])
+    many = _cache(w, q, k, v, L, rope, pattern)
+    o2 = torch.full((T, B, H, d), float("nan"), dtype=torch.float32, device=DEV)
+    e2 = torch.full((T, B, H), -7, dtype=torch.int32, device=DEV)
+    half = T // 2  # two calls: the second continues from the first's state
+    many.decode_steps(qd[:half], kd[:half], vd[:half], o2[:half], e2[:half])
+    many.decode_steps(qd[half:], kd[half:], vd[half:], o2[half:], e2[half:])
+    torch.cuda.synchronize()
+    _same(o1.cpu().numpy(), o2.cpu().numpy(), "outputs")
+    _same(e1.cpu().numpy(), e2.cpu().numpy(), "evictions")
+    r1, r2 = one.read(), many.read()
+    for key in ("pos", "score", "k", "v"):
+        _same(r1[key], r2[key], key)
+    assert one.info() == many.info()
+    # only the last output kept
+    last = _cache(w, q, k, v, L, rope, pattern)
+    o3 = torch.empty((B, H, d), dtype=torch.float32, device=DEV)
+    last.decode_steps(qd, kd, vd, o3, keep_all=False)
+    torch.cuda.synchronize()
+    _same(o3.cpu().numpy(), o1[-1].cpu().numpy(), "last output")
+    for c in (one, many, last):
+        c.close()
+
+
+def test_steps_argument_checks():
+    c = H2OCache(1, 2, 128, 4, 4, dtype="bf16", max_prompt=8)
+    buf = torch.zeros((4, 1, 2, 128), dtype=torch.bfloat16, device=DEV)
+    out = torch.zeros((4, 1, 2, 128), dtype=torch.float32, device=DEV)
+    p, o = buf.data_ptr(), out.data_ptr()
+    # before any prefill
+    assert h2o.h2o_decode_steps(c.handle, p, p, p, 4, o, 256, None, None) == h2o.H2O_ERR_STATE
+    prompt = torch.zeros((1, 2, 8, 128), dtype=torch.bfloat16, device=DEV)
+    c.prefill(prompt, prompt, prompt)
+    assert h2o.h2o_decode_steps(c.handle, p, p, p, -1, o, 256, None, None) == h2o.H2O_ERR_INVALID_ARG
+    assert h2o.h2o_decode_steps(c.handle, p, p, p, 4, o, 3, None, None) == h2o.H2O_ERR_INVALID_ARG
+    assert h2o.h2o_decode_steps(c.handle, p + 2, p, p, 4, o, 256, None, None) == h2o.H2O_ERR_INVALID_ARG
+    assert h2o.h2o_decode_steps(c.handle, None, p, p, 4, o, 256, None, None) == h2o.H2O_ERR_INVALID_ARG
+    assert h2o.h2o_decode_steps(c.handle, p, p, p, 0, None, 0, None, None) == h2o.H2O_OK
+    assert c.info()[1] == 8  # rejected calls left the step counter alone
+    assert h2o.h2o_decode_steps(c.handle, p, p, p, 4, o, 256, None, None) == h2o.H2O_OK
+    torch.cuda.synchronize()
+    assert c.info()[1] == 12
+    c.close()
