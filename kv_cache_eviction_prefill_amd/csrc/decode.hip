@@ -81,6 +81,31 @@ struct Layout {
   static_assert(LPR >= kUnroll, "one lane per in-flight slot stores its logit");
 };
 
+// Where one unit's state lives for a step: its slot rows and per-slot score,
+// compensation and position (global memory, or a block's shared-memory copy),
+// and the new token's q/k/v rows.
+template <typename T>
+struct UnitRefs {
+  T* k;
+  T* v;
+  float* sc;
+  float* cp;
+  int32_t* ps;
+  const T* qn;
+  const T* kn;
+  const T* vn;
+};
+
+// A unit's state in global memory.
+template <typename T, int D>
+__device__ inline UnitRefs<T> global_refs(const DecodeArgs& a, int unit) {
+  const size_t u = static_cast<size_t>(unit);
+  return {static_cast<T*>(a.kslots) + u * a.k * D, static_cast<T*>(a.vslots) + u * a.k * D,
+          a.score + u * a.kstride, a.comp + u * a.kstride, a.pos + u * a.kstride,
+          static_cast<const T*>(a.q) + u * D, static_cast<const T*>(a.knew) + u * D,
+          static_cast<const T*>(a.vnew) + u * D};
+}
+
 // Score pass of one unit (whole block): every occupied slot adds its weight
 // exp2(x_j - M) / L with a Kahan-compensated fp32 sum (with fixed scores nothing
 // is added and the new token's score is given); when the cache is full the
@@ -90,16 +115,19 @@ struct Layout {
 // thread's first NP slots' metadata, loaded early by the caller; lg: the unit's
 // logits, the new token's at index k; s_knew/s_vnew: its K/V rows, in LDS.
 template <typename T, int D, int NP, bool kPfX, int NT = kThreads>
-__device__ inline void score_pass(const DecodeArgs& a, int unit, float M, float invL, const float* lg, float x_new,
+__device__ inline void score_pass(const DecodeArgs& a, int unit, const UnitRefs<T>& ur, float M, float invL,
+                                  const float* lg, float x_new,
                                   const float (&pf_s)[NP], const float (&pf_c)[NP], const int32_t (&pf_p)[NP],
                                   const float (&pf_x)[NP], const uint4* s_knew, const uint4* s_vnew,
                                   uint64_t* s_key, int* s_slot, int* s_vrank) {
   using Lay = Layout<T, D>;
   constexpr int EPL = Lay::EPL, LPR = Lay::LPR;
   const int tid = threadIdx.x, g = tid / LPR, r = tid % LPR;
-  float* sc = a.score + static_cast<size_t>(unit) * a.kstride;
-  float* cp = a.comp + static_cast<size_t>(unit) * a.kstride;
-  int32_t* ps = a.pos + static_cast<size_t>(unit) * a.kstride;
+  float* sc = ur.sc;
+  float* cp = ur.cp;
+  int32_t* ps = ur.ps;
+  T* ku = ur.k;
+  T* vu = ur.v;
   const int cnt = a.count;
   const bool full = (cnt == a.k);
   const bool accumulate = a.fixed_new == nullptr;  // else scores are fixed (global comparator)
@@ -180,8 +208,8 @@ __device__ inline void score_pass(const DecodeArgs& a, int unit, float M, float 
             ps[vs] = a.new_pos;
           }
           if (lane < LPR) {
-            T* kd = static_cast<T*>(a.kslots) + (static_cast<size_t>(unit) * a.k + vs) * D;
-            T* vd = static_cast<T*>(a.vslots) + (static_cast<size_t>(unit) * a.k + vs) * D;
+            T* kd = ku + static_cast<size_t>(vs) * D;
+            T* vd = vu + static_cast<size_t>(vs) * D;
             st16(kd + r * EPL, s_knew[r]);
             st16(vd + r * EPL, s_vnew[r]);
           }
@@ -205,8 +233,8 @@ __device__ inline void score_pass(const DecodeArgs& a, int unit, float M, float 
       ps[dst] = a.new_pos;
     }
     if (g == 0) {  // s_knew/s_vnew were written before an earlier barrier
-      T* kd = static_cast<T*>(a.kslots) + (static_cast<size_t>(unit) * a.k + dst) * D;
-      T* vd = static_cast<T*>(a.vslots) + (static_cast<size_t>(unit) * a.k + dst) * D;
+      T* kd = ku + static_cast<size_t>(dst) * D;
+      T* vd = vu + static_cast<size_t>(dst) * D;
       st16(kd + r * EPL, s_knew[r]);
       st16(vd + r * EPL, s_vnew[r]);
     }
@@ -289,39 +317,50 @@ struct RopeLane {
   }
 };
 
-// 8 waves per SIMD: all blocks of a 2048-unit launch are resident at once.  A
-// one-wave block keeps its 8 slots per group in flight with up to 256 registers.
-template <typename T, int D, bool SPLIT, bool ROPE, int NT = kThreads, int UN = kUnroll>
-__global__ __launch_bounds__(NT, NT == kWaveThreads ? 2 : (ROPE || UN > kUnroll ? 4 : 8)) void decode_kernel(
-    DecodeArgs a) {
+// The block's shared memory for one decode step (the logits, [k + 1] on the
+// single-block path, are dynamic shared memory of the launch).
+template <typename T, int D, int NT>
+struct StepShared {
+  static constexpr int LPR = Layout<T, D, NT>::LPR, NG = Layout<T, D, NT>::NG;
+  float m[NG], l[NG];
+  float o[NG][D];
+  uint64_t key[NT / kWave];
+  uint4 knew[LPR], vnew[LPR];
+  int slot, vrank;
+};
+
+// One decode step of one unit (SPLIT: of one slice of its slots).  ku/vu: the
+// unit's slot rows, in global memory, or (LDSKV) the block's copy of them in
+// shared memory, which the step reads and overwrites in place.
+template <typename T, int D, bool SPLIT, bool ROPE, int NT, int UN, bool LDSKV>
+__device__ __forceinline__ void decode_step(const DecodeArgs& a, int unit, int split, const UnitRefs<T>& ur,
+                                            float* s_logit, StepShared<T, D, NT>& sh) {
   using Lay = Layout<T, D, NT>;
   constexpr int NP = NT >= kThreads ? kPrefetch : 512 / NT;  // score-pass slots prefetched per thread
   constexpr int NC = (D + NT - 1) / NT;                       // output columns per thread in the merge
   static_assert(Lay::LPR >= UN, "one lane per in-flight slot stores its logit");
   constexpr int EPL = Lay::EPL, LPR = Lay::LPR, NG = Lay::NG;
-  extern __shared__ float s_logit[];  // single-block path: [k + 1], new token at index k
-  __shared__ float s_m[NG], s_l[NG];
-  __shared__ float s_o[NG][D];
-  __shared__ uint64_t s_key[NT / kWave];
-  __shared__ uint4 s_knew[LPR], s_vnew[LPR];
-  __shared__ int s_slot, s_vrank;
+  float* s_m = sh.m;
+  float* s_l = sh.l;
+  float (*s_o)[D] = sh.o;
+  uint64_t* s_key = sh.key;
+  uint4* s_knew = sh.knew;
+  uint4* s_vnew = sh.vnew;
 
   const int tid = threadIdx.x;
   const int g = tid / LPR, r = tid % LPR;
-  const int unit = SPLIT ? blockIdx.x / a.nsplit : blockIdx.x;
-  const int split = SPLIT ? blockIdx.x % a.nsplit : 0;
   const int s0 = split * a.split_len;
   const int s1 = min(a.count, s0 + a.split_len);
 
-  const T* kb = static_cast<const T*>(a.kslots) + static_cast<size_t>(unit) * a.k * D;
-  const T* vb = static_cast<const T*>(a.vslots) + static_cast<size_t>(unit) * a.k * D;
-  const T* qn = static_cast<const T*>(a.q) + static_cast<size_t>(unit) * D;
-  const T* kn = static_cast<const T*>(a.knew) + static_cast<size_t>(unit) * D;
-  const T* vn = static_cast<const T*>(a.vnew) + static_cast<size_t>(unit) * D;
+  const T* kb = ur.k;
+  const T* vb = ur.v;
+  const T* qn = ur.qn;
+  const T* kn = ur.kn;
+  const T* vn = ur.vn;
   float* glog = SPLIT ? a.logits + static_cast<size_t>(unit) * (a.k + 1) : nullptr;
-  float* sc = a.score + static_cast<size_t>(unit) * a.kstride;
-  float* cp = a.comp + static_cast<size_t>(unit) * a.kstride;
-  int32_t* ps = a.pos + static_cast<size_t>(unit) * a.kstride;
+  const float* sc = ur.sc;
+  const float* cp = ur.cp;
+  const int32_t* ps = ur.ps;
 
   float qf[EPL];
   Elem<T>::unpack(ld16(qn + r * EPL), qf);
@@ -382,8 +421,13 @@ __global__ __launch_bounds__(NT, NT == kWaveThreads ? 2 : (ROPE || UN > kUnroll 
 #pragma unroll
     for (int u = 0; u < UN; ++u) {
       const int j = min(base + u * NG, s1 - 1);
-      kr[u] = ld16_stream(kb + static_cast<size_t>(j) * D + r * EPL);
-      vr[u] = ld16_stream(vb + static_cast<size_t>(j) * D + r * EPL);
+      if constexpr (LDSKV) {
+        kr[u] = ld16(kb + static_cast<size_t>(j) * D + r * EPL);
+        vr[u] = ld16(vb + static_cast<size_t>(j) * D + r * EPL);
+      } else {
+        kr[u] = ld16_stream(kb + static_cast<size_t>(j) * D + r * EPL);
+        vr[u] = ld16_stream(vb + static_cast<size_t>(j) * D + r * EPL);
+      }
       if constexpr (ROPE) rkj[u] = rkb[j];
     }
     float x[UN];
@@ -469,9 +513,21 @@ __global__ __launch_bounds__(NT, NT == kWaveThreads ? 2 : (ROPE || UN > kUnroll 
 #pragma unroll
     for (int c = 0; c < NC; ++c)
       if (tid + c * NT < D) a.out[static_cast<size_t>(unit) * D + tid + c * NT] = acc[c] / Ls;
-    score_pass<T, D, NP, false, NT>(a, unit, M, 1.f / Ls, s_logit, s_logit[a.k], pf_s, pf_c, pf_p, pf_s, s_knew,
-                                    s_vnew, s_key, &s_slot, &s_vrank);
+    score_pass<T, D, NP, false, NT>(a, unit, ur, M, 1.f / Ls, s_logit, s_logit[a.k], pf_s, pf_c, pf_p, pf_s,
+                                    s_knew, s_vnew, s_key, &sh.slot, &sh.vrank);
   }
+}
+
+// 8 waves per SIMD: all blocks of a 2048-unit launch are resident at once.  A
+// one-wave block keeps its 8 slots per group in flight with up to 256 registers.
+template <typename T, int D, bool SPLIT, bool ROPE, int NT = kThreads, int UN = kUnroll>
+__global__ __launch_bounds__(NT, NT == kWaveThreads ? 2 : (ROPE || UN > kUnroll ? 4 : 8)) void decode_kernel(
+    DecodeArgs a) {
+  extern __shared__ float s_logit[];  // single-block path: [k + 1], new token at index k
+  __shared__ StepShared<T, D, NT> sh;
+  const int unit = SPLIT ? blockIdx.x / a.nsplit : blockIdx.x;
+  const int split = SPLIT ? blockIdx.x % a.nsplit : 0;
+  decode_step<T, D, SPLIT, ROPE, NT, UN, false>(a, unit, split, global_refs<T, D>(a, unit), s_logit, sh);
 }
 
 // Second launch of the split path: one block per unit merges the nsplit
@@ -533,8 +589,135 @@ __global__ __launch_bounds__(kFinishThreads) void decode_finish(DecodeArgs a) {
     }
   }
   if (tid < D) a.out[static_cast<size_t>(unit) * D + tid] = og / Lg;
-  score_pass<T, D, NP, true, NT>(a, unit, Mg, 1.f / Lg, lg, x_new, pf_s, pf_c, pf_p, pf_x, s_knew, s_vnew, s_key,
-                             &s_slot, &s_vrank);
+  score_pass<T, D, NP, true, NT>(a, unit, global_refs<T, D>(a, unit), Mg, 1.f / Lg, lg, x_new, pf_s, pf_c, pf_p,
+                                 pf_x, s_knew, s_vnew, s_key, &s_slot, &s_vrank);
+}
+
+// Several decode steps per launch, one unit per block, with the unit's state
+// held in the block's shared memory for the whole launch: its K/V slot rows and
+// per-slot score, compensation and position are read once at the start and
+// written back once at the end, every step in between attends, scores, evicts
+// and overwrites in shared memory, and the next step's q/k/v rows are fetched
+// while the current step runs.  Each step is decode_step with the block shape
+// the one-step launch would use, so the results are bit-identical to `steps`
+// one-step launches; only where the state lives changes.  For caches on the
+// single-block path whose state fits in a block's shared memory.
+template <typename T, int D, int NT, int UN>
+__global__ __launch_bounds__(NT) void decode_resident(DecodeArgs a0, int steps, int64_t tok_bytes,
+                                                      int64_t out_step) {
+  constexpr int EPL = Layout<T, D, NT>::EPL, LPR = Layout<T, D, NT>::LPR;
+  static_assert(3 * LPR <= NT, "one lane per 16 bytes of the next token's q/k/v rows");
+  // [k + 1] logits | K rows | V rows | score | comp | pos | 2 x (q, k, v) rows,
+  // each part 16-byte aligned (resident_dyn_bytes)
+  extern __shared__ __align__(16) float s_dyn[];
+  __shared__ StepShared<T, D, NT> sh;
+  const int unit = blockIdx.x, k = a0.k, tid = threadIdx.x;
+  const int k4 = (k + 3) & ~3;
+  float* s_logit = s_dyn;
+  T* sk = reinterpret_cast<T*>(s_dyn + k4 + 4);
+  T* sv = sk + static_cast<size_t>(k) * D;
+  float* ssc = reinterpret_cast<float*>(sv + static_cast<size_t>(k) * D);
+  float* scp = ssc + k4;
+  int32_t* sps = reinterpret_cast<int32_t*>(scp + k4);
+  T* stok = reinterpret_cast<T*>(sps + k4);  // [2][3][D]: q, k, v of the current and the next step
+  const UnitRefs<T> g = global_refs<T, D>(a0, unit);
+  const int c0 = a0.count;
+  for (int i = tid; i < c0 * (D / EPL); i += NT) {
+    st16(sk + i * EPL, ld16(g.k + i * EPL));
+    st16(sv + i * EPL, ld16(g.v + i * EPL));
+  }
+  for (int j = tid; j < c0; j += NT) {
+    ssc[j] = g.sc[j];
+    scp[j] = g.cp[j];
+    sps[j] = g.ps[j];
+  }
+  // lanes 0..3*LPR-1 each move 16 bytes of the next token's q, k or v row
+  const int which = tid / LPR, part = tid % LPR;
+  const T* src = which == 0 ? g.qn : which == 1 ? g.kn : g.vn;
+  if (which < 3) st16(stok + which * D + part * EPL, ld16(src + part * EPL));
+  __syncthreads();
+  DecodeArgs a = a0;
+  for (int t = 0; t < steps; ++t) {
+    const int cur = t & 1;
+    uint4 nxt = make_uint4(0u, 0u, 0u, 0u);
+    if (which < 3 && t + 1 < steps)
+      nxt = ld16(reinterpret_cast<const char*>(src) + (t + 1) * tok_bytes + part * 16);
+    a.out = a0.out + t * out_step;
+    a.evicted = a0.evicted != nullptr ? a0.evicted + static_cast<size_t>(t) * gridDim.x : nullptr;
+    a.count = min(k, c0 + t);
+    a.split_len = max(a.count, 1);  // one block holds all of the unit's slots
+    a.new_pos = a0.new_pos + t;
+    a.cand_limit = a0.cand_limit + t;
+    const T* tk = stok + cur * 3 * D;
+    const UnitRefs<T> ur{sk, sv, ssc, scp, sps, tk, tk + D, tk + 2 * D};
+    decode_step<T, D, false, false, NT, UN, true>(a, unit, 0, ur, s_logit, sh);
+    if (which < 3 && t + 1 < steps) st16(stok + (cur ^ 1) * 3 * D + which * D + part * EPL, nxt);
+    __syncthreads();  // this step's writes and the next token's rows before the next step
+  }
+  const int c1 = min(k, c0 + steps);
+  for (int i = tid; i < c1 * (D / EPL); i += NT) {
+    st16(g.k + i * EPL, ld16(sk + i * EPL));
+    st16(g.v + i * EPL, ld16(sv + i * EPL));
+  }
+  for (int j = tid; j < c1; j += NT) {
+    g.sc[j] = ssc[j];
+    g.cp[j] = scp[j];
+    g.ps[j] = sps[j];
+  }
+}
+
+// Block shape of the one-step, single-block launch (launch_typed) for this cache.
+struct Shape {
+  int nt, un;
+};
+template <typename T, int D, bool ROPE>
+Shape single_block_shape(int units, int k) {
+  if constexpr (std::is_same<T, bf16_t>::value && D == 128 && !ROPE)
+    if (units >= kFewUnits && k > kSmallK) return {kWaveThreads, kWaveUnroll};
+  if (units < kFewUnits) return {kThreads, kUnrollFew};
+  if (k <= kSmallK && units >= kSmallKUnits) return {kSmallThreads, kUnroll};
+  return {kThreads, kUnroll};
+}
+
+// Dynamic shared memory of decode_resident: logits, K and V rows, score,
+// compensation and position per slot, two sets of the new token's q/k/v rows.
+template <typename T, int D>
+size_t resident_dyn_bytes(int k) {
+  const size_t k4 = static_cast<size_t>((k + 3) & ~3);
+  return (k4 + 4) * 4 + 2 * static_cast<size_t>(k) * D * sizeof(T) + 3 * k4 * 4 + 6 * D * sizeof(T);
+}
+
+template <typename T, int D>
+size_t resident_lds(int nt, int k) {
+  const size_t fixed = nt == kThreads ? sizeof(StepShared<T, D, kThreads>) : sizeof(StepShared<T, D, kSmallThreads>);
+  return resident_dyn_bytes<T, D>(k) + fixed;
+}
+
+constexpr size_t kResidentLdsMax = 64 * 1024;  // shared memory one block may use
+
+template <typename T, int D>
+bool resident_fits(int units, int k) {
+  const Shape sh = single_block_shape<T, D, false>(units, k);
+  return sh.nt != kWaveThreads && resident_lds<T, D>(sh.nt, k) <= kResidentLdsMax;
+}
+
+template <typename T, int D>
+hipError_t launch_resident_typed(const DecodeArgs& a, int units, int steps, int64_t tok_bytes, int64_t out_step,
+                                 hipStream_t s) {
+  const Shape sh = single_block_shape<T, D, false>(units, a.k);
+  const size_t dyn = resident_dyn_bytes<T, D>(a.k);
+  if (sh.nt == kThreads && sh.un == kUnrollFew)
+    hipLaunchKernelGGL((decode_resident<T, D, kThreads, kUnrollFew>), dim3(units), dim3(kThreads), dyn, s, a, steps,
+                       tok_bytes, out_step);
+  else if (sh.nt == kSmallThreads)
+    hipLaunchKernelGGL((decode_resident<T, D, kSmallThreads, kUnroll>), dim3(units), dim3(kSmallThreads), dyn, s, a,
+                       steps, tok_bytes, out_step);
+  else if (sh.nt == kThreads)
+    hipLaunchKernelGGL((decode_resident<T, D, kThreads, kUnroll>), dim3(units), dim3(kThreads), dyn, s, a, steps,
+                       tok_bytes, out_step);
+  else
+    return hipErrorInvalidConfiguration;
+  return hipGetLastError();
 }
 
 template <typename T, int D, bool ROPE>
@@ -572,6 +755,23 @@ hipError_t launch_typed(const DecodeArgs& a, int units, hipStream_t s) {
 }
 
 }  // namespace
+
+bool decode_resident_fits(int dtype, int head_dim, int units, int k) {
+  if (dtype == 0) return head_dim == 64 ? resident_fits<float, 64>(units, k) : resident_fits<float, 128>(units, k);
+  return head_dim == 64 ? resident_fits<bf16_t, 64>(units, k) : resident_fits<bf16_t, 128>(units, k);
+}
+
+hipError_t launch_decode_resident(int dtype, int head_dim, const DecodeArgs& a, int units, int steps,
+                                  int64_t tok_bytes, int64_t out_step, hipStream_t s) {
+  if (!decode_resident_fits(dtype, head_dim, units, a.k) || a.rank != nullptr || a.fixed_new != nullptr ||
+      a.nsplit != 1)
+    return hipErrorInvalidConfiguration;
+  if (dtype == 0)
+    return head_dim == 64 ? launch_resident_typed<float, 64>(a, units, steps, tok_bytes, out_step, s)
+                          : launch_resident_typed<float, 128>(a, units, steps, tok_bytes, out_step, s);
+  return head_dim == 64 ? launch_resident_typed<bf16_t, 64>(a, units, steps, tok_bytes, out_step, s)
+                        : launch_resident_typed<bf16_t, 128>(a, units, steps, tok_bytes, out_step, s);
+}
 
 hipError_t launch_decode(int dtype, int head_dim, const DecodeArgs& a, int units, hipStream_t s) {
   if (a.rank != nullptr) {

@@ -597,10 +597,9 @@ h2o_status h2o_prefill_scored(h2o_cache* c, const void* k, const void* v, int32_
 
 namespace {
 
-// One decode step of every unit: the launch and the host-side step counters.
-// The caller has validated the arguments and made the cache's device current.
-hipError_t decode_launch(h2o_cache* c, const void* q, const void* k, const void* v, const float* new_score,
-                         int32_t score_stride, float* out, int32_t* evicted, hipStream_t stream) {
+// The launch arguments of the cache's next decode step.
+h2o::DecodeArgs decode_args(const h2o_cache* c, const void* q, const void* k, const void* v, const float* new_score,
+                            int32_t score_stride, float* out, int32_t* evicted) {
   h2o::DecodeArgs a{};
   a.q = q;
   a.knew = k;
@@ -629,12 +628,23 @@ hipError_t decode_launch(h2o_cache* c, const void* q, const void* k, const void*
   a.rope_th = c->rope_th;
   a.nsplit = choose_nsplit(c, c->count, &a.split_len);
   a.c2 = c->c2;
+  return a;
+}
+
+// One decode step of every unit: the launch and the host-side step counters.
+// The caller has validated the arguments and made the cache's device current.
+hipError_t decode_launch(h2o_cache* c, const void* q, const void* k, const void* v, const float* new_score,
+                         int32_t score_stride, float* out, int32_t* evicted, hipStream_t stream) {
+  const h2o::DecodeArgs a = decode_args(c, q, k, v, new_score, score_stride, out, evicted);
   const hipError_t e = h2o::launch_decode(c->p.dtype, c->d, a, c->units, stream);
   if (e != hipSuccess) return e;
   if (c->count < c->k) ++c->count;
   ++c->next_pos;
   return hipSuccess;
 }
+
+// Steps per launch of the shared-memory-resident multi-step decode.
+constexpr int32_t kResidentSteps = 65536;
 
 h2o_status decode_common(h2o_cache* c, const void* q, const void* k, const void* v, const float* new_score,
                          int32_t score_stride, float* out, int32_t* evicted, void* stream) {
@@ -682,6 +692,28 @@ h2o_status h2o_decode_steps(h2o_cache* c, const void* q, const void* k, const vo
   const size_t tok = static_cast<size_t>(c->units) * c->d * c->esize;  // bytes of one step's q, k or v
   const size_t units = static_cast<size_t>(c->units);
   hipStream_t s = static_cast<hipStream_t>(stream);
+  // Caches on the single-block path for every one of these steps whose rows fit
+  // in a block's shared memory run several steps per launch with the rows held
+  // there (bit-identical to one launch per step).
+  const int64_t last_count = std::min<int64_t>(c->k, static_cast<int64_t>(c->count) + steps - 1);
+  const bool resident = c->rank == nullptr && (c->max_split == 1 || last_count < 2 * kMinSlotsPerSplit) &&
+                        h2o::decode_resident_fits(c->p.dtype, c->d, c->units, c->k);
+  if (resident) {
+    for (int32_t t0 = 0; t0 < steps; t0 += kResidentSteps) {
+      const int32_t n = std::min(kResidentSteps, steps - t0);
+      const size_t off = static_cast<size_t>(t0) * tok;
+      const h2o::DecodeArgs a =
+          decode_args(c, static_cast<const char*>(q) + off, static_cast<const char*>(k) + off,
+                      static_cast<const char*>(v) + off, nullptr, 1, out + t0 * out_step,
+                      evicted != nullptr ? evicted + t0 * units : nullptr);
+      const hipError_t e = h2o::launch_decode_resident(c->p.dtype, c->d, a, c->units, n,
+                                                       static_cast<int64_t>(tok), out_step, s);
+      if (e != hipSuccess) return hip_fail(e, "decode launch");
+      c->count = static_cast<int32_t>(std::min<int64_t>(c->k, static_cast<int64_t>(c->count) + n));
+      c->next_pos += n;
+    }
+    return H2O_OK;
+  }
   for (int32_t t = 0; t < steps; ++t) {
     const size_t off = static_cast<size_t>(t) * tok;
     const hipError_t e = decode_launch(c, static_cast<const char*>(q) + off, static_cast<const char*>(k) + off,

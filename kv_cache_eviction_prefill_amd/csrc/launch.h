@@ -39,6 +39,15 @@ struct DecodeArgs {
 
 hipError_t launch_decode(int dtype, int head_dim, const DecodeArgs& a, int units, hipStream_t s);
 
+// Several decode steps in one launch with every unit's K/V slot rows held in
+// shared memory (single-block path, no position rolling, no fixed scores):
+// `a` describes the first step; step t reads its q/k/v at + t * tok_bytes and
+// writes out + t * out_step and evicted + t * units.  Results equal `steps`
+// launch_decode calls.  decode_resident_fits says whether a cache's rows fit.
+bool decode_resident_fits(int dtype, int head_dim, int units, int k);
+hipError_t launch_decode_resident(int dtype, int head_dim, const DecodeArgs& a, int units, int steps,
+                                  int64_t tok_bytes, int64_t out_step, hipStream_t s);
+
 // Prefill stages: the two score passes (row normalisers, column sums) and the
 // select + fill.
 enum PrefillStage : int32_t { kStageScores = 1, kStageSelect = 2 };

@@ -1,7 +1,8 @@
 """h2o_decode_steps (several decode steps whose tokens are known in advance) through
 the C ABI (needs an MI355X): bit-identical to the same number of h2o_decode_step
 calls, on every decode path (small budgets, the split path for few units, the
-one-wave blocks, position rolling, a sparse pattern), outputs of every step
+one-wave blocks, position rolling, a sparse pattern, and the launches that hold
+each unit's rows in shared memory over all the steps), outputs of every step
 kept or only the last, and its argument checks."""
 import numpy as np
 import pytest
@@ -41,6 +42,12 @@ def _same(a, b, what):
     ("opt6.7b-layer-b16", 2, 3, 128, 120, 100, 30, 10, 10000.0, None),    # position rolling
     ("opt6.7b-layer-b16", 2, 3, 64, 120, 100, 30, 10, 0.0, ("strided", 8, 1)),  # sparse pattern
     ("tiny-fp32", 1, 2, 64, 256, 64, 26, 26, 0.0, None),                  # fp32 storage
+    # rows held in shared memory over the steps (one launch for all of them)
+    ("opt6.7b-layer-b16", 16, 32, 128, 512, 64, 52, 52, 0.0, None),      # the 512-token layer: 512 units, k = 104
+    ("opt6.7b-layer-b16", 8, 128, 128, 300, 40, 21, 21, 0.0, None),      # 1024 units, small budget
+    ("opt6.7b-layer-b16", 8, 128, 64, 300, 40, 100, 100, 0.0, None),     # 1024 units, d = 64, k = 200
+    ("opt6.7b-layer-b16", 2, 4, 128, 20, 60, 20, 20, 0.0, None),         # the cache fills during the steps
+    ("opt6.7b-layer-b16", 2, 4, 128, 100, 80, 40, 0, 0.0, None),         # K_r = 0: the new token may be the victim
 ])
 def test_steps_match_single_steps(wl, B, H, d, L, T, heavy, recent, rope, pattern):
     w = scaled(get(wl), batch=B, heads=H, head_dim=d, prompt_len=L, decode_steps=T, heavy_budget=heavy,
