@@ -131,6 +131,7 @@ __device__ inline void score_pass(const DecodeArgs& a, int unit, const UnitRefs<
   const int cnt = a.count;
   const bool full = (cnt == a.k);
   const bool accumulate = a.fixed_new == nullptr;  // else scores are fixed (global comparator)
+  const bool compensate = a.new_pos >= a.plain_until;
 
   uint64_t best = kNoKey;
   int best_slot = -1;
@@ -153,17 +154,21 @@ __device__ inline void score_pass(const DecodeArgs& a, int unit, const UnitRefs<
     } else {
       xj = lg[j];
       sj = sc[j];
-      cj = cp[j];
+      cj = compensate ? cp[j] : 0.f;
       pj = ps[j];
     }
     if (accumulate) {
       const float w = fast_exp2(xj - M) * invL;
-      const float y = w - cj;  // Kahan-compensated add of this step's weight
-      const float t = sj + y;
-      cj = (t - sj) - y;
-      sj = t;
+      if (compensate) {
+        const float y = w - cj;  // Kahan-compensated add of this step's weight
+        const float t = sj + y;
+        cj = (t - sj) - y;
+        sj = t;
+        cp[j] = cj;
+      } else {
+        sj = sj + w;  // the compensation stays 0 until compensated adds begin
+      }
       sc[j] = sj;
-      cp[j] = cj;
     }
     if (full && pj <= a.cand_limit) {
       const uint64_t key = evict_key(sj, pj) | pattern_bit(a.pat_kind, a.pat_period, a.pat_width, pj, a.new_pos);
@@ -386,7 +391,7 @@ __device__ __forceinline__ void decode_step(const DecodeArgs& a, int unit, int s
       const int j = tid + i * NT;
       const bool ok = j < a.count;
       pf_s[i] = ok ? sc[j] : 0.f;
-      pf_c[i] = ok ? cp[j] : 0.f;
+      pf_c[i] = ok && a.new_pos >= a.plain_until ? cp[j] : 0.f;
       pf_p[i] = ok ? ps[j] : 0;
     }
   }
@@ -560,7 +565,7 @@ __global__ __launch_bounds__(kFinishThreads) void decode_finish(DecodeArgs a) {
     const bool ok = j < a.count;
     pf_x[i] = ok ? lg[j] : 0.f;
     pf_s[i] = ok ? sc[j] : 0.f;
-    pf_c[i] = ok ? cp[j] : 0.f;
+    pf_c[i] = ok && a.new_pos >= a.plain_until ? cp[j] : 0.f;
     pf_p[i] = ok ? ps[j] : 0;
   }
   const float x_new = lg[a.k];

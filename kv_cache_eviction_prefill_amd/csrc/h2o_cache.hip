@@ -597,6 +597,15 @@ h2o_status h2o_prefill_scored(h2o_cache* c, const void* k, const void* v, int32_
 
 namespace {
 
+// Scores gain one weight per decode step.  The first kPlainSteps steps after a
+// prefill add them in plain fp32: a sum of n non-negative fp32 terms is within
+// (n - 1) * 2^-24 relative of the exact sum, so a score that started from its
+// prompt column sum is within 1024 * 2^-24 = 6.1e-5 after them, inside the
+// 1e-4 score tolerance, and the compensation array is neither read nor
+// written.  Later steps use Kahan-compensated adds (the 4 M-token stream needs
+// them: plain fp32 drifts to ~1e-3 there), starting from a compensation of 0.
+constexpr int32_t kPlainSteps = 1024;
+
 // The launch arguments of the cache's next decode step.
 h2o::DecodeArgs decode_args(const h2o_cache* c, const void* q, const void* k, const void* v, const float* new_score,
                             int32_t score_stride, float* out, int32_t* evicted) {
@@ -619,6 +628,7 @@ h2o::DecodeArgs decode_args(const h2o_cache* c, const void* q, const void* k, co
   a.new_pos = c->next_pos;
   a.cand_limit = c->next_pos - c->p.recent_budget;
   a.new_is_candidate = c->p.recent_budget == 0 ? 1 : 0;
+  a.plain_until = c->prompt_len > INT32_MAX - kPlainSteps ? INT32_MAX : c->prompt_len + kPlainSteps;
   a.fixed_new = new_score;
   a.fixed_stride = score_stride;
   a.pat_kind = c->pat_kind;

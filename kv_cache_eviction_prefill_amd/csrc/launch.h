@@ -29,6 +29,8 @@ struct DecodeArgs {
   int32_t new_pos;     // position i of the new token
   int32_t cand_limit;  // positions <= cand_limit are eviction candidates (i - K_r)
   int32_t new_is_candidate;  // K_r == 0: the new token competes for eviction
+  int32_t plain_until;  // steps at positions below this add weights to scores in plain fp32 (the
+                        // compensation stays 0); from it on, Kahan-compensated
   int32_t pat_kind, pat_period, pat_width;  // sparse pattern kept before heavy hitters
   int32_t* rank;       // position rolling: [units, kstride] slot positions inside the cache, or nullptr
   const float* rope_th;  // [d/2] (hi, lo) theta_m / (2 pi), when rank != nullptr
