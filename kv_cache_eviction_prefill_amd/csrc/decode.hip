@@ -65,6 +65,12 @@ constexpr int kWaveUnroll = 8;
 // launch, per step: slices of 64 slots 16.0 -> 15.1 us, of 128 16.6 -> 16.4 us;
 // with slices of 256 the 256-thread blocks stay faster, 19.4 against 21.1 us).
 constexpr int kWaveSplitLen = 128;
+// Slices of at most kTwoWaveSplitLen slots are attended by two-wave blocks (the
+// staged multi-step launch, 32 units x 2048 slots: 11.3 -> 10.3 us per step
+// against one wave).  Multi-step launches attend with the same block shapes as
+// one-step launches, so their partials round alike.
+constexpr int kTwoWaveSplitLen = 64;
+constexpr int kTwoWaveThreads = 128;
 constexpr int kPrefetch = 2;  // score-pass slots per thread whose metadata is loaded up front
 constexpr uint64_t kNoKey = ~0ull;
 constexpr int kNewSlot = -2;
@@ -104,6 +110,17 @@ __device__ inline UnitRefs<T> global_refs(const DecodeArgs& a, int unit) {
           a.score + u * a.kstride, a.comp + u * a.kstride, a.pos + u * a.kstride,
           static_cast<const T*>(a.q) + u * D, static_cast<const T*>(a.knew) + u * D,
           static_cast<const T*>(a.vnew) + u * D};
+}
+
+// Adds a step's weight w to a slot's score s with compensation c: a Kahan step
+// when compensating, a plain fp32 add otherwise (c stays 0).  No product is
+// contracted into these additions, so every kernel that scores rounds alike.
+__device__ inline void add_weight(float w, float& s, float& c, bool compensate) {
+#pragma clang fp contract(off)
+  const float y = w - c;
+  const float t = s + y;
+  c = compensate ? (t - s) - y : 0.f;
+  s = t;
 }
 
 // Score pass of one unit (whole block): every occupied slot adds its weight
@@ -158,16 +175,8 @@ __device__ inline void score_pass(const DecodeArgs& a, int unit, const UnitRefs<
       pj = ps[j];
     }
     if (accumulate) {
-      const float w = fast_exp2(xj - M) * invL;
-      if (compensate) {
-        const float y = w - cj;  // Kahan-compensated add of this step's weight
-        const float t = sj + y;
-        cj = (t - sj) - y;
-        sj = t;
-        cp[j] = cj;
-      } else {
-        sj = sj + w;  // the compensation stays 0 until compensated adds begin
-      }
+      add_weight(fast_exp2(xj - M) * invL, sj, cj, compensate);
+      if (compensate) cp[j] = cj;  // the compensation stays 0 until compensated adds begin
       sc[j] = sj;
     }
     if (full && pj <= a.cand_limit) {
@@ -322,6 +331,21 @@ struct RopeLane {
   }
 };
 
+// Barrier among a block's NT threads before they read each other's shared
+// memory: a one-wave block's lanes issue in order, so ordering the wave's own
+// shared-memory traffic is enough (and such a block may run inside a larger
+// launch whose other waves have left).
+template <int NT>
+__device__ inline void block_sync() {
+  if constexpr (NT == kWave) {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  } else {
+    __syncthreads();
+  }
+}
+
 // The block's shared memory for one decode step (the logits, [k + 1] on the
 // single-block path, are dynamic shared memory of the launch).
 template <typename T, int D, int NT>
@@ -336,7 +360,8 @@ struct StepShared {
 
 // One decode step of one unit (SPLIT: of one slice of its slots).  ku/vu: the
 // unit's slot rows, in global memory, or (LDSKV) the block's copy of them in
-// shared memory, which the step reads and overwrites in place.
+// shared memory, which the step reads and overwrites in place (a split step:
+// the copy of its slice's rows alone, row 0 the slice's first slot).
 template <typename T, int D, bool SPLIT, bool ROPE, int NT, int UN, bool LDSKV>
 __device__ __forceinline__ void decode_step(const DecodeArgs& a, int unit, int split, const UnitRefs<T>& ur,
                                             float* s_logit, StepShared<T, D, NT>& sh) {
@@ -427,8 +452,9 @@ __device__ __forceinline__ void decode_step(const DecodeArgs& a, int unit, int s
     for (int u = 0; u < UN; ++u) {
       const int j = min(base + u * NG, s1 - 1);
       if constexpr (LDSKV) {
-        kr[u] = ld16(kb + static_cast<size_t>(j) * D + r * EPL);
-        vr[u] = ld16(vb + static_cast<size_t>(j) * D + r * EPL);
+        const int jl = SPLIT ? j - s0 : j;  // a split block holds its slice alone
+        kr[u] = ld16(kb + static_cast<size_t>(jl) * D + r * EPL);
+        vr[u] = ld16(vb + static_cast<size_t>(jl) * D + r * EPL);
       } else {
         kr[u] = ld16_stream(kb + static_cast<size_t>(j) * D + r * EPL);
         vr[u] = ld16_stream(vb + static_cast<size_t>(j) * D + r * EPL);
@@ -489,7 +515,7 @@ __device__ __forceinline__ void decode_step(const DecodeArgs& a, int unit, int s
   }
 #pragma unroll
   for (int e = 0; e < EPL; ++e) s_o[g][r * EPL + e] = o[e];
-  __syncthreads();
+  block_sync<NT>();
   float M = -INFINITY;
 #pragma unroll 8
   for (int t = 0; t < NG; ++t) M = fmaxf(M, s_m[t]);
@@ -535,6 +561,44 @@ __global__ __launch_bounds__(NT, NT == kWaveThreads ? 2 : (ROPE || UN > kUnroll 
   decode_step<T, D, SPLIT, ROPE, NT, UN, false>(a, unit, split, global_refs<T, D>(a, unit), s_logit, sh);
 }
 
+// Butterfly reductions over the wave: at every level the two partner lanes
+// combine the same two values, so every lane ends with the same result.
+__device__ inline float wave_max_f(float v) {
+#pragma unroll
+  for (int m = kWave / 2; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m, kWave));
+  return v;
+}
+__device__ inline float wave_sum_f(float v) {
+#pragma unroll
+  for (int m = kWave / 2; m >= 1; m >>= 1) v += __shfl_xor(v, m, kWave);
+  return v;
+}
+
+// Merge of one unit's split partials (max m_q, sum l_q, numerator o_q), the
+// same in every wave: lane q holds partial q's (m_q, l_q) (pm, pl; -inf and 0
+// past nsplit), Mg = max_q m_q, the weight w_q = exp2(m_q - Mg) and
+// Lg = sum_q l_q w_q.  Returns this lane's w_q (0 past nsplit).
+__device__ inline float merge_weights(float pm, float pl, int nsplit, float& Mg, float& Lg) {
+#pragma clang fp contract(off)
+  const bool ok = static_cast<int>(threadIdx.x & (kWave - 1)) < nsplit;
+  Mg = wave_max_f(pm);
+  const float w = ok ? fast_exp2(pm - Mg) : 0.f;
+  Lg = wave_sum_f(pl * w);
+  return w;
+}
+
+// One column of the merged numerator, sum_q o_q w_q in order of q: po holds the
+// column of every partial (0 past nsplit), w the lanes' partial weights.
+template <int NS>
+__device__ inline float merge_column(const float (&po)[NS], float w) {
+  static_assert(NS <= kWave, "one lane per partial");
+  float og = 0.f;
+#pragma unroll
+  for (int q = 0; q < NS; ++q)
+    og = fmaf(po[q], __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), q)), og);
+  return og;
+}
+
 // Second launch of the split path: one block per unit merges the nsplit
 // partials of the first launch into the output and runs the score pass over the
 // logits it wrote.
@@ -544,7 +608,6 @@ __global__ __launch_bounds__(kFinishThreads) void decode_finish(DecodeArgs a) {
   constexpr int EPL = Lay::EPL, LPR = Lay::LPR;
   constexpr int NT = kFinishThreads;
   constexpr int NP = kFinishPrefetch;
-  __shared__ float s_pm[kMaxSplitBlocks], s_pl[kMaxSplitBlocks];
   __shared__ uint64_t s_key[NT / kWave];
   __shared__ uint4 s_knew[LPR], s_vnew[LPR];
   __shared__ int s_slot, s_vrank;
@@ -573,29 +636,242 @@ __global__ __launch_bounds__(kFinishThreads) void decode_finish(DecodeArgs a) {
 #pragma unroll
   for (int s = 0; s < kMaxSplitBlocks; ++s)
     po[s] = (tid < D && s < a.nsplit) ? pu[s * (2 + D) + 2 + tid] : 0.f;
-  if (tid < a.nsplit) {
-    s_pm[tid] = pu[tid * (2 + D)];
-    s_pl[tid] = pu[tid * (2 + D) + 1];
-  }
+  const int lane = tid & (kWave - 1);
+  const float pm = lane < a.nsplit ? pu[lane * (2 + D)] : -INFINITY;
+  const float pl = lane < a.nsplit ? pu[lane * (2 + D) + 1] : 0.f;
   if (tid < LPR) {
     s_knew[tid] = ld16(static_cast<const T*>(a.knew) + static_cast<size_t>(unit) * D + tid * EPL);
     s_vnew[tid] = ld16(static_cast<const T*>(a.vnew) + static_cast<size_t>(unit) * D + tid * EPL);
   }
   __syncthreads();
-  float Mg = -INFINITY;
-  for (int s = 0; s < a.nsplit; ++s) Mg = fmaxf(Mg, s_pm[s]);
-  float Lg = 0.f, og = 0.f;
-#pragma unroll
-  for (int s = 0; s < kMaxSplitBlocks; ++s) {
-    if (s < a.nsplit) {
-      const float ws = fast_exp2(s_pm[s] - Mg);
-      Lg = fmaf(s_pl[s], ws, Lg);
-      og = fmaf(po[s], ws, og);
-    }
-  }
-  if (tid < D) a.out[static_cast<size_t>(unit) * D + tid] = og / Lg;
+  float Mg, Lg;
+  const float ws = merge_weights(pm, pl, a.nsplit, Mg, Lg);
+  if (tid < D) a.out[static_cast<size_t>(unit) * D + tid] = merge_column(po, ws) / Lg;
   score_pass<T, D, NP, true, NT>(a, unit, global_refs<T, D>(a, unit), Mg, 1.f / Lg, lg, x_new, pf_s, pf_c, pf_p,
                                  pf_x, s_knew, s_vnew, s_key, &s_slot, &s_vrank);
+}
+
+// Split-path steps of a multi-step call, one launch per step instead of two.
+// Launch t finishes step t-1 and runs step t's slices: every block of a unit
+// repeats step t-1's finish (merge the unit's partials, add each weight to every
+// score, find the victim over all candidates) with the finish launch's
+// arithmetic, writes the updated score, compensation and position of the slots
+// in its own step-t slice to the other buffer of each (`ny`; nothing another
+// block still reads is overwritten), puts token t-1 into the victim's slot when
+// that slot is in its slice, and then runs step t's slice exactly as the split
+// launch does.  Block 0 of the unit writes step t-1's output and eviction.  The
+// result equals one split launch and one finish launch per step, bit for bit.
+//
+// STAGE: the block's step-t slice of K/V rows and step t's q/k/v rows are
+// fetched into shared memory at the start (the slice by direct-to-LDS loads,
+// which stay in flight through the finish), the victim's row is patched there,
+// and the slice is attended from shared memory; every load of the launch is then
+// issued before the first result is used.  Without it the slice is read from
+// global memory after the finish.
+constexpr int kFusedThreads = 256;
+constexpr int kFusedPrefetch = 8;  // slots per thread whose metadata is loaded in one batch
+constexpr int kStageLoads = 4;     // block-wide 4 KB direct loads per staged K or V slice
+constexpr int kStageBytes = kStageLoads * kFusedThreads * 16;  // largest staged K (or V) slice
+constexpr int kStagePartials = 32;  // most partials per unit of the staged launch
+
+// Blocks are dealt to the 8 XCDs round-robin.  With a grid that divides evenly,
+// block b runs as logical block (b mod 8) * grid/8 + b/8, so consecutive logical
+// blocks, the slices of one unit, share an XCD: each unit's metadata, logits and
+// partials are then fetched into one L2 and shared there by all of its blocks.
+constexpr int kXcds = 8;
+__device__ inline int xcd_block() {
+  const int b = blockIdx.x, g = gridDim.x;
+  return g % kXcds == 0 ? (b % kXcds) * (g / kXcds) + b / kXcds : b;
+}
+
+// Buffer descriptor over `bytes` bytes from `base`, and 4-byte loads through
+// one: an offset at or past the end (kPastEnd always is) reads 0.
+constexpr int kPastEnd = 0x7ffffff0;
+__device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, 0x00020000);
+}
+__device__ inline uint32_t ld_u32(__amdgpu_buffer_rsrc_t r, int off) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+}
+__device__ inline float ld_f32(__amdgpu_buffer_rsrc_t r, int off) { return __uint_as_float(ld_u32(r, off)); }
+
+// Barrier for shared memory alone: unlike __syncthreads it does not wait for the
+// block's global loads still in flight.
+__device__ inline void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// NS: step t-1's partials per unit held in registers (>= p.nsplit; the merge
+// adds the same terms in the same order for any NS >= nsplit).
+template <typename T, int D, int NTP, int UNP, bool STAGE, int NS>
+__global__ __launch_bounds__(kFusedThreads, 4) void decode_fused(DecodeArgs p, DecodeArgs b, float* ny_score,
+                                                             float* ny_comp, int32_t* ny_pos) {
+  constexpr int NT = kFusedThreads, EPL = Layout<T, D>::EPL, LPR = Layout<T, D>::LPR;
+  static_assert(NS <= kMaxSplitBlocks, "partials per unit");
+  static_assert(!STAGE || 3 * LPR <= kWave, "wave 0 moves step t's q/k/v rows");
+  __shared__ uint64_t s_key[NT / kWave];
+  __shared__ int s_slot;
+  __shared__ StepShared<T, D, NTP> sh;
+  __shared__ uint4 s_tok[3][LPR];                            // STAGE: step t's q, k, v rows
+  extern __shared__ __align__(16) unsigned char s_stage[];  // STAGE: K slice | V slice, kStageBytes each
+  const int tid = threadIdx.x, lb = xcd_block();
+  const int unit = lb / b.nsplit, split = lb % b.nsplit;
+  const int s0 = split * b.split_len, s1 = min(b.count, s0 + b.split_len);  // this block's step-t slots
+  const size_t uk = static_cast<size_t>(unit) * p.kstride;
+  const float* lg = p.logits + static_cast<size_t>(unit) * (p.k + 1);
+  const float* pu = p.part + static_cast<size_t>(unit) * p.nsplit * (2 + D);
+  const bool compensate = p.new_pos >= p.plain_until;
+  const int cnt = p.count;
+  const bool full = cnt == p.k;
+  // ---- every load first: step t's q/k/v rows, the first kFusedPrefetch slots'
+  // metadata per thread, the partials' (max, sum), token t-1's rows and then the
+  // K/V slice, so the block waits out one memory latency, not one per slot
+  const int which = tid / LPR, part = tid % LPR;
+  uint4 tok = {};
+  if (STAGE && which < 3) {
+    const T* src = static_cast<const T*>(which == 0 ? b.q : which == 1 ? b.knew : b.vnew);
+    tok = ld16(src + static_cast<size_t>(unit) * D + part * EPL);
+  }
+  // Through buffer descriptors bounded by the unit's occupied slots (and its
+  // partials): loads past the end read 0, so none needs a branch.
+  constexpr int NP = kFusedPrefetch;
+  const uint32_t nb = static_cast<uint32_t>(cnt) * 4;
+  const __amdgpu_buffer_rsrc_t r_lg = make_rsrc(lg, nb), r_sc = make_rsrc(p.score + uk, nb);
+  const __amdgpu_buffer_rsrc_t r_cp = make_rsrc(p.comp + uk, compensate ? nb : 0u);  // plain adds: c = 0
+  const __amdgpu_buffer_rsrc_t r_ps = make_rsrc(p.pos + uk, nb);
+  const __amdgpu_buffer_rsrc_t r_pu = make_rsrc(pu, static_cast<uint32_t>(p.nsplit) * (2 + D) * 4);
+  float rx[NP], rs[NP], rc[NP];
+  int32_t rp[NP];
+  const auto fetch = [&](int base) {
+#pragma unroll
+    for (int i = 0; i < NP; ++i) {
+      const int off = (base + tid + i * NT) * 4;
+      rx[i] = ld_f32(r_lg, off);
+      rs[i] = ld_f32(r_sc, off);
+      rc[i] = ld_f32(r_cp, off);
+      rp[i] = static_cast<int32_t>(ld_u32(r_ps, off));
+    }
+  };
+  fetch(0);
+  const int lane = tid & (kWave - 1);
+  const float pm = lane < p.nsplit ? ld_f32(r_pu, lane * (2 + D) * 4) : -INFINITY;
+  const float pl = ld_f32(r_pu, (lane * (2 + D) + 1) * 4);  // 0 past nsplit
+  float po[NS];
+  if (split == 0) {
+    const int col = tid < D ? (2 + tid) * 4 : kPastEnd;  // threads past the last column read 0
+#pragma unroll
+    for (int q = 0; q < NS; ++q) po[q] = ld_f32(r_pu, col + q * (2 + D) * 4);
+  }
+  // every thread holds the 16 bytes of token t-1's rows at its lane's row offset
+  const uint4 knew = ld16(static_cast<const T*>(p.knew) + static_cast<size_t>(unit) * D + part * EPL);
+  const uint4 vnew = ld16(static_cast<const T*>(p.vnew) + static_cast<size_t>(unit) * D + part * EPL);
+  const float x_new = lg[p.k];
+  unsigned char* s_k = s_stage;
+  unsigned char* s_v = s_stage + kStageBytes;
+  if constexpr (STAGE) {
+    const size_t row0 = static_cast<size_t>(unit) * b.k + s0;
+    const uint32_t bytes = static_cast<uint32_t>(s1 - s0) * D * sizeof(T);  // <= kStageBytes (host-checked)
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(static_cast<T*>(b.kslots) + row0 * D, bytes);
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(static_cast<T*>(b.vslots) + row0 * D, bytes);
+    const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+#pragma unroll
+    for (int c = 0; c < kStageLoads; ++c) {  // bytes past the slice read as zero
+      const int o = (c * NT + wave * kWave) * 16;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, s_k + o, 16, tid * 16, c * NT * 16, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, s_v + o, 16, tid * 16, c * NT * 16, 0, 0);
+    }
+  }
+  // ---- step t-1's finish
+  float Mg, Lg;
+  const float ws = merge_weights(pm, pl, p.nsplit, Mg, Lg);
+  if (split == 0 && tid < D) p.out[static_cast<size_t>(unit) * D + tid] = merge_column(po, ws) / Lg;
+  const float invL = 1.f / Lg;
+  uint64_t best = kNoKey;
+  int best_slot = -1;
+  for (int base = 0; base < cnt; base += NP * NT) {
+    if (base > 0) fetch(base);
+#pragma unroll
+    for (int i = 0; i < NP; ++i) {
+      const int j = base + tid + i * NT;
+      const bool occupied = j < cnt;
+      float sj = rs[i], cj = rc[i];
+      const int32_t pj = rp[i];
+      add_weight(fast_exp2(rx[i] - Mg) * invL, sj, cj, compensate);
+      if (occupied && j >= s0 && j < s1) {  // this block's slice carries the slot into the next buffer
+        ny_score[uk + j] = sj;
+        ny_comp[uk + j] = cj;
+        ny_pos[uk + j] = pj;
+      }
+      if (occupied && full && pj <= p.cand_limit) {
+        const uint64_t key = evict_key(sj, pj) | pattern_bit(p.pat_kind, p.pat_period, p.pat_width, pj, p.new_pos);
+        if (key < best) {
+          best = key;
+          best_slot = j;
+        }
+      }
+    }
+  }
+  const float w_new = fast_exp2(x_new - Mg) * invL;
+  int dst = cnt;  // cache not full: the new token takes the next free slot
+  int32_t ev = -1;
+  if (full) {
+    if (p.new_is_candidate && tid == 0) {
+      const uint64_t key =
+          evict_key(w_new, p.new_pos) | pattern_bit(p.pat_kind, p.pat_period, p.pat_width, p.new_pos, p.new_pos);
+      if (key < best) {
+        best = key;
+        best_slot = kNewSlot;
+      }
+    }
+    const uint64_t wm = wave_min_key(best);
+    if ((tid & (kWave - 1)) == 0) s_key[tid / kWave] = wm;
+    lds_barrier();
+    uint64_t bm = s_key[0];
+#pragma unroll
+    for (int w = 1; w < NT / kWave; ++w) bm = s_key[w] < bm ? s_key[w] : bm;
+    ev = static_cast<int32_t>(static_cast<uint32_t>(bm & 0xffffffffu));
+    if (best == bm) s_slot = best_slot;  // keys are unique: exactly one owner
+    lds_barrier();
+    dst = s_slot == kNewSlot ? -1 : s_slot;
+  }
+  if (split == 0 && tid == 0 && p.evicted != nullptr) p.evicted[unit] = ev;
+  const bool mine = dst >= s0 && dst < s1;  // token t-1 goes into a slot of this block's slice
+  if (mine) {
+    if (tid == 0) {
+      ny_score[uk + dst] = w_new;
+      ny_comp[uk + dst] = 0.f;
+      ny_pos[uk + dst] = p.new_pos;
+    }
+    if (tid < LPR) {
+      const size_t row = (static_cast<size_t>(unit) * p.k + dst) * D + tid * EPL;
+      st16(static_cast<T*>(p.kslots) + row, knew);
+      st16(static_cast<T*>(p.vslots) + row, vnew);
+    }
+  }
+  if constexpr (STAGE) {
+    if (which < 3) s_tok[which][part] = tok;
+    // the slice has landed in shared memory (each wave waits for its own loads)
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    lds_barrier();
+    if (tid >= NTP) return;
+    if (mine && tid < LPR) {  // wave 0 patches the victim's rows and then reads them
+      const int o = ((dst - s0) * D + tid * EPL) * static_cast<int>(sizeof(T));
+      *reinterpret_cast<uint4*>(s_k + o) = knew;
+      *reinterpret_cast<uint4*>(s_v + o) = vnew;
+    }
+    const T* tk = reinterpret_cast<const T*>(&s_tok[0][0]);
+    const UnitRefs<T> ur{reinterpret_cast<T*>(s_k), reinterpret_cast<T*>(s_v), nullptr, nullptr, nullptr,
+                         tk, tk + D, tk + 2 * D};
+    decode_step<T, D, true, false, NTP, UNP, true>(b, unit, split, ur, nullptr, sh);
+  } else {
+    // the slot rows written above are read below by this block: wait for them
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (tid >= NTP) return;
+    decode_step<T, D, true, false, NTP, UNP, false>(b, unit, split, global_refs<T, D>(b, unit), nullptr, sh);
+  }
 }
 
 // Several decode steps per launch, one unit per block, with the unit's state
@@ -725,6 +1001,37 @@ hipError_t launch_resident_typed(const DecodeArgs& a, int units, int steps, int6
   return hipGetLastError();
 }
 
+// Block shape of the split path's partial blocks for a slice length.
+enum class SplitShape { kTwoWave, kWave, kBlock };
+template <typename T, int D, bool ROPE>
+SplitShape split_shape(int split_len) {
+  if constexpr (std::is_same<T, bf16_t>::value && D == 128 && !ROPE) {
+    if (split_len <= kTwoWaveSplitLen) return SplitShape::kTwoWave;
+    if (split_len <= kWaveSplitLen) return SplitShape::kWave;
+  }
+  return SplitShape::kBlock;
+}
+
+// The split path's partial launch (one block per slice).
+template <typename T, int D, bool ROPE>
+void launch_partials(const DecodeArgs& a, int units, hipStream_t s) {
+  const dim3 grid(units * a.nsplit);
+  const SplitShape sh = split_shape<T, D, ROPE>(a.split_len);
+  if constexpr (std::is_same<T, bf16_t>::value && D == 128 && !ROPE) {
+    if (sh == SplitShape::kTwoWave) {
+      hipLaunchKernelGGL((decode_kernel<T, D, true, ROPE, kTwoWaveThreads, kWaveUnroll>), grid,
+                         dim3(kTwoWaveThreads), 0, s, a);
+      return;
+    }
+    if (sh == SplitShape::kWave) {
+      hipLaunchKernelGGL((decode_kernel<T, D, true, ROPE, kWaveThreads, kWaveUnroll>), grid, dim3(kWaveThreads), 0,
+                         s, a);
+      return;
+    }
+  }
+  hipLaunchKernelGGL((decode_kernel<T, D, true, ROPE>), grid, dim3(kThreads), 0, s, a);
+}
+
 template <typename T, int D, bool ROPE>
 hipError_t launch_typed(const DecodeArgs& a, int units, hipStream_t s) {
   if (a.nsplit == 1) {
@@ -745,13 +1052,7 @@ hipError_t launch_typed(const DecodeArgs& a, int units, hipStream_t s) {
     else
       hipLaunchKernelGGL((decode_kernel<T, D, false, ROPE>), dim3(units), dim3(kThreads), shm, s, a);
   } else {
-    bool wave_blocks = false;
-    if constexpr (std::is_same<T, bf16_t>::value && D == 128 && !ROPE) wave_blocks = a.split_len <= kWaveSplitLen;
-    if (wave_blocks)
-      hipLaunchKernelGGL((decode_kernel<T, D, true, ROPE, kWaveThreads, kWaveUnroll>), dim3(units * a.nsplit),
-                         dim3(kWaveThreads), 0, s, a);
-    else
-      hipLaunchKernelGGL((decode_kernel<T, D, true, ROPE>), dim3(units * a.nsplit), dim3(kThreads), 0, s, a);
+    launch_partials<T, D, ROPE>(a, units, s);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((decode_finish<T, D>), dim3(units), dim3(kFinishThreads), 0, s, a);
@@ -760,6 +1061,58 @@ hipError_t launch_typed(const DecodeArgs& a, int units, hipStream_t s) {
 }
 
 }  // namespace
+
+template <typename T, int D>
+hipError_t launch_split_typed(const DecodeArgs* p, const DecodeArgs& b, float* ny_score, float* ny_comp,
+                              int32_t* ny_pos, int units, hipStream_t s) {
+  const dim3 grid(units * b.nsplit);
+  const SplitShape sh = split_shape<T, D, false>(b.split_len);
+  if (p == nullptr) {  // the first step's slices alone
+    launch_partials<T, D, false>(b, units, s);
+    return hipGetLastError();
+  }
+  if constexpr (std::is_same<T, bf16_t>::value && D == 128) {
+    static_assert(kTwoWaveSplitLen * D * sizeof(T) <= kStageBytes, "a two-wave slice fits the stage");
+    if (sh == SplitShape::kTwoWave && p->nsplit <= kStagePartials) {  // the partials fit 32 registers
+      hipLaunchKernelGGL((decode_fused<T, D, kTwoWaveThreads, kWaveUnroll, true, kStagePartials>), grid,
+                         dim3(kFusedThreads), 2 * kStageBytes, s, *p, b, ny_score, ny_comp, ny_pos);
+    } else if (sh == SplitShape::kTwoWave) {
+      hipLaunchKernelGGL((decode_fused<T, D, kTwoWaveThreads, kWaveUnroll, false, kMaxSplitBlocks>), grid,
+                         dim3(kFusedThreads), 0, s, *p, b, ny_score, ny_comp, ny_pos);
+    } else if (sh == SplitShape::kWave) {
+      hipLaunchKernelGGL((decode_fused<T, D, kWaveThreads, kWaveUnroll, false, kMaxSplitBlocks>), grid,
+                         dim3(kFusedThreads), 0, s, *p, b, ny_score, ny_comp, ny_pos);
+    }
+    if (sh != SplitShape::kBlock) return hipGetLastError();
+  }
+  hipLaunchKernelGGL((decode_fused<T, D, kThreads, kUnroll, false, kMaxSplitBlocks>), grid, dim3(kFusedThreads), 0, s,
+                     *p, b, ny_score, ny_comp, ny_pos);
+  return hipGetLastError();
+}
+
+template <typename T, int D>
+hipError_t launch_finish_typed(const DecodeArgs& a, int units, hipStream_t s) {
+  hipLaunchKernelGGL((decode_finish<T, D>), dim3(units), dim3(kFinishThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_split(int dtype, int head_dim, const DecodeArgs* prev, const DecodeArgs& cur,
+                               float* ny_score, float* ny_comp, int32_t* ny_pos, int units, hipStream_t s) {
+  if (cur.rank != nullptr || cur.fixed_new != nullptr || cur.nsplit < 2 ||
+      (prev != nullptr && (prev->nsplit < 2 || prev->nsplit > kMaxSplitBlocks)))
+    return hipErrorInvalidConfiguration;
+  if (dtype == 0)
+    return head_dim == 64 ? launch_split_typed<float, 64>(prev, cur, ny_score, ny_comp, ny_pos, units, s)
+                          : launch_split_typed<float, 128>(prev, cur, ny_score, ny_comp, ny_pos, units, s);
+  return head_dim == 64 ? launch_split_typed<bf16_t, 64>(prev, cur, ny_score, ny_comp, ny_pos, units, s)
+                        : launch_split_typed<bf16_t, 128>(prev, cur, ny_score, ny_comp, ny_pos, units, s);
+}
+
+hipError_t launch_decode_finish(int dtype, int head_dim, const DecodeArgs& a, int units, hipStream_t s) {
+  if (dtype == 0)
+    return head_dim == 64 ? launch_finish_typed<float, 64>(a, units, s) : launch_finish_typed<float, 128>(a, units, s);
+  return head_dim == 64 ? launch_finish_typed<bf16_t, 64>(a, units, s) : launch_finish_typed<bf16_t, 128>(a, units, s);
+}
 
 bool decode_resident_fits(int dtype, int head_dim, int units, int k) {
   if (dtype == 0) return head_dim == 64 ? resident_fits<float, 64>(units, k) : resident_fits<float, 128>(units, k);

@@ -37,6 +37,13 @@ struct h2o_cache {
   int32_t* pos;
   float* part;
   float* logits;
+  // split path, several steps per call: the other buffer of each (one launch
+  // per step finishes the previous step into it)
+  float* score2;
+  float* comp2;
+  int32_t* pos2;
+  float* part2;
+  float* logits2;
   int32_t max_split;
   float* row_lse2;
   float* col_sum;
@@ -139,8 +146,11 @@ h2o_status check_params(const h2o_params* p, Sizes* sz) {
     sz->kv = 2 * u * kk * d * es;
     sz->meta = u * static_cast<size_t>(round32(static_cast<int32_t>(k))) * 12;
     sz->max_split = units < kSplitUnits ? kMaxSplit : 1;
+    // split path: partials and logits, and a second buffer of them and of the
+    // per-slot score, compensation and position (multi-step calls)
     sz->split = sz->max_split > 1
-                    ? u * sz->max_split * (2 + d) * 4 + u * (kk + 1) * 4
+                    ? 2 * (u * sz->max_split * (2 + d) * 4 + u * (kk + 1) * 4) +
+                          u * static_cast<size_t>(round32(static_cast<int32_t>(k))) * 12
                     : 0;
     sz->lpad = round32(p->max_prompt);
     sz->prefill = 2 * u * static_cast<size_t>(sz->lpad) * 4;
@@ -161,8 +171,9 @@ h2o_status check_params(const h2o_params* p, Sizes* sz) {
 }
 
 void free_all(h2o_cache* c) {
-  void* ptrs[] = {c->kslots, c->vslots, c->score, c->comp, c->pos, c->part, c->logits,
-                  c->row_lse2, c->col_sum, c->rank, c->rope_ops, c->rope_cs, c->rope_th};
+  void* ptrs[] = {c->kslots, c->vslots, c->score, c->comp, c->pos, c->part, c->logits, c->score2, c->comp2,
+                  c->pos2, c->part2, c->logits2, c->row_lse2, c->col_sum, c->rank, c->rope_ops, c->rope_cs,
+                  c->rope_th};
   for (void* q : ptrs)
     if (q != nullptr) (void)hipFree(q);
 }
@@ -357,6 +368,11 @@ h2o_status h2o_cache_create(const h2o_params* params, int device, h2o_cache** ou
       {reinterpret_cast<void**>(&c->pos), u * c->kstride * 4},
       {reinterpret_cast<void**>(&c->part), c->max_split > 1 ? u * c->max_split * (2 + d) * 4 : 0},
       {reinterpret_cast<void**>(&c->logits), c->max_split > 1 ? u * (kk + 1) * 4 : 0},
+      {reinterpret_cast<void**>(&c->score2), c->max_split > 1 ? u * c->kstride * 4 : 0},
+      {reinterpret_cast<void**>(&c->comp2), c->max_split > 1 ? u * c->kstride * 4 : 0},
+      {reinterpret_cast<void**>(&c->pos2), c->max_split > 1 ? u * c->kstride * 4 : 0},
+      {reinterpret_cast<void**>(&c->part2), c->max_split > 1 ? u * c->max_split * (2 + d) * 4 : 0},
+      {reinterpret_cast<void**>(&c->logits2), c->max_split > 1 ? u * (kk + 1) * 4 : 0},
       {reinterpret_cast<void**>(&c->row_lse2), u * c->lpad_cap * 4},
       {reinterpret_cast<void**>(&c->col_sum), u * c->lpad_cap * 4},
       {reinterpret_cast<void**>(&c->rank), rope ? u * c->kstride * 4 : 0},
@@ -724,13 +740,70 @@ h2o_status h2o_decode_steps(h2o_cache* c, const void* q, const void* k, const vo
     }
     return H2O_OK;
   }
-  for (int32_t t = 0; t < steps; ++t) {
+  // Steps on the split path (which, once reached, lasts: the count only grows)
+  // run one launch each: launch i finishes step i-1 and runs step i's slices,
+  // alternating two buffers of scores/compensations/positions and of
+  // partials/logits; a finish launch closes the run (bit-identical to a split
+  // launch and a finish launch per step).
+  const bool fuse = c->rank == nullptr && c->max_split > 1;
+  int32_t t = 0;
+  for (; t < steps; ++t) {
+    int32_t unused = 0;
+    if (fuse && choose_nsplit(c, c->count, &unused) > 1) break;
     const size_t off = static_cast<size_t>(t) * tok;
     const hipError_t e = decode_launch(c, static_cast<const char*>(q) + off, static_cast<const char*>(k) + off,
                                        static_cast<const char*>(v) + off, nullptr, 1, out + t * out_step,
                                        evicted != nullptr ? evicted + t * units : nullptr, s);
     if (e != hipSuccess) return hip_fail(e, "decode launch");
   }
+  if (t == steps) return H2O_OK;
+  // the rest on the split path, one launch per step
+  struct Buffers {
+    float* score;
+    float* comp;
+    int32_t* pos;
+    float* part;
+    float* logits;
+  } buf[2] = {{c->score, c->comp, c->pos, c->part, c->logits}, {c->score2, c->comp2, c->pos2, c->part2, c->logits2}};
+  auto step_args = [&](int32_t i, int which) {
+    const size_t off = static_cast<size_t>(i) * tok;
+    h2o::DecodeArgs a = decode_args(c, static_cast<const char*>(q) + off, static_cast<const char*>(k) + off,
+                                    static_cast<const char*>(v) + off, nullptr, 1, out + i * out_step,
+                                    evicted != nullptr ? evicted + i * units : nullptr);
+    a.score = buf[which].score;
+    a.comp = buf[which].comp;
+    a.pos = buf[which].pos;
+    a.part = buf[which].part;
+    a.logits = buf[which].logits;
+    return a;
+  };
+  auto advance = [&]() {
+    if (c->count < c->k) ++c->count;
+    ++c->next_pos;
+  };
+  int which = 0;  // buffer holding step `prev`'s scores and its partials
+  h2o::DecodeArgs prev = step_args(t, which);
+  hipError_t e = h2o::launch_decode_split(c->p.dtype, c->d, nullptr, prev, nullptr, nullptr, nullptr, c->units, s);
+  if (e != hipSuccess) return hip_fail(e, "decode launch");
+  advance();
+  for (++t; t < steps; ++t) {
+    h2o::DecodeArgs cur = step_args(t, which ^ 1);
+    e = h2o::launch_decode_split(c->p.dtype, c->d, &prev, cur, buf[which ^ 1].score, buf[which ^ 1].comp,
+                                 buf[which ^ 1].pos, c->units, s);
+    if (e != hipSuccess) return hip_fail(e, "decode launch");
+    advance();
+    which ^= 1;
+    prev = cur;
+  }
+  e = h2o::launch_decode_finish(c->p.dtype, c->d, prev, c->units, s);  // the last step's finish, in place
+  if (e == hipSuccess && which == 1) {  // the cache's own arrays receive the final state (occupied slots)
+    const size_t pitch = static_cast<size_t>(c->kstride) * 4, width = static_cast<size_t>(c->count) * 4;
+    const size_t rows = static_cast<size_t>(c->units);
+    e = hipMemcpy2DAsync(c->score, pitch, c->score2, pitch, width, rows, hipMemcpyDeviceToDevice, s);
+    if (e == hipSuccess) e = hipMemcpy2DAsync(c->comp, pitch, c->comp2, pitch, width, rows, hipMemcpyDeviceToDevice, s);
+    if (e == hipSuccess) e = hipMemcpy2DAsync(c->pos, pitch, c->pos2, pitch, width, rows, hipMemcpyDeviceToDevice, s);
+  }
+  if (e != hipSuccess) return hip_fail(e, "decode launch");
   return H2O_OK;
 }
 

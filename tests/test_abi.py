@@ -75,8 +75,9 @@ def test_cache_bytes_accounting():
     st, kv, tot = _bytes(batch=2, heads=3, head_dim=128, heavy=4, recent=4, dtype="bf16", max_prompt=64)
     assert st == 0 and kv == 2 * 6 * 8 * 128 * 2
     # + scores, compensation, positions (12 B / slot, rows padded to 32 slots)
-    # + split scratch (few units) + 2 prefill rows (row normaliser, column sum)
-    assert tot == kv + 6 * 32 * 12 + (6 * 64 * 130 * 4 + 6 * 9 * 4) + 2 * 6 * 64 * 4
+    # + split scratch (few units: partials and logits, twice, and a second score,
+    #   compensation and position array) + 2 prefill rows (row normaliser, column sum)
+    assert tot == kv + 6 * 32 * 12 + (2 * (6 * 64 * 130 * 4 + 6 * 9 * 4) + 6 * 32 * 12) + 2 * 6 * 64 * 4
     st, kv32, _ = _bytes(dtype="f32")
     assert kv32 == 2 * kv
     # position rolling adds slot ranks, the rotated prompt of a chunk of units (8

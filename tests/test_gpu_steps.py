@@ -2,8 +2,9 @@
 the C ABI (needs an MI355X): bit-identical to the same number of h2o_decode_step
 calls, on every decode path (small budgets, the split path for few units, the
 one-wave blocks, position rolling, a sparse pattern, and the launches that hold
-each unit's rows in shared memory over all the steps), outputs of every step
-kept or only the last, and its argument checks."""
+each unit's rows in shared memory over all the steps, and the split path's one
+launch per step that finishes the previous step), outputs of every step kept or
+only the last, and its argument checks."""
 import numpy as np
 import pytest
 import torch
@@ -48,6 +49,16 @@ def _same(a, b, what):
     ("opt6.7b-layer-b16", 8, 128, 64, 300, 40, 100, 100, 0.0, None),     # 1024 units, d = 64, k = 200
     ("opt6.7b-layer-b16", 2, 4, 128, 20, 60, 20, 20, 0.0, None),         # the cache fills during the steps
     ("opt6.7b-layer-b16", 2, 4, 128, 100, 80, 40, 0, 0.0, None),         # K_r = 0: the new token may be the victim
+    # split path, one launch per step (each finishing the previous step)
+    ("opt6.7b-layer-b16", 1, 32, 128, 512, 3000, 1024, 1024, 0.0, None),  # the stream's shape: fills, then splits
+    ("opt6.7b-layer-b16", 2, 1, 128, 60, 301, 200, 200, 0.0, None),       # from one block per unit into the split
+    ("opt6.7b-layer-b16", 2, 1, 64, 700, 150, 300, 300, 0.0, None),       # d = 64: 256-thread slices
+    ("opt6.7b-layer-b16", 1, 16, 128, 2400, 120, 1152, 1152, 0.0, None),  # 36 two-wave slices per unit: more
+                                                                          # partials than the staged launch holds
+    ("opt6.7b-layer-b16", 8, 32, 128, 2100, 41, 1024, 1024, 0.0, None),   # slices of 512 slots: 256-thread blocks
+    ("opt6.7b-layer-b16", 4, 1, 128, 400, 101, 300, 0, 0.0, None),        # K_r = 0 on the split path
+    ("opt6.7b-layer-b16", 2, 2, 128, 400, 120, 150, 150, 0.0, ("fixed", 16, 4)),  # a pattern on the split path
+    ("tiny-fp32", 2, 1, 128, 400, 90, 150, 150, 0.0, None),               # fp32 on the split path
 ])
 def test_steps_match_single_steps(wl, B, H, d, L, T, heavy, recent, rope, pattern):
     w = scaled(get(wl), batch=B, heads=H, head_dim=d, prompt_len=L, decode_steps=T, heavy_budget=heavy,
@@ -70,8 +81,11 @@ def test_steps_match_single_steps(wl, B, H, d, L, T, heavy, recent, rope, patter
     _same(o1.cpu().numpy(), o2.cpu().numpy(), "outputs")
     _same(e1.cpu().numpy(), e2.cpu().numpy(), "evictions")
     r1, r2 = one.read(), many.read()
-    for key in ("pos", "score", "k", "v"):
+    for key in ("pos", "score"):
         _same(r1[key], r2[key], key)
+    occupied = r1["pos"] >= 0  # rows of empty slots were never written
+    for key in ("k", "v"):
+        _same(r1[key][occupied], r2[key][occupied], key)
     assert one.info() == many.info()
     # only the last output kept
     last = _cache(w, q, k, v, L, rope, pattern)
