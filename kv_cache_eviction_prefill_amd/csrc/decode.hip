@@ -361,10 +361,11 @@ struct StepShared {
 // One decode step of one unit (SPLIT: of one slice of its slots).  ku/vu: the
 // unit's slot rows, in global memory, or (LDSKV) the block's copy of them in
 // shared memory, which the step reads and overwrites in place (a split step:
-// the copy of its slice's rows alone, row 0 the slice's first slot).
+// the copy of its slice's rows alone, row 0 the slice's first slot).  tid: the
+// thread's index among the NT threads that run the step.
 template <typename T, int D, bool SPLIT, bool ROPE, int NT, int UN, bool LDSKV>
 __device__ __forceinline__ void decode_step(const DecodeArgs& a, int unit, int split, const UnitRefs<T>& ur,
-                                            float* s_logit, StepShared<T, D, NT>& sh) {
+                                            float* s_logit, StepShared<T, D, NT>& sh, int tid) {
   using Lay = Layout<T, D, NT>;
   constexpr int NP = NT >= kThreads ? kPrefetch : 512 / NT;  // score-pass slots prefetched per thread
   constexpr int NC = (D + NT - 1) / NT;                       // output columns per thread in the merge
@@ -377,7 +378,6 @@ __device__ __forceinline__ void decode_step(const DecodeArgs& a, int unit, int s
   uint4* s_knew = sh.knew;
   uint4* s_vnew = sh.vnew;
 
-  const int tid = threadIdx.x;
   const int g = tid / LPR, r = tid % LPR;
   const int s0 = split * a.split_len;
   const int s1 = min(a.count, s0 + a.split_len);
@@ -558,7 +558,8 @@ __global__ __launch_bounds__(NT, NT == kWaveThreads ? 2 : (ROPE || UN > kUnroll 
   __shared__ StepShared<T, D, NT> sh;
   const int unit = SPLIT ? blockIdx.x / a.nsplit : blockIdx.x;
   const int split = SPLIT ? blockIdx.x % a.nsplit : 0;
-  decode_step<T, D, SPLIT, ROPE, NT, UN, false>(a, unit, split, global_refs<T, D>(a, unit), s_logit, sh);
+  decode_step<T, D, SPLIT, ROPE, NT, UN, false>(a, unit, split, global_refs<T, D>(a, unit), s_logit, sh,
+                                                threadIdx.x);
 }
 
 // Butterfly reductions over the wave: at every level the two partner lanes
@@ -673,6 +674,10 @@ constexpr int kFusedPrefetch = 8;  // slots per thread whose metadata is loaded 
 constexpr int kStageLoads = 4;     // block-wide 4 KB direct loads per staged K or V slice
 constexpr int kStageBytes = kStageLoads * kFusedThreads * 16;  // largest staged K (or V) slice
 constexpr int kStagePartials = 32;  // most partials per unit of the staged launch
+// Staged launches over at least this many slices run two slices per block, each
+// attended by its own two waves, so half as many blocks repeat the finish
+// (32 units x 2048 slots: 10.4 -> 9.1 us per step).
+constexpr int kPairedSlices = 512;
 
 // Blocks are dealt to the 8 XCDs round-robin.  With a grid that divides evenly,
 // block b runs as logical block (b mod 8) * grid/8 + b/8, so consecutive logical
@@ -704,21 +709,28 @@ __device__ inline void lds_barrier() {
 }
 
 // NS: step t-1's partials per unit held in registers (>= p.nsplit; the merge
-// adds the same terms in the same order for any NS >= nsplit).
-template <typename T, int D, int NTP, int UNP, bool STAGE, int NS>
+// adds the same terms in the same order for any NS >= nsplit).  SPB: step-t
+// slices per block (1, or 2 when STAGE: one per NTP-thread group; the finish is
+// then repeated by half as many blocks).
+template <typename T, int D, int NTP, int UNP, bool STAGE, int NS, int SPB>
 __global__ __launch_bounds__(kFusedThreads, 4) void decode_fused(DecodeArgs p, DecodeArgs b, float* ny_score,
                                                              float* ny_comp, int32_t* ny_pos) {
   constexpr int NT = kFusedThreads, EPL = Layout<T, D>::EPL, LPR = Layout<T, D>::LPR;
+  constexpr int NGP = NTP / LPR;  // row groups of one slice's attending threads
   static_assert(NS <= kMaxSplitBlocks, "partials per unit");
   static_assert(!STAGE || 3 * LPR <= kWave, "wave 0 moves step t's q/k/v rows");
+  static_assert(SPB == 1 || (STAGE && SPB * NTP <= NT), "two slices per block: staged, one thread group each");
+  constexpr int KB = SPB * kStageBytes;  // staged K (or V) bytes
   __shared__ uint64_t s_key[NT / kWave];
   __shared__ int s_slot;
-  __shared__ StepShared<T, D, NTP> sh;
+  __shared__ StepShared<T, D, NTP> sh[SPB];
   __shared__ uint4 s_tok[3][LPR];                            // STAGE: step t's q, k, v rows
-  extern __shared__ __align__(16) unsigned char s_stage[];  // STAGE: K slice | V slice, kStageBytes each
+  extern __shared__ __align__(16) unsigned char s_stage[];  // STAGE: K rows | V rows of the block's slices
   const int tid = threadIdx.x, lb = xcd_block();
-  const int unit = lb / b.nsplit, split = lb % b.nsplit;
-  const int s0 = split * b.split_len, s1 = min(b.count, s0 + b.split_len);  // this block's step-t slots
+  const int bpu = b.nsplit / SPB;  // blocks per unit (the host makes nsplit a multiple of SPB)
+  const int unit = lb / bpu, split0 = (lb % bpu) * SPB;
+  // this block's step-t slots: slices split0 .. split0 + SPB - 1
+  const int s0 = split0 * b.split_len, s1 = min(b.count, s0 + SPB * b.split_len);
   const size_t uk = static_cast<size_t>(unit) * p.kstride;
   const float* lg = p.logits + static_cast<size_t>(unit) * (p.k + 1);
   const float* pu = p.part + static_cast<size_t>(unit) * p.nsplit * (2 + D);
@@ -727,7 +739,7 @@ __global__ __launch_bounds__(kFusedThreads, 4) void decode_fused(DecodeArgs p, D
   const bool full = cnt == p.k;
   // ---- every load first: step t's q/k/v rows, the first kFusedPrefetch slots'
   // metadata per thread, the partials' (max, sum), token t-1's rows and then the
-  // K/V slice, so the block waits out one memory latency, not one per slot
+  // K/V slices, so the block waits out one memory latency, not one per slot
   const int which = tid / LPR, part = tid % LPR;
   uint4 tok = {};
   if (STAGE && which < 3) {
@@ -758,8 +770,9 @@ __global__ __launch_bounds__(kFusedThreads, 4) void decode_fused(DecodeArgs p, D
   const int lane = tid & (kWave - 1);
   const float pm = lane < p.nsplit ? ld_f32(r_pu, lane * (2 + D) * 4) : -INFINITY;
   const float pl = ld_f32(r_pu, (lane * (2 + D) + 1) * 4);  // 0 past nsplit
+  const bool lead = split0 == 0;  // the unit's first block writes step t-1's output and eviction
   float po[NS];
-  if (split == 0) {
+  if (lead) {
     const int col = tid < D ? (2 + tid) * 4 : kPastEnd;  // threads past the last column read 0
 #pragma unroll
     for (int q = 0; q < NS; ++q) po[q] = ld_f32(r_pu, col + q * (2 + D) * 4);
@@ -769,15 +782,15 @@ __global__ __launch_bounds__(kFusedThreads, 4) void decode_fused(DecodeArgs p, D
   const uint4 vnew = ld16(static_cast<const T*>(p.vnew) + static_cast<size_t>(unit) * D + part * EPL);
   const float x_new = lg[p.k];
   unsigned char* s_k = s_stage;
-  unsigned char* s_v = s_stage + kStageBytes;
+  unsigned char* s_v = s_stage + KB;
   if constexpr (STAGE) {
     const size_t row0 = static_cast<size_t>(unit) * b.k + s0;
-    const uint32_t bytes = static_cast<uint32_t>(s1 - s0) * D * sizeof(T);  // <= kStageBytes (host-checked)
+    const uint32_t bytes = static_cast<uint32_t>(s1 - s0) * D * sizeof(T);  // <= KB (host-checked)
     const __amdgpu_buffer_rsrc_t rk = make_rsrc(static_cast<T*>(b.kslots) + row0 * D, bytes);
     const __amdgpu_buffer_rsrc_t rv = make_rsrc(static_cast<T*>(b.vslots) + row0 * D, bytes);
     const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
 #pragma unroll
-    for (int c = 0; c < kStageLoads; ++c) {  // bytes past the slice read as zero
+    for (int c = 0; c < KB / (NT * 16); ++c) {  // bytes past the slices read as zero
       const int o = (c * NT + wave * kWave) * 16;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, s_k + o, 16, tid * 16, c * NT * 16, 0, 0);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, s_v + o, 16, tid * 16, c * NT * 16, 0, 0);
@@ -786,7 +799,7 @@ __global__ __launch_bounds__(kFusedThreads, 4) void decode_fused(DecodeArgs p, D
   // ---- step t-1's finish
   float Mg, Lg;
   const float ws = merge_weights(pm, pl, p.nsplit, Mg, Lg);
-  if (split == 0 && tid < D) p.out[static_cast<size_t>(unit) * D + tid] = merge_column(po, ws) / Lg;
+  if (lead && tid < D) p.out[static_cast<size_t>(unit) * D + tid] = merge_column(po, ws) / Lg;
   const float invL = 1.f / Lg;
   uint64_t best = kNoKey;
   int best_slot = -1;
@@ -799,7 +812,7 @@ __global__ __launch_bounds__(kFusedThreads, 4) void decode_fused(DecodeArgs p, D
       float sj = rs[i], cj = rc[i];
       const int32_t pj = rp[i];
       add_weight(fast_exp2(rx[i] - Mg) * invL, sj, cj, compensate);
-      if (occupied && j >= s0 && j < s1) {  // this block's slice carries the slot into the next buffer
+      if (occupied && j >= s0 && j < s1) {  // this block's slices carry the slot into the next buffer
         ny_score[uk + j] = sj;
         ny_comp[uk + j] = cj;
         ny_pos[uk + j] = pj;
@@ -836,8 +849,8 @@ __global__ __launch_bounds__(kFusedThreads, 4) void decode_fused(DecodeArgs p, D
     lds_barrier();
     dst = s_slot == kNewSlot ? -1 : s_slot;
   }
-  if (split == 0 && tid == 0 && p.evicted != nullptr) p.evicted[unit] = ev;
-  const bool mine = dst >= s0 && dst < s1;  // token t-1 goes into a slot of this block's slice
+  if (lead && tid == 0 && p.evicted != nullptr) p.evicted[unit] = ev;
+  const bool mine = dst >= s0 && dst < s1;  // token t-1 goes into a slot of this block's slices
   if (mine) {
     if (tid == 0) {
       ny_score[uk + dst] = w_new;
@@ -852,25 +865,32 @@ __global__ __launch_bounds__(kFusedThreads, 4) void decode_fused(DecodeArgs p, D
   }
   if constexpr (STAGE) {
     if (which < 3) s_tok[which][part] = tok;
-    // the slice has landed in shared memory (each wave waits for its own loads)
+    // the slices have landed in shared memory (each wave waits for its own loads)
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     lds_barrier();
-    if (tid >= NTP) return;
-    if (mine && tid < LPR) {  // wave 0 patches the victim's rows and then reads them
-      const int o = ((dst - s0) * D + tid * EPL) * static_cast<int>(sizeof(T));
+    const int gi = tid / NTP, gt = tid % NTP;  // slice of this thread group, thread within it
+    const int split = split0 + gi;
+    if (gi >= SPB || split >= b.nsplit) return;
+    const int g0 = split * b.split_len;  // the group's first slot
+    if (mine && dst >= g0 && dst < g0 + b.split_len && gt / LPR == (dst - g0) % NGP) {
+      // the row group that attends the victim's slot writes token t-1's rows
+      // over it, each lane the 16 bytes it reads back
+      const int o = ((dst - s0) * D + part * EPL) * static_cast<int>(sizeof(T));
       *reinterpret_cast<uint4*>(s_k + o) = knew;
       *reinterpret_cast<uint4*>(s_v + o) = vnew;
     }
     const T* tk = reinterpret_cast<const T*>(&s_tok[0][0]);
-    const UnitRefs<T> ur{reinterpret_cast<T*>(s_k), reinterpret_cast<T*>(s_v), nullptr, nullptr, nullptr,
-                         tk, tk + D, tk + 2 * D};
-    decode_step<T, D, true, false, NTP, UNP, true>(b, unit, split, ur, nullptr, sh);
+    const size_t gofs = static_cast<size_t>(g0 - s0) * D * sizeof(T);
+    const UnitRefs<T> ur{reinterpret_cast<T*>(s_k + gofs), reinterpret_cast<T*>(s_v + gofs), nullptr, nullptr,
+                         nullptr, tk, tk + D, tk + 2 * D};
+    decode_step<T, D, true, false, NTP, UNP, true>(b, unit, split, ur, nullptr, sh[gi], gt);
   } else {
     // the slot rows written above are read below by this block: wait for them
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     if (tid >= NTP) return;
-    decode_step<T, D, true, false, NTP, UNP, false>(b, unit, split, global_refs<T, D>(b, unit), nullptr, sh);
+    decode_step<T, D, true, false, NTP, UNP, false>(b, unit, split0, global_refs<T, D>(b, unit), nullptr, sh[0],
+                                                    tid);
   }
 }
 
@@ -931,7 +951,7 @@ __global__ __launch_bounds__(NT) void decode_resident(DecodeArgs a0, int steps, 
     a.cand_limit = a0.cand_limit + t;
     const T* tk = stok + cur * 3 * D;
     const UnitRefs<T> ur{sk, sv, ssc, scp, sps, tk, tk + D, tk + 2 * D};
-    decode_step<T, D, false, false, NT, UN, true>(a, unit, 0, ur, s_logit, sh);
+    decode_step<T, D, false, false, NT, UN, true>(a, unit, 0, ur, s_logit, sh, tid);
     if (which < 3 && t + 1 < steps) st16(stok + (cur ^ 1) * 3 * D + which * D + part * EPL, nxt);
     __syncthreads();  // this step's writes and the next token's rows before the next step
   }
@@ -1074,19 +1094,25 @@ hipError_t launch_split_typed(const DecodeArgs* p, const DecodeArgs& b, float* n
   if constexpr (std::is_same<T, bf16_t>::value && D == 128) {
     static_assert(kTwoWaveSplitLen * D * sizeof(T) <= kStageBytes, "a two-wave slice fits the stage");
     if (sh == SplitShape::kTwoWave && p->nsplit <= kStagePartials) {  // the partials fit 32 registers
-      hipLaunchKernelGGL((decode_fused<T, D, kTwoWaveThreads, kWaveUnroll, true, kStagePartials>), grid,
-                         dim3(kFusedThreads), 2 * kStageBytes, s, *p, b, ny_score, ny_comp, ny_pos);
+      if (b.nsplit % 2 == 0 && units * b.nsplit >= kPairedSlices) {  // two slices per block
+        hipLaunchKernelGGL((decode_fused<T, D, kTwoWaveThreads, kWaveUnroll, true, kStagePartials, 2>),
+                           dim3(units * b.nsplit / 2), dim3(kFusedThreads), 4 * kStageBytes, s, *p, b, ny_score,
+                           ny_comp, ny_pos);
+      } else {
+        hipLaunchKernelGGL((decode_fused<T, D, kTwoWaveThreads, kWaveUnroll, true, kStagePartials, 1>), grid,
+                           dim3(kFusedThreads), 2 * kStageBytes, s, *p, b, ny_score, ny_comp, ny_pos);
+      }
     } else if (sh == SplitShape::kTwoWave) {
-      hipLaunchKernelGGL((decode_fused<T, D, kTwoWaveThreads, kWaveUnroll, false, kMaxSplitBlocks>), grid,
+      hipLaunchKernelGGL((decode_fused<T, D, kTwoWaveThreads, kWaveUnroll, false, kMaxSplitBlocks, 1>), grid,
                          dim3(kFusedThreads), 0, s, *p, b, ny_score, ny_comp, ny_pos);
     } else if (sh == SplitShape::kWave) {
-      hipLaunchKernelGGL((decode_fused<T, D, kWaveThreads, kWaveUnroll, false, kMaxSplitBlocks>), grid,
+      hipLaunchKernelGGL((decode_fused<T, D, kWaveThreads, kWaveUnroll, false, kMaxSplitBlocks, 1>), grid,
                          dim3(kFusedThreads), 0, s, *p, b, ny_score, ny_comp, ny_pos);
     }
     if (sh != SplitShape::kBlock) return hipGetLastError();
   }
-  hipLaunchKernelGGL((decode_fused<T, D, kThreads, kUnroll, false, kMaxSplitBlocks>), grid, dim3(kFusedThreads), 0, s,
-                     *p, b, ny_score, ny_comp, ny_pos);
+  hipLaunchKernelGGL((decode_fused<T, D, kThreads, kUnroll, false, kMaxSplitBlocks, 1>), grid, dim3(kFusedThreads),
+                     0, s, *p, b, ny_score, ny_comp, ny_pos);
   return hipGetLastError();
 }
 
