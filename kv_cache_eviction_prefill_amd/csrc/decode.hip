@@ -699,6 +699,10 @@ __device__ inline uint32_t ld_u32(__amdgpu_buffer_rsrc_t r, int off) {
   return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
 }
 __device__ inline float ld_f32(__amdgpu_buffer_rsrc_t r, int off) { return __uint_as_float(ld_u32(r, off)); }
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+__device__ inline u32x4 ld_u32x4(__amdgpu_buffer_rsrc_t r, int off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+}
 
 // Barrier for shared memory alone: unlike __syncthreads it does not wait for the
 // block's global loads still in flight.
@@ -737,9 +741,11 @@ __global__ __launch_bounds__(kFusedThreads, 4) void decode_fused(DecodeArgs p, D
   const bool compensate = p.new_pos >= p.plain_until;
   const int cnt = p.count;
   const bool full = cnt == p.k;
-  // ---- every load first: step t's q/k/v rows, the first kFusedPrefetch slots'
-  // metadata per thread, the partials' (max, sum), token t-1's rows and then the
-  // K/V slices, so the block waits out one memory latency, not one per slot
+  // ---- every load first: step t's q/k/v rows, the partials' (max, sum), the
+  // metadata of kFusedPrefetch consecutive slots per thread (16-byte loads),
+  // token t-1's rows and then the K/V slices, so the block waits out one memory
+  // latency, not one per slot; fewer than the 63 loads a wave can have in
+  // flight are issued before the slices, so no wait delays them
   const int which = tid / LPR, part = tid % LPR;
   uint4 tok = {};
   if (STAGE && which < 3) {
@@ -749,31 +755,38 @@ __global__ __launch_bounds__(kFusedThreads, 4) void decode_fused(DecodeArgs p, D
   // Through buffer descriptors bounded by the unit's occupied slots (and its
   // partials): loads past the end read 0, so none needs a branch.
   constexpr int NP = kFusedPrefetch;
+  static_assert(NP % 4 == 0, "whole 16-byte loads");
   const uint32_t nb = static_cast<uint32_t>(cnt) * 4;
   const __amdgpu_buffer_rsrc_t r_lg = make_rsrc(lg, nb), r_sc = make_rsrc(p.score + uk, nb);
   const __amdgpu_buffer_rsrc_t r_cp = make_rsrc(p.comp + uk, compensate ? nb : 0u);  // plain adds: c = 0
   const __amdgpu_buffer_rsrc_t r_ps = make_rsrc(p.pos + uk, nb);
   const __amdgpu_buffer_rsrc_t r_pu = make_rsrc(pu, static_cast<uint32_t>(p.nsplit) * (2 + D) * 4);
+  const int lane = tid & (kWave - 1);
+  float pm = lane < p.nsplit ? ld_f32(r_pu, lane * (2 + D) * 4) : -INFINITY;
+  float pl = ld_f32(r_pu, (lane * (2 + D) + 1) * 4);  // 0 past nsplit
   float rx[NP], rs[NP], rc[NP];
   int32_t rp[NP];
-  const auto fetch = [&](int base) {
+  const auto fetch = [&](int base) {  // slots base + tid * NP + i
 #pragma unroll
-    for (int i = 0; i < NP; ++i) {
-      const int off = (base + tid + i * NT) * 4;
-      rx[i] = ld_f32(r_lg, off);
-      rs[i] = ld_f32(r_sc, off);
-      rc[i] = ld_f32(r_cp, off);
-      rp[i] = static_cast<int32_t>(ld_u32(r_ps, off));
+    for (int i = 0; i < NP; i += 4) {
+      const int off = (base + tid * NP + i) * 4;
+      const u32x4 x = ld_u32x4(r_lg, off), sc = ld_u32x4(r_sc, off), c = ld_u32x4(r_cp, off),
+                  ps = ld_u32x4(r_ps, off);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        rx[i + e] = __uint_as_float(x[e]);
+        rs[i + e] = __uint_as_float(sc[e]);
+        rc[i + e] = __uint_as_float(c[e]);
+        rp[i + e] = static_cast<int32_t>(ps[e]);
+      }
     }
   };
   fetch(0);
-  const int lane = tid & (kWave - 1);
-  const float pm = lane < p.nsplit ? ld_f32(r_pu, lane * (2 + D) * 4) : -INFINITY;
-  const float pl = ld_f32(r_pu, (lane * (2 + D) + 1) * 4);  // 0 past nsplit
   const bool lead = split0 == 0;  // the unit's first block writes step t-1's output and eviction
+  // step t-1's output (the unit's first block): each partial's column of the numerator
   float po[NS];
   if (lead) {
-    const int col = tid < D ? (2 + tid) * 4 : kPastEnd;  // threads past the last column read 0
+    const int col = tid < D ? (2 + tid) * 4 : kPastEnd;  // other threads read 0
 #pragma unroll
     for (int q = 0; q < NS; ++q) po[q] = ld_f32(r_pu, col + q * (2 + D) * 4);
   }
@@ -783,6 +796,7 @@ __global__ __launch_bounds__(kFusedThreads, 4) void decode_fused(DecodeArgs p, D
   const float x_new = lg[p.k];
   unsigned char* s_k = s_stage;
   unsigned char* s_v = s_stage + KB;
+  asm volatile("" ::: "memory");  // the metadata loads go out before the slices'
   if constexpr (STAGE) {
     const size_t row0 = static_cast<size_t>(unit) * b.k + s0;
     const uint32_t bytes = static_cast<uint32_t>(s1 - s0) * D * sizeof(T);  // <= KB (host-checked)
@@ -796,36 +810,61 @@ __global__ __launch_bounds__(kFusedThreads, 4) void decode_fused(DecodeArgs p, D
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, s_v + o, 16, tid * 16, c * NT * 16, 0, 0);
     }
   }
+  // No result of the loads above is used before all of them are issued (the
+  // compiler would otherwise start the merge, and wait for the partials,
+  // between the slice loads).
+  asm volatile("" : "+v"(pm), "+v"(pl)::"memory");
   // ---- step t-1's finish
   float Mg, Lg;
   const float ws = merge_weights(pm, pl, p.nsplit, Mg, Lg);
-  if (lead && tid < D) p.out[static_cast<size_t>(unit) * D + tid] = merge_column(po, ws) / Lg;
   const float invL = 1.f / Lg;
+  if (lead && tid < D) p.out[static_cast<size_t>(unit) * D + tid] = merge_column(po, ws) / Lg;
   uint64_t best = kNoKey;
   int best_slot = -1;
-  for (int base = 0; base < cnt; base += NP * NT) {
-    if (base > 0) fetch(base);
+  // Branch-free over each thread's slots (selects, no divergent branches): every
+  // slot's updated score, one branch for the threads holding slots of this
+  // block's slices, and the candidates' minimum key (the pattern bit only when
+  // a pattern is set: the loop exists in both forms).
+  const auto finish_slots = [&](auto with_pattern) {
+    for (int base = 0; base < cnt; base += NP * NT) {
+      if (base > 0) fetch(base);
+      const int j0 = base + tid * NP;
+      float sn[NP], cn[NP];
 #pragma unroll
-    for (int i = 0; i < NP; ++i) {
-      const int j = base + tid + i * NT;
-      const bool occupied = j < cnt;
-      float sj = rs[i], cj = rc[i];
-      const int32_t pj = rp[i];
-      add_weight(fast_exp2(rx[i] - Mg) * invL, sj, cj, compensate);
-      if (occupied && j >= s0 && j < s1) {  // this block's slices carry the slot into the next buffer
-        ny_score[uk + j] = sj;
-        ny_comp[uk + j] = cj;
-        ny_pos[uk + j] = pj;
+      for (int i = 0; i < NP; ++i) {
+        sn[i] = rs[i];
+        cn[i] = rc[i];
+        add_weight(fast_exp2(rx[i] - Mg) * invL, sn[i], cn[i], compensate);
       }
-      if (occupied && full && pj <= p.cand_limit) {
-        const uint64_t key = evict_key(sj, pj) | pattern_bit(p.pat_kind, p.pat_period, p.pat_width, pj, p.new_pos);
-        if (key < best) {
-          best = key;
-          best_slot = j;
+      if (j0 < s1 && j0 + NP > s0) {  // this block's slices carry their slots into the next buffer
+#pragma unroll
+        for (int i = 0; i < NP; ++i) {
+          const int j = j0 + i;
+          if (j >= s0 && j < s1) {  // s1 <= cnt + 1; slot cnt (the next free one) is written below
+            if (j < cnt) {
+              ny_score[uk + j] = sn[i];
+              ny_comp[uk + j] = cn[i];
+              ny_pos[uk + j] = rp[i];
+            }
+          }
+        }
+      }
+      if (full) {
+#pragma unroll
+        for (int i = 0; i < NP; ++i) {
+          const int j = j0 + i;
+          uint64_t key = evict_key(sn[i], rp[i]);
+          if constexpr (decltype(with_pattern)::value)
+            key |= pattern_bit(p.pat_kind, p.pat_period, p.pat_width, rp[i], p.new_pos);
+          key = j < cnt && rp[i] <= p.cand_limit ? key : kNoKey;
+          best_slot = key < best ? j : best_slot;
+          best = key < best ? key : best;
         }
       }
     }
-  }
+  };
+  if (p.pat_kind == kPatternNone) finish_slots(std::false_type{});
+  else finish_slots(std::true_type{});
   const float w_new = fast_exp2(x_new - Mg) * invL;
   int dst = cnt;  // cache not full: the new token takes the next free slot
   int32_t ev = -1;
