@@ -436,7 +436,10 @@ def main():
                    "recent_budget": w.recent_budget, "storage": w.dtype, "accumulate": "fp32",
                    "prefill_out": bool(a.prefill_out), "variant": a.variant, "pattern": a.pattern,
                    "rope_base": a.rope},
-        "roofline": {"kernel": f"decode_kernel<{w.dtype},{d}>", "bound": "hbm", "achieved": achieved,
+        "roofline": {"kernel": (f"h2o_decode_steps<{w.dtype},{d}> (decode_resident, decode_fused or decode_kernel "
+                                f"by cache shape; figures per decode step)" if use_steps
+                                else f"decode_kernel<{w.dtype},{d}>"),
+                     "bound": "hbm", "achieved": achieved,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": (measured_traffic(w.name)
                                  if a.layers is None and not glob and a.pattern == "none" and not a.rope else None),
                      "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
