@@ -24,13 +24,17 @@
 //     fp32 sum; eviction candidates compete on a 64-bit key (score bits, pos),
 //     which orders by score then position exactly; a wave/LDS min picks the
 //     victim, whose slot the new token's K/V, position and score overwrite.
-//   * Split path (few units): nsplit blocks per unit (one-wave blocks for short
-//     bf16 d=128 slices) each stream a slice of the slots and write (max, sum,
-//     o) partials and their logits; a second launch,
-//     one block per unit, merges the partials and runs the score pass.  The
-//     launch boundary orders the two: no block waits for another and no
-//     device-scope fence is needed (on gfx950 each such fence writes back and
-//     invalidates the whole L2 of its XCD).
+//   * Split path (few units): nsplit blocks per unit (one- or two-wave blocks
+//     for short bf16 d=128 slices) each stream a slice of the slots and write
+//     (max, sum, o) partials and their logits; a second launch, one block per
+//     unit, merges the partials and runs the score pass.  The launch boundary
+//     orders the two: no block waits for another and no device-scope fence is
+//     needed (on gfx950 each such fence writes back and invalidates the whole
+//     L2 of its XCD).
+//   * Several steps per call: a unit whose state fits a block's shared memory
+//     keeps it there over all the steps (decode_resident); on the split path
+//     each launch repeats the previous step's finish in every block and then
+//     attends its own slices (decode_fused), one launch per step.
 #include <type_traits>
 
 #include "h2o_device.h"
