@@ -105,3 +105,48 @@ def check_unit(p: dict) -> dict:
         res["ok"] = False
         res["msg"] = "; ".join(msgs)
     return res
+
+
+def continue_unit(p: dict) -> dict:
+    """Snapshot mode: the oracle starts from the GPU's cache of one unit (``p["snap"]``:
+    positions, scores with the compensation folded in, K and V rows) at position
+    ``p["next_pos"]`` and runs the decode steps of ``p["q"], p["k"], p["v"]``
+    ([T, d]), adopting the GPU's eviction ``p["evicted"]`` only at near-ties.
+    Compared: every step's output with ``p["out"]`` (2e-3 absolute), every
+    eviction (exact), and the cache after the steps with ``p["after"]``
+    (positions exact, scores 1e-4 relative, K/V rows exact)."""
+    from oracle import TIE_RTOL, UnitCache, default_scale
+
+    tag = p["tag"]
+    pos, score, K, V = p["snap"]
+    d = K.shape[1]
+    uc = UnitCache(heavy=p["heavy"], recent=p["recent"], scale=default_scale(d), d=d,
+                   pos=np.asarray(pos, np.int64), K=np.asarray(K, np.float64), V=np.asarray(V, np.float64),
+                   score=np.asarray(score, np.float64), next_pos=int(p["next_pos"]))
+    res = {"tag": tag, "ok": True, "msg": "", "ties": 0, "out_err": 0.0, "score_rel": 0.0}
+    try:
+        for t in range(len(p["q"])):
+            o, u, info = uc.step(p["q"][t], p["k"][t], p["v"][t], prefer_victim=int(p["evicted"][t]),
+                                 tie_rtol=TIE_RTOL)
+            res["ties"] += int(info["tie_adopted"])
+            res["out_err"] = max(res["out_err"], float(np.max(np.abs(p["out"][t] - o))))
+    except ParityMismatch as e:
+        return {"tag": tag, "ok": False, "msg": f"decision mismatch: {e}"}
+    msgs = []
+    if res["out_err"] > OUT_ATOL:
+        msgs.append(f"out err {res['out_err']:.3g}")
+    op, osc, ok_, ov = uc.snapshot()
+    gpos, gscore, gk, gv = p["after"]
+    order = np.argsort(gpos)
+    if not np.array_equal(gpos[order], op):
+        msgs.append("positions differ after the steps")
+    else:
+        res["score_rel"] = float(np.max(_rel(gscore[order], osc)))
+        if res["score_rel"] > SCORE_RTOL:
+            msgs.append(f"score rel {res['score_rel']:.3g}")
+        if not (np.array_equal(gk[order], ok_) and np.array_equal(gv[order], ov)):
+            msgs.append("cached K/V rows differ from the inputs at those positions")
+    if msgs:
+        res["ok"] = False
+        res["msg"] = "; ".join(msgs)
+    return res

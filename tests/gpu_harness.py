@@ -119,6 +119,22 @@ def unit_payload(g, b, h, Q, K, V, L, heavy, recent, out_index=None, tag=None):
                                    fin["k"][b, h], fin["v"][b, h])}
 
 
+def parallel_map(fn, items, procs=None):
+    """``fn`` over ``items`` in spawned worker processes (at most 16: the host's
+    CPU share per GPU); ``fn`` must live in a module the workers can import."""
+    if HERE not in sys.path:
+        sys.path.insert(0, HERE)
+    procs = procs or min(16, len(os.sched_getaffinity(0)), max(1, len(items)))
+    if procs <= 1 or len(items) <= 1:
+        return [fn(x) for x in items]
+    pool = mp.get_context("spawn").Pool(procs)
+    try:
+        return pool.map(fn, items, chunksize=1)
+    finally:
+        pool.close()
+        pool.join()
+
+
 def check_payloads(payloads, procs=None):
     """Run the oracle comparison for every payload (spawned workers)."""
     if HERE not in sys.path:
