@@ -90,15 +90,15 @@ def test_opt67b_32layer_b64_full_shape(layer):
 
 @pytest.mark.parametrize("budget", ["4pct", "10pct", "20pct"])
 def test_opt30b_b128_full_shape(budget):
-    # 7,168 units, prompt 1024, 1024 decode steps, k = 42 / 104 / 206
+    # 7,168 units, prompt 1024, 1024 decode steps, k = 42 / 104 / 206; 64 sampled units
     w = get(f"opt30b-b128-{budget}")
-    _run_sampled(w, 0, _sample(w, 16, int(budget[:-3])))
+    _run_sampled(w, 0, _sample(w, 64, int(budget[:-3])))
 
 
 def test_opt30b_b128_100pct_is_full_attention():
     # k = N: nothing is ever evicted and every output is full causal attention
     w = get("opt30b-b128-100pct")
-    g, _ = _run_sampled(w, 0, _sample(w, 8, 100))
+    g, _ = _run_sampled(w, 0, _sample(w, 64, 100))
     assert (g["evicted"] == -1).all()
 
 
