@@ -661,11 +661,11 @@ __global__ __launch_bounds__(kFinishThreads) void decode_finish(DecodeArgs a) {
 // repeats step t-1's finish (merge the unit's partials, add each weight to every
 // score, find the victim over all candidates) with the finish launch's
 // arithmetic, writes the updated score, compensation and position of the slots
-// in its own step-t slice to the other buffer of each (`ny`; nothing another
+// in its own step-t slices to the other buffer of each (`ny`; nothing another
 // block still reads is overwritten), puts token t-1 into the victim's slot when
-// that slot is in its slice, and then runs step t's slice exactly as the split
-// launch does.  Block 0 of the unit writes step t-1's output and eviction.  The
-// result equals one split launch and one finish launch per step, bit for bit.
+// that slot is in its slices, and then runs step t's slices exactly as the split
+// launch does.  The unit's first block writes step t-1's output and eviction.
+// The result equals one split launch and one finish launch per step, bit for bit.
 //
 // STAGE: the block's step-t slice of K/V rows and step t's q/k/v rows are
 // fetched into shared memory at the start (the slice by direct-to-LDS loads,
@@ -757,7 +757,8 @@ __global__ __launch_bounds__(kFusedThreads, 4) void decode_fused(DecodeArgs p, D
     tok = ld16(src + static_cast<size_t>(unit) * D + part * EPL);
   }
   // Through buffer descriptors bounded by the unit's occupied slots (and its
-  // partials): loads past the end read 0, so none needs a branch.
+  // partials): bytes past the end read as 0, so no load needs a branch (slots
+  // past the occupied count are loaded but never used).
   constexpr int NP = kFusedPrefetch;
   static_assert(NP % 4 == 0, "whole 16-byte loads");
   const uint32_t nb = static_cast<uint32_t>(cnt) * 4;
