@@ -75,6 +75,10 @@ constexpr int kWaveSplitLen = 128;
 // one-step launches, so their partials round alike.
 constexpr int kTwoWaveSplitLen = 64;
 constexpr int kTwoWaveThreads = 128;
+// slots in flight per row group of the two-wave blocks (with position rolling
+// each also carries a turned query: 4, so the registers hold)
+template <bool ROPE>
+constexpr int kTwoWaveUnroll = ROPE ? 4 : kWaveUnroll;
 constexpr int kPrefetch = 2;  // score-pass slots per thread whose metadata is loaded up front
 constexpr uint64_t kNoKey = ~0ull;
 constexpr int kNewSlot = -2;
@@ -93,7 +97,8 @@ struct Layout {
 
 // Where one unit's state lives for a step: its slot rows and per-slot score,
 // compensation and position (global memory, or a block's shared-memory copy),
-// and the new token's q/k/v rows.
+// the new token's q/k/v rows, and (position rolling) the slots' places among
+// the cached entries.
 template <typename T>
 struct UnitRefs {
   T* k;
@@ -104,6 +109,7 @@ struct UnitRefs {
   const T* qn;
   const T* kn;
   const T* vn;
+  const int32_t* rk;
 };
 
 // A unit's state in global memory.
@@ -113,7 +119,7 @@ __device__ inline UnitRefs<T> global_refs(const DecodeArgs& a, int unit) {
   return {static_cast<T*>(a.kslots) + u * a.k * D, static_cast<T*>(a.vslots) + u * a.k * D,
           a.score + u * a.kstride, a.comp + u * a.kstride, a.pos + u * a.kstride,
           static_cast<const T*>(a.q) + u * D, static_cast<const T*>(a.knew) + u * D,
-          static_cast<const T*>(a.vnew) + u * D};
+          static_cast<const T*>(a.vnew) + u * D, a.rank != nullptr ? a.rank + u * a.kstride : nullptr};
 }
 
 // Adds a step's weight w to a slot's score s with compensation c: a Kahan step
@@ -399,7 +405,7 @@ __device__ __forceinline__ void decode_step(const DecodeArgs& a, int unit, int s
   float qf[EPL];
   Elem<T>::unpack(ld16(qn + r * EPL), qf);
   RopeLane<T, D> rope;
-  const int32_t* rkb = ROPE ? a.rank + static_cast<size_t>(unit) * a.kstride : nullptr;
+  const int32_t* rkb = ROPE ? ur.rk : nullptr;
   if constexpr (ROPE) rope.init(a, qf, r);
   // The new token's rows are loaded once: group 0 attends to them and parks them
   // in LDS for the overwrite at the end.
@@ -463,7 +469,7 @@ __device__ __forceinline__ void decode_step(const DecodeArgs& a, int unit, int s
         kr[u] = ld16_stream(kb + static_cast<size_t>(j) * D + r * EPL);
         vr[u] = ld16_stream(vb + static_cast<size_t>(j) * D + r * EPL);
       }
-      if constexpr (ROPE) rkj[u] = rkb[j];
+      if constexpr (ROPE) rkj[u] = rkb[LDSKV && SPLIT ? j - s0 : j];
     }
     float x[UN];
     float mx = m;
@@ -719,10 +725,12 @@ __device__ inline void lds_barrier() {
 // NS: step t-1's partials per unit held in registers (>= p.nsplit; the merge
 // adds the same terms in the same order for any NS >= nsplit).  SPB: step-t
 // slices per block (1, or 2 when STAGE: one per NTP-thread group; the finish is
-// then repeated by half as many blocks).
-template <typename T, int D, int NTP, int UNP, bool STAGE, int NS, int SPB>
+// then repeated by half as many blocks).  ROPE: position rolling; each block
+// also moves the places of its slices' slots past step t-1's eviction (to
+// ny_rank) and attends with them.
+template <typename T, int D, int NTP, int UNP, bool STAGE, int NS, int SPB, bool ROPE>
 __global__ __launch_bounds__(kFusedThreads, 4) void decode_fused(DecodeArgs p, DecodeArgs b, float* ny_score,
-                                                             float* ny_comp, int32_t* ny_pos) {
+                                                             float* ny_comp, int32_t* ny_pos, int32_t* ny_rank) {
   constexpr int NT = kFusedThreads, EPL = Layout<T, D>::EPL, LPR = Layout<T, D>::LPR;
   constexpr int NGP = NTP / LPR;  // row groups of one slice's attending threads
   static_assert(NS <= kMaxSplitBlocks, "partials per unit");
@@ -730,8 +738,9 @@ __global__ __launch_bounds__(kFusedThreads, 4) void decode_fused(DecodeArgs p, D
   static_assert(SPB == 1 || (STAGE && SPB * NTP <= NT), "two slices per block: staged, one thread group each");
   constexpr int KB = SPB * kStageBytes;  // staged K (or V) bytes
   __shared__ uint64_t s_key[NT / kWave];
-  __shared__ int s_slot;
+  __shared__ int s_slot, s_vrank;
   __shared__ StepShared<T, D, NTP> sh[SPB];
+  __shared__ int32_t s_rank[ROPE && STAGE ? SPB * kStageBytes / (D * sizeof(T)) : 1];  // the slices' places
   __shared__ uint4 s_tok[3][LPR];                            // STAGE: step t's q, k, v rows
   extern __shared__ __align__(16) unsigned char s_stage[];  // STAGE: K rows | V rows of the block's slices
   const int tid = threadIdx.x, lb = xcd_block();
@@ -765,12 +774,13 @@ __global__ __launch_bounds__(kFusedThreads, 4) void decode_fused(DecodeArgs p, D
   const __amdgpu_buffer_rsrc_t r_lg = make_rsrc(lg, nb), r_sc = make_rsrc(p.score + uk, nb);
   const __amdgpu_buffer_rsrc_t r_cp = make_rsrc(p.comp + uk, compensate ? nb : 0u);  // plain adds: c = 0
   const __amdgpu_buffer_rsrc_t r_ps = make_rsrc(p.pos + uk, nb);
+  const __amdgpu_buffer_rsrc_t r_rk = make_rsrc(ROPE ? p.rank + uk : p.pos + uk, ROPE ? nb : 0u);
   const __amdgpu_buffer_rsrc_t r_pu = make_rsrc(pu, static_cast<uint32_t>(p.nsplit) * (2 + D) * 4);
   const int lane = tid & (kWave - 1);
   float pm = lane < p.nsplit ? ld_f32(r_pu, lane * (2 + D) * 4) : -INFINITY;
   float pl = ld_f32(r_pu, (lane * (2 + D) + 1) * 4);  // 0 past nsplit
   float rx[NP], rs[NP], rc[NP];
-  int32_t rp[NP];
+  int32_t rp[NP], rr[NP];
   const auto fetch = [&](int base) {  // slots base + tid * NP + i
 #pragma unroll
     for (int i = 0; i < NP; i += 4) {
@@ -784,9 +794,17 @@ __global__ __launch_bounds__(kFusedThreads, 4) void decode_fused(DecodeArgs p, D
         rc[i + e] = __uint_as_float(c[e]);
         rp[i + e] = static_cast<int32_t>(ps[e]);
       }
+      if constexpr (ROPE) {
+        const u32x4 rk4 = ld_u32x4(r_rk, off);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) rr[i + e] = static_cast<int32_t>(rk4[e]);
+      }
     }
   };
   fetch(0);
+  // position rolling, staged: the place of this thread's slot of the block's slices
+  const int nmine = s1 - s0;  // staged: at most NT
+  const int32_t myrank = ROPE && STAGE && tid < nmine ? static_cast<int32_t>(ld_u32(r_rk, (s0 + tid) * 4)) : 0;
   const bool lead = split0 == 0;  // the unit's first block writes step t-1's output and eviction
   // step t-1's output (the unit's first block): each partial's column of the numerator
   float po[NS];
@@ -826,6 +844,7 @@ __global__ __launch_bounds__(kFusedThreads, 4) void decode_fused(DecodeArgs p, D
   if (lead && tid < D) p.out[static_cast<size_t>(unit) * D + tid] = merge_column(po, ws) / Lg;
   uint64_t best = kNoKey;
   int best_slot = -1;
+  int32_t best_rank = 0;  // position rolling: the place of best_slot
   // Branch-free over each thread's slots (selects, no divergent branches): every
   // slot's updated score, one branch for the threads holding slots of this
   // block's slices, and the candidates' minimum key (the pattern bit only when
@@ -863,6 +882,7 @@ __global__ __launch_bounds__(kFusedThreads, 4) void decode_fused(DecodeArgs p, D
             key |= pattern_bit(p.pat_kind, p.pat_period, p.pat_width, rp[i], p.new_pos);
           key = j < cnt && rp[i] <= p.cand_limit ? key : kNoKey;
           best_slot = key < best ? j : best_slot;
+          if constexpr (ROPE) best_rank = key < best ? rr[i] : best_rank;
           best = key < best ? key : best;
         }
       }
@@ -889,11 +909,34 @@ __global__ __launch_bounds__(kFusedThreads, 4) void decode_fused(DecodeArgs p, D
 #pragma unroll
     for (int w = 1; w < NT / kWave; ++w) bm = s_key[w] < bm ? s_key[w] : bm;
     ev = static_cast<int32_t>(static_cast<uint32_t>(bm & 0xffffffffu));
-    if (best == bm) s_slot = best_slot;  // keys are unique: exactly one owner
+    if (best == bm) {  // keys are unique: exactly one owner
+      s_slot = best_slot;
+      if (ROPE) s_vrank = best_rank;
+    }
     lds_barrier();
     dst = s_slot == kNewSlot ? -1 : s_slot;
   }
   if (lead && tid == 0 && p.evicted != nullptr) p.evicted[unit] = ev;
+  if constexpr (ROPE) {
+    // places after step t-1: not full, the new token is the latest entry (place
+    // cnt); full, the entries after the victim move down one place and the new
+    // token takes the last; the new token itself evicted, nothing moves
+    const int rv = full && dst >= 0 ? s_vrank : 0;
+    const auto moved = [&](int j, int32_t rk) {
+      if (!full) return j == cnt ? cnt : rk;
+      if (dst < 0) return rk;
+      return j == dst ? p.k - 1 : (rk > rv ? rk - 1 : rk);
+    };
+    if constexpr (STAGE) {
+      if (tid < nmine) {
+        const int32_t rk = moved(s0 + tid, myrank);
+        ny_rank[uk + s0 + tid] = rk;
+        s_rank[tid] = rk;
+      }
+    } else {
+      for (int j = s0 + tid; j < s1; j += NT) ny_rank[uk + j] = moved(j, static_cast<int32_t>(ld_u32(r_rk, j * 4)));
+    }
+  }
   const bool mine = dst >= s0 && dst < s1;  // token t-1 goes into a slot of this block's slices
   if (mine) {
     if (tid == 0) {
@@ -926,15 +969,15 @@ __global__ __launch_bounds__(kFusedThreads, 4) void decode_fused(DecodeArgs p, D
     const T* tk = reinterpret_cast<const T*>(&s_tok[0][0]);
     const size_t gofs = static_cast<size_t>(g0 - s0) * D * sizeof(T);
     const UnitRefs<T> ur{reinterpret_cast<T*>(s_k + gofs), reinterpret_cast<T*>(s_v + gofs), nullptr, nullptr,
-                         nullptr, tk, tk + D, tk + 2 * D};
-    decode_step<T, D, true, false, NTP, UNP, true>(b, unit, split, ur, nullptr, sh[gi], gt);
+                         nullptr, tk, tk + D, tk + 2 * D, ROPE ? s_rank + (g0 - s0) : nullptr};
+    decode_step<T, D, true, ROPE, NTP, UNP, true>(b, unit, split, ur, nullptr, sh[gi], gt);
   } else {
-    // the slot rows written above are read below by this block: wait for them
+    // the slot rows and places written above are read below by this block: wait for them
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     if (tid >= NTP) return;
-    decode_step<T, D, true, false, NTP, UNP, false>(b, unit, split0, global_refs<T, D>(b, unit), nullptr, sh[0],
-                                                    tid);
+    decode_step<T, D, true, ROPE, NTP, UNP, false>(b, unit, split0, global_refs<T, D>(b, unit), nullptr, sh[0],
+                                                   tid);
   }
 }
 
@@ -994,7 +1037,7 @@ __global__ __launch_bounds__(NT) void decode_resident(DecodeArgs a0, int steps, 
     a.new_pos = a0.new_pos + t;
     a.cand_limit = a0.cand_limit + t;
     const T* tk = stok + cur * 3 * D;
-    const UnitRefs<T> ur{sk, sv, ssc, scp, sps, tk, tk + D, tk + 2 * D};
+    const UnitRefs<T> ur{sk, sv, ssc, scp, sps, tk, tk + D, tk + 2 * D, nullptr};
     decode_step<T, D, false, false, NT, UN, true>(a, unit, 0, ur, s_logit, sh, tid);
     if (which < 3 && t + 1 < steps) st16(stok + (cur ^ 1) * 3 * D + which * D + part * EPL, nxt);
     __syncthreads();  // this step's writes and the next token's rows before the next step
@@ -1069,9 +1112,9 @@ hipError_t launch_resident_typed(const DecodeArgs& a, int units, int steps, int6
 enum class SplitShape { kTwoWave, kWave, kBlock };
 template <typename T, int D, bool ROPE>
 SplitShape split_shape(int split_len) {
-  if constexpr (std::is_same<T, bf16_t>::value && D == 128 && !ROPE) {
+  if constexpr (std::is_same<T, bf16_t>::value && D == 128) {
     if (split_len <= kTwoWaveSplitLen) return SplitShape::kTwoWave;
-    if (split_len <= kWaveSplitLen) return SplitShape::kWave;
+    if (!ROPE && split_len <= kWaveSplitLen) return SplitShape::kWave;
   }
   return SplitShape::kBlock;
 }
@@ -1081,12 +1124,14 @@ template <typename T, int D, bool ROPE>
 void launch_partials(const DecodeArgs& a, int units, hipStream_t s) {
   const dim3 grid(units * a.nsplit);
   const SplitShape sh = split_shape<T, D, ROPE>(a.split_len);
-  if constexpr (std::is_same<T, bf16_t>::value && D == 128 && !ROPE) {
+  if constexpr (std::is_same<T, bf16_t>::value && D == 128) {
     if (sh == SplitShape::kTwoWave) {
-      hipLaunchKernelGGL((decode_kernel<T, D, true, ROPE, kTwoWaveThreads, kWaveUnroll>), grid,
+      hipLaunchKernelGGL((decode_kernel<T, D, true, ROPE, kTwoWaveThreads, kTwoWaveUnroll<ROPE>>), grid,
                          dim3(kTwoWaveThreads), 0, s, a);
       return;
     }
+  }
+  if constexpr (std::is_same<T, bf16_t>::value && D == 128 && !ROPE) {
     if (sh == SplitShape::kWave) {
       hipLaunchKernelGGL((decode_kernel<T, D, true, ROPE, kWaveThreads, kWaveUnroll>), grid, dim3(kWaveThreads), 0,
                          s, a);
@@ -1126,38 +1171,53 @@ hipError_t launch_typed(const DecodeArgs& a, int units, hipStream_t s) {
 
 }  // namespace
 
-template <typename T, int D>
+template <typename T, int D, bool ROPE>
 hipError_t launch_split_typed(const DecodeArgs* p, const DecodeArgs& b, float* ny_score, float* ny_comp,
-                              int32_t* ny_pos, int units, hipStream_t s) {
+                              int32_t* ny_pos, int32_t* ny_rank, int units, hipStream_t s) {
   const dim3 grid(units * b.nsplit);
-  const SplitShape sh = split_shape<T, D, false>(b.split_len);
+  const SplitShape sh = split_shape<T, D, ROPE>(b.split_len);
   if (p == nullptr) {  // the first step's slices alone
-    launch_partials<T, D, false>(b, units, s);
+    launch_partials<T, D, ROPE>(b, units, s);
     return hipGetLastError();
   }
   if constexpr (std::is_same<T, bf16_t>::value && D == 128) {
     static_assert(kTwoWaveSplitLen * D * sizeof(T) <= kStageBytes, "a two-wave slice fits the stage");
-    if (sh == SplitShape::kTwoWave && p->nsplit <= kStagePartials) {  // the partials fit 32 registers
+    const bool stage = static_cast<size_t>(b.split_len) * D * sizeof(T) <= kStageBytes &&
+                       p->nsplit <= kStagePartials;  // the slice fits the stage, the partials 32 registers
+    constexpr int UN2 = kTwoWaveUnroll<ROPE>;
+    if (sh == SplitShape::kTwoWave && stage) {
       if (b.nsplit % 2 == 0 && units * b.nsplit >= kPairedSlices) {  // two slices per block
-        hipLaunchKernelGGL((decode_fused<T, D, kTwoWaveThreads, kWaveUnroll, true, kStagePartials, 2>),
+        hipLaunchKernelGGL((decode_fused<T, D, kTwoWaveThreads, UN2, true, kStagePartials, 2, ROPE>),
                            dim3(units * b.nsplit / 2), dim3(kFusedThreads), 4 * kStageBytes, s, *p, b, ny_score,
-                           ny_comp, ny_pos);
+                           ny_comp, ny_pos, ny_rank);
       } else {
-        hipLaunchKernelGGL((decode_fused<T, D, kTwoWaveThreads, kWaveUnroll, true, kStagePartials, 1>), grid,
-                           dim3(kFusedThreads), 2 * kStageBytes, s, *p, b, ny_score, ny_comp, ny_pos);
+        hipLaunchKernelGGL((decode_fused<T, D, kTwoWaveThreads, UN2, true, kStagePartials, 1, ROPE>), grid,
+                           dim3(kFusedThreads), 2 * kStageBytes, s, *p, b, ny_score, ny_comp, ny_pos, ny_rank);
       }
     } else if (sh == SplitShape::kTwoWave) {
-      hipLaunchKernelGGL((decode_fused<T, D, kTwoWaveThreads, kWaveUnroll, false, kMaxSplitBlocks, 1>), grid,
-                         dim3(kFusedThreads), 0, s, *p, b, ny_score, ny_comp, ny_pos);
+      hipLaunchKernelGGL((decode_fused<T, D, kTwoWaveThreads, UN2, false, kMaxSplitBlocks, 1, ROPE>), grid,
+                         dim3(kFusedThreads), 0, s, *p, b, ny_score, ny_comp, ny_pos, ny_rank);
     } else if (sh == SplitShape::kWave) {
-      hipLaunchKernelGGL((decode_fused<T, D, kWaveThreads, kWaveUnroll, false, kMaxSplitBlocks, 1>), grid,
-                         dim3(kFusedThreads), 0, s, *p, b, ny_score, ny_comp, ny_pos);
+      if constexpr (!ROPE)
+        hipLaunchKernelGGL((decode_fused<T, D, kWaveThreads, kWaveUnroll, false, kMaxSplitBlocks, 1, false>), grid,
+                           dim3(kFusedThreads), 0, s, *p, b, ny_score, ny_comp, ny_pos, ny_rank);
     }
     if (sh != SplitShape::kBlock) return hipGetLastError();
   }
-  hipLaunchKernelGGL((decode_fused<T, D, kThreads, kUnroll, false, kMaxSplitBlocks, 1>), grid, dim3(kFusedThreads),
-                     0, s, *p, b, ny_score, ny_comp, ny_pos);
+  if (ROPE && p->nsplit <= kStagePartials)  // position rolling: fewer partial registers leave room for the rotation
+    hipLaunchKernelGGL((decode_fused<T, D, kThreads, kUnroll, false, kStagePartials, 1, ROPE>), grid,
+                       dim3(kFusedThreads), 0, s, *p, b, ny_score, ny_comp, ny_pos, ny_rank);
+  else
+    hipLaunchKernelGGL((decode_fused<T, D, kThreads, kUnroll, false, kMaxSplitBlocks, 1, ROPE>), grid,
+                       dim3(kFusedThreads), 0, s, *p, b, ny_score, ny_comp, ny_pos, ny_rank);
   return hipGetLastError();
+}
+
+template <typename T, int D>
+hipError_t launch_split_any(const DecodeArgs* p, const DecodeArgs& b, float* ny_score, float* ny_comp,
+                            int32_t* ny_pos, int32_t* ny_rank, int units, hipStream_t s) {
+  if (b.rank != nullptr) return launch_split_typed<T, D, true>(p, b, ny_score, ny_comp, ny_pos, ny_rank, units, s);
+  return launch_split_typed<T, D, false>(p, b, ny_score, ny_comp, ny_pos, ny_rank, units, s);
 }
 
 template <typename T, int D>
@@ -1167,15 +1227,18 @@ hipError_t launch_finish_typed(const DecodeArgs& a, int units, hipStream_t s) {
 }
 
 hipError_t launch_decode_split(int dtype, int head_dim, const DecodeArgs* prev, const DecodeArgs& cur,
-                               float* ny_score, float* ny_comp, int32_t* ny_pos, int units, hipStream_t s) {
-  if (cur.rank != nullptr || cur.fixed_new != nullptr || cur.nsplit < 2 ||
-      (prev != nullptr && (prev->nsplit < 2 || prev->nsplit > kMaxSplitBlocks)))
+                               float* ny_score, float* ny_comp, int32_t* ny_pos, int32_t* ny_rank, int units,
+                               hipStream_t s) {
+  const bool rope = cur.rank != nullptr;
+  if (cur.fixed_new != nullptr || cur.nsplit < 2 ||
+      (prev != nullptr && (prev->nsplit < 2 || prev->nsplit > kMaxSplitBlocks || (prev->rank != nullptr) != rope ||
+                           (rope && ny_rank == nullptr))))
     return hipErrorInvalidConfiguration;
   if (dtype == 0)
-    return head_dim == 64 ? launch_split_typed<float, 64>(prev, cur, ny_score, ny_comp, ny_pos, units, s)
-                          : launch_split_typed<float, 128>(prev, cur, ny_score, ny_comp, ny_pos, units, s);
-  return head_dim == 64 ? launch_split_typed<bf16_t, 64>(prev, cur, ny_score, ny_comp, ny_pos, units, s)
-                        : launch_split_typed<bf16_t, 128>(prev, cur, ny_score, ny_comp, ny_pos, units, s);
+    return head_dim == 64 ? launch_split_any<float, 64>(prev, cur, ny_score, ny_comp, ny_pos, ny_rank, units, s)
+                          : launch_split_any<float, 128>(prev, cur, ny_score, ny_comp, ny_pos, ny_rank, units, s);
+  return head_dim == 64 ? launch_split_any<bf16_t, 64>(prev, cur, ny_score, ny_comp, ny_pos, ny_rank, units, s)
+                        : launch_split_any<bf16_t, 128>(prev, cur, ny_score, ny_comp, ny_pos, ny_rank, units, s);
 }
 
 hipError_t launch_decode_finish(int dtype, int head_dim, const DecodeArgs& a, int units, hipStream_t s) {

@@ -49,6 +49,7 @@ struct h2o_cache {
   float* col_sum;
   // position rolling (rope_base > 0), else null
   int32_t* rank;   // [units, kstride] position of each slot among the cached entries
+  int32_t* rank2;  // its second buffer (multi-step calls on the split path with position rolling)
   int32_t rope_units;  // units whose prompt is rotated and scored per pass
   void* rope_ops;  // the rotated prompt of rope_units units: fp32 q, k [rope_units, lpad_cap, d] each;
                    // bf16 q hi, q lo, k hi, k lo [rope_units, lpad_cap, d] each
@@ -154,14 +155,15 @@ h2o_status check_params(const h2o_params* p, Sizes* sz) {
                     : 0;
     sz->lpad = round32(p->max_prompt);
     sz->prefill = 2 * u * static_cast<size_t>(sz->lpad) * 4;
-    // position rolling: slot ranks, the rotated prompt of a chunk of units (8
+    // position rolling: slot ranks (two buffers on the split path), the rotated prompt of a chunk of units (8
     // bytes per element: fp32 q and k, or bf16 hi and lo of each), cos/sin per
     // prompt position and pair, per-pair frequencies (two floats)
     const size_t per_unit = static_cast<size_t>(sz->lpad) * d * 8;
     sz->rope_units = per_unit == 0 ? static_cast<int32_t>(units)
                                    : static_cast<int32_t>(std::min<size_t>(
                                          u, std::max<size_t>(8, kRopeScratchBytes / per_unit)));
-    sz->rope = p->rope_base > 0.f ? u * static_cast<size_t>(round32(static_cast<int32_t>(k))) * 4 +
+    sz->rope = p->rope_base > 0.f ? u * static_cast<size_t>(round32(static_cast<int32_t>(k))) * 4 *
+                                            (sz->max_split > 1 ? 2 : 1) +
                                         static_cast<size_t>(sz->rope_units) * per_unit +
                                         static_cast<size_t>(sz->lpad) * (d / 2) * 8 + (d / 2) * 8
                                   : 0;
@@ -172,8 +174,8 @@ h2o_status check_params(const h2o_params* p, Sizes* sz) {
 
 void free_all(h2o_cache* c) {
   void* ptrs[] = {c->kslots, c->vslots, c->score, c->comp, c->pos, c->part, c->logits, c->score2, c->comp2,
-                  c->pos2, c->part2, c->logits2, c->row_lse2, c->col_sum, c->rank, c->rope_ops, c->rope_cs,
-                  c->rope_th};
+                  c->pos2, c->part2, c->logits2, c->row_lse2, c->col_sum, c->rank, c->rank2, c->rope_ops,
+                  c->rope_cs, c->rope_th};
   for (void* q : ptrs)
     if (q != nullptr) (void)hipFree(q);
 }
@@ -376,6 +378,7 @@ h2o_status h2o_cache_create(const h2o_params* params, int device, h2o_cache** ou
       {reinterpret_cast<void**>(&c->row_lse2), u * c->lpad_cap * 4},
       {reinterpret_cast<void**>(&c->col_sum), u * c->lpad_cap * 4},
       {reinterpret_cast<void**>(&c->rank), rope ? u * c->kstride * 4 : 0},
+      {reinterpret_cast<void**>(&c->rank2), rope && c->max_split > 1 ? u * c->kstride * 4 : 0},
       {&c->rope_ops, rope ? static_cast<size_t>(c->rope_units) * c->lpad_cap * d * 8 : 0},
       {reinterpret_cast<void**>(&c->rope_cs), rope ? static_cast<size_t>(c->lpad_cap) * (d / 2) * 8 : 0},
       {reinterpret_cast<void**>(&c->rope_th), rope ? (d / 2) * 8 : 0},
@@ -742,10 +745,10 @@ h2o_status h2o_decode_steps(h2o_cache* c, const void* q, const void* k, const vo
   }
   // Steps on the split path (which, once reached, lasts: the count only grows)
   // run one launch each: launch i finishes step i-1 and runs step i's slices,
-  // alternating two buffers of scores/compensations/positions and of
-  // partials/logits; a finish launch closes the run (bit-identical to a split
-  // launch and a finish launch per step).
-  const bool fuse = c->rank == nullptr && c->max_split > 1;
+  // alternating two buffers of scores/compensations/positions (and places, with
+  // position rolling) and of partials/logits; a finish launch closes the run
+  // (bit-identical to a split launch and a finish launch per step).
+  const bool fuse = c->max_split > 1;
   int32_t t = 0;
   for (; t < steps; ++t) {
     int32_t unused = 0;
@@ -764,7 +767,9 @@ h2o_status h2o_decode_steps(h2o_cache* c, const void* q, const void* k, const vo
     int32_t* pos;
     float* part;
     float* logits;
-  } buf[2] = {{c->score, c->comp, c->pos, c->part, c->logits}, {c->score2, c->comp2, c->pos2, c->part2, c->logits2}};
+    int32_t* rank;
+  } buf[2] = {{c->score, c->comp, c->pos, c->part, c->logits, c->rank},
+              {c->score2, c->comp2, c->pos2, c->part2, c->logits2, c->rank2}};
   auto step_args = [&](int32_t i, int which) {
     const size_t off = static_cast<size_t>(i) * tok;
     h2o::DecodeArgs a = decode_args(c, static_cast<const char*>(q) + off, static_cast<const char*>(k) + off,
@@ -775,6 +780,7 @@ h2o_status h2o_decode_steps(h2o_cache* c, const void* q, const void* k, const vo
     a.pos = buf[which].pos;
     a.part = buf[which].part;
     a.logits = buf[which].logits;
+    a.rank = buf[which].rank;  // nullptr without position rolling
     return a;
   };
   auto advance = [&]() {
@@ -783,13 +789,14 @@ h2o_status h2o_decode_steps(h2o_cache* c, const void* q, const void* k, const vo
   };
   int which = 0;  // buffer holding step `prev`'s scores and its partials
   h2o::DecodeArgs prev = step_args(t, which);
-  hipError_t e = h2o::launch_decode_split(c->p.dtype, c->d, nullptr, prev, nullptr, nullptr, nullptr, c->units, s);
+  hipError_t e =
+      h2o::launch_decode_split(c->p.dtype, c->d, nullptr, prev, nullptr, nullptr, nullptr, nullptr, c->units, s);
   if (e != hipSuccess) return hip_fail(e, "decode launch");
   advance();
   for (++t; t < steps; ++t) {
     h2o::DecodeArgs cur = step_args(t, which ^ 1);
     e = h2o::launch_decode_split(c->p.dtype, c->d, &prev, cur, buf[which ^ 1].score, buf[which ^ 1].comp,
-                                 buf[which ^ 1].pos, c->units, s);
+                                 buf[which ^ 1].pos, buf[which ^ 1].rank, c->units, s);
     if (e != hipSuccess) return hip_fail(e, "decode launch");
     advance();
     which ^= 1;
@@ -802,6 +809,8 @@ h2o_status h2o_decode_steps(h2o_cache* c, const void* q, const void* k, const vo
     e = hipMemcpy2DAsync(c->score, pitch, c->score2, pitch, width, rows, hipMemcpyDeviceToDevice, s);
     if (e == hipSuccess) e = hipMemcpy2DAsync(c->comp, pitch, c->comp2, pitch, width, rows, hipMemcpyDeviceToDevice, s);
     if (e == hipSuccess) e = hipMemcpy2DAsync(c->pos, pitch, c->pos2, pitch, width, rows, hipMemcpyDeviceToDevice, s);
+    if (e == hipSuccess && c->rank != nullptr)
+      e = hipMemcpy2DAsync(c->rank, pitch, c->rank2, pitch, width, rows, hipMemcpyDeviceToDevice, s);
   }
   if (e != hipSuccess) return hip_fail(e, "decode launch");
   return H2O_OK;

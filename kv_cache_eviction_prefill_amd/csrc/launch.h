@@ -51,12 +51,14 @@ bool decode_resident_fits(int dtype, int head_dim, int units, int k);
 // Split-path steps of a multi-step call in one launch each.  prev == nullptr:
 // step `cur`'s slices alone (the split launch).  Otherwise the launch finishes
 // step `prev` (its partials and logits in prev.part / prev.logits; scores,
-// compensations and positions read from prev's arrays and written, for the
-// slots of each block's step-`cur` slice, to ny_*) and then runs step `cur`'s
-// slices.  launch_decode_finish is the finish launch alone (in place on a's
-// arrays).  No position rolling, no fixed scores; every step on the split path.
+// compensations, positions and, with position rolling, places read from prev's
+// arrays and written, for the slots of each block's step-`cur` slices, to ny_*,
+// which are cur's arrays) and then runs step `cur`'s slices.
+// launch_decode_finish is the finish launch alone (in place on a's arrays).  No
+// fixed scores; every step on the split path.
 hipError_t launch_decode_split(int dtype, int head_dim, const DecodeArgs* prev, const DecodeArgs& cur,
-                               float* ny_score, float* ny_comp, int32_t* ny_pos, int units, hipStream_t s);
+                               float* ny_score, float* ny_comp, int32_t* ny_pos, int32_t* ny_rank, int units,
+                               hipStream_t s);
 hipError_t launch_decode_finish(int dtype, int head_dim, const DecodeArgs& a, int units, hipStream_t s);
 hipError_t launch_decode_resident(int dtype, int head_dim, const DecodeArgs& a, int units, int steps,
                                   int64_t tok_bytes, int64_t out_step, hipStream_t s);

@@ -80,11 +80,12 @@ def test_cache_bytes_accounting():
     assert tot == kv + 6 * 32 * 12 + (2 * (6 * 64 * 130 * 4 + 6 * 9 * 4) + 6 * 32 * 12) + 2 * 6 * 64 * 4
     st, kv32, _ = _bytes(dtype="f32")
     assert kv32 == 2 * kv
-    # position rolling adds slot ranks, the rotated prompt of a chunk of units (8
-    # bytes per element: bf16 hi and lo of q and of k) and the rotary tables
+    # position rolling adds slot ranks (a second buffer of them on the split path),
+    # the rotated prompt of a chunk of units (8 bytes per element: bf16 hi and lo
+    # of q and of k) and the rotary tables
     st, _, tot_r = _bytes(batch=2, heads=3, head_dim=128, heavy=4, recent=4, dtype="bf16", max_prompt=64,
                           rope_base=10000.0)
-    assert st == 0 and tot_r == tot + 6 * 32 * 4 + 6 * 64 * 128 * 8 + 64 * 64 * 8 + 64 * 8
+    assert st == 0 and tot_r == tot + 2 * 6 * 32 * 4 + 6 * 64 * 128 * 8 + 64 * 64 * 8 + 64 * 8
     # the chunk is capped at 512 MiB of scratch: 256 units of a 2048-token prompt at d = 128
     kw = dict(batch=64, heads=32, head_dim=128, heavy=205, recent=205, dtype="bf16", max_prompt=2048)
     st, _, big = _bytes(**kw)
