@@ -347,6 +347,30 @@ def test_slot_order_does_not_matter():
         np.testing.assert_allclose(oa, ob, rtol=1e-12, atol=1e-13)
 
 
+@pytest.mark.parametrize("L,T,M,heavy,recent,seed", [(40, 90, 37, 8, 6, 0), (20, 60, 1, 5, 0, 1), (0, 50, 25, 4, 4, 2)])
+def test_snapshot_mode_continues_the_run(L, T, M, heavy, recent, seed):
+    # snapshot mode: a cache rebuilt from the state after M steps (positions,
+    # scores, K/V rows in any slot order, next position) runs the remaining steps
+    # exactly as the uninterrupted run does
+    d = 8
+    Q, K, V = _rand(L + T, d, seed)
+    Q = Q * 2.0
+    full = run_unit(Q, K, V, L, heavy, recent)
+    part = run_unit(Q[:L + M], K[:L + M], V[:L + M], L, heavy, recent)
+    c = part["cache"]
+    perm = np.random.default_rng(seed).permutation(len(c.pos))
+    snap = UnitCache(heavy=heavy, recent=recent, scale=c.scale, d=d, pos=c.pos[perm].copy(), K=c.K[perm].copy(),
+                     V=c.V[perm].copy(), score=c.score[perm].copy(), next_pos=L + M)
+    for t in range(M, T):
+        o, u, _ = snap.step(Q[L + t], K[L + t], V[L + t])
+        assert u == full["evicted"][t]
+        np.testing.assert_allclose(o, full["out"][t], rtol=1e-12, atol=1e-13)
+    fp, fs, fk, fv = full["cache"].snapshot()
+    sp, ss, sk, sv = snap.snapshot()
+    assert np.array_equal(fp, sp) and np.array_equal(fk, sk) and np.array_equal(fv, sv)
+    np.testing.assert_allclose(ss, fs, rtol=1e-12)
+
+
 def test_decode_replay_band_and_mismatch():
     K = np.array([[1.0, 0], [1.0, 0], [0.0, 0.0]])
     Q = np.tile([1.0, 0.0], (3, 1))
