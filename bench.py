@@ -271,7 +271,7 @@ def main():
     a = parse()
     if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: units are independent and the path has no cross-GPU step, "
-              "so only --gpus 1 is supported on this build.", file=sys.stderr)
+              "so only --gpus 1 is supported.", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np

@@ -65,7 +65,7 @@ typedef enum {
   H2O_ERR_STATE = 2,       /* call not valid in the cache's current state */
   H2O_ERR_OOM = 3,         /* device allocation failed */
   H2O_ERR_HIP = 4,         /* HIP runtime error (launch failure, async fault) */
-  H2O_ERR_UNSUPPORTED = 5  /* valid request this build does not implement */
+  H2O_ERR_UNSUPPORTED = 5  /* a valid request the library does not implement */
 } h2o_status;
 
 typedef struct {
