@@ -2,7 +2,7 @@
 AddressSanitizer and UndefinedBehaviorSanitizer on its host side only (device
 code is compiled as usual), linked into the driver ``tests/native/abi_checks.cpp``,
 and run.  Without a GPU the driver exercises every argument and state check
-that precedes a device call; on a GPU machine the same binary also drives a small
+that precedes a device call; with a GPU present the same binary also drives a small
 cache end to end (create, prefill, decode, read, statistics, destroy)."""
 import glob
 import os
