@@ -3,8 +3,9 @@ the C ABI (needs an MI355X): bit-identical to the same number of h2o_decode_step
 calls, on every decode path (small budgets, the split path for few units, the
 one-wave blocks, position rolling, a sparse pattern, and the launches that hold
 each unit's rows in shared memory over all the steps, and the split path's one
-launch per step that finishes the previous step), outputs of every step kept or
-only the last, and its argument checks."""
+launch per step that finishes the previous step), on listed cases and on 48
+seeded random shapes spread over calls of random lengths, outputs of every step
+kept or only the last, and its argument checks."""
 import numpy as np
 import pytest
 import torch
@@ -73,6 +74,44 @@ def test_steps_match_single_steps(wl, B, H, d, L, T, heavy, recent, rope, patter
     w = scaled(get(wl), batch=B, heads=H, head_dim=d, prompt_len=L, decode_steps=T, heavy_budget=heavy,
                recent_budget=recent, n_anchors=max(1, (L + T) // 50))
     log(f"case steps {w.dtype} B={B} H={H} d={d} L={L} T={T} k={heavy}+{recent} rope={rope} pattern={pattern}")
+    _compare(w, L, T, rope, pattern, [T // 2])
+
+
+def test_steps_random_sweep():
+    # seeded random shapes over every decode path, the steps split over three calls
+    g = np.random.default_rng(20240611)
+    patterns = [None, None, ("strided", 8, 1), ("fixed", 16, 4)]
+    for case in range(48):
+        B = int(g.choice([1, 2, 4, 8]))
+        H = int(g.choice([1, 2, 8, 16, 32, 64, 128]))
+        d = int(g.choice([64, 128]))
+        if case % 3 == 0:  # any budget
+            heavy = int(g.integers(0, 1200))
+            recent = int(g.integers(0 if heavy > 0 else 1, 1200))
+        elif case % 3 == 1:  # a multiple of 64 slots: slices of exactly 64 once full
+            kk = 64 * int(g.integers(2, 33))
+            recent = int(g.integers(0, kk))
+            heavy = kk - recent
+        else:  # small budgets: one block per unit
+            heavy = int(g.integers(0, 100))
+            recent = int(g.integers(0 if heavy > 0 else 1, 100))
+        L = int(g.integers(1, heavy + recent + 300))
+        T = int(g.integers(2, 200))
+        rope = float(g.choice([0.0, 10000.0]))
+        pattern = patterns[int(g.integers(0, 4))]
+        wl = "tiny-fp32" if case % 5 == 4 else "opt6.7b-layer-b16"
+        w = scaled(get(wl), batch=B, heads=H, head_dim=d, prompt_len=L, decode_steps=T, heavy_budget=heavy,
+                   recent_budget=recent, n_anchors=max(1, (L + T) // 50))
+        cuts = sorted(int(c) for c in g.integers(1, T, size=2))
+        log(f"sweep {case}: {w.dtype} B={B} H={H} d={d} L={L} T={T} k={heavy}+{recent} rope={rope} "
+            f"pattern={pattern} calls at {cuts}")
+        _compare(w, L, T, rope, pattern, cuts)
+
+
+def _compare(w, L, T, rope, pattern, cuts):
+    """h2o_decode_steps over calls split at `cuts` against one h2o_decode_step per
+    step: outputs, evictions, scores, positions, K/V rows and counters bit for bit."""
+    B, H, d = w.batch, w.heads, w.head_dim
     q, k, v = synth.torch_qkv(w, 0, 0, L + T, DEV)
     qd, kd, vd = (x[:, :, L:].permute(2, 0, 1, 3).contiguous() for x in (q, k, v))
     one = _cache(w, q, k, v, L, rope, pattern)
@@ -83,9 +122,9 @@ def test_steps_match_single_steps(wl, B, H, d, L, T, heavy, recent, rope, patter
     many = _cache(w, q, k, v, L, rope, pattern)
     o2 = torch.full((T, B, H, d), float("nan"), dtype=torch.float32, device=DEV)
     e2 = torch.full((T, B, H), -7, dtype=torch.int32, device=DEV)
-    half = T // 2  # two calls: the second continues from the first's state
-    many.decode_steps(qd[:half], kd[:half], vd[:half], o2[:half], e2[:half])
-    many.decode_steps(qd[half:], kd[half:], vd[half:], o2[half:], e2[half:])
+    bounds = [0] + list(cuts) + [T]  # several calls: each continues from the previous one's state
+    for t0, t1 in zip(bounds[:-1], bounds[1:]):
+        many.decode_steps(qd[t0:t1], kd[t0:t1], vd[t0:t1], o2[t0:t1], e2[t0:t1])
     torch.cuda.synchronize()
     _same(o1.cpu().numpy(), o2.cpu().numpy(), "outputs")
     _same(e1.cpu().numpy(), e2.cpu().numpy(), "evictions")
