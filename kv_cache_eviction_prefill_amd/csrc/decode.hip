@@ -681,13 +681,18 @@ __global__ __launch_bounds__(kFinishThreads) void decode_finish(DecodeArgs a) {
 // global memory after the finish.
 constexpr int kFusedThreads = 256;
 constexpr int kFusedPrefetch = 8;  // slots per thread whose metadata is loaded in one batch
-constexpr int kStageLoads = 4;     // block-wide 4 KB direct loads per staged K or V slice
-constexpr int kStageBytes = kStageLoads * kFusedThreads * 16;  // largest staged K (or V) slice
+constexpr int kStageBytes = 16 * 1024;  // largest staged K (or V) slice
 constexpr int kStagePartials = 32;  // most partials per unit of the staged launch
 // Staged launches over at least this many slices run two slices per block, each
 // attended by its own two waves, so half as many blocks repeat the finish
 // (32 units x 2048 slots: 10.4 -> 9.1 us per step).
 constexpr int kPairedSlices = 512;
+// Over at least this many slices a 512-thread block holds four slices (one
+// block per CU, 128 KB of staged rows): a quarter as many blocks repeat the
+// finish, each thread finishing half as many slots (32 units x 2048 slots:
+// 9.1-9.3 -> 8.5 us per step).
+constexpr int kQuadSlices = 1024;
+constexpr int kQuadThreads = 512;
 
 // Blocks are dealt to the 8 XCDs round-robin.  With a grid that divides evenly,
 // block b runs as logical block (b mod 8) * grid/8 + b/8, so consecutive logical
@@ -724,19 +729,22 @@ __device__ inline void lds_barrier() {
 
 // NS: step t-1's partials per unit held in registers (>= p.nsplit; the merge
 // adds the same terms in the same order for any NS >= nsplit).  SPB: step-t
-// slices per block (1, or 2 when STAGE: one per NTP-thread group; the finish is
-// then repeated by half as many blocks).  ROPE: position rolling; each block
+// slices per block (1, or 2 or 4 when STAGE: one per NTP-thread group; the
+// finish is then repeated by a half or a quarter as many blocks).  NT: threads
+// per block (256; 512 for four slices).  ROPE: position rolling; each block
 // also moves the places of its slices' slots past step t-1's eviction (to
 // ny_rank) and attends with them.
-template <typename T, int D, int NTP, int UNP, bool STAGE, int NS, int SPB, bool ROPE>
-__global__ __launch_bounds__(kFusedThreads, 4) void decode_fused(DecodeArgs p, DecodeArgs b, float* ny_score,
-                                                             float* ny_comp, int32_t* ny_pos, int32_t* ny_rank) {
-  constexpr int NT = kFusedThreads, EPL = Layout<T, D>::EPL, LPR = Layout<T, D>::LPR;
+template <typename T, int D, int NTP, int UNP, bool STAGE, int NS, int SPB, bool ROPE, int NT = kFusedThreads>
+__global__ __launch_bounds__(NT, NT > kFusedThreads ? 2 : 4) void decode_fused(DecodeArgs p, DecodeArgs b,
+                                                                           float* ny_score, float* ny_comp,
+                                                                           int32_t* ny_pos, int32_t* ny_rank) {
+  constexpr int EPL = Layout<T, D>::EPL, LPR = Layout<T, D>::LPR;
   constexpr int NGP = NTP / LPR;  // row groups of one slice's attending threads
   static_assert(NS <= kMaxSplitBlocks, "partials per unit");
   static_assert(!STAGE || 3 * LPR <= kWave, "wave 0 moves step t's q/k/v rows");
-  static_assert(SPB == 1 || (STAGE && SPB * NTP <= NT), "two slices per block: staged, one thread group each");
+  static_assert(SPB == 1 || (STAGE && SPB * NTP <= NT), "several slices per block: staged, one thread group each");
   constexpr int KB = SPB * kStageBytes;  // staged K (or V) bytes
+  static_assert(KB % (NT * 16) == 0, "the stage splits into block-wide 16-byte loads");
   __shared__ uint64_t s_key[NT / kWave];
   __shared__ int s_slot, s_vrank;
   __shared__ StepShared<T, D, NTP> sh[SPB];
@@ -768,7 +776,7 @@ __global__ __launch_bounds__(kFusedThreads, 4) void decode_fused(DecodeArgs p, D
   // Through buffer descriptors bounded by the unit's occupied slots (and its
   // partials): bytes past the end read as 0, so no load needs a branch (slots
   // past the occupied count are loaded but never used).
-  constexpr int NP = kFusedPrefetch;
+  constexpr int NP = kFusedPrefetch * kFusedThreads / NT;  // one batch covers the same slots at any NT
   static_assert(NP % 4 == 0, "whole 16-byte loads");
   const uint32_t nb = static_cast<uint32_t>(cnt) * 4;
   const __amdgpu_buffer_rsrc_t r_lg = make_rsrc(lg, nb), r_sc = make_rsrc(p.score + uk, nb);
@@ -1186,7 +1194,11 @@ hipError_t launch_split_typed(const DecodeArgs* p, const DecodeArgs& b, float* n
                        p->nsplit <= kStagePartials;  // the slice fits the stage, the partials 32 registers
     constexpr int UN2 = kTwoWaveUnroll<ROPE>;
     if (sh == SplitShape::kTwoWave && stage) {
-      if (b.nsplit % 2 == 0 && units * b.nsplit >= kPairedSlices) {  // two slices per block
+      if (b.nsplit % 4 == 0 && units * b.nsplit >= kQuadSlices) {  // four slices per block
+        hipLaunchKernelGGL((decode_fused<T, D, kTwoWaveThreads, UN2, true, kStagePartials, 4, ROPE, kQuadThreads>),
+                           dim3(units * b.nsplit / 4), dim3(kQuadThreads), 8 * kStageBytes, s, *p, b, ny_score,
+                           ny_comp, ny_pos, ny_rank);
+      } else if (b.nsplit % 2 == 0 && units * b.nsplit >= kPairedSlices) {  // two slices per block
         hipLaunchKernelGGL((decode_fused<T, D, kTwoWaveThreads, UN2, true, kStagePartials, 2, ROPE>),
                            dim3(units * b.nsplit / 2), dim3(kFusedThreads), 4 * kStageBytes, s, *p, b, ny_score,
                            ny_comp, ny_pos, ny_rank);

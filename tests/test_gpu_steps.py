@@ -56,15 +56,19 @@ def _same(a, b, what):
     ("opt6.7b-layer-b16", 2, 1, 64, 700, 150, 300, 300, 0.0, None),       # d = 64: 256-thread slices
     ("opt6.7b-layer-b16", 1, 16, 128, 2400, 120, 1152, 1152, 0.0, None),  # 36 two-wave slices per unit: more
                                                                           # partials than the staged launch holds
-    # slices of 64 slots staged in shared memory: one or two slices per block
+    # slices of 64 slots staged in shared memory: one, two or four slices per block
     ("opt6.7b-layer-b16", 2, 1, 128, 600, 80, 256, 256, 0.0, ("fixed", 16, 4)),  # one per block, a pattern
     ("opt6.7b-layer-b16", 1, 32, 128, 1100, 60, 512, 512, 0.0, ("strided", 8, 1)),  # two per block, a pattern
     ("opt6.7b-layer-b16", 1, 32, 128, 1100, 60, 1024, 0, 0.0, None),     # two per block, K_r = 0
+    ("opt6.7b-layer-b16", 1, 32, 128, 2100, 60, 1024, 1024, 0.0, ("strided", 8, 1)),  # four per block, a pattern
+    ("opt6.7b-layer-b16", 1, 32, 128, 2100, 60, 2048, 0, 0.0, None),     # four per block, K_r = 0
+    ("opt6.7b-layer-b16", 1, 64, 128, 1100, 30, 512, 512, 0.0, None),    # four per block, 64 units
     # position rolling on the split path: each launch also moves the slots' places
     ("opt6.7b-layer-b16", 2, 1, 128, 600, 150, 256, 256, 10000.0, None),  # slices of 64, staged
     ("opt6.7b-layer-b16", 1, 4, 128, 400, 200, 150, 150, 10000.0, None),  # slices of 75, from global memory
     ("opt6.7b-layer-b16", 2, 1, 128, 600, 100, 512, 0, 10000.0, None),    # K_r = 0: the new token may leave
     ("opt6.7b-layer-b16", 2, 1, 128, 60, 301, 200, 200, 10000.0, None),   # fills, then splits
+    ("opt6.7b-layer-b16", 1, 32, 128, 2100, 40, 1024, 1024, 10000.0, None),  # staged, four slices per block
     ("opt6.7b-layer-b16", 8, 32, 128, 2100, 41, 1024, 1024, 0.0, None),   # slices of 512 slots: 256-thread blocks
     ("opt6.7b-layer-b16", 4, 1, 128, 400, 101, 300, 0, 0.0, None),        # K_r = 0 on the split path
     ("opt6.7b-layer-b16", 2, 2, 128, 400, 120, 150, 150, 0.0, ("fixed", 16, 4)),  # a pattern on the split path
