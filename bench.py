@@ -109,6 +109,9 @@ def parse():
                          "extrapolated linearly to the whole decode (the 4 M-token stream)")
     ap.add_argument("--cpu-units", type=int, default=96,
                     help="units in the CPU-oracle sample (about 15 s of CPU work at this shape)")
+    ap.add_argument("--per-step", action="store_true",
+                    help="single-layer workloads: decode through one h2o_decode_step call per step (the call of "
+                         "ordinary generation) instead of one h2o_decode_steps call for all steps")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="accepted for older profiling commands: the 1 GiB copy and read that calibrate the "
                          "HBM byte counters and give the measured bandwidth ceilings now always run")
@@ -344,8 +347,9 @@ def main():
     ev_ptr = [ev[l].data_ptr() for l in range(NL)]
     prefill_c, decode_c, steps_c = lib.h2o_prefill, lib.h2o_decode_step, lib.h2o_decode_steps
     # one layer: the whole decode is one h2o_decode_steps call (each step's evicted
-    # positions kept in a [T, B, H] log, the last step's output in `out`)
-    use_steps = NL == 1 and not glob
+    # positions kept in a [T, B, H] log, the last step's output in `out`), unless
+    # asked for one h2o_decode_step call per step
+    use_steps = NL == 1 and not glob and not a.per_step
     ev_log = torch.empty((T, B, H), dtype=torch.int32, device=dev) if use_steps else None
     colsc_c, prefill_sc_c, decode_sc_c = lib.h2o_column_scores, lib.h2o_prefill_scored, lib.h2o_decode_step_scored
 
@@ -435,9 +439,12 @@ def main():
                    "prompt_len": L, "decode_steps": T, "heavy_budget": w.heavy_budget,
                    "recent_budget": w.recent_budget, "storage": w.dtype, "accumulate": "fp32",
                    "prefill_out": bool(a.prefill_out), "variant": a.variant, "pattern": a.pattern,
-                   "rope_base": a.rope},
+                   "rope_base": a.rope,
+                   "decode_call": "h2o_decode_steps" if use_steps else "h2o_decode_step"},
         "roofline": {"kernel": (f"h2o_decode_steps<{w.dtype},{d}> (decode_resident, decode_fused or decode_kernel "
                                 f"by cache shape; figures per decode step)" if use_steps
+                                else f"h2o_decode_step<{w.dtype},{d}> (decode_kernel, with decode_finish on the split "
+                                f"path; figures per decode step)" if a.per_step
                                 else f"decode_kernel<{w.dtype},{d}>"),
                      "bound": "hbm", "achieved": achieved,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": (measured_traffic(w.name)
