@@ -137,13 +137,15 @@ def test_one_wave_blocks(heavy, recent):
     _run(w, [(int(i) // w.heads, int(i) % w.heads) for i in sorted(idx)], 40)
 
 
-@pytest.mark.parametrize("variant", ["rope", "pattern", "fixed"])
-def test_one_wave_blocks_with_variants(variant):
-    # 1,024 bf16 units at k = 160: the pattern and fixed-score variants run on the
-    # one-wave blocks, position rolling on the 256-thread blocks
+@pytest.mark.parametrize("variant,heavy,recent", [("rope", 90, 70), ("rope", 170, 130), ("pattern", 90, 70),
+                                                  ("fixed", 90, 70)])
+def test_one_wave_blocks_with_variants(variant, heavy, recent):
+    # 1,024 bf16 units at k = 160 (and 300 with rolling: slots not a multiple of
+    # the 32 in flight per block): the pattern and fixed-score variants run on
+    # the one-wave blocks, position rolling on the two-wave blocks
     from gpu_harness import run_gpu_scored
 
-    L, T, heavy, recent = 330, 30, 90, 70
+    L, T = 330, 30
     w = scaled(get("opt6.7b-layer-b16"), layers=1, batch=32, heads=32, prompt_len=L, decode_steps=T,
                heavy_budget=heavy, recent_budget=recent, n_anchors=5)
     q, k, v = synth.torch_qkv(w, 0, 0, L + T, DEV)

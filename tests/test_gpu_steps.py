@@ -42,6 +42,7 @@ def _same(a, b, what):
     ("opt6.7b-layer-b16", 1, 4, 128, 400, 200, 150, 150, 0.0, None),      # split path (few units, k = 300)
     ("opt6.7b-layer-b16", 8, 128, 128, 300, 40, 100, 100, 0.0, None),     # one-wave blocks (1024 units, k > 128)
     ("opt6.7b-layer-b16", 2, 3, 128, 120, 100, 30, 10, 10000.0, None),    # position rolling
+    ("opt6.7b-layer-b16", 32, 32, 128, 330, 20, 90, 70, 10000.0, None),   # rolling on the two-wave blocks
     ("opt6.7b-layer-b16", 2, 3, 64, 120, 100, 30, 10, 0.0, ("strided", 8, 1)),  # sparse pattern
     ("tiny-fp32", 1, 2, 64, 256, 64, 26, 26, 0.0, None),                  # fp32 storage
     # rows held in shared memory over the steps (one launch for all of them)
