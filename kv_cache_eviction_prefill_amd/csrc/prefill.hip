@@ -275,6 +275,10 @@ __device__ inline float row_update(const floatx16& s, float c2, int lane, float&
   float r = 1.f;
   const uint64_t need = __ballot(!(ts <= 0x1p64f));
   moved = need != 0;
+  if (!moved) {  // wave-uniform: the common tile only adds its sum (l * 1 + ts, as below)
+    l += ts;
+    return r;
+  }
   const uint32_t pair = static_cast<uint32_t>(need) | static_cast<uint32_t>(need >> 32);
   if ((pair >> (lane & 31)) & 1u) {
     float tm = fmaxf(s[0], s[1]);
