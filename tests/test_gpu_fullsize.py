@@ -57,20 +57,23 @@ def _check_properties(w, g, L, T):
             assert set(range(max(0, L + T - w.recent_budget), L + T)) <= s
 
 
-def _run_sampled(w, layer, units, T=None, check_props=True):
+def _run_sampled(w, layer, units, T=None, check_props=True, rope=0.0):
     L = w.prompt_len
     T = w.decode_steps if T is None else T
     q, k, v = synth.torch_qkv(w, layer, 0, L + T, DEV)
-    log(f"case {w.name} layer {layer}: B={w.batch} H={w.heads} L={L} T={T} k={w.k}; "
+    log(f"case {w.name} layer {layer}: B={w.batch} H={w.heads} L={L} T={T} k={w.k} rope={rope}; "
         f"{len(units)} sampled units")
-    g = run_gpu(q, k, v, L, w.heavy_budget, w.recent_budget, w.dtype, out_units=units)
+    g = run_gpu(q, k, v, L, w.heavy_budget, w.recent_budget, w.dtype, out_units=units, rope_base=rope)
     if check_props:
         _check_properties(w, g, L, T)
     payloads = []
     for n, (b, h) in enumerate(units):
         Q, K, V = _host_unit(q, k, v, b, h)
-        payloads.append(unit_payload(g, b, h, Q, K, V, L, w.heavy_budget, w.recent_budget, out_index=n,
-                                     tag=f"{w.name}/L{layer}/b{b}h{h}"))
+        pl = unit_payload(g, b, h, Q, K, V, L, w.heavy_budget, w.recent_budget, out_index=n,
+                          tag=f"{w.name}/L{layer}/b{b}h{h}")
+        if rope:
+            pl.update(rope=(rope,))
+        payloads.append(pl)
     del q, k, v
     torch.cuda.empty_cache()
     results, bad = check_payloads(payloads)
@@ -86,6 +89,14 @@ def test_opt67b_32layer_b64_full_shape(layer):
     # steps, k = 410; 32 sampled units on each of three layers
     w = get("opt6.7b-32L-b64")
     _run_sampled(w, layer, _sample(w, 32, layer))
+
+
+def test_opt67b_full_shape_with_rolling():
+    # position rolling in the benchmark's launch configuration (2048 units,
+    # prompt 2048, k = 410: the two-wave rolling blocks), 200 decode steps, 8
+    # sampled units
+    w = get("opt6.7b-32L-b64")
+    _run_sampled(w, 3, _sample(w, 8, 3), T=200, rope=10000.0)
 
 
 @pytest.mark.parametrize("budget", ["4pct", "10pct", "20pct"])
