@@ -371,6 +371,18 @@ struct StepShared {
   int slot, vrank;
 };
 
+// Dot product of a lane's 8 bf16 key and query elements: four packed bf16
+// dot-product-accumulate steps, pairs (0,1), (2,3), (4,5), (6,7) in order.
+__device__ inline float dot8_bf16(const uint4& k, const uint4& q) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  float d = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, k.x), __builtin_bit_cast(bf16x2, q.x), 0.f,
+                                            false);
+  d = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, k.y), __builtin_bit_cast(bf16x2, q.y), d, false);
+  d = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, k.z), __builtin_bit_cast(bf16x2, q.z), d, false);
+  d = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, k.w), __builtin_bit_cast(bf16x2, q.w), d, false);
+  return d;
+}
+
 // One decode step of one unit (SPLIT: of one slice of its slots).  ku/vu: the
 // unit's slot rows, in global memory, or (LDSKV) the block's copy of them in
 // shared memory, which the step reads and overwrites in place (a split step:
@@ -406,7 +418,9 @@ __device__ __forceinline__ void decode_step(const DecodeArgs& a, int unit, int s
   const int32_t* ps = ur.ps;
 
   float qf[EPL];
-  Elem<T>::unpack(ld16(qn + r * EPL), qf);
+  const uint4 q_raw = ld16(qn + r * EPL);
+  Elem<T>::unpack(q_raw, qf);
+  constexpr bool kDot2 = std::is_same<T, bf16_t>::value && !ROPE;  // packed bf16 dot products
   RopeLane<T, D> rope;
   const int32_t* rkb = ROPE ? ur.rk : nullptr;
   if constexpr (ROPE) rope.init(a, qf, r);
@@ -445,8 +459,12 @@ __device__ __forceinline__ void decode_step(const DecodeArgs& a, int unit, int s
     Elem<T>::unpack(kn_raw, kf);
     Elem<T>::unpack(vn_raw, vf);
     float dot = 0.f;
+    if constexpr (kDot2) {
+      dot = dot8_bf16(kn_raw, q_raw);
+    } else {
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) dot = fmaf(qf[e], kf[e], dot);
+      for (int e = 0; e < EPL; ++e) dot = fmaf(qf[e], kf[e], dot);
+    }
     const float x = group_sum<LPR>(dot) * a.c2;
     m = x;
     l = 1.f;
@@ -478,15 +496,19 @@ __device__ __forceinline__ void decode_step(const DecodeArgs& a, int unit, int s
     float mx = m;
 #pragma unroll
     for (int u = 0; u < UN; ++u) {
-      float kf[EPL];
-      Elem<T>::unpack(kr[u], kf);
       float dot = 0.f;
-      if constexpr (ROPE) {
+      if constexpr (kDot2) {
+        dot = dot8_bf16(kr[u], q_raw);
+      } else if constexpr (ROPE) {
+        float kf[EPL];
+        Elem<T>::unpack(kr[u], kf);
         float qr[EPL];
         rope.turn(qf, rkj[u] - a.count, qr);
 #pragma unroll
         for (int e = 0; e < EPL; ++e) dot = fmaf(qr[e], kf[e], dot);
       } else {
+        float kf[EPL];
+        Elem<T>::unpack(kr[u], kf);
 #pragma unroll
         for (int e = 0; e < EPL; ++e) dot = fmaf(qf[e], kf[e], dot);
       }
