@@ -70,6 +70,8 @@ def _same(a, b, what):
     ("opt6.7b-layer-b16", 2, 1, 128, 600, 100, 512, 0, 10000.0, None),    # K_r = 0: the new token may leave
     ("opt6.7b-layer-b16", 2, 1, 128, 60, 301, 200, 200, 10000.0, None),   # fills, then splits
     ("opt6.7b-layer-b16", 1, 32, 128, 2100, 40, 1024, 1024, 10000.0, None),  # staged, four slices per block
+    ("opt6.7b-layer-b16", 1, 32, 128, 2100, 40, 1024, 1024, 10000.0, ("strided", 8, 1)),  # and a pattern
+    ("opt6.7b-layer-b16", 32, 32, 128, 330, 20, 90, 70, 10000.0, ("fixed", 16, 4)),  # two-wave rolling, a pattern
     ("opt6.7b-layer-b16", 8, 32, 128, 2100, 41, 1024, 1024, 0.0, None),   # slices of 512 slots: 256-thread blocks
     ("opt6.7b-layer-b16", 4, 1, 128, 400, 101, 300, 0, 0.0, None),        # K_r = 0 on the split path
     ("opt6.7b-layer-b16", 2, 2, 128, 400, 120, 150, 150, 0.0, ("fixed", 16, 4)),  # a pattern on the split path
