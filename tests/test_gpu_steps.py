@@ -152,6 +152,49 @@ def _compare(w, L, T, rope, pattern, cuts):
         c.close()
 
 
+@pytest.mark.parametrize("wl,B,H,d,L,T,heavy,recent,rope", [
+    ("opt6.7b-layer-b16", 1, 32, 128, 2100, 90, 1024, 1024, 0.0),     # four slices per staged block
+    ("opt6.7b-layer-b16", 1, 32, 128, 2100, 90, 1024, 1024, 10000.0),  # the same with rolling
+    ("opt6.7b-layer-b16", 32, 32, 128, 330, 40, 90, 70, 10000.0),      # two-wave rolling blocks
+])
+def test_steps_and_single_steps_interleaved(wl, B, H, d, L, T, heavy, recent, rope):
+    # one-step calls between multi-step calls continue the same run: each call
+    # finds the state the previous one left, whichever path wrote it
+    w = scaled(get(wl), batch=B, heads=H, head_dim=d, prompt_len=L, decode_steps=T, heavy_budget=heavy,
+               recent_budget=recent, n_anchors=max(1, (L + T) // 50))
+    log(f"case interleaved {w.dtype} B={B} H={H} L={L} T={T} k={heavy}+{recent} rope={rope}")
+    q, k, v = synth.torch_qkv(w, 0, 0, L + T, DEV)
+    qd, kd, vd = (x[:, :, L:].permute(2, 0, 1, 3).contiguous() for x in (q, k, v))
+    one = _cache(w, q, k, v, L, rope, None)
+    o1 = torch.empty((T, B, H, d), dtype=torch.float32, device=DEV)
+    e1 = torch.empty((T, B, H), dtype=torch.int32, device=DEV)
+    for t in range(T):
+        one.decode_step(qd[t], kd[t], vd[t], o1[t], e1[t])
+    mix = _cache(w, q, k, v, L, rope, None)
+    o2 = torch.full((T, B, H, d), float("nan"), dtype=torch.float32, device=DEV)
+    e2 = torch.full((T, B, H), -7, dtype=torch.int32, device=DEV)
+    t = 0
+    for n in (1, 7, 1, 1, 20, 1, 13):
+        if n == 1:
+            mix.decode_step(qd[t], kd[t], vd[t], o2[t], e2[t])
+        else:
+            mix.decode_steps(qd[t:t + n], kd[t:t + n], vd[t:t + n], o2[t:t + n], e2[t:t + n])
+        t += n
+    mix.decode_steps(qd[t:], kd[t:], vd[t:], o2[t:], e2[t:])
+    torch.cuda.synchronize()
+    _same(o1.cpu().numpy(), o2.cpu().numpy(), "outputs")
+    _same(e1.cpu().numpy(), e2.cpu().numpy(), "evictions")
+    r1, r2 = one.read(), mix.read()
+    for key in ("pos", "score"):
+        _same(r1[key], r2[key], key)
+    occupied = r1["pos"] >= 0
+    for key in ("k", "v"):
+        _same(r1[key][occupied], r2[key][occupied], key)
+    assert one.info() == mix.info()
+    one.close()
+    mix.close()
+
+
 def test_steps_argument_checks():
     c = H2OCache(1, 2, 128, 4, 4, dtype="bf16", max_prompt=8)
     buf = torch.zeros((4, 1, 2, 128), dtype=torch.bfloat16, device=DEV)
