@@ -5,7 +5,8 @@ one-wave blocks, position rolling, a sparse pattern, and the launches that hold
 each unit's rows in shared memory over all the steps, and the split path's one
 launch per step that finishes the previous step), on listed cases and on 48
 seeded random shapes spread over calls of random lengths, outputs of every step
-kept or only the last, and its argument checks."""
+kept or only the last, one-step calls interleaved with multi-step calls, a
+second prefill after decoding, and its argument checks."""
 import numpy as np
 import pytest
 import torch
@@ -193,6 +194,51 @@ def test_steps_and_single_steps_interleaved(wl, B, H, d, L, T, heavy, recent, ro
     assert one.info() == mix.info()
     one.close()
     mix.close()
+
+
+@pytest.mark.parametrize("B,H,L1,L2,heavy,recent,rope", [
+    (1, 32, 2100, 300, 1024, 1024, 0.0),    # split path, then a prompt shorter than the budget
+    (1, 32, 2100, 300, 1024, 1024, 10000.0),
+    (2, 4, 100, 10, 20, 20, 0.0),          # one block per unit
+])
+def test_second_prefill_starts_over(B, H, L1, L2, heavy, recent, rope):
+    # a prefill after decoding re-initialises the cache: the run that follows is
+    # the run of a fresh cache given the same prompt
+    T1, T2 = 60, 80
+    w = scaled(get("opt6.7b-layer-b16"), batch=B, heads=H, head_dim=128, prompt_len=L1, decode_steps=T1,
+               heavy_budget=heavy, recent_budget=recent, n_anchors=max(1, (L1 + T1) // 50))
+    log(f"case second prefill B={B} H={H} L={L1} then {L2} k={heavy}+{recent} rope={rope}")
+    q, k, v = synth.torch_qkv(w, 0, 0, L1 + T1, DEV)
+    q2, k2, v2 = synth.torch_qkv(w, 1, 0, L2 + T2, DEV)
+    qd, kd, vd = (x[:, :, L1:].permute(2, 0, 1, 3).contiguous() for x in (q, k, v))
+    qd2, kd2, vd2 = (x[:, :, L2:].permute(2, 0, 1, 3).contiguous() for x in (q2, k2, v2))
+    used = H2OCache(B, H, 128, heavy, recent, dtype="bf16", max_prompt=L1, rope_base=rope)
+    used.prefill(*(x[:, :, :L1].contiguous() for x in (q, k, v)))
+    junk = torch.empty((T1, B, H, 128), dtype=torch.float32, device=DEV)
+    used.decode_steps(qd[:T1 - 3], kd[:T1 - 3], vd[:T1 - 3], junk[:T1 - 3])
+    for t in range(T1 - 3, T1):
+        used.decode_step(qd[t], kd[t], vd[t], junk[t])
+    fresh = H2OCache(B, H, 128, heavy, recent, dtype="bf16", max_prompt=L1, rope_base=rope)
+    outs, evs = [], []
+    for c in (used, fresh):
+        c.prefill(*(x[:, :, :L2].contiguous() for x in (q2, k2, v2)))
+        o = torch.empty((T2, B, H, 128), dtype=torch.float32, device=DEV)
+        e = torch.empty((T2, B, H), dtype=torch.int32, device=DEV)
+        c.decode_steps(qd2, kd2, vd2, o, e)
+        outs.append(o)
+        evs.append(e)
+    torch.cuda.synchronize()
+    _same(outs[0].cpu().numpy(), outs[1].cpu().numpy(), "outputs")
+    _same(evs[0].cpu().numpy(), evs[1].cpu().numpy(), "evictions")
+    r1, r2 = used.read(), fresh.read()
+    for key in ("pos", "score"):
+        _same(r1[key], r2[key], key)
+    occupied = r2["pos"] >= 0
+    for key in ("k", "v"):
+        _same(r1[key][occupied], r2[key][occupied], key)
+    assert used.info() == fresh.info()
+    used.close()
+    fresh.close()
 
 
 def test_steps_argument_checks():
