@@ -11,12 +11,14 @@
 //
 // Work mapping (gfx950, wave64, 256 threads per block; 128 for small budgets
 // over many units; one wave per unit for bf16 d=128 at larger budgets over many
-// units):
+// units, two with position rolling):
 //   * A K/V row of d elements is 16 bytes per lane over LPR lanes (bf16 d=128:
 //     16 lanes), so one wave-wide load instruction moves 4 whole rows (1 KiB),
 //     fully coalesced.  The block's 16 row groups walk the unit's slots with
 //     2 (4 with few units) rows in flight per group, K and V of a slot loaded
 //     together.
+//   * bf16 dot products run as packed bf16 dot-product instructions (fp32
+//     accumulation), then a 16-lane DPP reduction per row.
 //   * Each group keeps an online softmax (max, sum, o) in registers; groups are
 //     merged through LDS.  Logits go to LDS (single-block path) or to a global
 //     scratch row (split path), so the score pass needs no second K read.
@@ -34,7 +36,8 @@
 //   * Several steps per call: a unit whose state fits a block's shared memory
 //     keeps it there over all the steps (decode_resident); on the split path
 //     each launch repeats the previous step's finish in every block and then
-//     attends its own slices (decode_fused), one launch per step.
+//     attends its own slices (decode_fused), one launch per step; short
+//     slices are staged in shared memory, up to four per 512-thread block.
 #include <type_traits>
 
 #include "h2o_device.h"
