@@ -270,6 +270,43 @@ def ceilings(torch, dev, lib, sp):
     return out
 
 
+def compute_ceilings(torch, dev, lib, sp):
+    """Measured rates of the prefill scoring passes' arithmetic on this GPU, best
+    of 3 timed with events: h2o_probe_mix runs, from registers alone, 16 MFMAs
+    32x32x16 bf16 per wave and iteration (mode 0), the same with 32 fma + exp2 +
+    add per lane beside them (mode 1: the passes' mix, the vector work
+    independent of the matrix results), and the vector work alone (mode 2),
+    at 4 waves per SIMD."""
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    iters = 4000
+    flops = cus * 16 * iters * 16 * 2.0 * 32 * 32 * 16  # 16 waves per CU
+    sink = torch.zeros(4, dtype=torch.int32, device=dev)
+
+    def run(mode, n):
+        st = lib.h2o_probe_mix(mode, n, sink.data_ptr(), sp)
+        if st:
+            raise RuntimeError(f"h2o_probe_mix failed with status {st}")
+
+    out = {}
+    for mode, name in ((0, "mfma_only_TFs"), (1, "mix_TFs"), (2, "vector_only_TFs")):
+        run(mode, 64)
+        best = None
+        for _ in range(3):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            run(mode, iters)
+            e1.record()
+            e1.synchronize()
+            t = e0.elapsed_time(e1) / 1e3
+            best = t if best is None else min(best, t)
+        # mode 2 executes no MFMA: its figure is the MFMA rate the vector work alone would allow
+        out[name] = flops / best / 1e12
+    out["note"] = ("h2o_probe_mix: 16 MFMAs 32x32x16 bf16 (one 64 x 32 logit tile at d = 128) and, per lane, "
+                   "32 x (fma, exp2, add) per wave-iteration, from registers, 4 waves per SIMD; TFLOP/s of the "
+                   "MFMA work (vector_only: the MFMA rate the vector work alone would allow)")
+    return out
+
+
 def main():
     a = parse()
     if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -386,6 +423,7 @@ def main():
             evs[2].record(stream)
 
     ceil = ceilings(torch, dev, lib, sp)  # untimed: bandwidth references and the counters' calibration copy
+    cceil = compute_ceilings(torch, dev, lib, sp)  # untimed: the scoring passes' arithmetic alone
 
     for _ in range(a.warmup):
         one_step()
@@ -461,7 +499,9 @@ def main():
         "prefill": {"tokens_per_s": B * L * K / t_pre, "ms": 1e3 * t_pre / K,
                     "mfma_tflops": pf_flops / t_pre / 1e12,
                     "mfma_frac": pf_flops / t_pre / 1e12 / BF16_MFMA_PEAK_TFLOPS,
-                    "alg_GBps": pf_bytes / t_pre / 1e9},
+                    "alg_GBps": pf_bytes / t_pre / 1e9,
+                    "measured_ceilings": cceil,
+                    "frac_of_measured_mix": pf_flops / t_pre / 1e12 / cceil["mix_TFs"]},
         "timing": {"wall_s": wall, "event_s": t_all, "input_gen_s": gen_s},
     }
 

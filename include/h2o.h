@@ -320,6 +320,20 @@ const char* h2o_last_error(void);
  * 16), H2O_ERR_HIP. */
 h2o_status h2o_probe_read(const void* buf, size_t bytes, uint32_t* sink, void* stream);
 
+/* Measurement aid, not part of the method: the instruction mix of a prefill
+ * scoring pass from registers alone, on `stream`.  Every wave (4 blocks of 256
+ * threads per compute unit, 4 waves per SIMD) runs `iters` iterations of
+ * 16 MFMAs 32x32x16 bf16 (mode 0 and 1) and, per lane, 32 times one fma, one
+ * exp2 and one add on values independent of the matrix results (mode 1 and 2):
+ * the arithmetic of one 64 x 32 logit tile at d = 128, with no memory traffic
+ * and no barriers.  Timing mode 0, 1 and 2 gives the matrix rate, the rate of
+ * the mix and the vector rate this GPU sustains; a mode-0 or mode-1 launch
+ * executes (compute units) * 16 waves * iters * 16 * 32768 MFMA flops.  `sink`
+ * (device, 4 bytes) is written with probability 2^-32 only.
+ * Errors: H2O_ERR_INVALID_ARG (mode not 0-2, iters < 1, NULL sink),
+ * H2O_ERR_HIP. */
+h2o_status h2o_probe_mix(int32_t mode, int32_t iters, uint32_t* sink, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

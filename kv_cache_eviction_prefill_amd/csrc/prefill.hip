@@ -57,9 +57,11 @@ __device__ inline int lane_id_here() {
 // ------------------------------------------------------------------ bf16 MFMA passes
 // Each of a block's 4 waves owns 64 rows (pass 1: queries, pass 2: keys) as two
 // 32-row subtiles whose operand stays in registers.  The other operand streams
-// through a ring of three 32-row LDS tiles, loaded straight from global memory to
-// LDS (buffer loads with the LDS flag: no registers, no LDS-store instructions),
-// two tiles ahead of the one in use, with one barrier per tile.  A block handles
+// through a ring of 32-row LDS tiles, loaded straight from global memory to LDS
+// (buffer loads with the LDS flag: no registers, no LDS-store instructions):
+// plain operands two tiles per barrier from a ring of four (the next two tiles
+// load while these are used), split operands one tile per barrier from a ring
+// of three, two tiles ahead.  A block handles
 // the row blocks b and nblk-1-b of its unit, so every block does the same amount
 // of causal work.  The blocks of one unit are numbered so they land on the same
 // XCD (blocks are dealt to the 8 XCDs round-robin) and walk the streamed tiles in
@@ -81,6 +83,17 @@ struct Pass {
   static constexpr int NA = SPLIT ? 2 : 1;  // bf16 arrays per operand (hi, lo)
   static constexpr int kWaveRows = 32 * NS;
   static constexpr int kBlockRows = 4 * kWaveRows;
+};
+
+// Tiles per barrier and the LDS ring they stream through.  Plain operands: two
+// tiles per barrier from a ring of four (one two-tile step computed while the
+// next one loads), halving the barriers a row block waits at.  Split operands,
+// whose tiles carry hi and lo rows (twice the bytes, 3 waves per SIMD): one tile
+// per barrier from a ring of three, loaded two tiles ahead.
+template <bool SPLIT>
+struct Ring {
+  static constexpr int kStep = SPLIT ? 1 : 2;
+  static constexpr int kBufs = SPLIT ? 3 : 4;
 };
 
 template <int D>
@@ -309,7 +322,8 @@ __global__ __launch_bounds__(kThreads, SPLIT ? 3 : 4) void rowstats_bf16(Prefill
   using T = Tile<D>;
   using P = Pass<SPLIT>;
   constexpr int NS = P::NS, NA = P::NA;
-  __shared__ __align__(256) unsigned char sK[kBufs][NA * T::kBytes];
+  constexpr int S = Ring<SPLIT>::kStep, R = Ring<SPLIT>::kBufs;
+  __shared__ __align__(256) unsigned char sK[R][NA * T::kBytes];
   const int npair = (nblk + 1) / 2;
   int unit, pb;
   if (!block_coords(npair, units, &unit, &pb)) return;
@@ -352,29 +366,40 @@ __global__ __launch_bounds__(kThreads, SPLIT ? 3 : 4) void rowstats_bf16(Prefill
       m[s] = -1e30f;
       l[s] = 0.f;
     }
-    for (int t = 0; t < ntile; ++t) {
-      if (t + 1 < ntile) wait_vm<NA * T::kLoads>();  // this tile landed; the next may be in flight
+    for (int t0 = 0; t0 < ntile; t0 += S) {
+      // this step's tiles landed (one tile per step: the next may be in flight)
+      if (S == 1 && t0 + 1 < ntile) wait_vm<NA * T::kLoads>();
       else wait_vm<0>();
       tile_barrier();
-      if (t + 2 < ntile) issue(t + 2, (t + 2) % kBufs);
-      const int k0 = t * kTile;
-      if (qw < L && k0 <= qw + P::kWaveRows - 1) {
-        uint32_t fb = lds_addr(sK[t % kBufs]) + xo;
-        asm volatile("" : "+v"(fb));  // keep the per-step offsets inside the loop
-        floatx16 acc[NS];
-        if constexpr (SPLIT) acc[0] = tile_mfma_split<D>(fb, fb + T::kBytes, bq[0], bql[0]);
-        else tile_mfma<D>(fb, bq, acc);
+      if constexpr (S == 1) {
+        if (t0 + 2 < ntile) issue(t0 + 2, (t0 + 2) % R);
+      } else {
 #pragma unroll
-        for (int s = 0; s < NS; ++s) {
-          if (k0 + kTile - 1 > qw + 32 * s) {  // diagonal tile: keys after the query leave the row
-            const int ln = lane_id_here();  // re-read here: keeping it live across the loop spills
-            const int rel = qw + 32 * s + (ln & 31) - k0 - 4 * (ln >> 5);
+        for (int u = 0; u < S; ++u)
+          if (t0 + S + u < ntile) issue(t0 + S + u, (t0 + S + u) % R);
+      }
 #pragma unroll
-            for (int i = 0; i < 16; ++i) acc[s][i] = (8 * (i >> 2) + (i & 3)) <= rel ? acc[s][i] : -INFINITY;
+      for (int u = 0; u < S; ++u) {
+        const int t = t0 + u;
+        const int k0 = t * kTile;
+        if (t < ntile && qw < L && k0 <= qw + P::kWaveRows - 1) {
+          uint32_t fb = lds_addr(sK[t % R]) + xo;
+          asm volatile("" : "+v"(fb));  // keep the per-step offsets inside the loop
+          floatx16 acc[NS];
+          if constexpr (SPLIT) acc[0] = tile_mfma_split<D>(fb, fb + T::kBytes, bq[0], bql[0]);
+          else tile_mfma<D>(fb, bq, acc);
+#pragma unroll
+          for (int s = 0; s < NS; ++s) {
+            if (k0 + kTile - 1 > qw + 32 * s) {  // diagonal tile: keys after the query leave the row
+              const int ln = lane_id_here();  // re-read here: keeping it live across the loop spills
+              const int rel = qw + 32 * s + (ln & 31) - k0 - 4 * (ln >> 5);
+#pragma unroll
+              for (int i = 0; i < 16; ++i) acc[s][i] = (8 * (i >> 2) + (i & 3)) <= rel ? acc[s][i] : -INFINITY;
+            }
+            floatx16 p;
+            bool moved;
+            row_update<false>(acc[s], a.c2, lane, m[s], l[s], p, moved);
           }
-          floatx16 p;
-          bool moved;
-          row_update<false>(acc[s], a.c2, lane, m[s], l[s], p, moved);
         }
       }
     }
@@ -400,7 +425,8 @@ __global__ __launch_bounds__(kThreads, SPLIT ? 3 : 4) void colsum_bf16(PrefillAr
   using P = Pass<SPLIT>;
   constexpr int NS = P::NS, NA = P::NA;
   constexpr int kBufBytes = NA * T::kBytes + 256;  // tile rows, normalisers, padding to 256 bytes
-  __shared__ __align__(256) unsigned char sQ[kBufs][kBufBytes];
+  constexpr int S = Ring<SPLIT>::kStep, R = Ring<SPLIT>::kBufs;
+  __shared__ __align__(256) unsigned char sQ[R][kBufBytes];
   const int npair = (nblk + 1) / 2;
   int unit, pb;
   if (!block_coords(npair, units, &unit, &pb)) return;
@@ -444,50 +470,61 @@ __global__ __launch_bounds__(kThreads, SPLIT ? 3 : 4) void colsum_bf16(PrefillAr
     float cs[NS];
 #pragma unroll
     for (int s = 0; s < NS; ++s) cs[s] = 0.f;
-    for (int t = tn; t >= t0; --t) {
-      const int it = tn - t;
-      if (t == t0) wait_vm<0>();
+    // tile t is the it-th of the walk (it = tn - t) and sits in buffer it % R
+    for (int i0 = 0; i0 <= tn - t0; i0 += S) {
+      // this step's tiles landed (one tile per step: the next may be in flight)
+      if (S > 1 || tn - i0 == t0) wait_vm<0>();
       else if (wave == 0) wait_vm<NA * T::kLoads + 1>();  // wave 0 also brings the normalisers
       else wait_vm<NA * T::kLoads>();
       tile_barrier();
-      if (t - 2 >= t0) issue(t - 2, (it + 2) % kBufs);
-      const int q0 = t * kTile;
-      if (kw < L && q0 + kTile - 1 >= kw) {
-        const uint32_t tile = lds_addr(sQ[it % kBufs]);
-        uint32_t fb = tile + xo;
-        asm volatile("" : "+v"(fb));
-        floatx16 acc[NS];
-        if constexpr (SPLIT) acc[0] = tile_mfma_split<D>(fb, fb + T::kBytes, bk[0], bkl[0]);
-        else tile_mfma<D>(fb, bk, acc);
-        if (q0 < kw + P::kWaveRows || q0 + kTile > L) {  // diagonal or ragged last tile
-          // rows above the key and rows past L leave the column: logit -> -inf
-          const int h4 = 4 * (lane >> 5);
+      if constexpr (S == 1) {
+        if (tn - i0 - 2 >= t0) issue(tn - i0 - 2, (i0 + 2) % R);
+      } else {
+#pragma unroll
+        for (int u = 0; u < S; ++u)
+          if (tn - (i0 + S + u) >= t0) issue(tn - (i0 + S + u), (i0 + S + u) % R);
+      }
+#pragma unroll
+      for (int u = 0; u < S; ++u) {
+        const int it = i0 + u, t = tn - it;
+        const int q0 = t * kTile;
+        if (t >= t0 && kw < L && q0 + kTile - 1 >= kw) {
+          const uint32_t tile = lds_addr(sQ[it % R]);
+          uint32_t fb = tile + xo;
+          asm volatile("" : "+v"(fb));
+          floatx16 acc[NS];
+          if constexpr (SPLIT) acc[0] = tile_mfma_split<D>(fb, fb + T::kBytes, bk[0], bkl[0]);
+          else tile_mfma<D>(fb, bk, acc);
+          if (q0 < kw + P::kWaveRows || q0 + kTile > L) {  // diagonal or ragged last tile
+            // rows above the key and rows past L leave the column: logit -> -inf
+            const int h4 = 4 * (lane >> 5);
+#pragma unroll
+            for (int s = 0; s < NS; ++s) {
+              const int lo = kw + 32 * s + fr - q0 - h4, hi = L - q0 - h4;
+#pragma unroll
+              for (int i = 0; i < 16; ++i) {
+                const int r = 8 * (i >> 2) + (i & 3);
+                acc[s][i] = (r >= lo && r < hi) ? acc[s][i] : -INFINITY;
+              }
+            }
+          }
+          // the 16 rows of this lane sit in 4 runs of 4 consecutive rows: one float4
+          // of normalisers per run
+          const uint32_t lrow = tile + NA * T::kBytes + 16 * (lane >> 5);
 #pragma unroll
           for (int s = 0; s < NS; ++s) {
-            const int lo = kw + 32 * s + fr - q0 - h4, hi = L - q0 - h4;
+            float part[4];
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-              const int r = 8 * (i >> 2) + (i & 3);
-              acc[s][i] = (r >= lo && r < hi) ? acc[s][i] : -INFINITY;
+            for (int g = 0; g < 4; ++g) {
+              const f32x4 f = lds_float4(lrow + 32 * g);
+#pragma unroll
+              for (int j = 0; j < 4; ++j) {
+                const float p = fast_exp2(fmaf(acc[s][4 * g + j], a.c2, -f[j]));
+                part[j] = g == 0 ? p : part[j] + p;
+              }
             }
+            cs[s] += (part[0] + part[1]) + (part[2] + part[3]);
           }
-        }
-        // the 16 rows of this lane sit in 4 runs of 4 consecutive rows: one float4
-        // of normalisers per run
-        const uint32_t lrow = tile + NA * T::kBytes + 16 * (lane >> 5);
-#pragma unroll
-        for (int s = 0; s < NS; ++s) {
-          float part[4];
-#pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            const f32x4 f = lds_float4(lrow + 32 * g);
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-              const float p = fast_exp2(fmaf(acc[s][4 * g + j], a.c2, -f[j]));
-              part[j] = g == 0 ? p : part[j] + p;
-            }
-          }
-          cs[s] += (part[0] + part[1]) + (part[2] + part[3]);
         }
       }
     }

@@ -1,8 +1,18 @@
-// Streaming-read probe: a measurement aid, not part of the method.  It reads a
-// buffer once with 16-byte non-temporal loads, 8 in flight per lane, each block
-// on contiguous 32 KiB runs, so timing it gives the read bandwidth this GPU
-// sustains for a plain stream - the practical ceiling for the decode kernel's
-// HBM fraction.
+// Measurement aids, not part of the method.
+//
+// Streaming-read probe: reads a buffer once with 16-byte non-temporal loads, 8
+// in flight per lane, each block on contiguous 32 KiB runs, so timing it gives
+// the read bandwidth this GPU sustains for a plain stream - the practical
+// ceiling for the decode kernel's HBM fraction.
+//
+// Matrix/vector mix probe: the instruction mix of a prefill scoring pass with
+// nothing else - per wave and iteration 16 MFMAs 32x32x16 bf16 (the work of one
+// 64 x 32 logit tile at d = 128) and, per lane, 32 times one fma, one exp2 and
+// one add (the terms and sums of those 2048 logits) - from registers only: no
+// memory traffic, no barriers, and the vector work independent of the matrix
+// results, so nothing but the two pipes and the clock bounds it.  Timing the
+// matrix part alone, the vector part alone and both together gives the rates
+// the passes could reach at best on this GPU.
 #include <hip/hip_runtime.h>
 
 #include "h2o.h"
@@ -40,6 +50,58 @@ __global__ __launch_bounds__(kProbeThreads) void read_probe(const uint4* p, size
   if (acc == 0x9e3779b9u) sink[0] = acc;
 }
 
+// Mix probe.  MODE 0: the MFMAs alone; 1: MFMAs and vector work; 2: vector work
+// alone.  Four accumulator chains keep the matrix pipe fed from one wave; the
+// vector values stay in (0, 1] (x -> exp2(-(x/2 + 1/2))).
+constexpr int kMixThreads = 256;
+constexpr int kMixBlocksPerCu = 4;  // 4 waves per SIMD, as the scoring passes run
+
+template <int MODE>
+__global__ __launch_bounds__(kMixThreads) void mix_probe(int iters, uint32_t* sink) {
+  const int lane = threadIdx.x % kWave;
+  bf16x8 fa, fb;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    fa[e] = static_cast<__bf16>(static_cast<float>((lane + e) % 7 - 3) * 0.125f);
+    fb[e] = static_cast<__bf16>(static_cast<float>((lane * 3 + e) % 5 - 2) * 0.25f);
+  }
+  floatx16 acc[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) acc[j] = floatx16{};
+  floatx16 x[2];
+#pragma unroll
+  for (int s = 0; s < 2; ++s)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) x[s][i] = 0.01f * static_cast<float>(lane % 9 + i + s);
+  float part[4] = {0.f, 0.f, 0.f, 0.f};
+  for (int it = 0; it < iters; ++it) {
+    if constexpr (MODE != 2) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa, fb, acc[j], 0, 0, 0);
+    }
+    if constexpr (MODE != 0) {
+#pragma unroll
+      for (int s = 0; s < 2; ++s)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          x[s][i] = fast_exp2(-fmaf(x[s][i], 0.5f, 0.5f));
+          part[i & 3] += x[s][i];
+        }
+    }
+    asm volatile("" : "+v"(fa), "+v"(fb));  // operands the compiler cannot treat as loop-invariant
+  }
+  float tot = (part[0] + part[1]) + (part[2] + part[3]);
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) tot += acc[j][i];
+  // every result feeds a value the kernel may store, so no work can be dropped;
+  // the store itself happens only on one chance in 2^32
+  if (__float_as_uint(tot) == 0x9e3779b9u) sink[0] = __float_as_uint(tot);
+}
+
 }  // namespace
 }  // namespace h2o
 
@@ -59,5 +121,19 @@ extern "C" h2o_status h2o_probe_read(const void* buf, size_t bytes, uint32_t* si
   const unsigned blocks = static_cast<unsigned>(want < need ? want : need);
   hipLaunchKernelGGL(h2o::read_probe, dim3(blocks), dim3(h2o::kProbeThreads), 0, static_cast<hipStream_t>(stream),
                      static_cast<const uint4*>(buf), n16, sink);
+  return hipGetLastError() == hipSuccess ? H2O_OK : H2O_ERR_HIP;
+}
+
+extern "C" h2o_status h2o_probe_mix(int32_t mode, int32_t iters, uint32_t* sink, void* stream) {
+  if (sink == nullptr || mode < 0 || mode > 2 || iters < 1) return H2O_ERR_INVALID_ARG;
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return H2O_ERR_HIP;
+  const dim3 grid(static_cast<unsigned>(cus * h2o::kMixBlocksPerCu)), block(h2o::kMixThreads);
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  if (mode == 0) hipLaunchKernelGGL(h2o::mix_probe<0>, grid, block, 0, s, iters, sink);
+  else if (mode == 1) hipLaunchKernelGGL(h2o::mix_probe<1>, grid, block, 0, s, iters, sink);
+  else hipLaunchKernelGGL(h2o::mix_probe<2>, grid, block, 0, s, iters, sink);
   return hipGetLastError() == hipSuccess ? H2O_OK : H2O_ERR_HIP;
 }

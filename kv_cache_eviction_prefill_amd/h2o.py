@@ -60,6 +60,7 @@ _SIGNATURES = {
     "h2o_prefill_scored": (_i32, [_vp, _vp, _vp, _i32, _i32, _vp, _vp]),
     "h2o_decode_step_scored": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _vp]),
     "h2o_probe_read": (_i32, [_vp, ctypes.c_size_t, _vp, _vp]),
+    "h2o_probe_mix": (_i32, [_i32, _i32, _vp, _vp]),
     "h2o_status_str": (ctypes.c_char_p, [_i32]),
     "h2o_last_error": (ctypes.c_char_p, []),
 }
@@ -132,6 +133,10 @@ def h2o_column_scores(cache, q, k, n, scores, stream):
 
 def h2o_probe_read(buf, nbytes, sink, stream):
     return load().h2o_probe_read(buf, nbytes, sink, stream)
+
+
+def h2o_probe_mix(mode, iters, sink, stream):
+    return load().h2o_probe_mix(mode, iters, sink, stream)
 
 
 def h2o_column_scores_noalloc(params, q, k, n, scores, stream):

@@ -135,3 +135,17 @@ def test_create_without_gpu_reports_hip_error(gpu_available):
     st = H.h2o_cache_create(ctypes.byref(p), -1, ctypes.byref(out))
     assert st in (H.H2O_ERR_HIP, H.H2O_ERR_OOM) and out.value is None
     assert H.h2o_last_error() != ""
+
+
+@pytest.mark.parametrize("mode,iters,sink", [(3, 10, 16), (-1, 10, 16), (0, 0, 16), (1, -5, 16), (2, 10, None)])
+def test_probe_mix_rejects_bad_arguments(mode, iters, sink):
+    """The compute-ceiling probe checks its arguments before touching the GPU
+    (`sink` is never dereferenced on the host: any non-NULL value passes)."""
+    assert H.h2o_probe_mix(mode, iters, sink, None) == H.H2O_ERR_INVALID_ARG
+
+
+def test_probe_read_rejects_bad_arguments():
+    assert H.h2o_probe_read(None, 16, 16, None) == H.H2O_ERR_INVALID_ARG
+    assert H.h2o_probe_read(16, 16, None, None) == H.H2O_ERR_INVALID_ARG
+    assert H.h2o_probe_read(17, 16, 16, None) == H.H2O_ERR_INVALID_ARG
+    assert H.h2o_probe_read(16, 15, 16, None) == H.H2O_ERR_INVALID_ARG
