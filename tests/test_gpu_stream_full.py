@@ -6,7 +6,7 @@ eviction log: the budget (no eviction while the cache fills, one per step
 after), the candidate bound (the recent window is never evicted), no position
 evicted twice, and the final cache holding exactly the positions never
 evicted.  Late in the stream the oracle takes over from the GPU's own state:
-at steps 1 M, 2 M, 3 M and 10,000 before the end the cache of four heads
+at steps 1 M, 2 M, 3 M and 10,000 before the end the cache of every head
 (positions, scores, K/V rows) is read, the oracle runs the next 10,000 steps from
 it, and its outputs (2e-3 absolute), evictions (exact, near-ties adopted) and
 the cache after the steps (positions and K/V rows exact, scores 1e-4 relative)
@@ -33,7 +33,7 @@ DEV = torch.device("cuda", 0)
 CHUNK = 1 << 18   # positions generated per call
 CALL = 1_000_000  # decode steps per h2o_decode_steps call
 REPLAY = 10_000   # steps the oracle runs from each snapshot
-HEADS = (3, 14, 21, 30)
+HEADS = tuple(range(32))  # every head of the stream
 
 
 def _window(w, snap, after, start, dec, out, ev):
