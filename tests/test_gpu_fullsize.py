@@ -93,10 +93,10 @@ def test_opt67b_32layer_b64_full_shape(layer):
 
 def test_opt67b_full_shape_with_rolling():
     # position rolling in the benchmark's launch configuration (2048 units,
-    # prompt 2048, k = 410: the two-wave rolling blocks), 200 decode steps, 8
+    # prompt 2048, k = 410: the two-wave rolling blocks), 200 decode steps, 64
     # sampled units
     w = get("opt6.7b-32L-b64")
-    _run_sampled(w, 3, _sample(w, 8, 3), T=200, rope=10000.0)
+    _run_sampled(w, 3, _sample(w, 64, 3), T=200, rope=10000.0)
 
 
 @pytest.mark.parametrize("budget", ["4pct", "10pct", "20pct"])
