@@ -234,22 +234,35 @@ def cpu_baseline(w, samples, procs, steps_run):
     return base, parity
 
 
-def ceilings(torch, dev, lib, sp):
+def ceilings(torch, dev, lib, sp, launch_bytes):
     """Measured HBM ceilings on this GPU, best of 5 timed with events: the
-    library's streaming-read probe over 4 GiB (reads only) and a 1 GiB
-    device-to-device copy (read + write)."""
+    library's streaming-read probe over 4 GiB (reads only), the same probe over
+    one decode launch's byte count (each run on a window of the 4 GiB buffer
+    that the run before did not touch, so nothing is served from the 256 MB
+    Infinity Cache: the ramp and tail of a launch of that size included) and a
+    1 GiB device-to-device copy (read + write)."""
     src = torch.empty(1 << 28, dtype=torch.float32, device=dev).fill_(1.0)
     dst = torch.empty_like(src)
     big = torch.ones(1 << 30, dtype=torch.float32, device=dev)
     sink = torch.zeros(4, dtype=torch.int32, device=dev)
 
-    def probe():
-        st = lib.h2o_probe_read(big.data_ptr(), big.numel() * 4, sink.data_ptr(), sp)
+    def probe(off=0, nbytes=big.numel() * 4):
+        st = lib.h2o_probe_read(big.data_ptr() + off, nbytes, sink.data_ptr(), sp)
         if st:
             raise RuntimeError(f"h2o_probe_read failed with status {st}")
 
+    # launch-sized windows: 256-byte multiples, cycled through the 4 GiB buffer
+    nb = min(big.numel() * 4, max(256, int(launch_bytes) // 256 * 256))
+    nwin = (big.numel() * 4) // nb
+    turn = [0]
+
+    def probe_window():
+        probe((turn[0] % nwin) * nb, nb)
+        turn[0] += 1
+
     out = {}
     for name, fn, nbytes in (("read", probe, big.numel() * 4),
+                             ("read_launch_size", probe_window, nb),
                              ("copy", lambda: dst.copy_(src), 2 * src.numel() * 4)):
         fn()
         best = None
@@ -264,7 +277,10 @@ def ceilings(torch, dev, lib, sp):
         out[f"{name}_GBps"] = nbytes / best / 1e9
     torch.cuda.synchronize()
     del src, dst, big, sink
+    out["launch_size_bytes"] = nb
     out["note"] = ("read: h2o_probe_read over 4 GiB (a plain stream of 16-byte non-temporal loads); "
+                   "read_launch_size: the same probe over one decode launch's algorithmic bytes, a fresh window "
+                   "of the 4 GiB buffer each run; "
                    "copy: torch's 1 GiB device copy (read + write bytes), which also calibrates the rocprofv3 "
                    "byte counters")
     return out
@@ -422,7 +438,10 @@ def main():
         if evs is not None:
             evs[2].record(stream)
 
-    ceil = ceilings(torch, dev, lib, sp)  # untimed: bandwidth references and the counters' calibration copy
+    # slots read by decode step t: the cached count before it, min(k, L + t)
+    dec_bytes_launch = B * H * sum(decode_bytes_per_unit(min(w.k, L + t), d, s, glob) for t in range(T)) / T
+    # untimed: bandwidth references and the counters' calibration copy
+    ceil = ceilings(torch, dev, lib, sp, dec_bytes_launch)
     cceil = compute_ceilings(torch, dev, lib, sp)  # untimed: the scoring passes' arithmetic alone
 
     for _ in range(a.warmup):
@@ -449,8 +468,6 @@ def main():
     K = a.steps
     tokens = B * T * K
     launches = NL * T * K
-    # slots read by decode step t: the cached count before it, min(k, L + t)
-    dec_bytes_launch = B * H * sum(decode_bytes_per_unit(min(w.k, L + t), d, s, glob) for t in range(T)) / T
     avg_dec_s = t_dec / launches
     achieved = dec_bytes_launch / avg_dec_s / 1e9
     kv_cache_bytes = B * H * w.k * (2 * d * s + 12)
@@ -490,7 +507,8 @@ def main():
                      "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
                      "bytes_per_launch": dec_bytes_launch, "avg_launch_us": 1e6 * avg_dec_s,
                      "launches": launches, "measured_ceilings": ceil,
-                     "frac_of_measured_read": achieved / ceil["read_GBps"]},
+                     "frac_of_measured_read": achieved / ceil["read_GBps"],
+                     "frac_of_measured_read_launch_size": achieved / ceil["read_launch_size_GBps"]},
         "decode": {"tokens_per_s": tokens / t_dec, "ms_per_token_step": 1e3 * t_dec / (T * K),
                    "GBps": achieved, "hbm_frac": achieved / HBM_PEAK_GBS,
                    # a cache that fits the 256 MB Infinity Cache is read from there, not HBM:
