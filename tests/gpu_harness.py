@@ -147,8 +147,12 @@ def check_payloads(payloads, procs=None):
         results = [_oracle_worker.check_unit(p) for p in payloads]
     else:
         ctx = mp.get_context("spawn")
-        with ctx.Pool(procs) as pool:
+        pool = ctx.Pool(procs)
+        try:
             results = pool.map(_oracle_worker.check_unit, payloads, chunksize=max(1, len(payloads) // (4 * procs)))
+        finally:  # let the workers exit on their own (terminate() would signal them)
+            pool.close()
+            pool.join()
     bad = [r for r in results if not r["ok"]]
     worst = {key: max((r.get(key, 0.0) for r in results), default=0.0)
              for key in ("out_err", "score_rel", "colsum_rel", "lse_err")}
