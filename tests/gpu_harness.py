@@ -149,7 +149,11 @@ def check_payloads(payloads, procs=None):
         ctx = mp.get_context("spawn")
         pool = ctx.Pool(procs)
         try:
-            results = pool.map(_oracle_worker.check_unit, payloads, chunksize=max(1, len(payloads) // (4 * procs)))
+            results, step = [], max(1, len(payloads) // 8)
+            for r in pool.imap(_oracle_worker.check_unit, payloads, chunksize=max(1, len(payloads) // (16 * procs))):
+                results.append(r)
+                if len(payloads) >= 256 and len(results) % step == 0:  # progress of a long check
+                    log(f"oracle: {len(results)} of {len(payloads)} units checked")
         finally:  # let the workers exit on their own (terminate() would signal them)
             pool.close()
             pool.join()

@@ -1,7 +1,8 @@
 """GPU ↔ oracle parity at the full workload shapes, in the launch configuration
-the benchmark times, on sampled units (needs an MI355X).
+the benchmark times, on every unit (the 100 % budget: on 2048 of its 7168
+units; the stream's deep replay: on four of its 32 heads) (needs an MI355X).
 
-Inputs come from the device-side generator; the oracle reads the sampled units'
+Inputs come from the device-side generator; the oracle reads the units'
 inputs back from those tensors (generator output, not GPU-path output) and runs
 each unit in full.  Properties that hold for every unit (budget, recent window,
 candidate bound, no re-entry) are checked on all units.
@@ -26,6 +27,10 @@ def _sample(w, n, seed):
     g = np.random.default_rng(seed)
     idx = g.choice(w.batch * w.heads, size=min(n, w.batch * w.heads), replace=False)
     return [(int(i) // w.heads, int(i) % w.heads) for i in sorted(idx)]
+
+
+def _every(w):
+    return [(b, h) for b in range(w.batch) for h in range(w.heads)]
 
 
 def _host_unit(q, k, v, b, h):
@@ -57,12 +62,12 @@ def _check_properties(w, g, L, T):
             assert set(range(max(0, L + T - w.recent_budget), L + T)) <= s
 
 
-def _run_sampled(w, layer, units, T=None, check_props=True, rope=0.0):
+def _run_units(w, layer, units, T=None, check_props=True, rope=0.0):
     L = w.prompt_len
     T = w.decode_steps if T is None else T
     q, k, v = synth.torch_qkv(w, layer, 0, L + T, DEV)
     log(f"case {w.name} layer {layer}: B={w.batch} H={w.heads} L={L} T={T} k={w.k} rope={rope}; "
-        f"{len(units)} sampled units")
+        f"{len(units)} units checked")
     g = run_gpu(q, k, v, L, w.heavy_budget, w.recent_budget, w.dtype, out_units=units, rope_base=rope)
     if check_props:
         _check_properties(w, g, L, T)
@@ -86,38 +91,41 @@ def _run_sampled(w, layer, units, T=None, check_props=True, rope=0.0):
 @pytest.mark.parametrize("layer", [0, 15, 31])
 def test_opt67b_32layer_b64_full_shape(layer):
     # the benchmark's launch configuration: 2048 units, prompt 2048, 1024 decode
-    # steps, k = 410; 512 sampled units (a quarter of the launch) on each of three layers
+    # steps, k = 410; every unit of the launch, on three layers of the stack
     w = get("opt6.7b-32L-b64")
-    _run_sampled(w, layer, _sample(w, 512, layer))
+    _, results = _run_units(w, layer, _every(w))
+    assert len(results) == w.batch * w.heads
 
 
 def test_opt67b_full_shape_with_rolling():
     # position rolling in the benchmark's launch configuration (2048 units,
-    # prompt 2048, k = 410: the two-wave rolling blocks), 200 decode steps, 64
-    # sampled units
+    # prompt 2048, k = 410: the two-wave rolling blocks), 200 decode steps, every
+    # unit
     w = get("opt6.7b-32L-b64")
-    _run_sampled(w, 3, _sample(w, 64, 3), T=200, rope=10000.0)
+    _run_units(w, 3, _every(w), T=200, rope=10000.0)
 
 
 @pytest.mark.parametrize("budget", ["4pct", "10pct", "20pct"])
 def test_opt30b_b128_full_shape(budget):
-    # 7,168 units, prompt 1024, 1024 decode steps, k = 42 / 104 / 206; 256 sampled units
+    # 7,168 units, prompt 1024, 1024 decode steps, k = 42 / 104 / 206; every unit
     w = get(f"opt30b-b128-{budget}")
-    _run_sampled(w, 0, _sample(w, 256, int(budget[:-3])))
+    _run_units(w, 0, _every(w))
 
 
 def test_opt30b_b128_100pct_is_full_attention():
-    # k = N: nothing is ever evicted and every output is full causal attention
+    # k = N: nothing is ever evicted and every output is full causal attention;
+    # 2048 of the 7168 units (a full-attention unit costs the oracle four times
+    # one at 20 %), the no-eviction property on every unit
     w = get("opt30b-b128-100pct")
-    g, _ = _run_sampled(w, 0, _sample(w, 128, 100))
+    g, _ = _run_units(w, 0, _sample(w, 2048, 100))
     assert (g["evicted"] == -1).all()
 
 
 def test_llama7b_stream_split_path():
     # one head per unit, 32 units: the slots of each unit are split over blocks;
-    # the first eviction happens at step k - L = 1536
+    # the first eviction happens at step k - L = 1536; every head, 6000 steps
     w = get("llama7b-stream-4m")
-    _run_sampled(w, 0, _sample(w, 4, 7), T=6000)
+    _run_units(w, 0, _every(w), T=6000)
 
 
 def test_llama7b_stream_deep_replay():
@@ -125,4 +133,4 @@ def test_llama7b_stream_deep_replay():
     # evicting) replayed in full by the oracle for four heads, so the compensated
     # scores and every eviction are checked far into the stream
     w = get("llama7b-stream-4m")
-    _run_sampled(w, 0, [(0, 5), (0, 12), (0, 19), (0, 26)], T=100000)
+    _run_units(w, 0, [(0, 5), (0, 12), (0, 19), (0, 26)], T=100000)
