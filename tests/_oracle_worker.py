@@ -150,3 +150,44 @@ def continue_unit(p: dict) -> dict:
         res["ok"] = False
         res["msg"] = "; ".join(msgs)
     return res
+
+
+# The prompt's own attention output: per-element bound rel * m_re + abs with
+# m_re = sum_j a_rj |v_je| (the derivation is in test_gpu_prefill_out.py);
+# with position rolling the relative part gains 4 max_j e_rj, e_rj = scale ROT
+# sum_e |q_re k_je|.
+PROMPT_OUT_REL = {"f32": 2e-5, "bf16": 2.0 ** -16 + 2e-5}
+PROMPT_OUT_ABS = {"f32": 1e-6, "bf16": 1e-6}
+PROMPT_OUT_ROT = {"f32": 2.0 ** -22, "bf16": 3 * 2.0 ** -18}
+
+
+def check_prompt_output(p):
+    """Compare one unit's [L, d] prompt output ``p["o"]`` with the oracle: every
+    element within OUT_ATOL and within the derived bound.  ``p``: dtype, Q, K, V
+    (float arrays [L, d]), o, tag, rope_base (0: none).  Returns the worst
+    err/bound; raises AssertionError on a miss."""
+    import math
+
+    from oracle import prefill_output, prefill_scores
+
+    Q, K, V = (np.asarray(p[x], np.float64) for x in ("Q", "K", "V"))
+    o, tag, dt = p["o"], p["tag"], p["dtype"]
+    rope = Rope(base=p["rope_base"]) if p.get("rope_base") else None
+    if rope is not None:
+        Q, K = rope.prompt(Q), rope.prompt(K)
+    scale = 1.0 / math.sqrt(Q.shape[1])
+    ref = prefill_output(Q, K, V, scale)
+    mag = prefill_scores(Q, K, scale).weights @ np.abs(V)
+    rel = PROMPT_OUT_REL[dt]
+    if rope is not None:
+        e = scale * PROMPT_OUT_ROT[dt] * (np.abs(Q) @ np.abs(K).T)
+        rel = rel + 4 * np.max(np.tril(e), axis=1, keepdims=True)
+    bound = rel * mag + PROMPT_OUT_ABS[dt]
+    assert np.isfinite(o).all(), f"{tag}: output not fully written"
+    err = np.abs(np.asarray(o, np.float64) - ref)
+    assert float(err.max()) <= OUT_ATOL, f"{tag}: max abs error {float(err.max()):.3g} above {OUT_ATOL}"
+    worst = float((err / bound).max())
+    bad = np.argwhere(err > bound)
+    assert bad.size == 0, (f"{tag}: {len(bad)} elements outside the bound, first (row, col) "
+                           f"{bad[0].tolist()}: got {o[tuple(bad[0])]}, oracle {ref[tuple(bad[0])]}")
+    return worst

@@ -17,8 +17,6 @@ by at most e_rj = scale ROT sum_e |q_re k_je|, each weight by at most twice the
 row's largest e_rj relative, and the bound gains 4 max_j e_rj m_re.
 A wrong weight, key or value row gives errors of the order of m_re itself.
 """
-import math
-
 import numpy as np
 import pytest
 import torch
@@ -30,15 +28,15 @@ pytestmark = pytest.mark.gpu
 if not torch.cuda.is_available():
     pytest.skip("no GPU", allow_module_level=True)
 
-from gpu_harness import log  # noqa: E402
+from gpu_harness import log, parallel_map  # noqa: E402
 from kv_cache_eviction_prefill_amd import H2OCache  # noqa: E402
-from oracle import Rope, prefill_output, prefill_scores  # noqa: E402
+from oracle import Rope  # noqa: E402
+
+from _oracle_worker import OUT_ATOL, check_prompt_output  # noqa: E402
+from _oracle_worker import PROMPT_OUT_ABS as ABS  # noqa: E402
+from _oracle_worker import PROMPT_OUT_REL as REL  # noqa: E402
 
 DEV = torch.device("cuda", 0)
-OUT_ATOL = 2e-3
-REL = {"f32": 2e-5, "bf16": 2.0 ** -16 + 2e-5}
-ABS = {"f32": 1e-6, "bf16": 1e-6}
-ROT = {"f32": 2.0 ** -22, "bf16": 3 * 2.0 ** -18}
 
 
 def _gpu_prefill_out(w, q, k, v, rope_base=0.0):
@@ -55,25 +53,8 @@ def _check_unit(w, Q, K, V, o, tag, rope=None):
     """Compare one unit's [L, d] output with the oracle (2e-3 absolute and the
     derived bound); returns the worst err/bound.  ``rope``: the prompt is
     attended on its queries and keys rotated to their positions."""
-    Q, K, V = (np.asarray(x, np.float64) for x in (Q, K, V))
-    if rope is not None:
-        Q, K = rope.prompt(Q), rope.prompt(K)
-    scale = 1.0 / math.sqrt(Q.shape[1])
-    ref = prefill_output(Q, K, V, scale)
-    mag = prefill_scores(Q, K, scale).weights @ np.abs(V)
-    rel = REL[w.dtype]
-    if rope is not None:
-        e = scale * ROT[w.dtype] * (np.abs(Q) @ np.abs(K).T)
-        rel = rel + 4 * np.max(np.tril(e), axis=1, keepdims=True)
-    bound = rel * mag + ABS[w.dtype]
-    assert np.isfinite(o).all(), f"{tag}: output not fully written"
-    err = np.abs(o.astype(np.float64) - ref)
-    assert float(err.max()) <= OUT_ATOL, f"{tag}: max abs error {float(err.max()):.3g} above {OUT_ATOL}"
-    worst = float((err / bound).max())
-    bad = np.argwhere(err > bound)
-    assert bad.size == 0, (f"{tag}: {len(bad)} elements outside the bound, first (row, col) "
-                           f"{bad[0].tolist()}: got {o[tuple(bad[0])]}, oracle {ref[tuple(bad[0])]}")
-    return worst
+    return check_prompt_output({"dtype": w.dtype, "Q": Q, "K": K, "V": V, "o": o, "tag": tag,
+                                "rope_base": rope.base if rope is not None else 0.0})
 
 
 def _run(w, units=None, rope_base=0.0):
@@ -156,18 +137,21 @@ def test_identical_keys_running_mean():
     assert (np.abs(g["out"] - mean) <= REL["bf16"] * mag + ABS["bf16"]).all()
 
 
-def test_bench_shape_sampled_units():
-    # the benchmark's launch configuration (2048 units, prompt 2048, d = 128) on sampled units
+def test_bench_shape_every_unit():
+    # the benchmark's launch configuration (2048 units, prompt 2048, d = 128),
+    # every unit checked by the oracle (worker processes)
     w = get("opt6.7b-32L-b64")
     L = w.prompt_len
     q, k, v = synth.torch_qkv(w, 0, 0, L, DEV)
     log(f"prefill output at full shape: B={w.batch} H={w.heads} L={L}")
     g = _gpu_prefill_out(w, q, k, v)
-    rng = np.random.default_rng(21)
-    idx = rng.choice(w.batch * w.heads, size=64, replace=False)
-    worst = 0.0
-    for i in sorted(idx):
-        b, h = int(i) // w.heads, int(i) % w.heads
-        Q, K, V = (x[b, h].to(torch.float32).cpu().numpy() for x in (q, k, v))
-        worst = max(worst, _check_unit(w, Q, K, V, g["out"][b, h].cpu().numpy(), f"b{b}h{h}"))
-    log(f"full shape: worst err/bound {worst:.3f}")
+    out = g["out"].cpu().numpy()
+    payloads = [{"dtype": w.dtype, "Q": q[b, h].to(torch.float32).cpu().numpy(),
+                 "K": k[b, h].to(torch.float32).cpu().numpy(), "V": v[b, h].to(torch.float32).cpu().numpy(),
+                 "o": out[b, h], "tag": f"b{b}h{h}", "rope_base": 0.0}
+                for b in range(w.batch) for h in range(w.heads)]
+    del q, k, v, g
+    torch.cuda.empty_cache()
+    worst = parallel_map(check_prompt_output, payloads)
+    assert len(worst) == w.batch * w.heads
+    log(f"full shape: {len(worst)} units, worst err/bound {max(worst):.3f}")
