@@ -1,6 +1,7 @@
 """GPU ↔ oracle parity at the full workload shapes, in the launch configuration
 the benchmark times (needs an MI355X): every unit of the 32-layer stack's
-2048-unit launch and of the 32-head stream; 2048 of the 7168 units of each
+2048-unit launch (plain, with position rolling and with a sparse pattern) and
+of the 32-head stream; 2048 of the 7168 units of each
 OPT-30B budget (1024 at 100 %); four heads of the stream's deep replay.
 
 Inputs come from the device-side generator; the oracle reads the units'
@@ -63,13 +64,14 @@ def _check_properties(w, g, L, T):
             assert set(range(max(0, L + T - w.recent_budget), L + T)) <= s
 
 
-def _run_units(w, layer, units, T=None, check_props=True, rope=0.0):
+def _run_units(w, layer, units, T=None, check_props=True, rope=0.0, pattern=None):
     L = w.prompt_len
     T = w.decode_steps if T is None else T
     q, k, v = synth.torch_qkv(w, layer, 0, L + T, DEV)
     log(f"case {w.name} layer {layer}: B={w.batch} H={w.heads} L={L} T={T} k={w.k} rope={rope}; "
         f"{len(units)} units checked")
-    g = run_gpu(q, k, v, L, w.heavy_budget, w.recent_budget, w.dtype, out_units=units, rope_base=rope)
+    g = run_gpu(q, k, v, L, w.heavy_budget, w.recent_budget, w.dtype, out_units=units, rope_base=rope,
+                pattern=pattern)
     if check_props:
         _check_properties(w, g, L, T)
     payloads = []
@@ -79,6 +81,8 @@ def _run_units(w, layer, units, T=None, check_props=True, rope=0.0):
                           tag=f"{w.name}/L{layer}/b{b}h{h}")
         if rope:
             pl.update(rope=(rope,))
+        if pattern is not None:
+            pl.update(pattern=pattern)
         payloads.append(pl)
     del q, k, v
     torch.cuda.empty_cache()
@@ -104,6 +108,14 @@ def test_opt67b_full_shape_with_rolling():
     # unit
     w = get("opt6.7b-32L-b64")
     _run_units(w, 3, _every(w), T=200, rope=10000.0)
+
+
+def test_opt67b_full_shape_with_pattern():
+    # heavy hitters on top of a strided pattern (period 64, the bench's
+    # --pattern strided:64) in the benchmark's launch configuration, 256 decode
+    # steps, every unit
+    w = get("opt6.7b-32L-b64")
+    _run_units(w, 5, _every(w), T=256, pattern=("strided", 64, 1))
 
 
 @pytest.mark.parametrize("budget", ["4pct", "10pct", "20pct"])
