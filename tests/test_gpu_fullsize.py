@@ -1,6 +1,7 @@
 """GPU ↔ oracle parity at the full workload shapes, in the launch configuration
 the benchmark times (needs an MI355X): every unit of the 32-layer stack's
-2048-unit launch (plain, with position rolling and with a sparse pattern) and
+2048-unit launch (plain, with position rolling, with a sparse pattern and
+under the global-score comparator) and
 of the 32-head stream; 2048 of the 7168 units of each
 OPT-30B budget (1024 at 100 %); four heads of the stream's deep replay.
 
@@ -20,7 +21,7 @@ pytestmark = pytest.mark.gpu
 if not torch.cuda.is_available():
     pytest.skip("no GPU", allow_module_level=True)
 
-from gpu_harness import check_payloads, log, run_gpu, unit_payload  # noqa: E402
+from gpu_harness import check_payloads, log, run_gpu, run_gpu_scored, unit_payload  # noqa: E402
 
 DEV = torch.device("cuda", 0)
 
@@ -116,6 +117,29 @@ def test_opt67b_full_shape_with_pattern():
     # steps, every unit
     w = get("opt6.7b-32L-b64")
     _run_units(w, 5, _every(w), T=256, pattern=("strided", 64, 1))
+
+
+def test_opt67b_full_shape_global_comparator():
+    # the global-score comparator (bench --variant global) in the benchmark's
+    # launch configuration: column scores of the whole 2304-token sequence,
+    # scored prefill, 256 fixed-score decode steps; every unit
+    w = get("opt6.7b-32L-b64")
+    L, T = w.prompt_len, 256
+    q, k, v = synth.torch_qkv(w, 9, 0, L + T, DEV)
+    log(f"case {w.name} layer 9 global comparator: B={w.batch} H={w.heads} L={L} T={T} k={w.k}; every unit")
+    g = run_gpu_scored(q, k, v, L, w.heavy_budget, w.recent_budget, w.dtype)
+    _check_properties(w, g, L, T)
+    payloads = []
+    for b, h in _every(w):
+        Q, K, V = _host_unit(q, k, v, b, h)
+        pl = unit_payload(g, b, h, Q, K, V, L, w.heavy_budget, w.recent_budget, tag=f"{w.name}/global/b{b}h{h}")
+        pl.update(mode="global", gscores=g["gscores"][b, h].astype(np.float64))
+        payloads.append(pl)
+    del q, k, v, g
+    torch.cuda.empty_cache()
+    results, bad = check_payloads(payloads)
+    assert not bad, bad[:3]
+    assert len(results) == w.batch * w.heads
 
 
 @pytest.mark.parametrize("budget", ["4pct", "10pct", "20pct"])
